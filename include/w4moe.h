@@ -1,0 +1,180 @@
+/*
+ * w4moe -- batched-concurrent int4 (W4A16, group-wise) MoE decode step on one
+ * MI355X (gfx950).  C ABI.
+ *
+ * The operation is one token's forward pass for B concurrent streams of a
+ * packed-int4 mixture-of-experts transformer ("Batched-concurrent 4-bit
+ * serving on Apple Silicon", section 1): every dense projection is applied to
+ * all B rows at once, so each packed-int4 weight is read once per step; the
+ * selected experts of all B streams run as one grouped operation against a
+ * device-resident expert bank; attention reads a fixed KV arena through a
+ * stable per-stream slot that is never wiped when the batch composition
+ * changes ("Per-stream KV-slot isolation ...", section 1: slot lifecycle
+ * seed-once at join, release on retire as a logical reset with the buffer
+ * reused; arena sized by max-stream count x context cap, over-cap requests
+ * rejected at admission, section 5).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers ("_dev") are caller-owned HIP device memory; the library
+ *    never allocates or frees device memory.  Host pointers ("_host") are read
+ *    during the call only.
+ *  - fp16 data are IEEE binary16 bit patterns (uint16_t), row-major.
+ *  - int4 weights arrive in the canonical layout: packed [N][K/2] bytes, byte
+ *    j of a row holds element 2j in bits 0-3 and element 2j+1 in bits 4-7,
+ *    each a 4-bit two's-complement code in [-8, 7]; scales [N][K/group] fp16.
+ *    The dequantised weight is code * scale; y = x . W^T.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls that take a
+ *    stream enqueue work on it and return; the caller synchronises.
+ *  - Errors are negative status codes (W4_E_*), never traps.  Every argument
+ *    is validated before anything is enqueued or any host state changes, so a
+ *    failed call has no effect.  w4_last_error() gives a message.
+ *  - One context is used by one host thread at a time; calls that enqueue on
+ *    one device must not overlap in time with other calls on the same context.
+ */
+#ifndef W4MOE_H
+#define W4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct w4_ctx w4_ctx;
+
+/* Model geometry.  Requirements: hidden, n_q_heads*head_dim and moe_inter are
+ * multiples of 128 and at most 4096; head_dim is 64 or 128; n_q_heads is a
+ * multiple of n_kv_heads with at most 16 q heads per kv head; top_k <= 16,
+ * top_k <= n_experts <= 256; group is 32, 64 or 128. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_experts, top_k, moe_inter, vocab, group;
+  float rms_eps, rope_theta;
+} w4_model_desc;
+
+enum {
+  W4_OK = 0,
+  W4_E_INVALID = -1,     /* bad argument or geometry */
+  W4_E_NO_SLOT = -2,     /* every slot is live */
+  W4_E_CONTEXT_CAP = -3, /* prompt_len + max_new_tokens > cap, or a stream is at the cap */
+  W4_E_BAD_SLOT = -4,    /* slot not live, duplicated in one call, or seeded twice */
+  W4_E_NOT_READY = -5,   /* slot has a prompt that was not seeded yet */
+  W4_E_HIP = -6,         /* a HIP runtime call failed (see w4_last_error) */
+  W4_E_UNSUPPORTED = -7  /* device is not gfx950, or a size beyond the limits above */
+};
+
+/* Weight tensor ids for w4_bank_load. */
+enum {
+  W4_T_QKV = 0,      /* [(n_q + 2 n_kv) * head_dim][hidden]: q heads, then k heads, then v heads */
+  W4_T_O = 1,        /* [hidden][n_q * head_dim] */
+  W4_T_ROUTER = 2,   /* [n_experts][hidden] */
+  W4_T_GATE = 3,     /* per expert [moe_inter][hidden] */
+  W4_T_UP = 4,       /* per expert [moe_inter][hidden] */
+  W4_T_DOWN = 5,     /* per expert [hidden][moe_inter] */
+  W4_T_EMBED = 6,    /* [vocab][hidden] (layer ignored) */
+  W4_T_LM_HEAD = 7,  /* [vocab][hidden] (layer ignored) */
+  W4_T_ATTN_NORM = 8,  /* fp16 [hidden] RMSNorm gain, scales_dev unused */
+  W4_T_MOE_NORM = 9,   /* fp16 [hidden] */
+  W4_T_FINAL_NORM = 10 /* fp16 [hidden] (layer ignored) */
+};
+
+/* Bytes the caller must provide.  Arena: the KV store, sized by max_streams x
+ * ctx_cap x geometry (a standing cost, reported at creation).  Bank: every
+ * weight in the library's own tiled layout.  Workspace: per-step activations. */
+size_t w4_arena_bytes(const w4_model_desc* desc, int32_t max_streams, int32_t ctx_cap);
+size_t w4_bank_bytes(const w4_model_desc* desc);
+size_t w4_workspace_bytes(const w4_model_desc* desc, int32_t max_streams, int32_t ctx_cap);
+
+/* Create a context over caller memory (sizes from the queries above; 256-byte
+ * aligned).  max_streams in [1, 32]; ctx_cap a positive multiple of 64.
+ * No device work is done here. */
+int w4_create(const w4_model_desc* desc, int32_t max_streams, int32_t ctx_cap, void* arena_dev,
+              void* bank_dev, void* workspace_dev, w4_ctx** out);
+void w4_destroy(w4_ctx* ctx);
+
+/* Copy one canonical tensor into the bank (repacked on the device).  expert:
+ * index for W4_T_GATE/UP/DOWN, or -1 to load all experts at once from
+ * [n_experts][N][K/2] / [n_experts][N][K/group]; ignored otherwise.  The
+ * source buffers must stay valid until the stream reaches this work. */
+int w4_bank_load(w4_ctx* ctx, int32_t layer, int32_t tensor, int32_t expert, const void* packed_dev,
+                 const void* scales_dev, void* stream);
+
+/* Slot lifecycle.  alloc: admission; takes the lowest free slot; rejects with
+ * W4_E_CONTEXT_CAP when prompt_len + max_new_tokens > ctx_cap and with
+ * W4_E_NO_SLOT when none is free.  The slot's position starts at 0.
+ * seed: once per join, writes the prompt's K/V (canonical
+ * [n_layers][prompt_len][n_kv][head_dim] fp16, keys already rotary-embedded)
+ * into the slot and sets its position to prompt_len.  A slot allocated with
+ * prompt_len > 0 cannot decode before it is seeded.
+ * release: logical reset; nothing is wiped, the slot's memory is reused by the
+ * next alloc.  Other slots are never touched by any of these calls. */
+int w4_slot_alloc(w4_ctx* ctx, int32_t prompt_len, int32_t max_new_tokens, int32_t* slot_out);
+int w4_slot_seed(w4_ctx* ctx, int32_t slot, const void* k_dev, const void* v_dev, void* stream);
+int w4_slot_release(w4_ctx* ctx, int32_t slot);
+/* Current position (tokens cached) of a live slot. */
+int w4_slot_position(const w4_ctx* ctx, int32_t slot, int32_t* pos_out);
+/* Advance the positions of n distinct live slots by one (used with the
+ * per-layer entry points, which do not move positions). */
+int w4_slots_advance(w4_ctx* ctx, int32_t n, const int32_t* slots_host);
+
+/* One decode step for B streams: row b is the stream in slots_host[b] at its
+ * current position p_b.  tokens_dev int32 [B] input ids.  Writes the new K/V
+ * at p_b of each slot, returns fp16 logits [B][vocab] (logits_dev may be
+ * NULL) and the greedy next ids int32 [B] (ties to the lower id).
+ * route_ids_dev: optional int32 [n_layers][B][top_k] expert ids per rank.
+ * On success every listed slot's position advances by one.  A row's result
+ * is bit-identical whatever the other rows, their order and the slot ids. */
+int w4_decode_step(w4_ctx* ctx, int32_t B, const int32_t* slots_host, const int32_t* tokens_dev,
+                   void* logits_dev, int32_t* next_dev, int32_t* route_ids_dev, void* stream);
+
+/* ---- per-stage entry points (same kernels as w4_decode_step) ---- */
+
+/* Dense W4A16 product with a bank tensor: y = x . dequant(W)^T, fp32
+ * accumulation.  x fp16 [B][K]; y fp16 [B][N], except W4_T_ROUTER which
+ * writes fp32 [B][n_experts].  expert selects one expert of GATE/UP/DOWN.
+ * B in [1, max_streams]. */
+int w4_gemm(w4_ctx* ctx, int32_t layer, int32_t tensor, int32_t expert, int32_t B, const void* x_dev,
+            void* y_dev, void* stream);
+
+/* Top-k softmax routing and (stream, expert) bucketing for B streams.
+ * logits fp32 [B][n_experts] -> ids int32 [B][top_k] (ranked by logit,
+ * ties to the lower id), w fp32 [B][top_k] (softmax over the selected),
+ * counts int32 [n_experts], offsets int32 [n_experts + 1], and the pairs
+ * ordered by (expert, stream): pair_stream, pair_rank int32 [B * top_k].
+ * Any output pointer except ids and w may be NULL. */
+int w4_route(w4_ctx* ctx, int32_t B, const float* logits_dev, int32_t* ids_dev, float* w_dev,
+             int32_t* counts_dev, int32_t* offsets_dev, int32_t* pair_stream_dev,
+             int32_t* pair_rank_dev, void* stream);
+
+/* MoE block of one layer for B rows (no residual): y = sum_r w_r * expert_r(x)
+ * with SwiGLU experts.  x fp16 [B][hidden] is the block's (normalised) input.
+ * router_logits_dev fp32 [B][n_experts], or NULL to compute them from x with
+ * the layer's router.  route_ids_dev optional int32 [B][top_k]. */
+int w4_moe(w4_ctx* ctx, int32_t layer, int32_t B, const void* x_dev, const float* router_logits_dev,
+           void* y_dev, int32_t* route_ids_dev, void* stream);
+
+/* Slot-indexed GQA decode attention of one layer: q fp16 [B][n_q][head_dim]
+ * (already rotary-embedded), k_new / v_new fp16 [B][n_kv][head_dim] are
+ * written at each slot's current position p_b, then attention over 0..p_b
+ * -> o fp16 [B][n_q][head_dim].  Positions do not move. */
+int w4_attn_decode(w4_ctx* ctx, int32_t layer, int32_t B, const int32_t* slots_host, const void* q_dev,
+                   const void* k_new_dev, const void* v_new_dev, void* o_dev, void* stream);
+
+/* One decoder layer for B streams at their current positions: h fp16
+ * [B][hidden] residual stream, updated in place.  Positions do not move.
+ * route_ids_dev optional int32 [B][top_k]. */
+int w4_layer_step(w4_ctx* ctx, int32_t layer, int32_t B, const int32_t* slots_host, void* h_dev,
+                  int32_t* route_ids_dev, void* stream);
+
+/* ---- diagnostics ---- */
+const char* w4_status_string(int32_t status);
+const char* w4_last_error(const w4_ctx* ctx);
+/* Kernel launches and host-device synchronisations issued by the last
+ * w4_decode_step (the library itself never synchronises inside a step). */
+int w4_last_step_counts(const w4_ctx* ctx, int32_t* launches, int32_t* syncs);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4MOE_H */

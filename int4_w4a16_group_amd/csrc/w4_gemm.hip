@@ -1,0 +1,430 @@
+// W4A16 products on gfx950 MFMA: bank repack, the dense M-row GEMM (one
+// weight read for all B rows), and the grouped expert GEMMs (gate/up with a
+// SwiGLU epilogue, down) over the (expert, stream) buckets.
+//
+// Operation: y[b][n] = sum_k x[b][k] * q[n][k] * s[n][k/g] with fp32
+// accumulation (dense projections applied to all B rows at once and the
+// selected experts run as one grouped operation: "Batched-concurrent 4-bit
+// serving on Apple Silicon", section 1).
+//
+// Arithmetic of one output, identical for every batch size B, every row
+// position and every tile schedule:
+//   * K is cut into slices of KS = 256 columns (128 when K % 256 != 0);
+//     wave w of a work-group owns slice w.  KS depends on K only.
+//   * within a slice, for each group of g columns: part = MFMA chain
+//     (v_mfma_f32_16x16x32_f16, x rows as the A operand, int4 codes converted
+//     exactly to fp16 as the B operand) started from zero; then
+//     acc = fma(scale, part, acc).
+//   * the work-group sums the slices' acc in slice order through LDS.
+// MFMA computes each output element from its own A row and B column only, so
+// a row's bits do not depend on which other rows share its 16-row tile.
+#include "w4_device.h"
+#include "w4_internal.h"
+
+namespace w4 {
+
+// ------------------------------------------------------------------ repack
+// One thread per 16-byte lane chunk of the destination.
+__global__ void k_repack(const uint8_t* __restrict__ src, int N, int K, int Np, int count,
+                         uint4* __restrict__ dst) {
+  const size_t per = (size_t)Np / 16 * (K / 128) * 64;
+  const size_t total = per * count;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < total;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const size_t e = idx / per;
+    size_t r = idx - e * per;
+    const int lane = (int)(r & 63);
+    r >>= 6;
+    const int kc = (int)(r % (K / 128));
+    const int t = (int)(r / (K / 128));
+    const int n = t * 16 + (lane & 15);
+    const int q = lane >> 4;
+    uint32_t out[4];
+    for (int s = 0; s < 4; ++s) {
+      uint32_t d = 0x88888888u;  // code 0 in offset binary
+      if (n < N) {
+        const uint8_t* row = src + (e * (size_t)N + n) * (size_t)(K / 2) + kc * 64 + 16 * s + 4 * q;
+        uint32_t c = (uint32_t)row[0] | ((uint32_t)row[1] << 8) | ((uint32_t)row[2] << 16) |
+                     ((uint32_t)row[3] << 24);
+        c ^= 0x88888888u;  // two's complement -> offset binary, per nibble
+        d = 0;
+        for (int j = 0; j < 4; ++j) {
+          d |= ((c >> (8 * j)) & 0xFu) << (4 * j);            // element 2j  -> nibble j
+          d |= ((c >> (8 * j + 4)) & 0xFu) << (4 * (j + 4));  // element 2j+1 -> nibble j+4
+        }
+      }
+      out[s] = d;
+    }
+    dst[idx] = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+}
+
+__global__ void k_copy_scales(const uint16_t* __restrict__ src, int N, int Np, int G, int count,
+                              uint16_t* __restrict__ dst) {
+  const size_t total = (size_t)count * Np * G;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t e = i / ((size_t)Np * G);
+    const size_t r = i - e * (size_t)Np * G;
+    const int n = (int)(r / G), j = (int)(r % G);
+    dst[i] = n < N ? src[(e * N + n) * (size_t)G + j] : (uint16_t)0;
+  }
+}
+
+hipError_t launch_repack(const uint8_t* src_packed, const uint16_t* src_scales, int count, int N, int K, int g,
+                         uint4* dst_tiles, uint16_t* dst_scales, hipStream_t st) {
+  const int Np = (N + 15) / 16 * 16;
+  const size_t total = (size_t)Np / 16 * (K / 128) * 64 * count;
+  const int blocks = (int)std::min<size_t>((total + 255) / 256, 65536);
+  hipLaunchKernelGGL(k_repack, dim3(blocks), dim3(256), 0, st, src_packed, N, K, Np, count, dst_tiles);
+  const size_t ts = (size_t)count * Np * (K / g);
+  const int b2 = (int)std::min<size_t>((ts + 255) / 256, 65536);
+  hipLaunchKernelGGL(k_copy_scales, dim3(b2), dim3(256), 0, st, src_scales, N, Np, K / g, count, dst_scales);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ core
+// x slice of one wave in registers: xa[mt][ks] is the A operand of k-step ks
+// for rows 16mt + lane%16.
+template <int MT, int NKS>
+struct XRegs {
+  h8 a[MT][NKS];
+};
+
+// Multiply-accumulate one 16-column tile over the wave's slice.
+// wv: the slice's repacked chunks; sv: its scales (one per group, column
+// n = 16t + lane%16); acc[mt] += over groups fma(scale, MFMA chain).
+template <int MT, int NCH, int G>
+__device__ __forceinline__ void tile_mac(const XRegs<MT, NCH * 4>& x, const uint4 (&wv)[NCH],
+                                         const float (&sv)[NCH * 128 / G], f4 (&acc)[MT], int mts) {
+  constexpr int SPG = G / 32;
+  f4 part[MT];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t wd[4] = {wv[c].x, wv[c].y, wv[c].z, wv[c].w};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int ks = c * 4 + s;
+      const h8 b = dq8(wd[s]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (ks % SPG == 0) part[mt] = f4{0.f, 0.f, 0.f, 0.f};
+        if (mt < mts) part[mt] = mfma16x16x32(x.a[mt][ks], b, part[mt]);
+      }
+      if ((ks + 1) % SPG == 0) {
+        const float sc = sv[ks / SPG];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt][0] = fmaf(sc, part[mt][0], acc[mt][0]);
+          acc[mt][1] = fmaf(sc, part[mt][1], acc[mt][1]);
+          acc[mt][2] = fmaf(sc, part[mt][2], acc[mt][2]);
+          acc[mt][3] = fmaf(sc, part[mt][3], acc[mt][3]);
+        }
+      }
+    }
+  }
+}
+
+template <int NCH>
+__device__ __forceinline__ void load_tile(const uint4* __restrict__ tiles, int K, int t, int w, int lane,
+                                          uint4 (&wv)[NCH]) {
+  const uint4* p = tiles + ((size_t)t * (K / 128) + (size_t)w * NCH) * 64 + lane;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) wv[c] = p[c * 64];
+}
+
+template <int NCH, int G>
+__device__ __forceinline__ void load_scales(const uint16_t* __restrict__ scales, int K, int t, int w, int lane,
+                                            float (&sv)[NCH * 128 / G]) {
+  const uint16_t* p = scales + (size_t)(t * 16 + (lane & 15)) * (K / G) + (size_t)w * (NCH * 128 / G);
+#pragma unroll
+  for (int i = 0; i < NCH * 128 / G; ++i) sv[i] = h2f(p[i]);
+}
+
+// A-operand rows: row i of the tile reads rowptr(i) (nullptr = zero row).
+template <int MT, int NCH, class RowPtr>
+__device__ __forceinline__ void load_x(XRegs<MT, NCH * 4>& x, RowPtr rowptr, int kbase, int lane) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint16_t* p = rowptr(mt * 16 + (lane & 15));
+#pragma unroll
+    for (int ks = 0; ks < NCH * 4; ++ks)
+      x.a[mt][ks] = p ? ld_h8(p + kbase + ks * 32 + 8 * (lane >> 4)) : h8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+}
+
+// Sum the waves' partial tiles (red: [NW][MT][64 lanes][4]) in wave order and
+// hand each output (row, col-in-tile, value) to epi.  Consecutive threads take
+// consecutive columns.
+template <int MT, class EpiF>
+__device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) {
+  const int nt = blockDim.x;
+  for (int o = threadIdx.x; o < MT * 256; o += nt) {
+    const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
+    const int ln = (i >> 2) * 16 + j, r = i & 3;
+    const int idx = mt * 256 + ln * 4 + r;
+    float v = red[idx];
+    for (int w = 1; w < NW; ++w) v = v + red[w * MT * 256 + idx];
+    epi(mt * 16 + i, j, v);
+  }
+}
+
+// ------------------------------------------------------------------ dense
+struct DenseArgs {
+  const uint4* tiles;
+  const uint16_t* scales;
+  int N, K, ntiles;
+  const uint16_t* x;
+  int ldx, B;
+  void* y;
+  int ldy;
+};
+
+template <int MT, int NCH, int G, int EPI, int LB>
+__global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
+  extern __shared__ float red[];
+  const int NW = blockDim.x >> 6;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kbase = w * NCH * 128;
+  XRegs<MT, NCH * 4> x;
+  load_x<MT, NCH>(x, [&](int row) -> const uint16_t* { return row < a.B ? a.x + (size_t)row * a.ldx : nullptr; },
+                  kbase, lane);
+  const int mts = (a.B + 15) >> 4;
+  int t = blockIdx.x;
+  if (t >= a.ntiles) return;
+  uint4 wv[NCH];
+  load_tile<NCH>(a.tiles, a.K, t, w, lane, wv);
+  for (; t < a.ntiles; t += gridDim.x) {
+    const int tn = t + gridDim.x;
+    uint4 wn[NCH];
+    if (tn < a.ntiles) load_tile<NCH>(a.tiles, a.K, tn, w, lane, wn);
+    float sv[NCH * 128 / G];
+    load_scales<NCH, G>(a.scales, a.K, t, w, lane, sv);
+    f4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
+    tile_mac<MT, NCH, G>(x, wv, sv, acc, mts);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(red)[(w * MT + mt) * 64 + lane] = acc[mt];
+    __syncthreads();
+    reduce_tile<MT>(red, NW, [&](int row, int j, float v) {
+      const int n = t * 16 + j;
+      if (row < a.B && n < a.N) {
+        if (EPI == EPI_F32) {
+          reinterpret_cast<float*>(a.y)[(size_t)row * a.ldy + n] = v;
+        } else if (EPI == EPI_F16) {
+          reinterpret_cast<uint16_t*>(a.y)[(size_t)row * a.ldy + n] = f2h(v);
+        } else {
+          uint16_t* h = reinterpret_cast<uint16_t*>(a.y) + (size_t)row * a.ldy + n;
+          *h = f2h(h2f(*h) + h2f(f2h(v)));
+        }
+      }
+    });
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) wv[c] = wn[c];
+  }
+}
+
+typedef void (*DenseKernel)(DenseArgs);
+
+// LB: launch bound; 512 threads (<= 8 waves) leaves up to 256 VGPRs per lane.
+template <int MT, int NCH, int G, int LB>
+static DenseKernel pick_epi(int epi) {
+  switch (epi) {
+    case EPI_F16: return k_gemm_dense<MT, NCH, G, EPI_F16, LB>;
+    case EPI_F32: return k_gemm_dense<MT, NCH, G, EPI_F32, LB>;
+    default: return k_gemm_dense<MT, NCH, G, EPI_RESID, LB>;
+  }
+}
+template <int MT, int NCH, int LB>
+static DenseKernel pick_g_lb(int g, int epi) {
+  switch (g) {
+    case 32: return pick_epi<MT, NCH, 32, LB>(epi);
+    case 64: return pick_epi<MT, NCH, 64, LB>(epi);
+    default: return pick_epi<MT, NCH, 128, LB>(epi);
+  }
+}
+template <int MT, int NCH>
+static DenseKernel pick_g(int g, int epi, int nw) {
+  return nw <= 8 ? pick_g_lb<MT, NCH, 512>(g, epi) : pick_g_lb<MT, NCH, 1024>(g, epi);
+}
+
+// Slice width: 256 columns, or 128 when K is not a multiple of 256.
+static inline int nch_for(int K) { return (K % 256 == 0) ? 2 : 1; }
+
+hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi,
+                       hipStream_t st) {
+  const int nch = nch_for(w.K);
+  const int NW = w.K / (nch * 128);
+  const int MT = B > 16 ? 2 : 1;
+  DenseKernel k;
+  if (MT == 1)
+    k = nch == 2 ? pick_g<1, 2>(w.g, epi, NW) : pick_g<1, 1>(w.g, epi, NW);
+  else
+    k = nch == 2 ? pick_g<2, 2>(w.g, epi, NW) : pick_g<2, 1>(w.g, epi, NW);
+  const int ntiles = w.ntiles();
+  // enough work-groups to fill 256 CUs at ~16 waves each, each looping over tiles
+  const int target = std::max(1, 4096 / NW);
+  const int grid = std::min(ntiles, target);
+  DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy};
+  hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), NW * MT * 1024, st, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ grouped experts
+struct MoeArgs {
+  const uint4* t0;        // gate (or down) tiles of expert 0; experts consecutive
+  const uint4* t1;        // up tiles (gate/up only)
+  const uint16_t* s0;
+  const uint16_t* s1;
+  int N, K, ntiles;       // per expert
+  size_t tile_stride;     // uint4 per expert
+  size_t scale_stride;    // halves per expert
+  int chunks, per_chunk;  // tile chunks per expert
+  const uint16_t* x;      // gate/up: rows by stream; down: rows by pair
+  int ldx;
+  const int32_t* offsets;
+  const int32_t* pair_stream;
+  const int32_t* used;
+  const int32_t* n_used;
+  uint16_t* out;          // [pairs][N]
+};
+
+template <int MT, int NCH, int G, bool GATEUP, int LB>
+__global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
+  extern __shared__ float red[];
+  const int NW = blockDim.x >> 6;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int u = blockIdx.x / a.chunks, ch = blockIdx.x - u * a.chunks;
+  if (u >= *a.n_used) return;
+  const int e = a.used[u];
+  const int off = a.offsets[e];
+  const int m = a.offsets[e + 1] - off;
+  const int mts = (m + 15) >> 4;
+  const int kbase = w * NCH * 128;
+  XRegs<MT, NCH * 4> x;
+  load_x<MT, NCH>(
+      x,
+      [&](int i) -> const uint16_t* {
+        if (i >= m) return nullptr;
+        const int row = GATEUP ? a.pair_stream[off + i] : off + i;
+        return a.x + (size_t)row * a.ldx;
+      },
+      kbase, lane);
+  const uint4* T0 = a.t0 + a.tile_stride * e;
+  const uint4* T1 = GATEUP ? a.t1 + a.tile_stride * e : nullptr;
+  const uint16_t* S0 = a.s0 + a.scale_stride * e;
+  const uint16_t* S1 = GATEUP ? a.s1 + a.scale_stride * e : nullptr;
+  const int t_begin = ch * a.per_chunk;
+  const int t_end = min(t_begin + a.per_chunk, a.ntiles);
+  for (int t = t_begin; t < t_end; ++t) {
+    uint4 w0[NCH], w1[NCH];
+    load_tile<NCH>(T0, a.K, t, w, lane, w0);
+    if (GATEUP) load_tile<NCH>(T1, a.K, t, w, lane, w1);
+    float s0[NCH * 128 / G], s1[NCH * 128 / G];
+    load_scales<NCH, G>(S0, a.K, t, w, lane, s0);
+    if (GATEUP) load_scales<NCH, G>(S1, a.K, t, w, lane, s1);
+    f4 acc0[MT], acc1[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc1[mt] = f4{0.f, 0.f, 0.f, 0.f};
+    tile_mac<MT, NCH, G>(x, w0, s0, acc0, mts);
+    if (GATEUP) tile_mac<MT, NCH, G>(x, w1, s1, acc1, mts);
+    f4* r4 = reinterpret_cast<f4*>(red);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      r4[(w * MT + mt) * 64 + lane] = acc0[mt];
+      if (GATEUP) r4[((NW + w) * MT + mt) * 64 + lane] = acc1[mt];
+    }
+    __syncthreads();
+    if (GATEUP) {
+      const float* red1 = red + NW * MT * 256;
+      const int nt = blockDim.x;
+      for (int o = threadIdx.x; o < MT * 256; o += nt) {
+        const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
+        const int idx = mt * 256 + ((i >> 2) * 16 + j) * 4 + (i & 3);
+        float vg = red[idx], vu = red1[idx];
+        for (int ww = 1; ww < NW; ++ww) {
+          vg = vg + red[ww * MT * 256 + idx];
+          vu = vu + red1[ww * MT * 256 + idx];
+        }
+        const int row = mt * 16 + i, n = t * 16 + j;
+        if (row < m && n < a.N) {
+          const float gt = h2f(f2h(vg)), up = h2f(f2h(vu));
+          const float silu = gt / (1.0f + expf(-gt));
+          a.out[(size_t)(off + row) * a.N + n] = f2h(silu * up);
+        }
+      }
+    } else {
+      reduce_tile<MT>(red, NW, [&](int row, int j, float v) {
+        const int n = t * 16 + j;
+        if (row < m && n < a.N) a.out[(size_t)(off + row) * a.N + n] = f2h(v);
+      });
+    }
+    __syncthreads();
+  }
+}
+
+typedef void (*MoeKernel)(MoeArgs);
+
+template <bool GU, int MT, int NCH, int LB>
+static MoeKernel moe_pick_g(int g) {
+  switch (g) {
+    case 32: return k_moe<MT, NCH, 32, GU, LB>;
+    case 64: return k_moe<MT, NCH, 64, GU, LB>;
+    default: return k_moe<MT, NCH, 128, GU, LB>;
+  }
+}
+template <bool GU, int LB>
+static MoeKernel moe_pick_lb(int MT, int nch, int g) {
+  if (MT == 1) return nch == 2 ? moe_pick_g<GU, 1, 2, LB>(g) : moe_pick_g<GU, 1, 1, LB>(g);
+  return nch == 2 ? moe_pick_g<GU, 2, 2, LB>(g) : moe_pick_g<GU, 2, 1, LB>(g);
+}
+template <bool GU>
+static MoeKernel moe_pick(int MT, int nch, int g, int nw) {
+  return nw <= 8 ? moe_pick_lb<GU, 512>(MT, nch, g) : moe_pick_lb<GU, 1024>(MT, nch, g);
+}
+
+static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, int E, int B, int max_used,
+                                    const uint16_t* x, int ldx, const RouteOut& r, uint16_t* out, int per_chunk,
+                                    hipStream_t st) {
+  const int nch = nch_for(m0.K);
+  const int NW = m0.K / (nch * 128);
+  const int MT = B > 16 ? 2 : 1;
+  MoeArgs a;
+  a.t0 = m0.tiles;
+  a.t1 = m1 ? m1->tiles : nullptr;
+  a.s0 = m0.scales;
+  a.s1 = m1 ? m1->scales : nullptr;
+  a.N = m0.N;
+  a.K = m0.K;
+  a.ntiles = m0.ntiles();
+  a.tile_stride = (size_t)m0.Np() / 16 * (m0.K / 128) * 64;
+  a.scale_stride = (size_t)m0.Np() * (m0.K / m0.g);
+  a.per_chunk = per_chunk;
+  a.chunks = (a.ntiles + per_chunk - 1) / per_chunk;
+  a.x = x;
+  a.ldx = ldx;
+  a.offsets = r.offsets;
+  a.pair_stream = r.pair_stream;
+  a.used = r.used;
+  a.n_used = r.n_used;
+  a.out = out;
+  MoeKernel k = gateup ? moe_pick<true>(MT, nch, m0.g, NW) : moe_pick<false>(MT, nch, m0.g, NW);
+  const int grid = max_used * a.chunks;
+  const size_t shm = (size_t)(gateup ? 2 : 1) * NW * MT * 1024;
+  hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), shm, st, a);
+  (void)E;
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, int E, int B, int max_used, const uint16_t* x,
+                             int ldx, const RouteOut& r, uint16_t* act, hipStream_t st) {
+  return launch_moe_common(true, gate0, &up0, E, B, max_used, x, ldx, r, act, 1, st);
+}
+
+hipError_t launch_moe_down(const Mat& down0, int E, int B, int max_used, const uint16_t* act, const RouteOut& r,
+                           uint16_t* y, hipStream_t st) {
+  return launch_moe_common(false, down0, nullptr, E, B, max_used, act, down0.K, r, y, 2, st);
+}
+
+}  // namespace w4

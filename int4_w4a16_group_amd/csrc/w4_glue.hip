@@ -1,0 +1,310 @@
+// Per-stream glue of the decode step on gfx950: embedding gather, RMSNorm,
+// top-k softmax routing with (stream, expert) bucketing, expert combine with
+// the residual, and greedy argmax.  Each stream's row is handled by its own
+// work-group with a fixed reduction order, so a row's result never depends on
+// the other rows ("Batched-concurrent 4-bit serving on Apple Silicon",
+// section 3: per-stream glue runs at per-stream offsets).
+#include "w4_device.h"
+#include "w4_internal.h"
+
+namespace w4 {
+
+static constexpr int kNormThreads = 256;
+
+// Block-wide sum with a fixed order (wave shuffles, then waves in order).
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = v + __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh[w] = v;
+  __syncthreads();
+  float t = sh[0];
+  for (int i = 1; i < nw; ++i) t = t + sh[i];
+  return t;
+}
+
+// out = x * (1/sqrt(mean(x^2) + eps)) * gamma, row held in registers (H <= 16*256).
+template <int PER>
+__device__ __forceinline__ void norm_row(const float (&v)[PER], int H, const uint16_t* __restrict__ gamma, float eps,
+                                         uint16_t* __restrict__ out, float* sh) {
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * kNormThreads;
+    if (i < H) ss = ss + v[j] * v[j];
+  }
+  ss = block_sum(ss, sh);
+  const float r = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + j * kNormThreads;
+    if (i < H) out[i] = f2h((v[j] * r) * h2f(gamma[i]));
+  }
+}
+
+constexpr int kPer = 16;  // hidden <= 4096
+
+__global__ void __launch_bounds__(kNormThreads) k_rmsnorm(int H, const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ gamma, float eps,
+                                                          uint16_t* __restrict__ out) {
+  __shared__ float sh[16];
+  const int b = blockIdx.x;
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + j * kNormThreads;
+    v[j] = i < H ? h2f(x[(size_t)b * H + i]) : 0.f;
+  }
+  norm_row<kPer>(v, H, gamma, eps, out + (size_t)b * H, sh);
+}
+
+hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma, float eps, uint16_t* out,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(kNormThreads), 0, st, H, x, gamma, eps, out);
+  return hipGetLastError();
+}
+
+// h[b] = fp16(code * scale) of the token's embedding row (token ids outside
+// [0, V) read row 0); xn[b] = RMSNorm(h[b]).
+__global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, const int32_t* __restrict__ tokens,
+                                                        const uint8_t* __restrict__ emb_p,
+                                                        const uint16_t* __restrict__ emb_s, uint16_t* __restrict__ h,
+                                                        const uint16_t* __restrict__ gamma, float eps,
+                                                        uint16_t* __restrict__ xn) {
+  __shared__ float sh[16];
+  const int b = blockIdx.x;
+  int t = tokens[b];
+  if (t < 0 || t >= V) t = 0;
+  const uint8_t* row = emb_p + (size_t)t * (H / 2);
+  const uint16_t* srow = emb_s + (size_t)t * (H / g);
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + j * kNormThreads;
+    v[j] = 0.f;
+    if (i < H) {
+      const unsigned byte = row[i >> 1];
+      const unsigned nib = (i & 1) ? (byte >> 4) : (byte & 15u);
+      const int q = (int)nib - ((nib & 8u) ? 16 : 0);
+      const uint16_t hv = f2h((float)q * h2f(srow[i / g]));
+      h[(size_t)b * H + i] = hv;
+      v[j] = h2f(hv);
+    }
+  }
+  norm_row<kPer>(v, H, gamma, eps, xn + (size_t)b * H, sh);
+}
+
+hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const uint8_t* emb_p,
+                        const uint16_t* emb_s, uint16_t* h, const uint16_t* gamma, float eps, uint16_t* xn,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(k_embed, dim3(B), dim3(kNormThreads), 0, st, H, V, g, tokens, emb_p, emb_s, h, gamma, eps, xn);
+  return hipGetLastError();
+}
+
+// moe = fp16(sum_r w_r * y_r) in rank order; resid: h = fp16(h + moe), else h = moe.
+// Then (gamma != null) xn = RMSNorm(h) * gamma.
+__global__ void __launch_bounds__(kNormThreads) k_combine(int H, int k, const float* __restrict__ w,
+                                                          const int32_t* __restrict__ inv,
+                                                          const uint16_t* __restrict__ y, uint16_t* __restrict__ h,
+                                                          int resid, const uint16_t* __restrict__ gamma, float eps,
+                                                          uint16_t* __restrict__ xn) {
+  __shared__ float sh[16];
+  __shared__ int s_inv[16];
+  __shared__ float s_w[16];
+  const int b = blockIdx.x;
+  if (threadIdx.x < k) {
+    s_inv[threadIdx.x] = inv[b * k + threadIdx.x];
+    s_w[threadIdx.x] = w[b * k + threadIdx.x];
+  }
+  __syncthreads();
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int i = threadIdx.x + j * kNormThreads;
+    v[j] = 0.f;
+    if (i < H) {
+      float acc = 0.f;
+      for (int r = 0; r < k; ++r) acc = acc + s_w[r] * h2f(y[(size_t)s_inv[r] * H + i]);
+      const uint16_t mo = f2h(acc);
+      const uint16_t hv = resid ? f2h(h2f(h[(size_t)b * H + i]) + h2f(mo)) : mo;
+      h[(size_t)b * H + i] = hv;
+      v[j] = h2f(hv);
+    }
+  }
+  if (gamma) norm_row<kPer>(v, H, gamma, eps, xn + (size_t)b * H, sh);
+}
+
+hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* inv, const uint16_t* y, uint16_t* h,
+                          bool resid, const uint16_t* gamma, float eps, uint16_t* xn, hipStream_t st) {
+  hipLaunchKernelGGL(k_combine, dim3(B), dim3(kNormThreads), 0, st, H, k, w, inv, y, h, resid ? 1 : 0, gamma, eps,
+                     xn);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ routing
+// One work-group.  Per stream (one wave each, streams strided over waves):
+// k rounds of "largest remaining logit, ties to the lower id", then
+// w_r = exp(l_r - l_0) / sum_r' exp(l_r' - l_0).  Then bucketing: counts,
+// exclusive offsets, used-expert list, and each pair's place in the
+// (expert, stream) order: offsets[e] + #(earlier pairs with expert e).
+constexpr int kRouteMaxPairs = 32 * 16;
+constexpr int kRouteMaxE = 256;
+
+__global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits, int B, int E, int k, RouteOut o) {
+  __shared__ int s_ids[kRouteMaxPairs];
+  __shared__ float s_lv[kRouteMaxPairs];
+  __shared__ int s_cnt[kRouteMaxE];
+  __shared__ int s_off[kRouteMaxE + 1];
+  const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int b = w; b < B; b += nw) {
+    float v[kRouteMaxE / 64];
+    bool taken[kRouteMaxE / 64];
+#pragma unroll
+    for (int j = 0; j < kRouteMaxE / 64; ++j) {
+      const int e = lane + 64 * j;
+      float x = e < E ? logits[(size_t)b * E + e] : -INFINITY;
+      if (x != x) x = -INFINITY;  // NaN ranks last
+      v[j] = x;
+      taken[j] = e >= E;
+    }
+    for (int r = 0; r < k; ++r) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < kRouteMaxE / 64; ++j) {
+        const int e = lane + 64 * j;
+        if (!taken[j] && (v[j] > bv || (v[j] == bv && e < bi))) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oi = __shfl_xor(bi, off, 64);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kRouteMaxE / 64; ++j)
+        if (lane + 64 * j == bi) taken[j] = true;
+      if (lane == 0) {
+        s_ids[b * k + r] = bi;
+        s_lv[b * k + r] = bv;
+      }
+    }
+    if (lane == 0) {
+      const float l0 = s_lv[b * k];
+      float ev[16];
+      float sum = 0.f;
+      for (int r = 0; r < k; ++r) {
+        ev[r] = expf(s_lv[b * k + r] - l0);
+        sum = sum + ev[r];
+      }
+      for (int r = 0; r < k; ++r) {
+        o.ids[b * k + r] = s_ids[b * k + r];
+        o.w[b * k + r] = ev[r] / sum;
+      }
+    }
+  }
+  __syncthreads();
+  const int P = B * k;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+    for (int j = 0; j < P; ++j) c += (s_ids[j] == e);
+    s_cnt[e] = c;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int off = 0, nu = 0;
+    for (int j = 0; j < e; ++j) {
+      off += s_cnt[j];
+      nu += s_cnt[j] > 0;
+    }
+    s_off[e] = off;
+    if (s_cnt[e] > 0) o.used[nu] = e;
+    if (o.counts) o.counts[e] = s_cnt[e];
+    if (o.offsets) o.offsets[e] = off;
+    if (e == E - 1) {
+      s_off[E] = off + s_cnt[e];
+      if (o.offsets) o.offsets[E] = off + s_cnt[e];
+      *o.n_used = nu + (s_cnt[e] > 0);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < P; i += blockDim.x) {
+    const int e = s_ids[i];
+    int rank = 0;
+    for (int j = 0; j < i; ++j) rank += (s_ids[j] == e);
+    const int pos = s_off[e] + rank;
+    if (o.pair_stream) o.pair_stream[pos] = i / k;
+    if (o.pair_rank) o.pair_rank[pos] = i % k;
+    o.inv[i] = pos;
+  }
+}
+
+hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st) {
+  hipLaunchKernelGGL(k_route, dim3(1), dim3(1024), 0, st, logits, B, E, k, o);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ argmax
+// Largest fp16 logit per row, ties to the lower id (NaN never wins).
+__global__ void __launch_bounds__(1024) k_argmax(int V, const uint16_t* __restrict__ logits, int32_t* __restrict__ next) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  const int b = blockIdx.x;
+  const uint16_t* row = logits + (size_t)b * V;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += blockDim.x) {
+    const float x = h2f(row[i]);
+    if (x > bv || (x == bv && i < bi)) {
+      bv = x;
+      bi = i;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off, 64);
+    const int oi = __shfl_xor(bi, off, 64);
+    if (ov > bv || (ov == bv && oi < bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[w] = bv;
+    si[w] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int j = 1; j < (int)(blockDim.x >> 6); ++j)
+      if (sv[j] > bv || (sv[j] == bv && si[j] < bi)) {
+        bv = sv[j];
+        bi = si[j];
+      }
+    next[b] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, hipStream_t st) {
+  hipLaunchKernelGGL(k_argmax, dim3(B), dim3(1024), 0, st, V, logits, next);
+  return hipGetLastError();
+}
+
+__global__ void k_fill_u32(uint32_t* p, uint32_t v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st) {
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_fill_u32, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace w4

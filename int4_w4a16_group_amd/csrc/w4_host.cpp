@@ -1,0 +1,671 @@
+// Host side of the w4moe C ABI: geometry checks, bank and workspace layout,
+// the slot table (stable per-stream KV slots with seed-once / logical-reset
+// lifecycle, admission against the context cap), and the enqueue order of
+// one decode step.  The library owns host state only; all device memory is
+// the caller's.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "w4_internal.h"
+
+using namespace w4;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kRing = 8;
+constexpr int kMaxStreams = 32;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Loc {  // one int4 tensor in the bank (expert 0 for expert tensors)
+  size_t tiles = 0, scales = 0;
+  int N = 0, K = 0;
+  size_t tile_bytes() const { return (size_t)((N + 15) / 16 * 16) * K / 2; }
+};
+
+struct LayerLoc {
+  size_t attn_norm = 0, moe_norm = 0;
+  Loc qkv, o, router, gate, up, down;
+};
+
+struct BankPlan {
+  std::vector<LayerLoc> layers;
+  size_t emb_p = 0, emb_s = 0, final_norm = 0;
+  Loc lm;
+  size_t total = 0;
+};
+
+struct WsPlan {
+  size_t h, xn, qkv, q, attn_o, part_o, part_ml, rlogits, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+      used, n_used, act, y, logits, next, rows, table, total;
+};
+
+bool geometry_ok(const w4_model_desc* d, std::string* why) {
+  auto bad = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (!d) return bad("null model description");
+  if (d->n_layers < 1) return bad("n_layers must be >= 1");
+  if (d->hidden < 128 || d->hidden % 128 || d->hidden > 4096) return bad("hidden must be a multiple of 128 in [128, 4096]");
+  if (d->head_dim != 64 && d->head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
+  if (d->n_q_heads / d->n_kv_heads > 16) return bad("at most 16 query heads per kv head");
+  const int qd = d->n_q_heads * d->head_dim;
+  if (qd % 128 || qd > 4096) return bad("n_q_heads*head_dim must be a multiple of 128, at most 4096");
+  if (d->moe_inter < 128 || d->moe_inter % 128 || d->moe_inter > 4096) return bad("moe_inter must be a multiple of 128 in [128, 4096]");
+  if (d->top_k < 1 || d->top_k > 16) return bad("top_k must be in [1, 16]");
+  if (d->n_experts < d->top_k || d->n_experts > 256) return bad("n_experts must be in [top_k, 256]");
+  if (d->group != 32 && d->group != 64 && d->group != 128) return bad("group must be 32, 64 or 128");
+  if (d->vocab < 1) return bad("vocab must be >= 1");
+  if (!(d->rms_eps >= 0.f) || !(d->rope_theta > 0.f)) return bad("rms_eps >= 0 and rope_theta > 0 required");
+  return true;
+}
+
+bool sizes_ok(int32_t max_streams, int32_t cap, std::string* why) {
+  if (max_streams < 1 || max_streams > kMaxStreams) {
+    if (why) *why = "max_streams must be in [1, 32]";
+    return false;
+  }
+  if (cap < 64 || cap % 64 || cap > 16384) {
+    if (why) *why = "ctx_cap must be a multiple of 64 in [64, 16384]";
+    return false;
+  }
+  return true;
+}
+
+BankPlan plan_bank(const w4_model_desc& d) {
+  BankPlan p;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  auto tensor = [&](int N, int K, int count) {
+    Loc l;
+    l.N = N;
+    l.K = K;
+    const size_t Np = (size_t)(N + 15) / 16 * 16;
+    l.tiles = take(Np * K / 2 * count);
+    l.scales = take(Np * (K / d.group) * 2 * count);
+    return l;
+  };
+  const int H = d.hidden, E = d.n_experts, I = d.moe_inter;
+  const int nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, qd = d.n_q_heads * d.head_dim;
+  p.layers.resize(d.n_layers);
+  for (auto& L : p.layers) {
+    L.attn_norm = take((size_t)H * 2);
+    L.moe_norm = take((size_t)H * 2);
+    L.qkv = tensor(nqkv, H, 1);
+    L.o = tensor(H, qd, 1);
+    L.router = tensor(E, H, 1);
+    L.gate = tensor(I, H, E);
+    L.up = tensor(I, H, E);
+    L.down = tensor(H, I, E);
+  }
+  p.emb_p = take((size_t)d.vocab * H / 2);
+  p.emb_s = take((size_t)d.vocab * (H / d.group) * 2);
+  p.final_norm = take((size_t)H * 2);
+  p.lm = tensor(d.vocab, H, 1);
+  p.total = cur;
+  return p;
+}
+
+WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
+  WsPlan w;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  const size_t H = d.hidden, E = d.n_experts, k = d.top_k, I = d.moe_inter, Hq = d.n_q_heads, D = d.head_dim;
+  const size_t nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * D, nch = cap / 64;
+  w.h = take(Bm * H * 2);
+  w.xn = take(Bm * H * 2);
+  w.qkv = take(Bm * nqkv * 2);
+  w.q = take(Bm * Hq * D * 2);
+  w.attn_o = take(Bm * Hq * D * 2);
+  w.part_o = take(Bm * Hq * nch * D * 4);
+  w.part_ml = take(Bm * Hq * nch * 2 * 4);
+  w.rlogits = take(Bm * E * 4);
+  w.ids = take(Bm * k * 4);
+  w.w = take(Bm * k * 4);
+  w.counts = take(E * 4);
+  w.offsets = take((E + 1) * 4);
+  w.pair_stream = take(Bm * k * 4);
+  w.pair_rank = take(Bm * k * 4);
+  w.inv = take(Bm * k * 4);
+  w.used = take(E * 4);
+  w.n_used = take(4);
+  w.act = take(Bm * k * I * 2);
+  w.y = take(Bm * k * H * 2);
+  w.logits = take((size_t)Bm * d.vocab * 2);
+  w.next = take(Bm * 4);
+  w.rows = take(2 * Bm * 4);  // slot ids then positions of the current rows
+  w.table = take((size_t)cap * (D / 2) * 8);
+  w.total = cur;
+  return w;
+}
+
+}  // namespace
+
+struct w4_ctx {
+  w4_model_desc d{};
+  int Bm = 0, cap = 0;
+  char* arena = nullptr;
+  char* bank = nullptr;
+  char* ws = nullptr;
+  BankPlan bp;
+  WsPlan wp{};
+  std::vector<int32_t> pos, prompt;
+  std::vector<uint8_t> live, need_seed;
+  bool dev_ready = false, table_ready = false;
+  int device = -1;
+  int32_t* pinned = nullptr;
+  hipEvent_t ev[kRing] = {};
+  bool ev_used[kRing] = {};
+  int ring = 0;
+  std::string err;
+  int launches = 0, syncs = 0;
+  int last_launches = 0, last_syncs = 0;
+
+  template <class T>
+  T* W(size_t off) { return reinterpret_cast<T*>(ws + off); }
+  template <class T>
+  T* Bk(size_t off) { return reinterpret_cast<T*>(bank + off); }
+  Mat mat(const Loc& l, int expert = 0) {
+    const size_t Np = (size_t)(l.N + 15) / 16 * 16;
+    Mat m;
+    m.tiles = reinterpret_cast<const uint4*>(bank + l.tiles + (size_t)expert * Np * l.K / 2);
+    m.scales = reinterpret_cast<const uint16_t*>(bank + l.scales + (size_t)expert * Np * (l.K / d.group) * 2);
+    m.N = l.N;
+    m.K = l.K;
+    m.g = d.group;
+    return m;
+  }
+  KV kv() {
+    KV k;
+    const size_t half = (size_t)d.n_layers * Bm * d.n_kv_heads * cap * d.head_dim;
+    k.K = reinterpret_cast<uint16_t*>(arena);
+    k.VT = reinterpret_cast<uint16_t*>(arena) + half;
+    k.S = Bm;
+    k.Hkv = d.n_kv_heads;
+    k.cap = cap;
+    k.D = d.head_dim;
+    return k;
+  }
+  RouteOut route_out(int32_t* ids_user = nullptr) {
+    RouteOut r;
+    r.ids = ids_user ? ids_user : W<int32_t>(wp.ids);
+    r.w = W<float>(wp.w);
+    r.counts = W<int32_t>(wp.counts);
+    r.offsets = W<int32_t>(wp.offsets);
+    r.pair_stream = W<int32_t>(wp.pair_stream);
+    r.pair_rank = W<int32_t>(wp.pair_rank);
+    r.inv = W<int32_t>(wp.inv);
+    r.used = W<int32_t>(wp.used);
+    r.n_used = W<int32_t>(wp.n_used);
+    return r;
+  }
+};
+
+namespace {
+
+int fail(w4_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  return code;
+}
+
+#define HIPCHK(ctx, expr)                                                                           \
+  do {                                                                                              \
+    hipError_t e_ = (expr);                                                                         \
+    if (e_ != hipSuccess) return fail(ctx, W4_E_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+int ensure_device(w4_ctx* c, hipStream_t st) {
+  if (!c->dev_ready) {
+    int dev = -1;
+    HIPCHK(c, hipGetDevice(&dev));
+    hipDeviceProp_t prop;
+    HIPCHK(c, hipGetDeviceProperties(&prop, dev));
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+      return fail(c, W4_E_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", library built for gfx950");
+    HIPCHK(c, hipHostMalloc((void**)&c->pinned, sizeof(int32_t) * 2 * c->Bm * kRing, hipHostMallocDefault));
+    for (int i = 0; i < kRing; ++i) HIPCHK(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
+    c->device = dev;
+    c->dev_ready = true;
+  }
+  if (!c->table_ready) {
+    HIPCHK(c, launch_rope_table(c->cap, c->d.head_dim, (double)c->d.rope_theta, c->W<float2>(c->wp.table), st));
+    c->launches++;
+    c->table_ready = true;
+  }
+  return W4_OK;
+}
+
+// All-or-nothing check of a row list: distinct, live, seeded, below the cap.
+int check_rows(w4_ctx* c, int32_t B, const int32_t* slots) {
+  if (B < 1 || B > c->Bm) return fail(c, W4_E_INVALID, "B must be in [1, max_streams]");
+  if (!slots) return fail(c, W4_E_INVALID, "null slot list");
+  std::vector<uint8_t> seen(c->Bm, 0);
+  for (int b = 0; b < B; ++b) {
+    const int s = slots[b];
+    if (s < 0 || s >= c->Bm || !c->live[s]) return fail(c, W4_E_BAD_SLOT, "slot " + std::to_string(s) + " is not live");
+    if (seen[s]) return fail(c, W4_E_BAD_SLOT, "slot " + std::to_string(s) + " listed twice");
+    seen[s] = 1;
+    if (c->need_seed[s]) return fail(c, W4_E_NOT_READY, "slot " + std::to_string(s) + " has an unseeded prompt");
+    if (c->pos[s] >= c->cap) return fail(c, W4_E_CONTEXT_CAP, "slot " + std::to_string(s) + " is at the context cap");
+  }
+  return W4_OK;
+}
+
+// Slot ids and positions of the rows -> workspace, through a pinned ring.
+int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int* max_pos) {
+  const int i = c->ring;
+  c->ring = (c->ring + 1) % kRing;
+  if (c->ev_used[i] && hipEventQuery(c->ev[i]) == hipErrorNotReady) {
+    HIPCHK(c, hipEventSynchronize(c->ev[i]));
+    c->syncs++;
+  }
+  int32_t* p = c->pinned + (size_t)i * 2 * c->Bm;
+  int mp = 0;
+  for (int b = 0; b < B; ++b) {
+    p[b] = slots[b];
+    p[c->Bm + b] = c->pos[slots[b]];
+    mp = std::max(mp, c->pos[slots[b]]);
+  }
+  HIPCHK(c, hipMemcpyAsync(c->W<int32_t>(c->wp.rows), p, sizeof(int32_t) * 2 * c->Bm, hipMemcpyHostToDevice, st));
+  HIPCHK(c, hipEventRecord(c->ev[i], st));
+  c->ev_used[i] = true;
+  if (max_pos) *max_pos = mp;
+  return W4_OK;
+}
+
+#define LCHK(ctx, n, expr)                                                                      \
+  do {                                                                                          \
+    hipError_t e_ = (expr);                                                                     \
+    (ctx)->launches += (n);                                                                     \
+    if (e_ != hipSuccess) return fail(ctx, W4_E_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+// One decoder layer on rows whose slot/pos vectors are uploaded.  Input: h
+// (residual) and xn = RMSNorm_attn(h).  Output: h updated; if next_gamma,
+// xn = RMSNorm(h) * next_gamma.
+int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xn, int32_t* ids_out,
+               const uint16_t* next_gamma, hipStream_t st) {
+  const w4_model_desc& d = c->d;
+  const LayerLoc& L = c->bp.layers[l];
+  const int H = d.hidden, nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, qd = d.n_q_heads * d.head_dim;
+  const int32_t* slot = c->W<int32_t>(c->wp.rows);
+  const int32_t* pos = slot + c->Bm;
+  KV kv = c->kv();
+  uint16_t* qkv = c->W<uint16_t>(c->wp.qkv);
+  LCHK(c, 1, launch_gemm(c->mat(L.qkv), B, xn, H, qkv, nqkv, EPI_F16, st));
+  LCHK(c, 1, launch_rope_append(B, l, d.n_q_heads, kv, slot, pos, qkv, nqkv, c->W<float2>(c->wp.table),
+                                c->W<uint16_t>(c->wp.q), st));
+  LCHK(c, 2, launch_attention(B, l, d.n_q_heads, kv, slot, pos, max_pos, c->W<uint16_t>(c->wp.q),
+                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), c->W<uint16_t>(c->wp.attn_o), st));
+  LCHK(c, 1, launch_gemm(c->mat(L.o), B, c->W<uint16_t>(c->wp.attn_o), qd, h, H, EPI_RESID, st));
+  LCHK(c, 1, launch_rmsnorm(B, H, h, c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn, st));
+  LCHK(c, 1, launch_gemm(c->mat(L.router), B, xn, H, c->W<float>(c->wp.rlogits), d.n_experts, EPI_F32, st));
+  RouteOut r = c->route_out(ids_out);
+  LCHK(c, 1, launch_route(c->W<float>(c->wp.rlogits), B, d.n_experts, d.top_k, r, st));
+  const int max_used = std::min(B * d.top_k, d.n_experts);
+  LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), d.n_experts, B, max_used, xn, H, r,
+                               c->W<uint16_t>(c->wp.act), st));
+  LCHK(c, 1, launch_moe_down(c->mat(L.down), d.n_experts, B, max_used, c->W<uint16_t>(c->wp.act), r,
+                             c->W<uint16_t>(c->wp.y), st));
+  LCHK(c, 1, launch_combine(B, H, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), h, true, next_gamma, d.rms_eps,
+                            xn, st));
+  return W4_OK;
+}
+
+}  // namespace
+
+// =========================================================================== C ABI
+extern "C" {
+
+size_t w4_arena_bytes(const w4_model_desc* d, int32_t max_streams, int32_t cap) {
+  if (!geometry_ok(d, nullptr) || !sizes_ok(max_streams, cap, nullptr)) return 0;
+  return 2 * (size_t)d->n_layers * max_streams * d->n_kv_heads * (size_t)cap * d->head_dim * 2;
+}
+
+size_t w4_bank_bytes(const w4_model_desc* d) {
+  if (!geometry_ok(d, nullptr)) return 0;
+  return plan_bank(*d).total;
+}
+
+size_t w4_workspace_bytes(const w4_model_desc* d, int32_t max_streams, int32_t cap) {
+  if (!geometry_ok(d, nullptr) || !sizes_ok(max_streams, cap, nullptr)) return 0;
+  return plan_ws(*d, max_streams, cap).total;
+}
+
+int w4_create(const w4_model_desc* d, int32_t max_streams, int32_t cap, void* arena_dev, void* bank_dev,
+              void* ws_dev, w4_ctx** out) {
+  std::string why;
+  if (!out) return W4_E_INVALID;
+  *out = nullptr;
+  if (!geometry_ok(d, &why) || !sizes_ok(max_streams, cap, &why)) {
+    std::fprintf(stderr, "w4_create: %s\n", why.c_str());
+    return W4_E_INVALID;
+  }
+  if (!arena_dev || !bank_dev || !ws_dev) return W4_E_INVALID;
+  if (((uintptr_t)arena_dev | (uintptr_t)bank_dev | (uintptr_t)ws_dev) % kAlign) return W4_E_INVALID;
+  w4_ctx* c = new w4_ctx;
+  c->d = *d;
+  c->Bm = max_streams;
+  c->cap = cap;
+  c->arena = static_cast<char*>(arena_dev);
+  c->bank = static_cast<char*>(bank_dev);
+  c->ws = static_cast<char*>(ws_dev);
+  c->bp = plan_bank(*d);
+  c->wp = plan_ws(*d, max_streams, cap);
+  c->pos.assign(max_streams, 0);
+  c->prompt.assign(max_streams, 0);
+  c->live.assign(max_streams, 0);
+  c->need_seed.assign(max_streams, 0);
+  *out = c;
+  return W4_OK;
+}
+
+void w4_destroy(w4_ctx* c) {
+  if (!c) return;
+  if (c->dev_ready) {
+    for (int i = 0; i < kRing; ++i)
+      if (c->ev[i]) (void)hipEventSynchronize(c->ev[i]), (void)hipEventDestroy(c->ev[i]);
+    if (c->pinned) (void)hipHostFree(c->pinned);
+  }
+  delete c;
+}
+
+int w4_bank_load(w4_ctx* c, int32_t layer, int32_t tensor, int32_t expert, const void* packed, const void* scales,
+                 void* stream) {
+  if (!c) return W4_E_INVALID;
+  const w4_model_desc& d = c->d;
+  const bool global = tensor == W4_T_EMBED || tensor == W4_T_LM_HEAD || tensor == W4_T_FINAL_NORM;
+  if (!global && (layer < 0 || layer >= d.n_layers)) return fail(c, W4_E_INVALID, "layer out of range");
+  if (!packed) return fail(c, W4_E_INVALID, "null source");
+  const bool is_norm = tensor == W4_T_ATTN_NORM || tensor == W4_T_MOE_NORM || tensor == W4_T_FINAL_NORM;
+  if (!is_norm && !scales) return fail(c, W4_E_INVALID, "null scales");
+  const bool is_expert = tensor == W4_T_GATE || tensor == W4_T_UP || tensor == W4_T_DOWN;
+  if (is_expert && (expert < -1 || expert >= d.n_experts)) return fail(c, W4_E_INVALID, "expert out of range");
+  hipStream_t st = (hipStream_t)stream;
+  int rc = ensure_device(c, st);
+  if (rc) return rc;
+  const LayerLoc* L = global ? nullptr : &c->bp.layers[layer];
+  const size_t H2 = (size_t)d.hidden * 2;
+  auto copy = [&](size_t off, const void* src, size_t bytes) -> int {
+    HIPCHK(c, hipMemcpyAsync(c->bank + off, src, bytes, hipMemcpyDeviceToDevice, st));
+    return W4_OK;
+  };
+  switch (tensor) {
+    case W4_T_ATTN_NORM: return copy(L->attn_norm, packed, H2);
+    case W4_T_MOE_NORM: return copy(L->moe_norm, packed, H2);
+    case W4_T_FINAL_NORM: return copy(c->bp.final_norm, packed, H2);
+    case W4_T_EMBED:
+      rc = copy(c->bp.emb_p, packed, (size_t)d.vocab * d.hidden / 2);
+      if (rc) return rc;
+      return copy(c->bp.emb_s, scales, (size_t)d.vocab * (d.hidden / d.group) * 2);
+    default: break;
+  }
+  const Loc* loc = nullptr;
+  switch (tensor) {
+    case W4_T_QKV: loc = &L->qkv; break;
+    case W4_T_O: loc = &L->o; break;
+    case W4_T_ROUTER: loc = &L->router; break;
+    case W4_T_GATE: loc = &L->gate; break;
+    case W4_T_UP: loc = &L->up; break;
+    case W4_T_DOWN: loc = &L->down; break;
+    case W4_T_LM_HEAD: loc = &c->bp.lm; break;
+    default: return fail(c, W4_E_INVALID, "unknown tensor id");
+  }
+  const int count = (is_expert && expert < 0) ? d.n_experts : 1;
+  const int first = (is_expert && expert >= 0) ? expert : 0;
+  Mat m = c->mat(*loc, first);
+  LCHK(c, 2, launch_repack(static_cast<const uint8_t*>(packed), static_cast<const uint16_t*>(scales), count, loc->N,
+                           loc->K, d.group, const_cast<uint4*>(m.tiles), const_cast<uint16_t*>(m.scales), st));
+  return W4_OK;
+}
+
+int w4_slot_alloc(w4_ctx* c, int32_t prompt_len, int32_t max_new, int32_t* slot_out) {
+  if (!c || !slot_out) return W4_E_INVALID;
+  if (prompt_len < 0 || max_new < 0) return fail(c, W4_E_INVALID, "negative length");
+  if ((int64_t)prompt_len + max_new > c->cap)
+    return fail(c, W4_E_CONTEXT_CAP, "prompt_len + max_new_tokens exceeds the context cap");
+  for (int s = 0; s < c->Bm; ++s)
+    if (!c->live[s]) {
+      c->live[s] = 1;
+      c->pos[s] = 0;
+      c->prompt[s] = prompt_len;
+      c->need_seed[s] = prompt_len > 0;
+      *slot_out = s;
+      return W4_OK;
+    }
+  return fail(c, W4_E_NO_SLOT, "every slot is live");
+}
+
+int w4_slot_seed(w4_ctx* c, int32_t slot, const void* k, const void* v, void* stream) {
+  if (!c) return W4_E_INVALID;
+  if (slot < 0 || slot >= c->Bm || !c->live[slot]) return fail(c, W4_E_BAD_SLOT, "slot is not live");
+  if (!c->need_seed[slot]) return fail(c, W4_E_BAD_SLOT, "slot has no unseeded prompt (seed once per join)");
+  if (!k || !v) return fail(c, W4_E_INVALID, "null K/V");
+  hipStream_t st = (hipStream_t)stream;
+  int rc = ensure_device(c, st);
+  if (rc) return rc;
+  LCHK(c, 1, launch_seed(c->d.n_layers, c->prompt[slot], slot, c->kv(), static_cast<const uint16_t*>(k),
+                         static_cast<const uint16_t*>(v), st));
+  c->need_seed[slot] = 0;
+  c->pos[slot] = c->prompt[slot];
+  return W4_OK;
+}
+
+int w4_slot_release(w4_ctx* c, int32_t slot) {
+  if (!c) return W4_E_INVALID;
+  if (slot < 0 || slot >= c->Bm || !c->live[slot]) return fail(c, W4_E_BAD_SLOT, "slot is not live");
+  c->live[slot] = 0;
+  c->need_seed[slot] = 0;
+  c->pos[slot] = 0;
+  return W4_OK;
+}
+
+int w4_slot_position(const w4_ctx* c, int32_t slot, int32_t* pos_out) {
+  if (!c || !pos_out) return W4_E_INVALID;
+  if (slot < 0 || slot >= c->Bm || !c->live[slot]) return W4_E_BAD_SLOT;
+  *pos_out = c->pos[slot];
+  return W4_OK;
+}
+
+int w4_slots_advance(w4_ctx* c, int32_t n, const int32_t* slots) {
+  if (!c) return W4_E_INVALID;
+  int rc = check_rows(c, n, slots);
+  if (rc) return rc;
+  for (int b = 0; b < n; ++b) c->pos[slots[b]]++;
+  return W4_OK;
+}
+
+int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* tokens, void* logits, int32_t* next,
+                   int32_t* route_ids, void* stream) {
+  if (!c) return W4_E_INVALID;
+  int rc = check_rows(c, B, slots);
+  if (rc) return rc;
+  if (!tokens || !next) return fail(c, W4_E_INVALID, "null tokens or next");
+  hipStream_t st = (hipStream_t)stream;
+  rc = ensure_device(c, st);
+  if (rc) return rc;
+  const int l0 = c->launches, s0 = c->syncs;
+  const w4_model_desc& d = c->d;
+  int max_pos = 0;
+  rc = upload_rows(c, B, slots, st, &max_pos);
+  if (rc) return rc;
+  uint16_t* h = c->W<uint16_t>(c->wp.h);
+  uint16_t* xn = c->W<uint16_t>(c->wp.xn);
+  LCHK(c, 1, launch_embed(B, d.hidden, d.vocab, d.group, tokens, c->Bk<uint8_t>(c->bp.emb_p),
+                          c->Bk<uint16_t>(c->bp.emb_s), h, c->Bk<uint16_t>(c->bp.layers[0].attn_norm), d.rms_eps, xn,
+                          st));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const uint16_t* ng = l + 1 < d.n_layers ? c->Bk<uint16_t>(c->bp.layers[l + 1].attn_norm)
+                                            : c->Bk<uint16_t>(c->bp.final_norm);
+    rc = layer_body(c, l, B, max_pos, h, xn, route_ids ? route_ids + (size_t)l * B * d.top_k : nullptr, ng, st);
+    if (rc) return rc;
+  }
+  uint16_t* lg = logits ? static_cast<uint16_t*>(logits) : c->W<uint16_t>(c->wp.logits);
+  LCHK(c, 1, launch_gemm(c->mat(c->bp.lm), B, xn, d.hidden, lg, d.vocab, EPI_F16, st));
+  LCHK(c, 1, launch_argmax(B, d.vocab, lg, next, st));
+  for (int b = 0; b < B; ++b) c->pos[slots[b]]++;
+  c->last_launches = c->launches - l0;
+  c->last_syncs = c->syncs - s0;
+  return W4_OK;
+}
+
+int w4_gemm(w4_ctx* c, int32_t layer, int32_t tensor, int32_t expert, int32_t B, const void* x, void* y,
+            void* stream) {
+  if (!c) return W4_E_INVALID;
+  const w4_model_desc& d = c->d;
+  if (B < 1 || B > c->Bm) return fail(c, W4_E_INVALID, "B must be in [1, max_streams]");
+  if (!x || !y) return fail(c, W4_E_INVALID, "null x or y");
+  const bool global = tensor == W4_T_LM_HEAD;
+  if (!global && (layer < 0 || layer >= d.n_layers)) return fail(c, W4_E_INVALID, "layer out of range");
+  const LayerLoc* L = global ? nullptr : &c->bp.layers[layer];
+  const Loc* loc = nullptr;
+  int e = 0;
+  switch (tensor) {
+    case W4_T_QKV: loc = &L->qkv; break;
+    case W4_T_O: loc = &L->o; break;
+    case W4_T_ROUTER: loc = &L->router; break;
+    case W4_T_GATE: loc = &L->gate; e = expert; break;
+    case W4_T_UP: loc = &L->up; e = expert; break;
+    case W4_T_DOWN: loc = &L->down; e = expert; break;
+    case W4_T_LM_HEAD: loc = &c->bp.lm; break;
+    default: return fail(c, W4_E_INVALID, "tensor has no product");
+  }
+  if (e < 0 || e >= d.n_experts) return fail(c, W4_E_INVALID, "expert out of range");
+  hipStream_t st = (hipStream_t)stream;
+  int rc = ensure_device(c, st);
+  if (rc) return rc;
+  const int epi = tensor == W4_T_ROUTER ? EPI_F32 : EPI_F16;
+  LCHK(c, 1, launch_gemm(c->mat(*loc, e), B, static_cast<const uint16_t*>(x), loc->K, y, loc->N, epi, st));
+  return W4_OK;
+}
+
+int w4_route(w4_ctx* c, int32_t B, const float* logits, int32_t* ids, float* w, int32_t* counts, int32_t* offsets,
+             int32_t* pair_stream, int32_t* pair_rank, void* stream) {
+  if (!c) return W4_E_INVALID;
+  if (B < 1 || B > c->Bm) return fail(c, W4_E_INVALID, "B must be in [1, max_streams]");
+  if (!logits || !ids || !w) return fail(c, W4_E_INVALID, "null logits, ids or w");
+  hipStream_t st = (hipStream_t)stream;
+  int rc = ensure_device(c, st);
+  if (rc) return rc;
+  RouteOut r = c->route_out();
+  r.ids = ids;
+  r.w = w;
+  r.counts = counts;
+  r.offsets = offsets;
+  r.pair_stream = pair_stream;
+  r.pair_rank = pair_rank;
+  LCHK(c, 1, launch_route(logits, B, c->d.n_experts, c->d.top_k, r, st));
+  return W4_OK;
+}
+
+int w4_moe(w4_ctx* c, int32_t layer, int32_t B, const void* x, const float* router_logits, void* y,
+           int32_t* route_ids, void* stream) {
+  if (!c) return W4_E_INVALID;
+  const w4_model_desc& d = c->d;
+  if (layer < 0 || layer >= d.n_layers) return fail(c, W4_E_INVALID, "layer out of range");
+  if (B < 1 || B > c->Bm) return fail(c, W4_E_INVALID, "B must be in [1, max_streams]");
+  if (!x || !y) return fail(c, W4_E_INVALID, "null x or y");
+  hipStream_t st = (hipStream_t)stream;
+  int rc = ensure_device(c, st);
+  if (rc) return rc;
+  const LayerLoc& L = c->bp.layers[layer];
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  const float* lg = router_logits;
+  if (!lg) {
+    LCHK(c, 1, launch_gemm(c->mat(L.router), B, xh, d.hidden, c->W<float>(c->wp.rlogits), d.n_experts, EPI_F32, st));
+    lg = c->W<float>(c->wp.rlogits);
+  }
+  RouteOut r = c->route_out(route_ids);
+  LCHK(c, 1, launch_route(lg, B, d.n_experts, d.top_k, r, st));
+  const int max_used = std::min(B * d.top_k, d.n_experts);
+  LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), d.n_experts, B, max_used, xh, d.hidden, r,
+                               c->W<uint16_t>(c->wp.act), st));
+  LCHK(c, 1, launch_moe_down(c->mat(L.down), d.n_experts, B, max_used, c->W<uint16_t>(c->wp.act), r,
+                             c->W<uint16_t>(c->wp.y), st));
+  LCHK(c, 1, launch_combine(B, d.hidden, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), static_cast<uint16_t*>(y),
+                            false, nullptr, d.rms_eps, nullptr, st));
+  return W4_OK;
+}
+
+int w4_attn_decode(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, const void* q, const void* k_new,
+                   const void* v_new, void* o, void* stream) {
+  if (!c) return W4_E_INVALID;
+  if (layer < 0 || layer >= c->d.n_layers) return fail(c, W4_E_INVALID, "layer out of range");
+  int rc = check_rows(c, B, slots);
+  if (rc) return rc;
+  if (!q || !k_new || !v_new || !o) return fail(c, W4_E_INVALID, "null q, k_new, v_new or o");
+  hipStream_t st = (hipStream_t)stream;
+  rc = ensure_device(c, st);
+  if (rc) return rc;
+  int max_pos = 0;
+  rc = upload_rows(c, B, slots, st, &max_pos);
+  if (rc) return rc;
+  const int32_t* slot = c->W<int32_t>(c->wp.rows);
+  const int32_t* pos = slot + c->Bm;
+  KV kv = c->kv();
+  LCHK(c, 1, launch_append(B, layer, kv, slot, pos, static_cast<const uint16_t*>(k_new),
+                           static_cast<const uint16_t*>(v_new), st));
+  LCHK(c, 2, launch_attention(B, layer, c->d.n_q_heads, kv, slot, pos, max_pos, static_cast<const uint16_t*>(q),
+                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), static_cast<uint16_t*>(o), st));
+  return W4_OK;
+}
+
+int w4_layer_step(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, void* h, int32_t* route_ids,
+                  void* stream) {
+  if (!c) return W4_E_INVALID;
+  if (layer < 0 || layer >= c->d.n_layers) return fail(c, W4_E_INVALID, "layer out of range");
+  int rc = check_rows(c, B, slots);
+  if (rc) return rc;
+  if (!h) return fail(c, W4_E_INVALID, "null h");
+  hipStream_t st = (hipStream_t)stream;
+  rc = ensure_device(c, st);
+  if (rc) return rc;
+  int max_pos = 0;
+  rc = upload_rows(c, B, slots, st, &max_pos);
+  if (rc) return rc;
+  uint16_t* hh = static_cast<uint16_t*>(h);
+  uint16_t* xn = c->W<uint16_t>(c->wp.xn);
+  LCHK(c, 1, launch_rmsnorm(B, c->d.hidden, hh, c->Bk<uint16_t>(c->bp.layers[layer].attn_norm), c->d.rms_eps, xn, st));
+  return layer_body(c, layer, B, max_pos, hh, xn, route_ids, nullptr, st);
+}
+
+const char* w4_status_string(int32_t s) {
+  switch (s) {
+    case W4_OK: return "ok";
+    case W4_E_INVALID: return "invalid argument";
+    case W4_E_NO_SLOT: return "no free slot";
+    case W4_E_CONTEXT_CAP: return "context cap exceeded";
+    case W4_E_BAD_SLOT: return "bad slot";
+    case W4_E_NOT_READY: return "slot not seeded";
+    case W4_E_HIP: return "HIP runtime error";
+    case W4_E_UNSUPPORTED: return "unsupported device or size";
+    default: return "unknown status";
+  }
+}
+
+const char* w4_last_error(const w4_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+int w4_last_step_counts(const w4_ctx* c, int32_t* launches, int32_t* syncs) {
+  if (!c) return W4_E_INVALID;
+  if (launches) *launches = c->last_launches;
+  if (syncs) *syncs = c->last_syncs;
+  return W4_OK;
+}
+
+}  // extern "C"

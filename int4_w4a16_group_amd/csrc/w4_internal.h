@@ -1,0 +1,92 @@
+// Internal declarations shared by the gfx950 kernels and the host side of
+// the w4moe library.  Nothing here is part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "w4moe.h"
+
+namespace w4 {
+
+// ---------------------------------------------------------------------------
+// Repacked bank layout of one int4 tensor W[N][K] (N padded to Np = 16*ceil(N/16)).
+//
+// tiles: [Np/16][K/128][64 lanes][16 bytes].  Lane L of tile (t, c) holds, for
+// MFMA k-steps s = 0..3, one dword with the 8 codes of row n = 16t + L%16,
+// columns k = 128c + 32s + 8(L/16) + j, j = 0..7, as offset-binary nibbles
+// (code + 8): nibble j holds element 2j and nibble j+4 holds element 2j+1, so
+// ((w >> 4j) & 0x000F000F) | 0x64006400 is the fp16 pair (1024 + u_2j, 1024 +
+// u_2j+1).  Pad rows hold code 0.  A wave reads a (16 x 128) block as one
+// fully coalesced 1 KiB load.
+// scales: [Np][K/g] fp16, pad rows zero.
+// ---------------------------------------------------------------------------
+struct Mat {
+  const uint4* tiles;
+  const uint16_t* scales;
+  int N, K, g;
+  int Np() const { return (N + 15) / 16 * 16; }
+  int ntiles() const { return (N + 15) / 16; }
+};
+
+enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_RESID = 2 };
+
+// ---- launchers (kernels in *.hip); all return hipGetLastError() ----
+hipError_t launch_repack(const uint8_t* src_packed, const uint16_t* src_scales, int count, int N, int K,
+                         int g, uint4* dst_tiles, uint16_t* dst_scales, hipStream_t st);
+hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi,
+                       hipStream_t st);
+
+struct RouteOut {
+  int32_t* ids;          // [B][k]
+  float* w;              // [B][k]
+  int32_t* counts;       // [E]
+  int32_t* offsets;      // [E+1]
+  int32_t* pair_stream;  // [B*k]
+  int32_t* pair_rank;    // [B*k]
+  int32_t* inv;          // [B][k] position of pair (b, r) in expert order
+  int32_t* used;         // [E] used experts, ascending
+  int32_t* n_used;       // [1]
+};
+hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st);
+
+// Grouped expert GEMMs over the bucketed pairs.  max_used bounds the grid.
+hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, int E, int B, int max_used,
+                             const uint16_t* x, int ldx, const RouteOut& r, uint16_t* act, hipStream_t st);
+hipError_t launch_moe_down(const Mat& down0, int E, int B, int max_used, const uint16_t* act,
+                           const RouteOut& r, uint16_t* y, hipStream_t st);
+// h[b] = fp16(h[b] + fp16(sum_r w[b][r] * y[inv[b][r]]))  (resid), or out = fp16(sum ...) (no resid);
+// then optionally xn[b] = RMSNorm(h[b]) * gamma.
+hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* inv, const uint16_t* y,
+                          uint16_t* h, bool resid, const uint16_t* gamma, float eps, uint16_t* xn,
+                          hipStream_t st);
+hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma, float eps, uint16_t* out,
+                          hipStream_t st);
+hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const uint8_t* emb_p,
+                        const uint16_t* emb_s, uint16_t* h, const uint16_t* gamma, float eps, uint16_t* xn,
+                        hipStream_t st);
+hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, hipStream_t st);
+
+struct KV {
+  uint16_t* K;   // [L][S][Hkv][cap][D]
+  uint16_t* VT;  // [L][S][Hkv][D][cap]
+  int S, Hkv, cap, D;
+};
+hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStream_t st);
+// q/k rotary at each stream's position, K/V append into the arena; q_out [B][Hq][D].
+hipError_t launch_rope_append(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
+                              const uint16_t* qkv, int ldqkv, const float2* table, uint16_t* q_out,
+                              hipStream_t st);
+// plain K/V append (no rotary): k_new/v_new [B][Hkv][D].
+hipError_t launch_append(int B, int layer, const KV& kv, const int32_t* slot, const int32_t* pos,
+                         const uint16_t* k_new, const uint16_t* v_new, hipStream_t st);
+hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, const uint16_t* v,
+                       hipStream_t st);
+// split-KV decode attention; part_o [B][Hq][nchmax][D] f32, part_ml [B][Hq][nchmax][2].
+hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
+                            int max_pos, const uint16_t* q, float* part_o, float* part_ml, uint16_t* o,
+                            hipStream_t st);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
+
+}  // namespace w4

@@ -1,0 +1,150 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every entry
+point the header declares, sizes its buffers, and runs the host-side slot
+logic and argument checks (all of which finish before any device work)."""
+import os
+import re
+
+import pytest
+
+from int4_w4a16_group_amd import _lib as L
+from int4_w4a16_group_amd import build, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    build.build(force=False)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "w4moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 20
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(L.exported_names()) == names
+
+
+def test_buffer_sizes_full_model():
+    d = inputs.FULL
+    arena = L.w4_arena_bytes(d, 32, 4096)
+    assert arena == 2 * 48 * 32 * 4 * 4096 * 128 * 2          # K and V, fp16
+    bank = L.w4_bank_bytes(d)
+    # packed int4 + fp16 group scales of every tensor, canonical embedding, norms
+    # (1/2 byte per code + 2 bytes per 128-code group) = 33/64 byte per weight
+    per_layer = (5120 * 2048 + 2048 * 4096 + 128 * 2048 + 3 * 128 * 768 * 2048) * 33 // 64 + 2 * 2048 * 2
+    want = 48 * per_layer + 2 * 151936 * 2048 * 33 // 64 + 2048 * 2
+    assert want == 15_743_414_272
+    assert want <= bank <= want + 48 * 16 * 256 + 16 * 256
+    assert L.w4_workspace_bytes(d, 32, 4096) > 0
+
+
+def test_geometry_and_size_limits():
+    d = inputs.TINY
+    assert L.w4_bank_bytes(d) > 0
+    import dataclasses
+    for bad in (dict(hidden=200), dict(head_dim=96), dict(group=16), dict(top_k=0), dict(n_experts=1, top_k=2),
+                dict(n_q_heads=3), dict(moe_inter=100)):
+        assert L.w4_bank_bytes(dataclasses.replace(d, **bad)) == 0, bad
+    assert L.w4_arena_bytes(d, 33, 128) == 0
+    assert L.w4_arena_bytes(d, 8, 100) == 0
+    assert L.w4_arena_bytes(d, 8, 128) > 0
+
+
+FAKE = 1 << 20   # 256-aligned stand-in addresses; never dereferenced by host-side paths
+
+
+def make_ctx(max_streams=4, cap=128):
+    return L.w4_create(inputs.TINY, max_streams, cap, FAKE, 2 * FAKE, 3 * FAKE)
+
+
+def test_slot_lifecycle_and_admission():
+    c = make_ctx()
+    try:
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slot_alloc(c, 100, 29)                        # 129 > cap 128: rejected at admission
+        assert e.value.status == L.W4_E_CONTEXT_CAP
+        slots = [L.w4_slot_alloc(c, 0, 128) for _ in range(4)]
+        assert slots == [0, 1, 2, 3]                           # lowest free slot first
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slot_alloc(c, 0, 1)
+        assert e.value.status == L.W4_E_NO_SLOT
+        L.w4_slot_release(c, 2)
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slot_release(c, 2)                            # double release
+        assert e.value.status == L.W4_E_BAD_SLOT
+        assert L.w4_slot_alloc(c, 0, 5) == 2                   # reuse of the released slot
+        assert L.w4_slot_position(c, 2) == 0
+        L.w4_slots_advance(c, [2, 0])
+        L.w4_slots_advance(c, [2])
+        assert L.w4_slot_position(c, 2) == 2 and L.w4_slot_position(c, 0) == 1
+        L.w4_slot_release(c, 2)
+        assert L.w4_slot_alloc(c, 0, 5) == 2 and L.w4_slot_position(c, 2) == 0   # logical reset
+    finally:
+        L.w4_destroy(c)
+
+
+def test_decode_step_argument_checks_are_all_or_nothing():
+    c = make_ctx()
+    try:
+        a = L.w4_slot_alloc(c, 0, 10)
+        b = L.w4_slot_alloc(c, 7, 10)                          # prompt not seeded yet
+        cases = [
+            ([a, a], L.W4_E_BAD_SLOT),                         # duplicate row
+            ([a, 3], L.W4_E_BAD_SLOT),                         # slot 3 not live
+            ([a, b], L.W4_E_NOT_READY),
+            ([], L.W4_E_INVALID),
+            ([0, 1, 2, 3, 0], L.W4_E_INVALID),                 # B > max_streams
+        ]
+        for rows, status in cases:
+            with pytest.raises(L.W4Error) as e:
+                L.w4_decode_step(c, rows, FAKE, FAKE, FAKE)
+            assert e.value.status == status, rows
+            assert L.w4_slot_position(c, a) == 0                # nothing moved
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slot_seed(c, a, FAKE, FAKE)                   # nothing to seed
+        assert e.value.status == L.W4_E_BAD_SLOT
+        with pytest.raises(L.W4Error) as e:
+            L.w4_attn_decode(c, 5, [a], FAKE, FAKE, FAKE, FAKE)  # layer out of range
+        assert e.value.status == L.W4_E_INVALID
+    finally:
+        L.w4_destroy(c)
+
+
+def test_stream_at_cap_is_rejected():
+    c = L.w4_create(inputs.TINY, 2, 64, FAKE, 2 * FAKE, 3 * FAKE)
+    try:
+        s = L.w4_slot_alloc(c, 0, 64)
+        for _ in range(64):
+            L.w4_slots_advance(c, [s])
+        with pytest.raises(L.W4Error) as e:
+            L.w4_decode_step(c, [s], FAKE, FAKE, FAKE)
+        assert e.value.status == L.W4_E_CONTEXT_CAP
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slots_advance(c, [s])
+        assert e.value.status == L.W4_E_CONTEXT_CAP
+        assert L.w4_slot_position(c, s) == 64
+    finally:
+        L.w4_destroy(c)
+
+
+def test_create_rejects_bad_buffers():
+    with pytest.raises(L.W4Error):
+        L.w4_create(inputs.TINY, 4, 128, 0, FAKE, FAKE)
+    with pytest.raises(L.W4Error):
+        L.w4_create(inputs.TINY, 4, 128, FAKE + 8, FAKE, FAKE)
+
+
+def test_no_vendor_blas_linked():
+    """No vendor BLAS on the device path: the library links none."""
+    import subprocess
+    out = subprocess.run(["ldd", L.LIB_PATH], capture_output=True, text=True).stdout
+    for name in ("rocblas", "hipblas", "hipblaslt", "miopen", "libtorch"):
+        assert name not in out.lower(), name
