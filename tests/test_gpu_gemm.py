@@ -12,7 +12,7 @@ from int4_w4a16_group_amd import _lib as L
 from int4_w4a16_group_amd import inputs
 from int4_w4a16_group_amd.engine import Context
 from tests.gpu_util import empty_f16, to_dev, to_host, ulp_diff
-from tests.util import assert_normwise, f16v
+from tests.util import assert_normwise, assert_within_reorder_bound, f16v, gemm_abs_sum
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -47,8 +47,8 @@ def test_dense_projection_parity_and_batch_identity(dense_ctx, gpu, tensor, N, K
     ref = oracle.w4_gemm(x32, w.packed, w.scales, 128)
     y32 = run(ctx, tensor, x32, N, gpu)
     assert_normwise(f16v(y32), f16v(ref), TOL, "dense vs oracle")
-    d = ulp_diff(y32, ref)
-    assert d.max() <= 1, f"max ulp difference {d.max()}"
+    assert_within_reorder_bound(y32, ref, gemm_abs_sum(x32, w.packed, w.scales, 128), K, "dense vs oracle")
+    assert (ulp_diff(y32, ref) > 1).mean() < 1e-3
     for B in (1, 2, 4, 8, 16, 17):
         yb = run(ctx, tensor, x32[:B], N, gpu)
         assert np.array_equal(yb, y32[:B]), f"rows differ between B={B} and B=32"
@@ -69,7 +69,7 @@ def test_ragged_shapes_and_groups(gpu, N, K, g, B):
         y = run(ctx, L.W4_T_LM_HEAD, x, N, gpu)
         ref = oracle.w4_gemm(x, w.packed, w.scales, g)
         assert_normwise(f16v(y), f16v(ref), TOL, "ragged vs oracle")
-        assert ulp_diff(y, ref).max() <= 1
+        assert_within_reorder_bound(y, ref, gemm_abs_sum(x, w.packed, w.scales, g), K, "ragged vs oracle")
         y1 = run(ctx, L.W4_T_LM_HEAD, x[-1:], N, gpu)
         assert np.array_equal(y1[0], y[-1])
     finally:

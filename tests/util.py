@@ -28,3 +28,25 @@ def ulp16(v) -> np.ndarray:
     a = np.abs(np.asarray(v, dtype=np.float64))
     e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
     return 2.0 ** (e - 10)
+
+
+def gemm_abs_sum(x_bits, packed, scales, group) -> np.ndarray:
+    """sum_k |x_k| |w_nk| per output (for summation-order error bounds)."""
+    p = np.asarray(packed).astype(np.int16)
+    q = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.float64)
+    lo, hi = p & 15, (p >> 4) & 15
+    q[..., 0::2] = np.where(lo > 7, lo - 16, lo)
+    q[..., 1::2] = np.where(hi > 7, hi - 16, hi)
+    s = np.repeat(f16v(scales), group, axis=-1)
+    return np.abs(f16v(x_bits)) @ np.abs(q * s).T
+
+
+def assert_within_reorder_bound(got_bits, ref_bits, abs_sum, K, what=""):
+    """Two fp32 summations of the same K products, each rounded once to fp16:
+    |got - ref| <= 2 gamma_K sum|x w| + one fp16 ulp (Higham's bound per side)."""
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    g, r = f16v(got_bits), f16v(ref_bits)
+    lim = 2 * gamma * abs_sum + ulp16(np.maximum(np.abs(g), np.abs(r)))
+    bad = np.abs(g - r) > lim
+    assert not bad.any(), f"{what}: {bad.sum()} outputs beyond the summation bound"
