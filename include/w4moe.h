@@ -174,6 +174,20 @@ const char* w4_last_error(const w4_ctx* ctx);
  * w4_decode_step (the library itself never synchronises inside a step). */
 int w4_last_step_counts(const w4_ctx* ctx, int32_t* launches, int32_t* syncs);
 
+/* Kernel families that w4_profile_begin can time. */
+enum {
+  W4_K_DENSE = 1,      /* every dense W4A16 product (q/k/v, o, router, output projection) */
+  W4_K_MOE_GATEUP = 2, /* grouped expert gate/up + SwiGLU */
+  W4_K_MOE_DOWN = 3,   /* grouped expert down */
+  W4_K_ATTENTION = 4   /* split-KV attention (chunk pass; the chunk reduce is not included) */
+};
+/* Record a HIP event pair around every launch of one kernel family in the
+ * calls that follow (on the stream each call is given), until
+ * w4_profile_end, which waits for the last event and returns the summed
+ * kernel time in milliseconds and the number of launches timed. */
+int w4_profile_begin(w4_ctx* ctx, int32_t kernel);
+int w4_profile_end(w4_ctx* ctx, double* total_ms, int32_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

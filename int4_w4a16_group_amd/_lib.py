@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libw4moe.so")
 
 W4_OK, W4_E_INVALID, W4_E_NO_SLOT, W4_E_CONTEXT_CAP, W4_E_BAD_SLOT, W4_E_NOT_READY, W4_E_HIP, W4_E_UNSUPPORTED = \
     0, -1, -2, -3, -4, -5, -6, -7
+W4_K_DENSE, W4_K_MOE_GATEUP, W4_K_MOE_DOWN, W4_K_ATTENTION = 1, 2, 3, 4
 (W4_T_QKV, W4_T_O, W4_T_ROUTER, W4_T_GATE, W4_T_UP, W4_T_DOWN, W4_T_EMBED, W4_T_LM_HEAD, W4_T_ATTN_NORM,
  W4_T_MOE_NORM, W4_T_FINAL_NORM) = range(11)
 
@@ -56,6 +57,8 @@ _SIGS = {
     "w4_status_string": (C.c_char_p, [_i32]),
     "w4_last_error": (C.c_char_p, [_vp]),
     "w4_last_step_counts": (C.c_int, [_vp, C.POINTER(_i32), C.POINTER(_i32)]),
+    "w4_profile_begin": (C.c_int, [_vp, _i32]),
+    "w4_profile_end": (C.c_int, [_vp, C.POINTER(C.c_double), C.POINTER(_i32)]),
 }
 
 
@@ -217,3 +220,13 @@ def w4_last_step_counts(ctx):
     a, b = _i32(), _i32()
     _check(ctx, lib().w4_last_step_counts(ctx, C.byref(a), C.byref(b)))
     return a.value, b.value
+
+
+def w4_profile_begin(ctx, kernel: int):
+    return _check(ctx, lib().w4_profile_begin(ctx, kernel))
+
+
+def w4_profile_end(ctx):
+    ms, n = C.c_double(), _i32()
+    _check(ctx, lib().w4_profile_end(ctx, C.byref(ms), C.byref(n)))
+    return ms.value, n.value

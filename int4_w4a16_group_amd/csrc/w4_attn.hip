@@ -262,31 +262,41 @@ __global__ void __launch_bounds__(64) k_attn(AttnArgs a) {
   }
 }
 
-// One wave per (head, stream): combine the stream's chunks in order.
+// One wave per (head, stream): combine the stream's chunks.  Lane c holds
+// chunk c (c + 64, ... beyond 64 chunks); M and L are wave reductions with a
+// fixed tree, then every lane sums its columns over the chunks in order.
 // nchmax <= 256 (ctx_cap <= 16384, checked at context creation).
 __global__ void __launch_bounds__(64) k_attn_reduce(int Hq, int D, int nchmax, const int32_t* __restrict__ pos,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml, uint16_t* __restrict__ o) {
   __shared__ float wgt[256];
-  __shared__ float Lsum;
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int nch = (pos[b] + 1 + 63) / 64;
   const float* ml = part_ml + ((size_t)b * Hq + h) * nchmax * 2;
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, ml[2 * c]);
-    float L = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float e = expf(ml[2 * c] - M);
-      wgt[c] = e;
-      L = L + ml[2 * c + 1] * e;
-    }
-    Lsum = L;
+  float mv[4], lv[4];
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = lane + 64 * j;
+    mv[j] = c < nch ? ml[2 * c] : -INFINITY;
+    lv[j] = c < nch ? ml[2 * c + 1] : 0.f;
+    M = fmaxf(M, mv[j]);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float L = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = lane + 64 * j;
+    const float e = c < nch ? expf(mv[j] - M) : 0.f;
+    if (c < nch) wgt[c] = e;
+    L = L + lv[j] * e;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L = L + __shfl_xor(L, off, 64);
   __syncthreads();
-  const float L = Lsum;
   const float* po = part_o + ((size_t)b * Hq + h) * nchmax * D;
-  for (int d = threadIdx.x; d < D; d += 64) {
+  for (int d = lane; d < D; d += 64) {
     float acc = 0.f;
     for (int c = 0; c < nch; ++c) acc = acc + po[(size_t)c * D + d] * wgt[c];
     o[((size_t)b * Hq + h) * D + d] = f2h(acc / L);
@@ -295,7 +305,7 @@ __global__ void __launch_bounds__(64) k_attn_reduce(int Hq, int D, int nchmax, c
 
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
                             int max_pos, const uint16_t* q, float* part_o, float* part_ml, uint16_t* o,
-                            hipStream_t st) {
+                            hipStream_t st, void* prof) {
   AttnArgs a;
   a.kv = kv;
   a.layer = layer;
@@ -309,10 +319,12 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   a.scale = (float)(1.0 / sqrt((double)kv.D));
   const int nch = (max_pos + 1 + 63) / 64;
   dim3 grid(nch, kv.Hkv, B);
+  if (prof) prof_mark(prof, st);
   if (kv.D == 128)
     hipLaunchKernelGGL(k_attn<128>, grid, dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL(k_attn<64>, grid, dim3(64), 0, st, a);
+  if (prof) prof_mark(prof, st);
   hipLaunchKernelGGL(k_attn_reduce, dim3(Hq, B), dim3(64), 0, st, Hq, kv.D, a.nchmax, pos, part_o, part_ml, o);
   return hipGetLastError();
 }

@@ -290,7 +290,13 @@ struct MoeArgs {
   uint16_t* out;          // [pairs][N]
 };
 
-template <int MT, int NCH, int G, bool GATEUP, int LB>
+// One work-group per (used expert, chunk of column tiles); its NW waves own
+// the K slices.  Rows are the expert's pairs, 16 at a time (an expert with
+// more than 16 rows repeats the chunk for each 16-row tile; the arithmetic of
+// a row is the same in every tile).  The x slice of a row tile stays in
+// registers for the whole chunk; the next tile's weights are loaded before the
+// current tile is reduced.
+template <int NCH, int G, bool GATEUP, int LB>
 __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   extern __shared__ float red[];
   const int NW = blockDim.x >> 6;
@@ -300,96 +306,103 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   const int e = a.used[u];
   const int off = a.offsets[e];
   const int m = a.offsets[e + 1] - off;
-  const int mts = (m + 15) >> 4;
   const int kbase = w * NCH * 128;
-  XRegs<MT, NCH * 4> x;
-  load_x<MT, NCH>(
-      x,
-      [&](int i) -> const uint16_t* {
-        if (i >= m) return nullptr;
-        const int row = GATEUP ? a.pair_stream[off + i] : off + i;
-        return a.x + (size_t)row * a.ldx;
-      },
-      kbase, lane);
   const uint4* T0 = a.t0 + a.tile_stride * e;
   const uint4* T1 = GATEUP ? a.t1 + a.tile_stride * e : nullptr;
   const uint16_t* S0 = a.s0 + a.scale_stride * e;
   const uint16_t* S1 = GATEUP ? a.s1 + a.scale_stride * e : nullptr;
   const int t_begin = ch * a.per_chunk;
   const int t_end = min(t_begin + a.per_chunk, a.ntiles);
-  for (int t = t_begin; t < t_end; ++t) {
+  for (int r0 = 0; r0 < m; r0 += 16) {
+    XRegs<1, NCH * 4> x;
+    load_x<1, NCH>(
+        x,
+        [&](int i) -> const uint16_t* {
+          if (r0 + i >= m) return nullptr;
+          const int row = GATEUP ? a.pair_stream[off + r0 + i] : off + r0 + i;
+          return a.x + (size_t)row * a.ldx;
+        },
+        kbase, lane);
     uint4 w0[NCH], w1[NCH];
-    load_tile<NCH>(T0, a.K, t, w, lane, w0);
-    if (GATEUP) load_tile<NCH>(T1, a.K, t, w, lane, w1);
-    float s0[NCH * 128 / G], s1[NCH * 128 / G];
-    load_scales<NCH, G>(S0, a.K, t, w, lane, s0);
-    if (GATEUP) load_scales<NCH, G>(S1, a.K, t, w, lane, s1);
-    f4 acc0[MT], acc1[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc0[mt] = acc1[mt] = f4{0.f, 0.f, 0.f, 0.f};
-    tile_mac<MT, NCH, G>(x, w0, s0, acc0, mts);
-    if (GATEUP) tile_mac<MT, NCH, G>(x, w1, s1, acc1, mts);
-    f4* r4 = reinterpret_cast<f4*>(red);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      r4[(w * MT + mt) * 64 + lane] = acc0[mt];
-      if (GATEUP) r4[((NW + w) * MT + mt) * 64 + lane] = acc1[mt];
-    }
-    __syncthreads();
-    if (GATEUP) {
-      const float* red1 = red + NW * MT * 256;
-      const int nt = blockDim.x;
-      for (int o = threadIdx.x; o < MT * 256; o += nt) {
-        const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
-        const int idx = mt * 256 + ((i >> 2) * 16 + j) * 4 + (i & 3);
-        float vg = red[idx], vu = red1[idx];
-        for (int ww = 1; ww < NW; ++ww) {
-          vg = vg + red[ww * MT * 256 + idx];
-          vu = vu + red1[ww * MT * 256 + idx];
+    load_tile<NCH>(T0, a.K, t_begin, w, lane, w0);
+    if (GATEUP) load_tile<NCH>(T1, a.K, t_begin, w, lane, w1);
+    for (int t = t_begin; t < t_end; ++t) {
+      uint4 n0[NCH], n1[NCH];
+      if (t + 1 < t_end) {
+        load_tile<NCH>(T0, a.K, t + 1, w, lane, n0);
+        if (GATEUP) load_tile<NCH>(T1, a.K, t + 1, w, lane, n1);
+      }
+      float s0[NCH * 128 / G], s1[NCH * 128 / G];
+      load_scales<NCH, G>(S0, a.K, t, w, lane, s0);
+      if (GATEUP) load_scales<NCH, G>(S1, a.K, t, w, lane, s1);
+      f4 acc0[1] = {f4{0.f, 0.f, 0.f, 0.f}}, acc1[1] = {f4{0.f, 0.f, 0.f, 0.f}};
+      tile_mac<1, NCH, G>(x, w0, s0, acc0, 1);
+      if (GATEUP) tile_mac<1, NCH, G>(x, w1, s1, acc1, 1);
+      f4* r4 = reinterpret_cast<f4*>(red);
+      r4[w * 64 + lane] = acc0[0];
+      if (GATEUP) r4[(NW + w) * 64 + lane] = acc1[0];
+      __syncthreads();
+      if (GATEUP) {
+        const float* red1 = red + NW * 256;
+        for (int o = threadIdx.x; o < 256; o += blockDim.x) {
+          const int i = o >> 4, j = o & 15;
+          const int idx = ((i >> 2) * 16 + j) * 4 + (i & 3);
+          float vg = red[idx], vu = red1[idx];
+          for (int ww = 1; ww < NW; ++ww) {
+            vg = vg + red[ww * 256 + idx];
+            vu = vu + red1[ww * 256 + idx];
+          }
+          const int row = r0 + i, n = t * 16 + j;
+          if (row < m && n < a.N) {
+            const float gt = h2f(f2h(vg)), up = h2f(f2h(vu));
+            const float silu = gt / (1.0f + expf(-gt));
+            a.out[(size_t)(off + row) * a.N + n] = f2h(silu * up);
+          }
         }
-        const int row = mt * 16 + i, n = t * 16 + j;
-        if (row < m && n < a.N) {
-          const float gt = h2f(f2h(vg)), up = h2f(f2h(vu));
-          const float silu = gt / (1.0f + expf(-gt));
-          a.out[(size_t)(off + row) * a.N + n] = f2h(silu * up);
+      } else {
+        reduce_tile<1>(red, NW, [&](int i, int j, float v) {
+          const int row = r0 + i, n = t * 16 + j;
+          if (row < m && n < a.N) a.out[(size_t)(off + row) * a.N + n] = f2h(v);
+        });
+      }
+      __syncthreads();
+      if (t + 1 < t_end) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          w0[c] = n0[c];
+          if (GATEUP) w1[c] = n1[c];
         }
       }
-    } else {
-      reduce_tile<MT>(red, NW, [&](int row, int j, float v) {
-        const int n = t * 16 + j;
-        if (row < m && n < a.N) a.out[(size_t)(off + row) * a.N + n] = f2h(v);
-      });
     }
-    __syncthreads();
   }
 }
 
 typedef void (*MoeKernel)(MoeArgs);
 
-template <bool GU, int MT, int NCH, int LB>
+template <bool GU, int NCH, int LB>
 static MoeKernel moe_pick_g(int g) {
   switch (g) {
-    case 32: return k_moe<MT, NCH, 32, GU, LB>;
-    case 64: return k_moe<MT, NCH, 64, GU, LB>;
-    default: return k_moe<MT, NCH, 128, GU, LB>;
+    case 32: return k_moe<NCH, 32, GU, LB>;
+    case 64: return k_moe<NCH, 64, GU, LB>;
+    default: return k_moe<NCH, 128, GU, LB>;
   }
 }
-template <bool GU, int LB>
-static MoeKernel moe_pick_lb(int MT, int nch, int g) {
-  if (MT == 1) return nch == 2 ? moe_pick_g<GU, 1, 2, LB>(g) : moe_pick_g<GU, 1, 1, LB>(g);
-  return nch == 2 ? moe_pick_g<GU, 2, 2, LB>(g) : moe_pick_g<GU, 2, 1, LB>(g);
-}
 template <bool GU>
-static MoeKernel moe_pick(int MT, int nch, int g, int nw) {
-  return nw <= 8 ? moe_pick_lb<GU, 512>(MT, nch, g) : moe_pick_lb<GU, 1024>(MT, nch, g);
+static MoeKernel moe_pick(int nch, int g, int nw) {
+  if (nw <= 8) return nch == 2 ? moe_pick_g<GU, 2, 512>(g) : moe_pick_g<GU, 1, 512>(g);
+  return nch == 2 ? moe_pick_g<GU, 2, 1024>(g) : moe_pick_g<GU, 1, 1024>(g);
 }
 
+// Column tiles per work-group: enough work-groups to cover the chip
+// (target_wg) when max_used experts are busy, and the x slice of a row tile is
+// loaded once per chunk.
 static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, int E, int B, int max_used,
-                                    const uint16_t* x, int ldx, const RouteOut& r, uint16_t* out, int per_chunk,
+                                    const uint16_t* x, int ldx, const RouteOut& r, uint16_t* out, int target_wg,
                                     hipStream_t st) {
   const int nch = nch_for(m0.K);
   const int NW = m0.K / (nch * 128);
-  const int MT = B > 16 ? 2 : 1;
+  const int ntiles = m0.ntiles();
+  const int per_chunk = std::max(1, std::min(ntiles, (max_used * ntiles + target_wg - 1) / target_wg));
   MoeArgs a;
   a.t0 = m0.tiles;
   a.t1 = m1 ? m1->tiles : nullptr;
@@ -409,9 +422,9 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, i
   a.used = r.used;
   a.n_used = r.n_used;
   a.out = out;
-  MoeKernel k = gateup ? moe_pick<true>(MT, nch, m0.g, NW) : moe_pick<false>(MT, nch, m0.g, NW);
+  MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);
   const int grid = max_used * a.chunks;
-  const size_t shm = (size_t)(gateup ? 2 : 1) * NW * MT * 1024;
+  const size_t shm = (size_t)(gateup ? 2 : 1) * NW * 1024;
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), shm, st, a);
   (void)E;
   return hipGetLastError();
@@ -419,12 +432,12 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, i
 
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, int E, int B, int max_used, const uint16_t* x,
                              int ldx, const RouteOut& r, uint16_t* act, hipStream_t st) {
-  return launch_moe_common(true, gate0, &up0, E, B, max_used, x, ldx, r, act, 1, st);
+  return launch_moe_common(true, gate0, &up0, E, B, max_used, x, ldx, r, act, 2048, st);
 }
 
 hipError_t launch_moe_down(const Mat& down0, int E, int B, int max_used, const uint16_t* act, const RouteOut& r,
                            uint16_t* y, hipStream_t st) {
-  return launch_moe_common(false, down0, nullptr, E, B, max_used, act, down0.K, r, y, 2, st);
+  return launch_moe_common(false, down0, nullptr, E, B, max_used, act, down0.K, r, y, 4096, st);
 }
 
 }  // namespace w4

@@ -103,8 +103,11 @@ hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const
 }
 
 // moe = fp16(sum_r w_r * y_r) in rank order; resid: h = fp16(h + moe), else h = moe.
-// Then (gamma != null) xn = RMSNorm(h) * gamma.
-__global__ void __launch_bounds__(kNormThreads) k_combine(int H, int k, const float* __restrict__ w,
+// Then (gamma != null) xn = RMSNorm(h) * gamma.  One work-group per row; each
+// thread owns column pairs, so every rank's row is read as coalesced half2.
+constexpr int kCombThreads = 1024;
+
+__global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const float* __restrict__ w,
                                                           const int32_t* __restrict__ inv,
                                                           const uint16_t* __restrict__ y, uint16_t* __restrict__ h,
                                                           int resid, const uint16_t* __restrict__ gamma, float eps,
@@ -118,26 +121,55 @@ __global__ void __launch_bounds__(kNormThreads) k_combine(int H, int k, const fl
     s_w[threadIdx.x] = w[b * k + threadIdx.x];
   }
   __syncthreads();
-  float v[kPer];
+  constexpr int PER = 2;  // H <= 4096 = 2 columns x 2 x 1024 threads
+  float v[2 * PER];
+  float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = threadIdx.x + j * kNormThreads;
-    v[j] = 0.f;
+  for (int j = 0; j < PER; ++j) {
+    const int i = 2 * (threadIdx.x + j * kCombThreads);
+    v[2 * j] = v[2 * j + 1] = 0.f;
     if (i < H) {
-      float acc = 0.f;
-      for (int r = 0; r < k; ++r) acc = acc + s_w[r] * h2f(y[(size_t)s_inv[r] * H + i]);
-      const uint16_t mo = f2h(acc);
-      const uint16_t hv = resid ? f2h(h2f(h[(size_t)b * H + i]) + h2f(mo)) : mo;
-      h[(size_t)b * H + i] = hv;
-      v[j] = h2f(hv);
+      uint32_t yr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r < k) yr[r] = *reinterpret_cast<const uint32_t*>(y + (size_t)s_inv[r] * H + i);
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (r < k) {
+          a0 = a0 + s_w[r] * h2f((uint16_t)(yr[r] & 0xFFFFu));
+          a1 = a1 + s_w[r] * h2f((uint16_t)(yr[r] >> 16));
+        }
+      uint16_t m0 = f2h(a0), m1 = f2h(a1);
+      uint32_t* hp = reinterpret_cast<uint32_t*>(h + (size_t)b * H + i);
+      if (resid) {
+        const uint32_t hv = *hp;
+        m0 = f2h(h2f((uint16_t)(hv & 0xFFFFu)) + h2f(m0));
+        m1 = f2h(h2f((uint16_t)(hv >> 16)) + h2f(m1));
+      }
+      *hp = (uint32_t)m0 | ((uint32_t)m1 << 16);
+      v[2 * j] = h2f(m0);
+      v[2 * j + 1] = h2f(m1);
+      ss = ss + (v[2 * j] * v[2 * j] + v[2 * j + 1] * v[2 * j + 1]);
     }
   }
-  if (gamma) norm_row<kPer>(v, H, gamma, eps, xn + (size_t)b * H, sh);
+  if (!gamma) return;
+  ss = block_sum(ss, sh);
+  const float rr = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = 2 * (threadIdx.x + j * kCombThreads);
+    if (i < H) {
+      const uint16_t o0 = f2h((v[2 * j] * rr) * h2f(gamma[i]));
+      const uint16_t o1 = f2h((v[2 * j + 1] * rr) * h2f(gamma[i + 1]));
+      *reinterpret_cast<uint32_t*>(xn + (size_t)b * H + i) = (uint32_t)o0 | ((uint32_t)o1 << 16);
+    }
+  }
 }
 
 hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* inv, const uint16_t* y, uint16_t* h,
                           bool resid, const uint16_t* gamma, float eps, uint16_t* xn, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(B), dim3(kNormThreads), 0, st, H, k, w, inv, y, h, resid ? 1 : 0, gamma, eps,
+  hipLaunchKernelGGL(k_combine, dim3(B), dim3(kCombThreads), 0, st, H, k, w, inv, y, h, resid ? 1 : 0, gamma, eps,
                      xn);
   return hipGetLastError();
 }
@@ -145,18 +177,20 @@ hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* in
 // ------------------------------------------------------------------ routing
 // One work-group.  Per stream (one wave each, streams strided over waves):
 // k rounds of "largest remaining logit, ties to the lower id", then
-// w_r = exp(l_r - l_0) / sum_r' exp(l_r' - l_0).  Then bucketing: counts,
-// exclusive offsets, used-expert list, and each pair's place in the
-// (expert, stream) order: offsets[e] + #(earlier pairs with expert e).
-constexpr int kRouteMaxPairs = 32 * 16;
+// w_r = exp(l_r - l_0) / sum_r' exp(l_r' - l_0).  Bucketing uses, per expert,
+// the bit mask of the streams (B <= 32) that selected it: count = popcount,
+// a pair's place among the expert's pairs = popcount of the lower streams'
+// bits, and the per-expert offsets are an exclusive scan over experts in
+// expert order.  All integer, so the result is exact and order-free.
 constexpr int kRouteMaxE = 256;
 
 __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits, int B, int E, int k, RouteOut o) {
-  __shared__ int s_ids[kRouteMaxPairs];
-  __shared__ float s_lv[kRouteMaxPairs];
-  __shared__ int s_cnt[kRouteMaxE];
-  __shared__ int s_off[kRouteMaxE + 1];
+  __shared__ int s_ids[32 * 16];
+  __shared__ unsigned s_mask[kRouteMaxE];
+  __shared__ int s_off[kRouteMaxE];
   const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0u;
+  __syncthreads();
   for (int b = w; b < B; b += nw) {
     float v[kRouteMaxE / 64];
     bool taken[kRouteMaxE / 64];
@@ -168,6 +202,8 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
       v[j] = x;
       taken[j] = e >= E;
     }
+    float l0 = 0.f, sum = 0.f, myv = 0.f;
+    int myid = 0;
     for (int r = 0; r < k; ++r) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
@@ -191,63 +227,65 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
 #pragma unroll
       for (int j = 0; j < kRouteMaxE / 64; ++j)
         if (lane + 64 * j == bi) taken[j] = true;
-      if (lane == 0) {
-        s_ids[b * k + r] = bi;
-        s_lv[b * k + r] = bv;
+      if (r == 0) l0 = bv;
+      const float ev = expf(bv - l0);
+      sum = sum + ev;  // rank order, identical in every lane
+      if (lane == r) {
+        myv = ev;
+        myid = bi;
       }
     }
+    if (lane < k) {
+      o.ids[b * k + lane] = myid;
+      o.w[b * k + lane] = myv / sum;
+      s_ids[b * k + lane] = myid;
+      atomicOr(&s_mask[myid], 1u << b);
+    }
+  }
+  __syncthreads();
+  if (w == 0) {  // exclusive scans over experts: offsets and the used-expert list
+    int base = 0, ubase = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = e < E ? __popc(s_mask[e]) : 0;
+      const int u = c > 0;
+      int inc = c, uinc = u;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(inc, d, 64), tu = __shfl_up(uinc, d, 64);
+        if (lane >= d) {
+          inc += t;
+          uinc += tu;
+        }
+      }
+      if (e < E) {
+        s_off[e] = base + inc - c;
+        if (o.counts) o.counts[e] = c;
+        if (o.offsets) o.offsets[e] = base + inc - c;
+        if (u) o.used[ubase + uinc - 1] = e;
+      }
+      base += __shfl(inc, 63, 64);
+      ubase += __shfl(uinc, 63, 64);
+    }
     if (lane == 0) {
-      const float l0 = s_lv[b * k];
-      float ev[16];
-      float sum = 0.f;
-      for (int r = 0; r < k; ++r) {
-        ev[r] = expf(s_lv[b * k + r] - l0);
-        sum = sum + ev[r];
-      }
-      for (int r = 0; r < k; ++r) {
-        o.ids[b * k + r] = s_ids[b * k + r];
-        o.w[b * k + r] = ev[r] / sum;
-      }
+      if (o.offsets) o.offsets[E] = base;
+      *o.n_used = ubase;
     }
   }
   __syncthreads();
   const int P = B * k;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int j = 0; j < P; ++j) c += (s_ids[j] == e);
-    s_cnt[e] = c;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int off = 0, nu = 0;
-    for (int j = 0; j < e; ++j) {
-      off += s_cnt[j];
-      nu += s_cnt[j] > 0;
-    }
-    s_off[e] = off;
-    if (s_cnt[e] > 0) o.used[nu] = e;
-    if (o.counts) o.counts[e] = s_cnt[e];
-    if (o.offsets) o.offsets[e] = off;
-    if (e == E - 1) {
-      s_off[E] = off + s_cnt[e];
-      if (o.offsets) o.offsets[E] = off + s_cnt[e];
-      *o.n_used = nu + (s_cnt[e] > 0);
-    }
-  }
-  __syncthreads();
   for (int i = threadIdx.x; i < P; i += blockDim.x) {
-    const int e = s_ids[i];
-    int rank = 0;
-    for (int j = 0; j < i; ++j) rank += (s_ids[j] == e);
-    const int pos = s_off[e] + rank;
-    if (o.pair_stream) o.pair_stream[pos] = i / k;
-    if (o.pair_rank) o.pair_rank[pos] = i % k;
+    const int b = i / k, e = s_ids[i];
+    const int pos = s_off[e] + __popc(s_mask[e] & ((1u << b) - 1u));
+    if (o.pair_stream) o.pair_stream[pos] = b;
+    if (o.pair_rank) o.pair_rank[pos] = i - b * k;
     o.inv[i] = pos;
   }
 }
 
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st) {
-  hipLaunchKernelGGL(k_route, dim3(1), dim3(1024), 0, st, logits, B, E, k, o);
+  const int threads = 64 * std::min(16, std::max(B, 4));
+  hipLaunchKernelGGL(k_route, dim3(1), dim3(threads), 0, st, logits, B, E, k, o);
   return hipGetLastError();
 }
 

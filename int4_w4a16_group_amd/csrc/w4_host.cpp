@@ -176,6 +176,18 @@ struct w4_ctx {
   std::string err;
   int launches = 0, syncs = 0;
   int last_launches = 0, last_syncs = 0;
+  // kernel timing (w4_profile_begin/end)
+  int prof_kernel = 0;
+  std::vector<hipEvent_t> prof_ev;  // pool, used in (start, stop) pairs
+  size_t prof_used = 0;
+  void prof_record(hipStream_t st) {
+    if (prof_used == prof_ev.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      prof_ev.push_back(e);
+    }
+    (void)hipEventRecord(prof_ev[prof_used++], st);
+  }
 
   template <class T>
   T* W(size_t off) { return reinterpret_cast<T*>(ws + off); }
@@ -289,6 +301,19 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
   return W4_OK;
 }
 
+// Event pair around one launch of the profiled kernel family.
+struct ProfScope {
+  w4_ctx* c;
+  hipStream_t st;
+  bool on;
+  ProfScope(w4_ctx* c_, int kernel, hipStream_t st_) : c(c_), st(st_), on(c_->prof_kernel == kernel) {
+    if (on) c->prof_record(st);
+  }
+  ~ProfScope() {
+    if (on) c->prof_record(st);
+  }
+};
+
 #define LCHK(ctx, n, expr)                                                                      \
   do {                                                                                          \
     hipError_t e_ = (expr);                                                                     \
@@ -308,27 +333,47 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xn, 
   const int32_t* pos = slot + c->Bm;
   KV kv = c->kv();
   uint16_t* qkv = c->W<uint16_t>(c->wp.qkv);
-  LCHK(c, 1, launch_gemm(c->mat(L.qkv), B, xn, H, qkv, nqkv, EPI_F16, st));
+  {
+    ProfScope ps(c, W4_K_DENSE, st);
+    LCHK(c, 1, launch_gemm(c->mat(L.qkv), B, xn, H, qkv, nqkv, EPI_F16, st));
+  }
   LCHK(c, 1, launch_rope_append(B, l, d.n_q_heads, kv, slot, pos, qkv, nqkv, c->W<float2>(c->wp.table),
                                 c->W<uint16_t>(c->wp.q), st));
   LCHK(c, 2, launch_attention(B, l, d.n_q_heads, kv, slot, pos, max_pos, c->W<uint16_t>(c->wp.q),
-                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), c->W<uint16_t>(c->wp.attn_o), st));
-  LCHK(c, 1, launch_gemm(c->mat(L.o), B, c->W<uint16_t>(c->wp.attn_o), qd, h, H, EPI_RESID, st));
+                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), c->W<uint16_t>(c->wp.attn_o), st,
+                              c->prof_kernel == W4_K_ATTENTION ? c : nullptr));
+  {
+    ProfScope ps(c, W4_K_DENSE, st);
+    LCHK(c, 1, launch_gemm(c->mat(L.o), B, c->W<uint16_t>(c->wp.attn_o), qd, h, H, EPI_RESID, st));
+  }
   LCHK(c, 1, launch_rmsnorm(B, H, h, c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn, st));
-  LCHK(c, 1, launch_gemm(c->mat(L.router), B, xn, H, c->W<float>(c->wp.rlogits), d.n_experts, EPI_F32, st));
+  {
+    ProfScope ps(c, W4_K_DENSE, st);
+    LCHK(c, 1, launch_gemm(c->mat(L.router), B, xn, H, c->W<float>(c->wp.rlogits), d.n_experts, EPI_F32, st));
+  }
   RouteOut r = c->route_out(ids_out);
   LCHK(c, 1, launch_route(c->W<float>(c->wp.rlogits), B, d.n_experts, d.top_k, r, st));
   const int max_used = std::min(B * d.top_k, d.n_experts);
-  LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), d.n_experts, B, max_used, xn, H, r,
-                               c->W<uint16_t>(c->wp.act), st));
-  LCHK(c, 1, launch_moe_down(c->mat(L.down), d.n_experts, B, max_used, c->W<uint16_t>(c->wp.act), r,
-                             c->W<uint16_t>(c->wp.y), st));
+  {
+    ProfScope ps(c, W4_K_MOE_GATEUP, st);
+    LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), d.n_experts, B, max_used, xn, H, r,
+                                 c->W<uint16_t>(c->wp.act), st));
+  }
+  {
+    ProfScope ps(c, W4_K_MOE_DOWN, st);
+    LCHK(c, 1, launch_moe_down(c->mat(L.down), d.n_experts, B, max_used, c->W<uint16_t>(c->wp.act), r,
+                               c->W<uint16_t>(c->wp.y), st));
+  }
   LCHK(c, 1, launch_combine(B, H, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), h, true, next_gamma, d.rms_eps,
                             xn, st));
   return W4_OK;
 }
 
 }  // namespace
+
+namespace w4 {
+void prof_mark(void* ctx, hipStream_t st) { static_cast<w4_ctx*>(ctx)->prof_record(st); }
+}  // namespace w4
 
 // =========================================================================== C ABI
 extern "C" {
@@ -378,6 +423,7 @@ int w4_create(const w4_model_desc* d, int32_t max_streams, int32_t cap, void* ar
 
 void w4_destroy(w4_ctx* c) {
   if (!c) return;
+  for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
   if (c->dev_ready) {
     for (int i = 0; i < kRing; ++i)
       if (c->ev[i]) (void)hipEventSynchronize(c->ev[i]), (void)hipEventDestroy(c->ev[i]);
@@ -517,7 +563,10 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
     if (rc) return rc;
   }
   uint16_t* lg = logits ? static_cast<uint16_t*>(logits) : c->W<uint16_t>(c->wp.logits);
-  LCHK(c, 1, launch_gemm(c->mat(c->bp.lm), B, xn, d.hidden, lg, d.vocab, EPI_F16, st));
+  {
+    ProfScope ps(c, W4_K_DENSE, st);
+    LCHK(c, 1, launch_gemm(c->mat(c->bp.lm), B, xn, d.hidden, lg, d.vocab, EPI_F16, st));
+  }
   LCHK(c, 1, launch_argmax(B, d.vocab, lg, next, st));
   for (int b = 0; b < B; ++b) c->pos[slots[b]]++;
   c->last_launches = c->launches - l0;
@@ -622,7 +671,8 @@ int w4_attn_decode(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, co
   LCHK(c, 1, launch_append(B, layer, kv, slot, pos, static_cast<const uint16_t*>(k_new),
                            static_cast<const uint16_t*>(v_new), st));
   LCHK(c, 2, launch_attention(B, layer, c->d.n_q_heads, kv, slot, pos, max_pos, static_cast<const uint16_t*>(q),
-                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), static_cast<uint16_t*>(o), st));
+                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), static_cast<uint16_t*>(o), st,
+                              c->prof_kernel == W4_K_ATTENTION ? c : nullptr));
   return W4_OK;
 }
 
@@ -660,6 +710,31 @@ const char* w4_status_string(int32_t s) {
 }
 
 const char* w4_last_error(const w4_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+int w4_profile_begin(w4_ctx* c, int32_t kernel) {
+  if (!c) return W4_E_INVALID;
+  if (kernel < W4_K_DENSE || kernel > W4_K_ATTENTION) return fail(c, W4_E_INVALID, "unknown kernel family");
+  c->prof_kernel = kernel;
+  c->prof_used = 0;
+  return W4_OK;
+}
+
+int w4_profile_end(w4_ctx* c, double* total_ms, int32_t* launches) {
+  if (!c) return W4_E_INVALID;
+  double ms = 0;
+  const size_t n = c->prof_used / 2;
+  if (n) HIPCHK(c, hipEventSynchronize(c->prof_ev[2 * n - 1]));
+  for (size_t i = 0; i < n; ++i) {
+    float t = 0.f;
+    HIPCHK(c, hipEventElapsedTime(&t, c->prof_ev[2 * i], c->prof_ev[2 * i + 1]));
+    ms += t;
+  }
+  c->prof_kernel = 0;
+  c->prof_used = 0;
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = (int32_t)n;
+  return W4_OK;
+}
 
 int w4_last_step_counts(const w4_ctx* c, int32_t* launches, int32_t* syncs) {
   if (!c) return W4_E_INVALID;

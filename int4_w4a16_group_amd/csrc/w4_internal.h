@@ -84,9 +84,11 @@ hipError_t launch_append(int B, int layer, const KV& kv, const int32_t* slot, co
 hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, const uint16_t* v,
                        hipStream_t st);
 // split-KV decode attention; part_o [B][Hq][nchmax][D] f32, part_ml [B][Hq][nchmax][2].
+// prof: when non-null, an event is recorded (prof_mark) right before and after the chunk pass.
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
                             int max_pos, const uint16_t* q, float* part_o, float* part_ml, uint16_t* o,
-                            hipStream_t st);
+                            hipStream_t st, void* prof = nullptr);
+void prof_mark(void* ctx, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
 
 }  // namespace w4

@@ -69,11 +69,12 @@ def splitmix_key(*ids: int) -> int:
 
 
 def splitmix_bytes(key: int, nbytes: int, start: int = 0, out: np.ndarray | None = None,
-                   threads: int | None = None) -> np.ndarray:
+                   threads: int | None = None, lut: np.ndarray | None = None) -> np.ndarray:
     """Bytes ``start .. start+nbytes`` of the SplitMix64 stream for ``key``.
 
     Output word i is mix(key + (i+1)*golden); its 8 little-endian bytes are
-    stream bytes 8i..8i+7.  ``start`` must be a multiple of 8.
+    stream bytes 8i..8i+7.  ``start`` must be a multiple of 8.  ``lut`` (256
+    bytes) optionally maps every byte afterwards.
     """
     assert start % 8 == 0
     if out is None:
@@ -91,7 +92,7 @@ def splitmix_bytes(key: int, nbytes: int, start: int = 0, out: np.ndarray | None
         b = z.view(np.uint8)
         lo = c0 * 8
         hi = min(c1 * 8, nbytes)
-        out[lo:hi] = b[: hi - lo]
+        out[lo:hi] = b[: hi - lo] if lut is None else lut[b[: hi - lo]]
 
     starts = range(0, nwords, chunk)
     if threads is None:
@@ -172,12 +173,29 @@ class W4Tensor:
         return self.packed.shape[-1] * 2
 
 
+def _zero_mean_lut() -> np.ndarray:
+    b = np.arange(256)
+    lo, hi = b & 15, b >> 4
+    lo = np.where(lo == 8, 0, lo)
+    hi = np.where(hi == 8, 0, hi)
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+ZERO_MEAN_LUT = _zero_mean_lut()
+
+
 def w4_tensor(seed: int, tag: int, stag: int, lead: tuple, n: int, k: int, g: int,
-              ids: tuple = (), scale_lo: float = 0.005, scale_hi: float = 0.02) -> W4Tensor:
-    """Uniform int4 codes in [-8, 7] and fp16 scales ~ U(lo, hi) (float64 draw, RNE)."""
+              ids: tuple = (), scale_lo: float = 0.005, scale_hi: float = 0.02, codes: str = "uniform") -> W4Tensor:
+    """int4 codes and fp16 scales ~ U(lo, hi) (float64 draw, RNE).
+
+    codes="uniform": every code in [-8, 7] equally likely (mean -1/2).
+    codes="zero_mean": the uniform draw with code -8 replaced by 0, so codes
+    lie in [-7, 7], symmetric, mean 0 (P(0) = 2/16, the others 1/16 each)."""
     shape = tuple(lead) + (n, k // 2)
     nbytes = int(np.prod(shape))
-    packed = splitmix_bytes(splitmix_key(seed, tag, *ids), nbytes).reshape(shape)
+    lut = ZERO_MEAN_LUT if codes == "zero_mean" else None
+    assert codes in ("uniform", "zero_mean")
+    packed = splitmix_bytes(splitmix_key(seed, tag, *ids), nbytes, lut=lut).reshape(shape)
     scales = uniform_f16(rng(seed, stag, *ids), scale_lo, scale_hi, tuple(lead) + (n, k // g))
     return W4Tensor(packed, scales)
 
@@ -225,28 +243,33 @@ class ModelWeights:
 ONE_F16 = 0x3C00
 
 
-def make_layer(desc: ModelDesc, seed: int, layer: int) -> LayerWeights:
+def make_layer(desc: ModelDesc, seed: int, layer: int, codes: str = "uniform") -> LayerWeights:
     d, g = desc, desc.group
     H, E, I = d.hidden, d.n_experts, d.moe_inter
     ones = np.full(H, ONE_F16, dtype=np.uint16)    # RMSNorm gain 1 (random-init reading)
+    c = dict(codes=codes)
     return LayerWeights(
         attn_norm=ones.copy(),
-        qkv=w4_tensor(seed, T_QKV, T_QKV_S, (), d.n_qkv, H, g, (layer,)),
-        o=w4_tensor(seed, T_O, T_O_S, (), H, d.q_dim, g, (layer,)),
+        qkv=w4_tensor(seed, T_QKV, T_QKV_S, (), d.n_qkv, H, g, (layer,), **c),
+        o=w4_tensor(seed, T_O, T_O_S, (), H, d.q_dim, g, (layer,), **c),
         moe_norm=ones.copy(),
-        router=w4_tensor(seed, T_ROUTER, T_ROUTER_S, (), E, H, g, (layer,)),
-        gate=w4_tensor(seed, T_GATE, T_GATE_S, (E,), I, H, g, (layer,)),
-        up=w4_tensor(seed, T_UP, T_UP_S, (E,), I, H, g, (layer,)),
-        down=w4_tensor(seed, T_DOWN, T_DOWN_S, (E,), H, I, g, (layer,)),
+        router=w4_tensor(seed, T_ROUTER, T_ROUTER_S, (), E, H, g, (layer,), **c),
+        gate=w4_tensor(seed, T_GATE, T_GATE_S, (E,), I, H, g, (layer,), **c),
+        up=w4_tensor(seed, T_UP, T_UP_S, (E,), I, H, g, (layer,), **c),
+        down=w4_tensor(seed, T_DOWN, T_DOWN_S, (E,), H, I, g, (layer,), **c),
     )
 
 
-def make_model(desc: ModelDesc, seed: int = 0, with_vocab: bool = True) -> ModelWeights:
-    layers = [make_layer(desc, seed, l) for l in range(desc.n_layers)]
+def make_model(desc: ModelDesc, seed: int = 0, with_vocab: bool = True, codes: str = "uniform") -> ModelWeights:
+    """codes="zero_mean" is the full random-init model's reading: the uniform
+    [-8, 7] draw has mean -1/2, which adds the same direction to every
+    projection's output for every stream; through the layers it comes to
+    dominate the router input and every stream picks the same few experts."""
+    layers = [make_layer(desc, seed, l, codes) for l in range(desc.n_layers)]
     emb = lm = fn = None
     if with_vocab:
-        emb = w4_tensor(seed, T_EMBED, T_EMBED_S, (), desc.vocab, desc.hidden, desc.group)
-        lm = w4_tensor(seed, T_LM, T_LM_S, (), desc.vocab, desc.hidden, desc.group)
+        emb = w4_tensor(seed, T_EMBED, T_EMBED_S, (), desc.vocab, desc.hidden, desc.group, codes=codes)
+        lm = w4_tensor(seed, T_LM, T_LM_S, (), desc.vocab, desc.hidden, desc.group, codes=codes)
         fn = np.full(desc.hidden, ONE_F16, dtype=np.uint16)
     return ModelWeights(desc, layers, emb, fn, lm)
 

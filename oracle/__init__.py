@@ -68,6 +68,7 @@ def lib():
                                       C.c_void_p, _i32p, C.c_void_p, C.c_void_p]
         L.orc_attn_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
                                     _u16p, _u16p, _u16p, _u16p]
+        L.orc_threads.restype = C.c_int
         L.orc_init()
         _lib = L
     return _lib
@@ -80,6 +81,10 @@ def _c(a, dt):
 
 def _ptr(a):
     return None if a is None else a.ctypes.data
+
+
+def threads() -> int:
+    return lib().orc_threads()
 
 
 # ---------------------------------------------------------------- primitives

@@ -24,7 +24,20 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 #define EXPORT __attribute__((visibility("default")))
+
+/* Threads the oracle's parallel loops use (1 without OpenMP). */
+EXPORT int orc_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* IEEE 754 binary16 <-> binary32, round to nearest, ties to even.           */

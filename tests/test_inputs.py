@@ -56,3 +56,16 @@ def test_ragged_schedule_changes_batch_often():
     assert min(sizes) >= 1 and max(sizes) <= 16
     changes = sum(1 for i in range(1, len(sizes)) if sizes[i] != sizes[i - 1])
     assert changes >= 10
+
+
+def test_zero_mean_codes():
+    w = inputs.w4_tensor(0, inputs.T_GATE, inputs.T_GATE_S, (), 256, 2048, 128, codes="zero_mean")
+    c = inputs.unpack_codes(w.packed)
+    assert c.min() == -7 and c.max() == 7
+    counts = np.bincount(c.ravel() + 8, minlength=16)
+    assert counts[0] == 0
+    assert abs(c.mean()) < 0.01 and abs(counts[8] / c.size - 2 / 16) < 0.002
+    u = inputs.w4_tensor(0, inputs.T_GATE, inputs.T_GATE_S, (), 256, 2048, 128)
+    # same draw: only the -8 codes differ
+    cu = inputs.unpack_codes(u.packed)
+    assert np.array_equal(np.where(cu == -8, 0, cu), c)
