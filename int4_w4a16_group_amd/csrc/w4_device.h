@@ -19,15 +19,40 @@ __device__ __forceinline__ f4 mfma16x16x32(const h8& a, const h8& b, const f4& c
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// One repacked dword (8 offset-binary codes, see Mat in w4_internal.h) to the
-// 8 fp16 codes of k = k0 .. k0+7 in order.  (1024 + u) - 1032 = u - 8 = code,
-// exact in fp16.
-__device__ __forceinline__ h8 dq8(uint32_t w) {
+// One repacked dword (8 offset-binary codes u = code + 8, see Mat in
+// w4_internal.h: nibble j holds element 2j, nibble j+4 holds element 2j+1) to
+// the 8 fp16 codes of k = k0 .. k0+7 in order, 9 VALU operations:
+//   pair (2j, 2j+1) for j = 0, 2: (w' & 0x000F000F) | 0x6400 6400 is the fp16
+//     pair (1024 + u, 1024 + u'), minus 1032 gives the codes;
+//   pair for j = 1, 3: (w' & 0x00F000F0) | 0x6400 6400 is (1024 + 16u, ...),
+//     times 1/16 minus 72 (one fma) gives the codes;
+// with w' = w for j = 0, 1 and w >> 8 for j = 2, 3.  Every step is exact in
+// fp16 (integers below 2048, a power-of-two scale, one rounding of an exact
+// integer result).  The masks sit in VGPRs so each and-or is one v_and_or_b32
+// (two literal operands would not encode in one VOP3 instruction).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t vmask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(vmask), "s"(magic));
+  return r;
+}
+
+struct DqConst {
+  uint32_t m_lo, m_hi;  // 0x000F000F, 0x00F000F0 held in VGPRs
+  __device__ __forceinline__ DqConst() {
+    asm("v_mov_b32 %0, 0x000F000F" : "=v"(m_lo));
+    asm("v_mov_b32 %0, 0x00F000F0" : "=v"(m_hi));
+  }
+};
+
+__device__ __forceinline__ h8 dq8(uint32_t w, const DqConst& k) {
   const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const h2 p0 = __builtin_bit_cast(h2, (w & 0x000F000Fu) | 0x64006400u) + bias;
-  const h2 p1 = __builtin_bit_cast(h2, ((w >> 4) & 0x000F000Fu) | 0x64006400u) + bias;
-  const h2 p2 = __builtin_bit_cast(h2, ((w >> 8) & 0x000F000Fu) | 0x64006400u) + bias;
-  const h2 p3 = __builtin_bit_cast(h2, ((w >> 12) & 0x000F000Fu) | 0x64006400u) + bias;
+  const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const h2 bias16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t ws = w >> 8;
+  const h2 p0 = __builtin_bit_cast(h2, and_or(w, k.m_lo, 0x64006400u)) + bias;
+  const h2 p1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w, k.m_hi, 0x64006400u)), sixteenth, bias16);
+  const h2 p2 = __builtin_bit_cast(h2, and_or(ws, k.m_lo, 0x64006400u)) + bias;
+  const h2 p3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(ws, k.m_hi, 0x64006400u)), sixteenth, bias16);
   return h8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 

@@ -95,7 +95,8 @@ struct XRegs {
 // n = 16t + lane%16); acc[mt] += over groups fma(scale, MFMA chain).
 template <int MT, int NCH, int G>
 __device__ __forceinline__ void tile_mac(const XRegs<MT, NCH * 4>& x, const uint4 (&wv)[NCH],
-                                         const float (&sv)[NCH * 128 / G], f4 (&acc)[MT], int mts) {
+                                         const float (&sv)[NCH * 128 / G], f4 (&acc)[MT], int mts,
+                                         const DqConst& dk) {
   constexpr int SPG = G / 32;
   f4 part[MT];
 #pragma unroll
@@ -104,7 +105,7 @@ __device__ __forceinline__ void tile_mac(const XRegs<MT, NCH * 4>& x, const uint
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int ks = c * 4 + s;
-      const h8 b = dq8(wd[s]);
+      const h8 b = dq8(wd[s], dk);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (ks % SPG == 0) part[mt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -139,6 +140,33 @@ __device__ __forceinline__ void load_scales(const uint16_t* __restrict__ scales,
 #pragma unroll
   for (int i = 0; i < NCH * 128 / G; ++i) sv[i] = h2f(p[i]);
 }
+
+// One pipeline stage: a tile's weight chunks and raw scale bits for this wave's
+// K slice (scales kept as the loaded dwords, two fp16 per dword, and only
+// unpacked when the stage is used), so the loads stay in flight while the
+// other stage is computed.
+template <int NCH, int G>
+struct Stage {
+  static constexpr int NS = NCH * 128 / G;       // scales per lane per tile
+  static constexpr int ND = NS >= 2 ? NS / 2 : 1;  // dwords holding them
+  uint4 w[NCH];
+  uint32_t s[ND];
+  __device__ __forceinline__ void load(const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales, int K,
+                                       int t, int wv, int lane) {
+    load_tile<NCH>(tiles, K, t, wv, lane, w);
+    const uint16_t* p = scales + (size_t)(t * 16 + (lane & 15)) * (K / G) + (size_t)wv * NS;
+    if (NS >= 2) {
+#pragma unroll
+      for (int i = 0; i < ND; ++i) s[i] = reinterpret_cast<const uint32_t*>(p)[i];
+    } else {
+      s[0] = p[0];
+    }
+  }
+  __device__ __forceinline__ void scales_f32(float (&sv)[NS]) const {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) sv[i] = h2f((uint16_t)(s[i / 2] >> (16 * (i & 1))));
+  }
+};
 
 // A-operand rows: row i of the tile reads rowptr(i) (nullptr = zero row).
 template <int MT, int NCH, class RowPtr>
@@ -181,34 +209,33 @@ struct DenseArgs {
 
 template <int MT, int NCH, int G, int EPI, int LB>
 __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
-  extern __shared__ float red[];
+  extern __shared__ float red[];  // two buffers of [NW][MT][64][4]
+  constexpr int NS = NCH * 128 / G;
   const int NW = blockDim.x >> 6;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kbase = w * NCH * 128;
+  const int G0 = gridDim.x;
+  if ((int)blockIdx.x >= a.ntiles) return;
   XRegs<MT, NCH * 4> x;
   load_x<MT, NCH>(x, [&](int row) -> const uint16_t* { return row < a.B ? a.x + (size_t)row * a.ldx : nullptr; },
                   kbase, lane);
   const int mts = (a.B + 15) >> 4;
-  int t = blockIdx.x;
-  if (t >= a.ntiles) return;
-  uint4 wv[NCH];
-  load_tile<NCH>(a.tiles, a.K, t, w, lane, wv);
-  for (; t < a.ntiles; t += gridDim.x) {
-    const int tn = t + gridDim.x;
-    uint4 wn[NCH];
-    if (tn < a.ntiles) load_tile<NCH>(a.tiles, a.K, tn, w, lane, wn);
-    float sv[NCH * 128 / G];
-    load_scales<NCH, G>(a.scales, a.K, t, w, lane, sv);
+  const DqConst dk;
+  int buf = 0;
+  auto run = [&](const Stage<NCH, G>& st, int t, bool valid) {
+    float sv[NS];
+    st.scales_f32(sv);
     f4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
-    tile_mac<MT, NCH, G>(x, wv, sv, acc, mts);
+    tile_mac<MT, NCH, G>(x, st.w, sv, acc, mts, dk);
+    float* rb = red + buf * NW * MT * 256;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(red)[(w * MT + mt) * 64 + lane] = acc[mt];
-    __syncthreads();
-    reduce_tile<MT>(red, NW, [&](int row, int j, float v) {
+    for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(rb)[(w * MT + mt) * 64 + lane] = acc[mt];
+    __syncthreads();  // partials of this tile visible; the other buffer's readers are done
+    reduce_tile<MT>(rb, NW, [&](int row, int j, float v) {
       const int n = t * 16 + j;
-      if (row < a.B && n < a.N) {
+      if (valid && row < a.B && n < a.N) {
         if (EPI == EPI_F32) {
           reinterpret_cast<float*>(a.y)[(size_t)row * a.ldy + n] = v;
         } else if (EPI == EPI_F16) {
@@ -219,9 +246,24 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
         }
       }
     });
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) wv[c] = wn[c];
+    buf ^= 1;
+  };
+  // this work-group's tiles: blockIdx.x + i*G0, i < n; processed in pairs,
+  // with every load issued unconditionally (indices clamped to the last tile)
+  const int n = (a.ntiles - (int)blockIdx.x + G0 - 1) / G0;
+  const int last = blockIdx.x + (n - 1) * G0;
+  Stage<NCH, G> sa, sb;
+  sa.load(a.tiles, a.scales, a.K, blockIdx.x, w, lane);
+  if (n == 1) {
+    run(sa, blockIdx.x, true);
+    return;
+  }
+  for (int i = 0; i < n; i += 2) {
+    const int ta = blockIdx.x + i * G0, tb = ta + G0;
+    sb.load(a.tiles, a.scales, a.K, min(tb, last), w, lane);
+    run(sa, ta, true);
+    sa.load(a.tiles, a.scales, a.K, min(tb + G0, last), w, lane);
+    run(sb, tb, i + 1 < n);
   }
 }
 
@@ -267,7 +309,7 @@ hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y,
   const int target = std::max(1, 4096 / NW);
   const int grid = std::min(ntiles, target);
   DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy};
-  hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), NW * MT * 1024, st, a);
+  hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), 2 * NW * MT * 1024, st, a);
   return hipGetLastError();
 }
 
@@ -280,40 +322,51 @@ struct MoeArgs {
   int N, K, ntiles;       // per expert
   size_t tile_stride;     // uint4 per expert
   size_t scale_stride;    // halves per expert
-  int chunks, per_chunk;  // tile chunks per expert
   const uint16_t* x;      // gate/up: rows by stream; down: rows by pair
   int ldx;
   const int32_t* offsets;
   const int32_t* pair_stream;
-  const int32_t* used;
-  const int32_t* n_used;
+  const int2* units;      // (expert, first row) of every 16-row unit, experts ascending
+  const int32_t* n_units;
   uint16_t* out;          // [pairs][N]
 };
 
-// One work-group per (used expert, chunk of column tiles); its NW waves own
-// the K slices.  Rows are the expert's pairs, 16 at a time (an expert with
-// more than 16 rows repeats the chunk for each 16-row tile; the arithmetic of
-// a row is the same in every tile).  The x slice of a row tile stays in
-// registers for the whole chunk; the next tile's weights are loaded before the
-// current tile is reduced.
+// Persistent grouped GEMM.  The work is the flattened list of (unit, column
+// tile) items, unit = 16 rows of one used expert (the routing kernel builds
+// the unit list on the device); work-group i takes items
+// [i*total/grid, (i+1)*total/grid), so every work-group gets the same share
+// whatever the routing.  Its NW waves own the K slices (as in the dense
+// product); the x slice of the current unit stays in registers; tiles go
+// through two register stages, the next tile's loads in flight while the
+// current one is multiplied and reduced.  The arithmetic of an output does
+// not depend on which work-group computes it.
 template <int NCH, int G, bool GATEUP, int LB>
 __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
-  extern __shared__ float red[];
+  extern __shared__ float red[];  // two buffers of [GATEUP ? 2 : 1][NW][64][4]
+  constexpr int NS = NCH * 128 / G;
   const int NW = blockDim.x >> 6;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int u = blockIdx.x / a.chunks, ch = blockIdx.x - u * a.chunks;
-  if (u >= *a.n_used) return;
-  const int e = a.used[u];
-  const int off = a.offsets[e];
-  const int m = a.offsets[e + 1] - off;
+  const int T = a.ntiles;
+  const long long total = (long long)(*a.n_units) * T;
+  const int f_begin = (int)(blockIdx.x * total / gridDim.x);
+  const int f_end = (int)((blockIdx.x + 1) * total / gridDim.x);
   const int kbase = w * NCH * 128;
-  const uint4* T0 = a.t0 + a.tile_stride * e;
-  const uint4* T1 = GATEUP ? a.t1 + a.tile_stride * e : nullptr;
-  const uint16_t* S0 = a.s0 + a.scale_stride * e;
-  const uint16_t* S1 = GATEUP ? a.s1 + a.scale_stride * e : nullptr;
-  const int t_begin = ch * a.per_chunk;
-  const int t_end = min(t_begin + a.per_chunk, a.ntiles);
-  for (int r0 = 0; r0 < m; r0 += 16) {
+  const int bufsz = (GATEUP ? 2 : 1) * NW * 256;
+  const DqConst dk;
+  int buf = 0;
+  for (int f = f_begin; f < f_end;) {
+    const int unit = f / T;
+    const int t0 = f - unit * T;
+    const int t1 = min(T, t0 + (f_end - f));  // this work-group's tiles of this unit: [t0, t1)
+    f += t1 - t0;
+    const int2 un = a.units[unit];
+    const int e = un.x, r0 = un.y;
+    const int off = a.offsets[e];
+    const int m = a.offsets[e + 1] - off;
+    const uint4* T0 = a.t0 + a.tile_stride * e;
+    const uint4* T1 = GATEUP ? a.t1 + a.tile_stride * e : nullptr;
+    const uint16_t* S0 = a.s0 + a.scale_stride * e;
+    const uint16_t* S1 = GATEUP ? a.s1 + a.scale_stride * e : nullptr;
     XRegs<1, NCH * 4> x;
     load_x<1, NCH>(
         x,
@@ -323,56 +376,57 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
           return a.x + (size_t)row * a.ldx;
         },
         kbase, lane);
-    uint4 w0[NCH], w1[NCH];
-    load_tile<NCH>(T0, a.K, t_begin, w, lane, w0);
-    if (GATEUP) load_tile<NCH>(T1, a.K, t_begin, w, lane, w1);
-    for (int t = t_begin; t < t_end; ++t) {
-      uint4 n0[NCH], n1[NCH];
-      if (t + 1 < t_end) {
-        load_tile<NCH>(T0, a.K, t + 1, w, lane, n0);
-        if (GATEUP) load_tile<NCH>(T1, a.K, t + 1, w, lane, n1);
-      }
-      float s0[NCH * 128 / G], s1[NCH * 128 / G];
-      load_scales<NCH, G>(S0, a.K, t, w, lane, s0);
-      if (GATEUP) load_scales<NCH, G>(S1, a.K, t, w, lane, s1);
+    auto run = [&](const Stage<NCH, G>& g0, const Stage<NCH, G>& g1, int t, bool valid) {
+      float sv0[NS], sv1[NS];
+      g0.scales_f32(sv0);
       f4 acc0[1] = {f4{0.f, 0.f, 0.f, 0.f}}, acc1[1] = {f4{0.f, 0.f, 0.f, 0.f}};
-      tile_mac<1, NCH, G>(x, w0, s0, acc0, 1);
-      if (GATEUP) tile_mac<1, NCH, G>(x, w1, s1, acc1, 1);
-      f4* r4 = reinterpret_cast<f4*>(red);
+      tile_mac<1, NCH, G>(x, g0.w, sv0, acc0, 1, dk);
+      if (GATEUP) {
+        g1.scales_f32(sv1);
+        tile_mac<1, NCH, G>(x, g1.w, sv1, acc1, 1, dk);
+      }
+      float* rb = red + buf * bufsz;
+      f4* r4 = reinterpret_cast<f4*>(rb);
       r4[w * 64 + lane] = acc0[0];
       if (GATEUP) r4[(NW + w) * 64 + lane] = acc1[0];
-      __syncthreads();
+      __syncthreads();  // this tile's partials visible; the other buffer's readers are done
       if (GATEUP) {
-        const float* red1 = red + NW * 256;
+        const float* red1 = rb + NW * 256;
         for (int o = threadIdx.x; o < 256; o += blockDim.x) {
           const int i = o >> 4, j = o & 15;
           const int idx = ((i >> 2) * 16 + j) * 4 + (i & 3);
-          float vg = red[idx], vu = red1[idx];
+          float vg = rb[idx], vu = red1[idx];
           for (int ww = 1; ww < NW; ++ww) {
-            vg = vg + red[ww * 256 + idx];
+            vg = vg + rb[ww * 256 + idx];
             vu = vu + red1[ww * 256 + idx];
           }
           const int row = r0 + i, n = t * 16 + j;
-          if (row < m && n < a.N) {
+          if (valid && row < m && n < a.N) {
             const float gt = h2f(f2h(vg)), up = h2f(f2h(vu));
             const float silu = gt / (1.0f + expf(-gt));
             a.out[(size_t)(off + row) * a.N + n] = f2h(silu * up);
           }
         }
       } else {
-        reduce_tile<1>(red, NW, [&](int i, int j, float v) {
+        reduce_tile<1>(rb, NW, [&](int i, int j, float v) {
           const int row = r0 + i, n = t * 16 + j;
-          if (row < m && n < a.N) a.out[(size_t)(off + row) * a.N + n] = f2h(v);
+          if (valid && row < m && n < a.N) a.out[(size_t)(off + row) * a.N + n] = f2h(v);
         });
       }
-      __syncthreads();
-      if (t + 1 < t_end) {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          w0[c] = n0[c];
-          if (GATEUP) w1[c] = n1[c];
-        }
-      }
+      buf ^= 1;
+    };
+    // tiles t0 .. t1-1 in pairs; loads unconditional, indices clamped to t1-1
+    Stage<NCH, G> a0, a1, b0, b1;
+    a0.load(T0, S0, a.K, t0, w, lane);
+    if (GATEUP) a1.load(T1, S1, a.K, t0, w, lane);
+    for (int t = t0; t < t1; t += 2) {
+      const int tb = min(t + 1, t1 - 1), tn = min(t + 2, t1 - 1);
+      b0.load(T0, S0, a.K, tb, w, lane);
+      if (GATEUP) b1.load(T1, S1, a.K, tb, w, lane);
+      run(a0, a1, t, true);
+      a0.load(T0, S0, a.K, tn, w, lane);
+      if (GATEUP) a1.load(T1, S1, a.K, tn, w, lane);
+      run(b0, b1, t + 1, t + 1 < t1);
     }
   }
 }
@@ -393,16 +447,35 @@ static MoeKernel moe_pick(int nch, int g, int nw) {
   return nch == 2 ? moe_pick_g<GU, 2, 1024>(g) : moe_pick_g<GU, 1, 1024>(g);
 }
 
-// Column tiles per work-group: enough work-groups to cover the chip
-// (target_wg) when max_used experts are busy, and the x slice of a row tile is
-// loaded once per chunk.
-static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, int E, int B, int max_used,
-                                    const uint16_t* x, int ldx, const RouteOut& r, uint16_t* out, int target_wg,
-                                    hipStream_t st) {
+// Grid = the number of work-groups the device keeps resident at once
+// (occupancy query, cached per kernel), so the persistent loop covers the
+// whole chip in one round.
+static int resident_grid(MoeKernel k, int threads, size_t shm) {
+  struct Entry {
+    MoeKernel k;
+    int threads;
+    int grid;
+  };
+  static Entry cache[64];
+  static int n = 0;
+  for (int i = 0; i < n; ++i)
+    if (cache[i].k == k && cache[i].threads == threads) return cache[i].grid;
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), threads, shm) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  const int grid = per_cu * cus;
+  if (n < 64) cache[n++] = Entry{k, threads, grid};
+  return grid;
+}
+
+static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, const uint16_t* x, int ldx,
+                                    const RouteOut& r, uint16_t* out, hipStream_t st) {
   const int nch = nch_for(m0.K);
   const int NW = m0.K / (nch * 128);
-  const int ntiles = m0.ntiles();
-  const int per_chunk = std::max(1, std::min(ntiles, (max_used * ntiles + target_wg - 1) / target_wg));
   MoeArgs a;
   a.t0 = m0.tiles;
   a.t1 = m1 ? m1->tiles : nullptr;
@@ -413,31 +486,27 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, i
   a.ntiles = m0.ntiles();
   a.tile_stride = (size_t)m0.Np() / 16 * (m0.K / 128) * 64;
   a.scale_stride = (size_t)m0.Np() * (m0.K / m0.g);
-  a.per_chunk = per_chunk;
-  a.chunks = (a.ntiles + per_chunk - 1) / per_chunk;
   a.x = x;
   a.ldx = ldx;
   a.offsets = r.offsets;
   a.pair_stream = r.pair_stream;
-  a.used = r.used;
-  a.n_used = r.n_used;
+  a.units = r.units;
+  a.n_units = r.n_units;
   a.out = out;
   MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);
-  const int grid = max_used * a.chunks;
-  const size_t shm = (size_t)(gateup ? 2 : 1) * NW * 1024;
+  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024;
+  const int grid = resident_grid(k, NW * 64, shm);
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), shm, st, a);
-  (void)E;
   return hipGetLastError();
 }
 
-hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, int E, int B, int max_used, const uint16_t* x,
-                             int ldx, const RouteOut& r, uint16_t* act, hipStream_t st) {
-  return launch_moe_common(true, gate0, &up0, E, B, max_used, x, ldx, r, act, 2048, st);
+hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
+                             uint16_t* act, hipStream_t st) {
+  return launch_moe_common(true, gate0, &up0, x, ldx, r, act, st);
 }
 
-hipError_t launch_moe_down(const Mat& down0, int E, int B, int max_used, const uint16_t* act, const RouteOut& r,
-                           uint16_t* y, hipStream_t st) {
-  return launch_moe_common(false, down0, nullptr, E, B, max_used, act, down0.K, r, y, 4096, st);
+hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st) {
+  return launch_moe_common(false, down0, nullptr, act, down0.K, r, y, st);
 }
 
 }  // namespace w4

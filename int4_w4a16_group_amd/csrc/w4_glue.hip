@@ -243,19 +243,21 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
     }
   }
   __syncthreads();
-  if (w == 0) {  // exclusive scans over experts: offsets and the used-expert list
-    int base = 0, ubase = 0;
+  if (w == 0) {  // exclusive scans over experts: offsets, used experts, 16-row units
+    int base = 0, ubase = 0, nbase = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + lane;
       const int c = e < E ? __popc(s_mask[e]) : 0;
       const int u = c > 0;
-      int inc = c, uinc = u;
+      const int nu = (c + 15) >> 4;
+      int inc = c, uinc = u, ninc = nu;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(inc, d, 64), tu = __shfl_up(uinc, d, 64);
+        const int t = __shfl_up(inc, d, 64), tu = __shfl_up(uinc, d, 64), tn = __shfl_up(ninc, d, 64);
         if (lane >= d) {
           inc += t;
           uinc += tu;
+          ninc += tn;
         }
       }
       if (e < E) {
@@ -263,13 +265,16 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
         if (o.counts) o.counts[e] = c;
         if (o.offsets) o.offsets[e] = base + inc - c;
         if (u) o.used[ubase + uinc - 1] = e;
+        for (int j = 0; j < nu; ++j) o.units[nbase + ninc - nu + j] = make_int2(e, 16 * j);
       }
       base += __shfl(inc, 63, 64);
       ubase += __shfl(uinc, 63, 64);
+      nbase += __shfl(ninc, 63, 64);
     }
     if (lane == 0) {
       if (o.offsets) o.offsets[E] = base;
       *o.n_used = ubase;
+      *o.n_units = nbase;
     }
   }
   __syncthreads();

@@ -43,7 +43,7 @@ struct BankPlan {
 
 struct WsPlan {
   size_t h, xn, qkv, q, attn_o, part_o, part_ml, rlogits, ids, w, counts, offsets, pair_stream, pair_rank, inv,
-      used, n_used, act, y, logits, next, rows, table, total;
+      used, n_used, units, n_units, act, y, logits, next, rows, table, total;
 };
 
 bool geometry_ok(const w4_model_desc* d, std::string* why) {
@@ -145,6 +145,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.inv = take(Bm * k * 4);
   w.used = take(E * 4);
   w.n_used = take(4);
+  w.units = take((E + Bm * k / 16 + 1) * 8);
+  w.n_units = take(4);
   w.act = take(Bm * k * I * 2);
   w.y = take(Bm * k * H * 2);
   w.logits = take((size_t)Bm * d.vocab * 2);
@@ -225,6 +227,8 @@ struct w4_ctx {
     r.inv = W<int32_t>(wp.inv);
     r.used = W<int32_t>(wp.used);
     r.n_used = W<int32_t>(wp.n_used);
+    r.units = W<int2>(wp.units);
+    r.n_units = W<int32_t>(wp.n_units);
     return r;
   }
 };
@@ -353,16 +357,13 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xn, 
   }
   RouteOut r = c->route_out(ids_out);
   LCHK(c, 1, launch_route(c->W<float>(c->wp.rlogits), B, d.n_experts, d.top_k, r, st));
-  const int max_used = std::min(B * d.top_k, d.n_experts);
   {
     ProfScope ps(c, W4_K_MOE_GATEUP, st);
-    LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), d.n_experts, B, max_used, xn, H, r,
-                                 c->W<uint16_t>(c->wp.act), st));
+    LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), xn, H, r, c->W<uint16_t>(c->wp.act), st));
   }
   {
     ProfScope ps(c, W4_K_MOE_DOWN, st);
-    LCHK(c, 1, launch_moe_down(c->mat(L.down), d.n_experts, B, max_used, c->W<uint16_t>(c->wp.act), r,
-                               c->W<uint16_t>(c->wp.y), st));
+    LCHK(c, 1, launch_moe_down(c->mat(L.down), c->W<uint16_t>(c->wp.act), r, c->W<uint16_t>(c->wp.y), st));
   }
   LCHK(c, 1, launch_combine(B, H, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), h, true, next_gamma, d.rms_eps,
                             xn, st));
@@ -642,11 +643,8 @@ int w4_moe(w4_ctx* c, int32_t layer, int32_t B, const void* x, const float* rout
   }
   RouteOut r = c->route_out(route_ids);
   LCHK(c, 1, launch_route(lg, B, d.n_experts, d.top_k, r, st));
-  const int max_used = std::min(B * d.top_k, d.n_experts);
-  LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), d.n_experts, B, max_used, xh, d.hidden, r,
-                               c->W<uint16_t>(c->wp.act), st));
-  LCHK(c, 1, launch_moe_down(c->mat(L.down), d.n_experts, B, max_used, c->W<uint16_t>(c->wp.act), r,
-                             c->W<uint16_t>(c->wp.y), st));
+  LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), xh, d.hidden, r, c->W<uint16_t>(c->wp.act), st));
+  LCHK(c, 1, launch_moe_down(c->mat(L.down), c->W<uint16_t>(c->wp.act), r, c->W<uint16_t>(c->wp.y), st));
   LCHK(c, 1, launch_combine(B, d.hidden, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), static_cast<uint16_t*>(y),
                             false, nullptr, d.rms_eps, nullptr, st));
   return W4_OK;

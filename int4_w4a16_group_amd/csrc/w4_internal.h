@@ -48,14 +48,15 @@ struct RouteOut {
   int32_t* inv;          // [B][k] position of pair (b, r) in expert order
   int32_t* used;         // [E] used experts, ascending
   int32_t* n_used;       // [1]
+  int2* units;           // [E + B*k/16] (expert, first row) per 16-row unit of each used expert
+  int32_t* n_units;      // [1]
 };
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st);
 
-// Grouped expert GEMMs over the bucketed pairs.  max_used bounds the grid.
-hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, int E, int B, int max_used,
-                             const uint16_t* x, int ldx, const RouteOut& r, uint16_t* act, hipStream_t st);
-hipError_t launch_moe_down(const Mat& down0, int E, int B, int max_used, const uint16_t* act,
-                           const RouteOut& r, uint16_t* y, hipStream_t st);
+// Grouped expert GEMMs over the bucketed pairs (persistent, work list from route).
+hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
+                             uint16_t* act, hipStream_t st);
+hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st);
 // h[b] = fp16(h[b] + fp16(sum_r w[b][r] * y[inv[b][r]]))  (resid), or out = fp16(sum ...) (no resid);
 // then optionally xn[b] = RMSNorm(h[b]) * gamma.
 hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* inv, const uint16_t* y,
