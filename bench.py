@@ -47,6 +47,8 @@ def main():
     ap.add_argument("--cpu-streams", type=int, default=4, help="streams in the oracle's timed sample")
     ap.add_argument("--cpu-steps", type=int, default=2, help="decode steps in the oracle's timed sample")
     ap.add_argument("--profile", choices=("on", "off"), default="on", help="HIP-event kernel timing passes")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 512 MiB device-to-device copy first (a known-size reference for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
@@ -62,6 +64,14 @@ def main():
         from int4_w4a16_group_amd import build
         build.build()
     dev = torch.device("cuda:0")
+    if args.calib_copy:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("calibration copy: 512 MiB read + 512 MiB written")
     d = inputs.FULL
     batches = [int(b) for b in args.batches.split(",")]
     Bmax, cap = 32, 4096

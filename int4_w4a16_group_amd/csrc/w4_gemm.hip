@@ -205,9 +205,14 @@ struct DenseArgs {
   int ldx, B;
   void* y;
   int ldy;
+  // RMSNorm prologue (NORM kernels): x is the raw row, multiplied by
+  // 1/sqrt(mean(x^2) + eps) * gamma before the product; work-group 0 writes it to xn.
+  const uint16_t* gamma;
+  float eps;
+  uint16_t* xn;
 };
 
-template <int MT, int NCH, int G, int EPI, int LB>
+template <int MT, int NCH, int G, int EPI, int LB, bool NORM>
 __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   extern __shared__ float red[];  // two buffers of [NW][MT][64][4]
   constexpr int NS = NCH * 128 / G;
@@ -219,6 +224,47 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   XRegs<MT, NCH * 4> x;
   load_x<MT, NCH>(x, [&](int row) -> const uint16_t* { return row < a.B ? a.x + (size_t)row * a.ldx : nullptr; },
                   kbase, lane);
+  if (NORM) {
+    // The NW slices cover K: per-row sum of squares of each slice (lane values,
+    // then the 4 lanes of a row), then over slices in slice order.
+    __shared__ float s_ss[16 * 32];
+    __shared__ float s_r[32];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NCH * 4; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ss = ss + (float)x.a[mt][ks][j] * (float)x.a[mt][ks][j];
+      ss = ss + __shfl_xor(ss, 16, 64);
+      ss = ss + __shfl_xor(ss, 32, 64);
+      if (lane < 16) s_ss[w * 32 + mt * 16 + lane] = ss;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < a.B) {
+      float ss = s_ss[threadIdx.x];
+      for (int ww = 1; ww < NW; ++ww) ss = ss + s_ss[ww * 32 + threadIdx.x];
+      s_r[threadIdx.x] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = mt * 16 + (lane & 15);
+      if (row < a.B) {
+        const float r = s_r[row];
+#pragma unroll
+        for (int ks = 0; ks < NCH * 4; ++ks) {
+          const int k0 = kbase + ks * 32 + 8 * (lane >> 4);
+          const h8 gm = ld_h8(a.gamma + k0);
+          h8 v = x.a[mt][ks];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = (_Float16)(((float)v[j] * r) * (float)gm[j]);
+          x.a[mt][ks] = v;
+          if (blockIdx.x == 0) *reinterpret_cast<h8*>(a.xn + (size_t)row * a.K + k0) = v;
+        }
+      }
+    }
+  }
   const int mts = (a.B + 15) >> 4;
   const DqConst dk;
   int buf = 0;
@@ -273,9 +319,10 @@ typedef void (*DenseKernel)(DenseArgs);
 template <int MT, int NCH, int G, int LB>
 static DenseKernel pick_epi(int epi) {
   switch (epi) {
-    case EPI_F16: return k_gemm_dense<MT, NCH, G, EPI_F16, LB>;
-    case EPI_F32: return k_gemm_dense<MT, NCH, G, EPI_F32, LB>;
-    default: return k_gemm_dense<MT, NCH, G, EPI_RESID, LB>;
+    case EPI_F16: return k_gemm_dense<MT, NCH, G, EPI_F16, LB, false>;
+    case EPI_F32: return k_gemm_dense<MT, NCH, G, EPI_F32, LB, false>;
+    case EPI_F32_NORM: return k_gemm_dense<MT, NCH, G, EPI_F32, LB, true>;
+    default: return k_gemm_dense<MT, NCH, G, EPI_RESID, LB, false>;
   }
 }
 template <int MT, int NCH, int LB>
@@ -295,7 +342,7 @@ static DenseKernel pick_g(int g, int epi, int nw) {
 static inline int nch_for(int K) { return (K % 256 == 0) ? 2 : 1; }
 
 hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi,
-                       hipStream_t st) {
+                       hipStream_t st, const uint16_t* gamma, float eps, uint16_t* xn) {
   const int nch = nch_for(w.K);
   const int NW = w.K / (nch * 128);
   const int MT = B > 16 ? 2 : 1;
@@ -308,7 +355,7 @@ hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y,
   // enough work-groups to fill 256 CUs at ~16 waves each, each looping over tiles
   const int target = std::max(1, 4096 / NW);
   const int grid = std::min(ntiles, target);
-  DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy};
+  DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy, gamma, eps, xn};
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), 2 * NW * MT * 1024, st, a);
   return hipGetLastError();
 }

@@ -175,72 +175,126 @@ hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* in
 }
 
 // ------------------------------------------------------------------ routing
-// One work-group.  Per stream (one wave each, streams strided over waves):
-// k rounds of "largest remaining logit, ties to the lower id", then
-// w_r = exp(l_r - l_0) / sum_r' exp(l_r' - l_0).  Bucketing uses, per expert,
-// the bit mask of the streams (B <= 32) that selected it: count = popcount,
-// a pair's place among the expert's pairs = popcount of the lower streams'
-// bits, and the per-expert offsets are an exclusive scan over experts in
-// expert order.  All integer, so the result is exact and order-free.
+// One work-group of 1024 threads does the whole MoE front end for B <= 32
+// rows: (optional) RMSNorm of the block input, the fp32 router product on
+// MFMA, top-k softmax routing, and the (stream, expert) bucketing with the
+// 16-row work units of the grouped GEMMs.  All of it is per-row arithmetic
+// with fixed orders, so a row's routing never depends on the other rows.
 constexpr int kRouteMaxE = 256;
 
+// Order-preserving key of a logit: larger float -> larger unsigned; NaN
+// ranks as -inf and -0 as +0 (they compare equal as floats).
+__device__ __forceinline__ uint32_t sort_key(float v) {
+  if (v != v) v = -INFINITY;
+  if (v == 0.0f) v = 0.0f;
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Top-k of one row held by one wave (lane owns experts lane + 64j): ranks by
+// logit descending, ties to the lower id; w_r = exp(l_r - l_0) / sum, summed in
+// rank order.  Radix select of the k-th largest key over wave ballots, then
+// each selected expert's rank among the selected.
+template <int EPL>
+__device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane, int32_t* ids_out, float* w_out,
+                                         int32_t* s_ids, float* s_lv, unsigned* s_mask, int b) {
+  uint32_t key[EPL];
+  bool valid[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    valid[j] = e < E;
+    key[j] = valid[j] ? sort_key(lg[e]) : 0u;
+  }
+  uint32_t prefix = 0;
+  int need = k;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t want = (prefix | (1u << bit)) >> bit;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) cnt += __popcll(__ballot(valid[j] && (key[j] >> bit) == want));
+    if (cnt >= need)
+      prefix |= 1u << bit;
+    else
+      need -= cnt;
+  }
+  // selected: key > T, plus the `need` lowest-index experts with key == T
+  bool sel[EPL];
+  int before = 0;  // equal keys at lower indices in earlier slots
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const bool eq = valid[j] && key[j] == prefix;
+    const unsigned long long m = __ballot(eq);
+    const int below = before + __popcll(m & ((1ull << lane) - 1ull));
+    sel[j] = valid[j] && (key[j] > prefix || (eq && below < need));
+    before += __popcll(m);
+  }
+  // rank of each selected expert among the selected
+  int rank[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) rank[j] = 0;
+#pragma unroll
+  for (int j2 = 0; j2 < EPL; ++j2) {
+    unsigned long long m = __ballot(sel[j2]);
+    while (m) {
+      const int L = __ffsll((long long)m) - 1;
+      m &= m - 1;
+      const uint32_t k2 = __shfl(key[j2], L, 64);
+      const int e2 = L + 64 * j2;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + 64 * j;
+        rank[j] += (sel[j] && (k2 > key[j] || (k2 == key[j] && e2 < e))) ? 1 : 0;
+      }
+    }
+  }
+  // softmax over the selected, summed in rank order
+  float l0 = 0.f, sum = 0.f;
+  for (int r = 0; r < k; ++r) {
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const unsigned long long m = __ballot(sel[j] && rank[j] == r);
+      if (m) v = __shfl(valid[j] ? lg[min(lane + 64 * j, E - 1)] : 0.f, __ffsll((long long)m) - 1, 64);
+    }
+    if (v != v) v = -INFINITY;
+    if (r == 0) l0 = v;
+    sum = sum + expf(v - l0);
+  }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (sel[j]) {
+      const int e = lane + 64 * j;
+      float v = lg[e];
+      if (v != v) v = -INFINITY;
+      ids_out[b * k + rank[j]] = e;
+      w_out[b * k + rank[j]] = expf(v - l0) / sum;
+      s_ids[b * k + rank[j]] = e;
+      atomicOr(&s_mask[e], 1u << b);
+    }
+  (void)s_lv;
+}
+
+// One work-group of 1024 threads: top-k softmax of every row (one wave per
+// row), then the (stream, expert) bucketing and the 16-row work units of the
+// grouped GEMMs.
 __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits, int B, int E, int k, RouteOut o) {
+  __shared__ float s_lg[32 * kRouteMaxE];  // [B][E] fp32 logits
   __shared__ int s_ids[32 * 16];
   __shared__ unsigned s_mask[kRouteMaxE];
   __shared__ int s_off[kRouteMaxE];
-  const int nw = blockDim.x >> 6, w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0u;
+  for (int i = threadIdx.x; i < B * E; i += blockDim.x) s_lg[i] = logits[i];
   __syncthreads();
-  for (int b = w; b < B; b += nw) {
-    float v[kRouteMaxE / 64];
-    bool taken[kRouteMaxE / 64];
-#pragma unroll
-    for (int j = 0; j < kRouteMaxE / 64; ++j) {
-      const int e = lane + 64 * j;
-      float x = e < E ? logits[(size_t)b * E + e] : -INFINITY;
-      if (x != x) x = -INFINITY;  // NaN ranks last
-      v[j] = x;
-      taken[j] = e >= E;
-    }
-    float l0 = 0.f, sum = 0.f, myv = 0.f;
-    int myid = 0;
-    for (int r = 0; r < k; ++r) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int j = 0; j < kRouteMaxE / 64; ++j) {
-        const int e = lane + 64 * j;
-        if (!taken[j] && (v[j] > bv || (v[j] == bv && e < bi))) {
-          bv = v[j];
-          bi = e;
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kRouteMaxE / 64; ++j)
-        if (lane + 64 * j == bi) taken[j] = true;
-      if (r == 0) l0 = bv;
-      const float ev = expf(bv - l0);
-      sum = sum + ev;  // rank order, identical in every lane
-      if (lane == r) {
-        myv = ev;
-        myid = bi;
-      }
-    }
-    if (lane < k) {
-      o.ids[b * k + lane] = myid;
-      o.w[b * k + lane] = myv / sum;
-      s_ids[b * k + lane] = myid;
-      atomicOr(&s_mask[myid], 1u << b);
-    }
+  // top-k per row, one wave per row
+  for (int b = w; b < B; b += 16) {
+    if (E <= 64)
+      topk_row<1>(s_lg + b * E, E, k, lane, o.ids, o.w, s_ids, nullptr, s_mask, b);
+    else if (E <= 128)
+      topk_row<2>(s_lg + b * E, E, k, lane, o.ids, o.w, s_ids, nullptr, s_mask, b);
+    else
+      topk_row<4>(s_lg + b * E, E, k, lane, o.ids, o.w, s_ids, nullptr, s_mask, b);
   }
   __syncthreads();
   if (w == 0) {  // exclusive scans over experts: offsets, used experts, 16-row units
@@ -253,9 +307,9 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
       int inc = c, uinc = u, ninc = nu;
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(inc, d, 64), tu = __shfl_up(uinc, d, 64), tn = __shfl_up(ninc, d, 64);
+        const int tt = __shfl_up(inc, d, 64), tu = __shfl_up(uinc, d, 64), tn = __shfl_up(ninc, d, 64);
         if (lane >= d) {
-          inc += t;
+          inc += tt;
           uinc += tu;
           ninc += tn;
         }
@@ -289,8 +343,7 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
 }
 
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st) {
-  const int threads = 64 * std::min(16, std::max(B, 4));
-  hipLaunchKernelGGL(k_route, dim3(1), dim3(threads), 0, st, logits, B, E, k, o);
+  hipLaunchKernelGGL(k_route, dim3(1), dim3(1024), 0, st, logits, B, E, k, o);
   return hipGetLastError();
 }
 

@@ -350,10 +350,10 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xn, 
     ProfScope ps(c, W4_K_DENSE, st);
     LCHK(c, 1, launch_gemm(c->mat(L.o), B, c->W<uint16_t>(c->wp.attn_o), qd, h, H, EPI_RESID, st));
   }
-  LCHK(c, 1, launch_rmsnorm(B, H, h, c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn, st));
   {
     ProfScope ps(c, W4_K_DENSE, st);
-    LCHK(c, 1, launch_gemm(c->mat(L.router), B, xn, H, c->W<float>(c->wp.rlogits), d.n_experts, EPI_F32, st));
+    LCHK(c, 1, launch_gemm(c->mat(L.router), B, h, H, c->W<float>(c->wp.rlogits), d.n_experts, EPI_F32_NORM, st,
+                           c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn));
   }
   RouteOut r = c->route_out(ids_out);
   LCHK(c, 1, launch_route(c->W<float>(c->wp.rlogits), B, d.n_experts, d.top_k, r, st));

@@ -30,13 +30,14 @@ struct Mat {
   int ntiles() const { return (N + 15) / 16; }
 };
 
-enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_RESID = 2 };
+// EPI_F32_NORM: fp32 output of RMSNorm(x) * gamma . W^T (gamma, eps, xn given; x rows are raw).
+enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_RESID = 2, EPI_F32_NORM = 3 };
 
 // ---- launchers (kernels in *.hip); all return hipGetLastError() ----
 hipError_t launch_repack(const uint8_t* src_packed, const uint16_t* src_scales, int count, int N, int K,
                          int g, uint4* dst_tiles, uint16_t* dst_scales, hipStream_t st);
 hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi,
-                       hipStream_t st);
+                       hipStream_t st, const uint16_t* gamma = nullptr, float eps = 0.f, uint16_t* xn = nullptr);
 
 struct RouteOut {
   int32_t* ids;          // [B][k]
@@ -51,6 +52,7 @@ struct RouteOut {
   int2* units;           // [E + B*k/16] (expert, first row) per 16-row unit of each used expert
   int32_t* n_units;      // [1]
 };
+// Routing in one work-group: top-k softmax of fp32 logits [B][E], bucketing and 16-row units.  B <= 32.
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st);
 
 // Grouped expert GEMMs over the bucketed pairs (persistent, work list from route).
