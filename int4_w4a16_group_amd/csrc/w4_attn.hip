@@ -1,18 +1,20 @@
 // Slot-indexed GQA decode attention on gfx950.
 //
-// KV arena of one layer: K [slots][Hkv][cap][D] and V stored transposed,
-// VT [slots][Hkv][D][cap], so both MFMA operands of a position chunk are
-// 16-byte contiguous loads per lane.  A stream reads and writes only its own
+// KV arena of one layer: K [slots][Hkv][cap][D] and V stored transposed in
+// 64-position tiles, VT [slots][Hkv][cap/64][D][64], so both MFMA operands of
+// a position chunk are 16-byte loads per lane and a chunk's K and V are each
+// one contiguous 64*D*2-byte block (a whole-cap transpose would scatter a
+// chunk's V over D rows cap*2 bytes apart).  A stream reads and writes only its own
 // slot ("Per-stream KV-slot isolation ...", section 1: a stable per-stream
 // slot, never wiped when the batch changes).
 //
 // Split-KV: work-group (chunk c, kv head g, stream b) handles positions
 // 64c .. 64c+63 of that stream for the n_q/n_kv query heads of head g:
-//   S = Q K^T (MFMA, fp32), z = S / sqrt(D), masked beyond the stream's p;
-//   m_c = max z, P = exp(z - m_c), l_c = sum P;
+//   S = Q K^T (MFMA, fp32), z = S log2(e) / sqrt(D) (log2 units), masked beyond
+//   the stream's p; m_c = max z, P = 2^(z - m_c) (v_exp_f32), l_c = sum P;
 //   O_c = P V (MFMA on P split into fp16 hi + lo parts, fp32 accumulate).
 // The reduce kernel combines chunks in chunk order:
-//   M = max m_c, L = sum l_c e^(m_c - M), o = sum O_c e^(m_c - M) / L.
+//   M = max m_c, L = sum l_c 2^(m_c - M), o = sum O_c 2^(m_c - M) / L.
 // The chunk count is a function of the stream's own position only, so a
 // stream's result is the same in any batch.
 #include "w4_device.h"
@@ -38,8 +40,35 @@ hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStr
   return hipGetLastError();
 }
 
+// Value of lane (lane's DPP source) within a 16-lane row.
+template <int CTRL>
+static __device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Max / sum over the 16 lanes of a row: swap neighbours, swap pairs, mirror
+// within 8, mirror within 16.  Each step combines two values that the paired
+// lane combines in the other order, so every lane ends with the same result.
+static __device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  return v;
+}
+static __device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_f<0xB1>(v);
+  v = v + dpp_f<0x4E>(v);
+  v = v + dpp_f<0x141>(v);
+  v = v + dpp_f<0x140>(v);
+  return v;
+}
+
 static __device__ __forceinline__ size_t kv_base(const KV& kv, int layer, int slot, int g) {
   return (((size_t)layer * kv.S + slot) * kv.Hkv + g) * (size_t)kv.cap * kv.D;
+}
+// Offset of V[p][d] within a (layer, slot, head) block of VT.
+static __device__ __forceinline__ size_t vt_off(int D, int p, int d) {
+  return (size_t)(p >> 6) * 64 * D + (size_t)d * 64 + (p & 63);
 }
 
 // Rotary on the q and k heads of qkv[b] (rotate-half pairs (i, i+D/2)), then
@@ -71,7 +100,7 @@ __global__ void k_rope_append(int layer, int Hq, KV kv, const int32_t* __restric
   const uint16_t* vsrc = src + (Hq + Hkv) * D;
   for (int idx = threadIdx.x; idx < Hkv * D; idx += blockDim.x) {
     const int g = idx / D, d = idx - g * D;
-    kv.VT[kv_base(kv, layer, s, g) + (size_t)d * kv.cap + p] = vsrc[idx];
+    kv.VT[kv_base(kv, layer, s, g) + vt_off(D, p, d)] = vsrc[idx];
   }
 }
 
@@ -90,7 +119,7 @@ __global__ void k_append(int layer, KV kv, const int32_t* __restrict__ slot, con
     const int g = idx / D, d = idx - g * D;
     const size_t base = kv_base(kv, layer, s, g);
     kv.K[base + (size_t)p * D + d] = k_new[(size_t)b * kv.Hkv * D + idx];
-    kv.VT[base + (size_t)d * kv.cap + p] = v_new[(size_t)b * kv.Hkv * D + idx];
+    kv.VT[base + vt_off(D, p, d)] = v_new[(size_t)b * kv.Hkv * D + idx];
   }
 }
 
@@ -118,7 +147,7 @@ __global__ void k_seed(int P, int slot, KV kv, const uint16_t* __restrict__ k, c
   __syncthreads();
   for (int idx = threadIdx.x; idx < np * D; idx += blockDim.x) {
     const int d = idx / np, pp = idx - d * np;
-    kv.VT[base + (size_t)d * kv.cap + p0 + pp] = tile[pp][d];
+    kv.VT[base + vt_off(D, p0 + pp, d)] = tile[pp][d];
   }
 }
 
@@ -136,8 +165,8 @@ struct AttnArgs {
   const int32_t* pos;
   const uint16_t* q;  // [B][Hq][D]
   float* part_o;      // [B][Hq][nchmax][D]
-  float* part_ml;     // [B][Hq][nchmax][2]
-  float scale;
+  float* part_ml;     // [B][Hq][nchmax][2]  (row max in log2 units, row sum)
+  float scale;        // log2(e) / sqrt(D): scores are kept in log2 units, p = 2^(z - max)
 };
 
 template <int D>
@@ -158,12 +187,19 @@ __global__ void __launch_bounds__(64) k_attn(AttnArgs a) {
   const int col = lane & 15, quad = lane >> 4;
   const bool last = (c0 + 63 > p);
 
-  // V operands first (longest latency), masked beyond p.
+  // K operands first (the scores need them first), then V, all in flight together.
+  h8 kb[4][KSQ];
+#pragma unroll
+  for (int pt = 0; pt < 4; ++pt) {
+    const uint16_t* kp = Kb + (size_t)(c0 + pt * 16 + col) * D + 8 * quad;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(kp + 32 * ks);
+  }
   h8 vop[NDT][2];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vb + (size_t)(dt * 16 + col) * a.kv.cap + c0 + 32 * ks + 8 * quad);
+    for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vb + (size_t)c * 64 * D + (dt * 16 + col) * 64 + 32 * ks + 8 * quad);
   // Q operand: rows = the G query heads of kv head g (rows >= G are zero).
   h8 qa[KSQ];
   {
@@ -175,13 +211,9 @@ __global__ void __launch_bounds__(64) k_attn(AttnArgs a) {
   f4 S[4];
 #pragma unroll
   for (int pt = 0; pt < 4; ++pt) {
-    const uint16_t* kp = Kb + (size_t)(c0 + pt * 16 + col) * D + 8 * quad;
-    h8 kb[KSQ];
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) kb[ks] = ld_h8(kp + 32 * ks);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(qa[ks], kb[ks], acc);
+    for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(qa[ks], kb[pt][ks], acc);
     S[pt] = acc;
   }
   float mrow[4], lrow[4];
@@ -195,17 +227,15 @@ __global__ void __launch_bounds__(64) k_attn(AttnArgs a) {
       S[pt][r] = pp > p ? -INFINITY : z;
       m = fmaxf(m, S[pt][r]);
     }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    m = row16_max(m);
     float l = 0.f;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-      const float e = expf(S[pt][r] - m);
+      const float e = __builtin_amdgcn_exp2f(S[pt][r] - m);
       S[pt][r] = e;
       l = l + e;
     }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) l = l + __shfl_xor(l, o, 16);
+    l = row16_sum(l);
     mrow[r] = m;
     lrow[r] = l;
   }
@@ -288,7 +318,7 @@ __global__ void __launch_bounds__(64) k_attn_reduce(int Hq, int D, int nchmax, c
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int c = lane + 64 * j;
-    const float e = c < nch ? expf(mv[j] - M) : 0.f;
+    const float e = c < nch ? __builtin_amdgcn_exp2f(mv[j] - M) : 0.f;
     if (c < nch) wgt[c] = e;
     L = L + lv[j] * e;
   }
@@ -316,7 +346,7 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   a.q = q;
   a.part_o = part_o;
   a.part_ml = part_ml;
-  a.scale = (float)(1.0 / sqrt((double)kv.D));
+  a.scale = (float)(1.4426950408889634 / sqrt((double)kv.D));
   const int nch = (max_pos + 1 + 63) / 64;
   dim3 grid(nch, kv.Hkv, B);
   if (prof) prof_mark(prof, st);

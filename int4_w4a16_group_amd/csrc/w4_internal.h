@@ -73,7 +73,7 @@ hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, hi
 
 struct KV {
   uint16_t* K;   // [L][S][Hkv][cap][D]
-  uint16_t* VT;  // [L][S][Hkv][D][cap]
+  uint16_t* VT;  // [L][S][Hkv][cap/64][D][64]
   int S, Hkv, cap, D;
 };
 hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStream_t st);
