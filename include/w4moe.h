@@ -44,7 +44,8 @@ extern "C" {
 typedef struct w4_ctx w4_ctx;
 
 /* Model geometry.  Requirements: hidden, n_q_heads*head_dim and moe_inter are
- * multiples of 128 and at most 4096; head_dim is 64 or 128; n_q_heads is a
+ * multiples of 128 and at most 4096 (at most 2048 unless a multiple of 256);
+ * head_dim is 64 or 128; n_q_heads is a
  * multiple of n_kv_heads with at most 16 q heads per kv head; top_k <= 16,
  * top_k <= n_experts <= 256; group is 32, 64 or 128. */
 typedef struct {

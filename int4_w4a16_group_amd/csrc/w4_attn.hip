@@ -1,12 +1,18 @@
 // Slot-indexed GQA decode attention on gfx950.
 //
-// KV arena of one layer: K [slots][Hkv][cap][D] and V stored transposed in
-// 64-position tiles, VT [slots][Hkv][cap/64][D][64], so both MFMA operands of
-// a position chunk are 16-byte loads per lane and a chunk's K and V are each
-// one contiguous 64*D*2-byte block (a whole-cap transpose would scatter a
-// chunk's V over D rows cap*2 bytes apart).  A stream reads and writes only its own
-// slot ("Per-stream KV-slot isolation ...", section 1: a stable per-stream
-// slot, never wiped when the batch changes).
+// KV arena of one layer: per (slot, kv head) a run of 64-position chunks; a
+// chunk holds its K block (64 x D) and, in a separate array, its V block, each
+// stored in MFMA operand order so that every operand load of a wave is one
+// contiguous 1 KB (64 lanes x 16 bytes, with each 4-lane group reading 64
+// contiguous bytes, the rate at which the vector memory unit takes 16-byte
+// loads):
+//   K: (pos, d) at [pt = pos/16][ks = d/32][quad = d%32/8][col = pos%16][d%8],
+//      the B operand of S = Q K^T for position tile pt and k-step ks;
+//   V: (pos, d) at [dt = d/16][ks = pos/32][quad = pos%32/8][col = d%16][pos%8],
+//      the B operand of O = P V for d tile dt and k-step ks.
+// A stream reads and writes only its own slot ("Per-stream KV-slot isolation
+// ...", section 1: a stable per-stream slot, never wiped when the batch
+// changes).
 //
 // Split-KV: work-group (chunk c, kv head g, stream b) handles positions
 // 64c .. 64c+63 of that stream for the n_q/n_kv query heads of head g:
@@ -66,9 +72,15 @@ static __device__ __forceinline__ float row16_sum(float v) {
 static __device__ __forceinline__ size_t kv_base(const KV& kv, int layer, int slot, int g) {
   return (((size_t)layer * kv.S + slot) * kv.Hkv + g) * (size_t)kv.cap * kv.D;
 }
-// Offset of V[p][d] within a (layer, slot, head) block of VT.
-static __device__ __forceinline__ size_t vt_off(int D, int p, int d) {
-  return (size_t)(p >> 6) * 64 * D + (size_t)d * 64 + (p & 63);
+// Offsets of K[p][d] and V[p][d] within a (layer, slot, head) block.
+static __device__ __forceinline__ size_t k_off(int D, int p, int d) {
+  const int q = p & 63;
+  return (size_t)(p >> 6) * 64 * D +
+         (size_t)(((((q >> 4) * (D >> 5) + (d >> 5)) * 4 + ((d & 31) >> 3)) * 16 + (q & 15)) * 8 + (d & 7));
+}
+static __device__ __forceinline__ size_t v_off(int D, int p, int d) {
+  const int q = p & 63;
+  return (size_t)(p >> 6) * 64 * D + (size_t)(((((d >> 4) * 2 + (q >> 5)) * 4 + ((q & 31) >> 3)) * 16 + (d & 15)) * 8 + (q & 7));
 }
 
 // Rotary on the q and k heads of qkv[b] (rotate-half pairs (i, i+D/2)), then
@@ -91,16 +103,15 @@ __global__ void k_rope_append(int layer, int Hq, KV kv, const int32_t* __restric
       q_out[((size_t)b * Hq + h) * D + i] = o0;
       q_out[((size_t)b * Hq + h) * D + i + half] = o1;
     } else {
-      const int g = h - Hq;
-      uint16_t* kr = kv.K + kv_base(kv, layer, s, g) + (size_t)p * D;
-      kr[i] = o0;
-      kr[i + half] = o1;
+      uint16_t* kb = kv.K + kv_base(kv, layer, s, h - Hq);
+      kb[k_off(D, p, i)] = o0;
+      kb[k_off(D, p, i + half)] = o1;
     }
   }
   const uint16_t* vsrc = src + (Hq + Hkv) * D;
   for (int idx = threadIdx.x; idx < Hkv * D; idx += blockDim.x) {
     const int g = idx / D, d = idx - g * D;
-    kv.VT[kv_base(kv, layer, s, g) + vt_off(D, p, d)] = vsrc[idx];
+    kv.VT[kv_base(kv, layer, s, g) + v_off(D, p, d)] = vsrc[idx];
   }
 }
 
@@ -118,8 +129,8 @@ __global__ void k_append(int layer, KV kv, const int32_t* __restrict__ slot, con
   for (int idx = threadIdx.x; idx < kv.Hkv * D; idx += blockDim.x) {
     const int g = idx / D, d = idx - g * D;
     const size_t base = kv_base(kv, layer, s, g);
-    kv.K[base + (size_t)p * D + d] = k_new[(size_t)b * kv.Hkv * D + idx];
-    kv.VT[base + vt_off(D, p, d)] = v_new[(size_t)b * kv.Hkv * D + idx];
+    kv.K[base + k_off(D, p, d)] = k_new[(size_t)b * kv.Hkv * D + idx];
+    kv.VT[base + v_off(D, p, d)] = v_new[(size_t)b * kv.Hkv * D + idx];
   }
 }
 
@@ -129,10 +140,8 @@ hipError_t launch_append(int B, int layer, const KV& kv, const int32_t* slot, co
   return hipGetLastError();
 }
 
-// Seed a slot from canonical k, v [L][P][Hkv][D].  Block (pos chunk of 64, layer*Hkv + g);
-// V goes through LDS so the transposed store is coalesced along positions.
+// Seed a slot from canonical k, v [L][P][Hkv][D].  Block (pos chunk of 64, layer*Hkv + g).
 __global__ void k_seed(int P, int slot, KV kv, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v) {
-  __shared__ uint16_t tile[64][129];
   const int p0 = blockIdx.x * 64;
   const int l = blockIdx.y / kv.Hkv, g = blockIdx.y - l * kv.Hkv;
   const int D = kv.D;
@@ -141,13 +150,8 @@ __global__ void k_seed(int P, int slot, KV kv, const uint16_t* __restrict__ k, c
   for (int idx = threadIdx.x; idx < np * D; idx += blockDim.x) {
     const int pp = idx / D, d = idx - pp * D;
     const size_t src = (((size_t)l * P + p0 + pp) * kv.Hkv + g) * D + d;
-    kv.K[base + (size_t)(p0 + pp) * D + d] = k[src];
-    tile[pp][d] = v[src];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < np * D; idx += blockDim.x) {
-    const int d = idx / np, pp = idx - d * np;
-    kv.VT[base + vt_off(D, p0 + pp, d)] = tile[pp][d];
+    kv.K[base + k_off(D, p0 + pp, d)] = k[src];
+    kv.VT[base + v_off(D, p0 + pp, d)] = v[src];
   }
 }
 
@@ -187,19 +191,20 @@ __global__ void __launch_bounds__(64) k_attn(AttnArgs a) {
   const int col = lane & 15, quad = lane >> 4;
   const bool last = (c0 + 63 > p);
 
-  // K operands first (the scores need them first), then V, all in flight together.
+  // K operands first (the scores need them first), then V, all in flight
+  // together; each load is 1 KB contiguous across the wave.
+  const uint16_t* Kc = Kb + (size_t)c * 64 * D + lane * 8;
+  const uint16_t* Vc = Vb + (size_t)c * 64 * D + lane * 8;
   h8 kb[4][KSQ];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    const uint16_t* kp = Kb + (size_t)(c0 + pt * 16 + col) * D + 8 * quad;
+  for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(kp + 32 * ks);
-  }
+    for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(Kc + (pt * KSQ + ks) * 512);
   h8 vop[NDT][2];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vb + (size_t)c * 64 * D + (dt * 16 + col) * 64 + 32 * ks + 8 * quad);
+    for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
   // Q operand: rows = the G query heads of kv head g (rows >= G are zero).
   h8 qa[KSQ];
   {

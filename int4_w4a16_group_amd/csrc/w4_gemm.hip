@@ -95,8 +95,7 @@ struct XRegs {
 // n = 16t + lane%16); acc[mt] += over groups fma(scale, MFMA chain).
 template <int MT, int NCH, int G>
 __device__ __forceinline__ void tile_mac(const XRegs<MT, NCH * 4>& x, const uint4 (&wv)[NCH],
-                                         const float (&sv)[NCH * 128 / G], f4 (&acc)[MT], int mts,
-                                         const DqConst& dk) {
+                                         const float (&sv)[NCH * 128 / G], f4 (&acc)[MT], const DqConst& dk) {
   constexpr int SPG = G / 32;
   f4 part[MT];
 #pragma unroll
@@ -109,7 +108,7 @@ __device__ __forceinline__ void tile_mac(const XRegs<MT, NCH * 4>& x, const uint
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (ks % SPG == 0) part[mt] = f4{0.f, 0.f, 0.f, 0.f};
-        if (mt < mts) part[mt] = mfma16x16x32(x.a[mt][ks], b, part[mt]);
+        part[mt] = mfma16x16x32(x.a[mt][ks], b, part[mt]);
       }
       if ((ks + 1) % SPG == 0) {
         const float sc = sv[ks / SPG];
@@ -183,6 +182,8 @@ __device__ __forceinline__ void load_x(XRegs<MT, NCH * 4>& x, RowPtr rowptr, int
 // Sum the waves' partial tiles (red: [NW][MT][64 lanes][4]) in wave order and
 // hand each output (row, col-in-tile, value) to epi.  Consecutive threads take
 // consecutive columns.
+// All NW (<= 16) reads are issued before the in-order sum; slots w >= NW
+// re-read the last slice and are not added.
 template <int MT, class EpiF>
 __device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) {
   const int nt = blockDim.x;
@@ -190,8 +191,12 @@ __device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) 
     const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
     const int ln = (i >> 2) * 16 + j, r = i & 3;
     const int idx = mt * 256 + ln * 4 + r;
-    float v = red[idx];
-    for (int w = 1; w < NW; ++w) v = v + red[w * MT * 256 + idx];
+    float p[16];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) p[w] = red[min(w, NW - 1) * MT * 256 + idx];
+    float v = p[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) v = w < NW ? v + p[w] : v;
     epi(mt * 16 + i, j, v);
   }
 }
@@ -265,7 +270,6 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
       }
     }
   }
-  const int mts = (a.B + 15) >> 4;
   const DqConst dk;
   int buf = 0;
   auto run = [&](const Stage<NCH, G>& st, int t, bool valid) {
@@ -274,7 +278,7 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
     f4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
-    tile_mac<MT, NCH, G>(x, st.w, sv, acc, mts, dk);
+    tile_mac<MT, NCH, G>(x, st.w, sv, acc, dk);
     float* rb = red + buf * NW * MT * 256;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(rb)[(w * MT + mt) * 64 + lane] = acc[mt];
@@ -427,10 +431,10 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
       float sv0[NS], sv1[NS];
       g0.scales_f32(sv0);
       f4 acc0[1] = {f4{0.f, 0.f, 0.f, 0.f}}, acc1[1] = {f4{0.f, 0.f, 0.f, 0.f}};
-      tile_mac<1, NCH, G>(x, g0.w, sv0, acc0, 1, dk);
+      tile_mac<1, NCH, G>(x, g0.w, sv0, acc0, dk);
       if (GATEUP) {
         g1.scales_f32(sv1);
-        tile_mac<1, NCH, G>(x, g1.w, sv1, acc1, 1, dk);
+        tile_mac<1, NCH, G>(x, g1.w, sv1, acc1, dk);
       }
       float* rb = red + buf * bufsz;
       f4* r4 = reinterpret_cast<f4*>(rb);

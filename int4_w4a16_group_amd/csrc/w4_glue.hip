@@ -347,6 +347,297 @@ hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ router
+// The whole MoE front end of a decode layer in one launch.  Work-group b
+// (1024 threads) owns stream row b:
+//   xn = RMSNorm(h[b]) * gamma (fp16; written out for the expert GEMMs);
+//   logits[e] = sum over 128-column chunks c, in chunk order, of
+//     P[e][c] = sum over the chunk's groups of fma(scale, MFMA chain, .) from 0;
+//   top-k softmax of the row (ranked by logit, ties to the lower id).
+// Then each work-group takes a ticket; the last one buckets all rows.  Every
+// order above depends on the geometry only, never on B or on the other rows.
+constexpr int kRouterMaxUnits = 16 * 32;  // (E <= 256) / 16 tiles x (H <= 4096) / 128 chunks
+
+struct RouterArgs {
+  const uint16_t* h;       // [B][H] residual rows
+  const uint16_t* gamma;   // [H]
+  float eps;
+  uint16_t* xn;            // [B][H] out
+  const uint4* tiles;      // router bank tiles [Ep/16][H/128][64] x 16 B
+  const uint16_t* scales;  // [Ep][H/g]
+  int H, E, k, B;
+  RouteOut o;
+  unsigned* ticket;        // zero between launches
+};
+
+// Exclusive prefix sum over the wave of small non-negative values (< 2^BITS),
+// and the wave total, from one ballot per bit.
+template <int BITS>
+__device__ __forceinline__ int wave_excl_sum(int v, int lane, int* total) {
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int ex = 0, tot = 0;
+#pragma unroll
+  for (int bit = 0; bit < BITS; ++bit) {
+    const unsigned long long m = __ballot((v >> bit) & 1);
+    ex += __popcll(m & lt) << bit;
+    tot += __popcll(m) << bit;
+  }
+  *total = tot;
+  return ex;
+}
+
+// Bucketing of all B rows by the last work-group: per-expert stream masks,
+// exclusive scans over experts (wave bit-sliced prefix sums, then waves in
+// order), the 16-row work units, and the pair scatter.
+__device__ void bucket_rows(const RouterArgs& a, unsigned* s_mask, int* s_off, int* s_tot, int* s_ids) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int E = a.E, k = a.k, P = a.B * a.k;
+  const RouteOut& o = a.o;
+  if (tid < E) s_mask[tid] = 0u;
+  __syncthreads();
+  for (int i = tid; i < P; i += blockDim.x) {
+    const int e = __hip_atomic_load(&o.ids[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ids[i] = e;
+    atomicOr(&s_mask[e], 1u << (i / k));
+  }
+  __syncthreads();
+  int c = 0, u = 0, nu = 0, ec = 0, eu = 0, en = 0;
+  const int e = tid;
+  if (w < 4) {  // experts 64w .. 64w+63
+    c = e < E ? __popc(s_mask[e]) : 0;
+    u = c > 0;
+    nu = (c + 15) >> 4;
+    int tc, tu, tn;
+    ec = wave_excl_sum<6>(c, lane, &tc);
+    eu = wave_excl_sum<1>(u, lane, &tu);
+    en = wave_excl_sum<2>(nu, lane, &tn);
+    if (lane == 0) {
+      s_tot[3 * w] = tc;
+      s_tot[3 * w + 1] = tu;
+      s_tot[3 * w + 2] = tn;
+    }
+  }
+  __syncthreads();
+  if (w < 4) {
+    for (int ww = 0; ww < w; ++ww) {
+      ec += s_tot[3 * ww];
+      eu += s_tot[3 * ww + 1];
+      en += s_tot[3 * ww + 2];
+    }
+    if (e < E) {
+      s_off[e] = ec;
+      if (o.counts) o.counts[e] = c;
+      if (o.offsets) o.offsets[e] = ec;
+      if (u) o.used[eu] = e;
+      for (int j = 0; j < nu; ++j) o.units[en + j] = make_int2(e, 16 * j);
+    }
+    if (e == E - 1) {
+      if (o.offsets) o.offsets[E] = ec + c;
+      *o.n_used = eu + u;
+      *o.n_units = en + nu;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < P; i += blockDim.x) {
+    const int b = i / k, ex = s_ids[i];
+    const int pos = s_off[ex] + __popc(s_mask[ex] & ((1u << b) - 1u));
+    if (o.pair_stream) o.pair_stream[pos] = b;
+    if (o.pair_rank) o.pair_rank[pos] = i - b * k;
+    o.inv[i] = pos;
+  }
+}
+
+template <int G>
+__global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
+  constexpr int SPG = G / 32;   // k-steps per group
+  constexpr int NGC = 128 / G;  // groups per 128-column chunk
+  __shared__ __align__(16) uint16_t s_x[4096];
+  __shared__ float s_part[kRouterMaxUnits * 16];
+  __shared__ float s_lg[kRouteMaxE];
+  __shared__ float sh[16];
+  __shared__ __align__(16) uint32_t s_key[kRouteMaxE];
+  __shared__ int s_rank[kRouteMaxE];
+  __shared__ int s_te[16];
+  __shared__ float s_tl[16], s_ex[16];
+  __shared__ unsigned s_mask[kRouteMaxE];
+  __shared__ int s_off[kRouteMaxE];
+  __shared__ int s_tot[12];
+  __shared__ int s_ids[32 * 16];
+  __shared__ int s_last;
+  const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int H = a.H, E = a.E, k = a.k;
+  const int NC = H >> 7, NT = (E + 15) >> 4, NU = NT * NC;
+
+  // The row and gain are requested first (their wait comes first); then this wave's
+  // first batch of weights, whose latency overlaps the norm.  Wave w owns the
+  // 128-column chunks c = w, w + 16, ... and, for each, the router tiles in
+  // batches of eight; every load of a batch is issued before any is used
+  // (tile indices clamped, results of clamped tiles dropped).
+  const int i0 = 4 * tid;
+  uint2 hraw = make_uint2(0u, 0u), graw = make_uint2(0u, 0u);
+  if (i0 < H) {
+    hraw = *reinterpret_cast<const uint2*>(a.h + (size_t)b * H + i0);
+    graw = *reinterpret_cast<const uint2*>(a.gamma + i0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep these two loads ahead of the weight loads
+  uint4 wv[8];
+  uint16_t sr[8][NGC];
+  auto load_batch = [&](int c, int t0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = min(t0 + i, NT - 1);
+      wv[i] = a.tiles[((size_t)t * NC + c) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < NGC; ++j) sr[i][j] = a.scales[(size_t)(16 * t + (lane & 15)) * (H / G) + c * NGC + j];
+    }
+  };
+  // Unconditional (chunk clamped): a load under a branch would make every
+  // later wait on the row count the weight loads too.
+  load_batch(min(w, NC - 1), 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 1. RMSNorm of the row: 4 columns per thread, fixed-order block sum.
+  {
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    if (i0 < H) {
+      v[0] = h2f((uint16_t)(hraw.x & 0xFFFFu));
+      v[1] = h2f((uint16_t)(hraw.x >> 16));
+      v[2] = h2f((uint16_t)(hraw.y & 0xFFFFu));
+      v[3] = h2f((uint16_t)(hraw.y >> 16));
+      ss = v[0] * v[0];
+      ss = ss + v[1] * v[1];
+      ss = ss + v[2] * v[2];
+      ss = ss + v[3] * v[3];
+    }
+    ss = block_sum(ss, sh);
+    const float r = 1.0f / sqrtf(ss / (float)H + a.eps);
+    if (i0 < H) {
+      const uint16_t o0 = f2h((v[0] * r) * h2f((uint16_t)(graw.x & 0xFFFFu)));
+      const uint16_t o1 = f2h((v[1] * r) * h2f((uint16_t)(graw.x >> 16)));
+      const uint16_t o2 = f2h((v[2] * r) * h2f((uint16_t)(graw.y & 0xFFFFu)));
+      const uint16_t o3 = f2h((v[3] * r) * h2f((uint16_t)(graw.y >> 16)));
+      const uint2 packed = make_uint2((uint32_t)o0 | ((uint32_t)o1 << 16), (uint32_t)o2 | ((uint32_t)o3 << 16));
+      *reinterpret_cast<uint2*>(s_x + i0) = packed;
+      *reinterpret_cast<uint2*>(a.xn + (size_t)b * H + i0) = packed;
+    }
+  }
+  __syncthreads();
+
+  // 2. Chunk partials P[t][c] (stored at unit t * NC + c).  Every A-operand
+  // row is the normalised row, so D row 0 (lanes 0..15, element 0) is the
+  // result; the A operand of a chunk is read from LDS once.
+  const DqConst dk;
+  auto run_batch = [&](int c, int t0, const h8 (&xa)[4]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + i;
+      if (t < NT) {
+        const uint32_t wd[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+        f4 acc = {0.f, 0.f, 0.f, 0.f}, part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s % SPG == 0) part = f4{0.f, 0.f, 0.f, 0.f};
+          part = mfma16x16x32(xa[s], dq8(wd[s], dk), part);
+          if ((s + 1) % SPG == 0) {
+            const float sc = h2f(sr[i][s / SPG]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, part[r], acc[r]);
+          }
+        }
+        // All four rows are equal; keeping every element of the MFMA results
+        // live stops the compiler from reusing a destination register of an
+        // MFMA still in flight for the next operand.
+        asm volatile("" ::"v"(acc));
+        if (lane < 16) s_part[(t * NC + c) * 16 + lane] = acc[0];
+      }
+    }
+  };
+  for (int c = w; c < NC; c += 16) {
+    h8 xa[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const h8*>(s_x + 128 * c + 32 * s + 8 * (lane >> 4));
+    for (int t0 = 0; t0 < NT; t0 += 8) {
+      if (c != w || t0 != 0) load_batch(c, t0);
+      run_batch(c, t0, xa);
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int t = tid >> 4, col = tid & 15;
+    float l = s_part[(t * NC) * 16 + col];
+    for (int c = 1; c < NC; ++c) l = l + s_part[(t * NC + c) * 16 + col];
+    s_lg[tid] = l;
+  }
+  __syncthreads();
+
+  // 3. Top-k of the row by rank counting: rank(e) = #{e' : key e' > key e, or
+  // equal keys and e' < e} (NaN ranks as -inf); thread (e, part) counts over
+  // one part of the experts, integer LDS adds combine the parts.  The experts
+  // of rank < k are the top-k in rank order.
+  {
+    const int NE = E <= 128 ? 128 : 256, parts = 1024 / NE, per = NE / parts;
+    const int e = tid & (NE - 1), p = tid / NE;
+    if (tid < NE) {
+      s_key[tid] = tid < E ? sort_key(s_lg[tid]) : 0u;  // padding ranks below every expert
+      s_rank[tid] = 0;
+    }
+    __syncthreads();
+    const uint32_t ke = s_key[e];
+    int cnt = 0;
+    for (int j = p * per; j < (p + 1) * per; j += 4) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(s_key + j);
+      cnt += (kk.x > ke || (kk.x == ke && j < e)) ? 1 : 0;
+      cnt += (kk.y > ke || (kk.y == ke && j + 1 < e)) ? 1 : 0;
+      cnt += (kk.z > ke || (kk.z == ke && j + 2 < e)) ? 1 : 0;
+      cnt += (kk.w > ke || (kk.w == ke && j + 3 < e)) ? 1 : 0;
+    }
+    if (cnt) atomicAdd(&s_rank[e], cnt);
+    __syncthreads();
+    if (tid < E && s_rank[tid] < k) {
+      float v = s_lg[tid];
+      if (v != v) v = -INFINITY;
+      s_te[s_rank[tid]] = tid;
+      s_tl[s_rank[tid]] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < k) s_ex[tid] = expf(s_tl[tid] - s_tl[0]);
+  __syncthreads();
+  if (tid < k) {
+    float sum = 0.f;
+    for (int r = 0; r < k; ++r) sum = sum + s_ex[r];
+    // ids are read by the last work-group within this launch: device-scope
+    // atomic stores, complete (vmcnt 0) before the ticket is taken.  The
+    // other outputs are read by later launches only.
+    __hip_atomic_store(&a.o.ids[b * k + tid], s_te[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.o.w[b * k + tid] = s_ex[tid] / sum;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // 4. Ticket: the last work-group to arrive buckets every row.
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  bucket_rows(a, s_mask, s_off, s_tot, s_ids);
+  if (tid == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
+                         uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
+                         unsigned* ticket, hipStream_t st) {
+  RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket};
+  switch (g) {
+    case 32: hipLaunchKernelGGL(k_router<32>, dim3(B), dim3(1024), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_router<64>, dim3(B), dim3(1024), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_router<128>, dim3(B), dim3(1024), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ argmax
 // Largest fp16 logit per row, ties to the lower id (NaN never wins).
 __global__ void __launch_bounds__(1024) k_argmax(int V, const uint16_t* __restrict__ logits, int32_t* __restrict__ next) {

@@ -42,7 +42,7 @@ struct BankPlan {
 };
 
 struct WsPlan {
-  size_t h, xn, qkv, q, attn_o, part_o, part_ml, rlogits, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+  size_t h, xn, qkv, q, attn_o, part_o, part_ml, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
       used, n_used, units, n_units, act, y, logits, next, rows, table, total;
 };
 
@@ -60,6 +60,9 @@ bool geometry_ok(const w4_model_desc* d, std::string* why) {
   const int qd = d->n_q_heads * d->head_dim;
   if (qd % 128 || qd > 4096) return bad("n_q_heads*head_dim must be a multiple of 128, at most 4096");
   if (d->moe_inter < 128 || d->moe_inter % 128 || d->moe_inter > 4096) return bad("moe_inter must be a multiple of 128 in [128, 4096]");
+  // every product's K is cut into at most 16 slices of 256 (128 when K % 256 != 0)
+  for (int K : {d->hidden, qd, d->moe_inter})
+    if (K % 256 != 0 && K > 2048) return bad("a reduction length that is not a multiple of 256 must be at most 2048");
   if (d->top_k < 1 || d->top_k > 16) return bad("top_k must be in [1, 16]");
   if (d->n_experts < d->top_k || d->n_experts > 256) return bad("n_experts must be in [top_k, 256]");
   if (d->group != 32 && d->group != 64 && d->group != 128) return bad("group must be 32, 64 or 128");
@@ -136,6 +139,7 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.part_o = take(Bm * Hq * nch * D * 4);
   w.part_ml = take(Bm * Hq * nch * 2 * 4);
   w.rlogits = take(Bm * E * 4);
+  w.ticket = take(64);
   w.ids = take(Bm * k * 4);
   w.w = take(Bm * k * 4);
   w.counts = take(E * 4);
@@ -261,7 +265,8 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
   }
   if (!c->table_ready) {
     HIPCHK(c, launch_rope_table(c->cap, c->d.head_dim, (double)c->d.rope_theta, c->W<float2>(c->wp.table), st));
-    c->launches++;
+    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.ticket), 0u, 16, st));
+    c->launches += 2;
     c->table_ready = true;
   }
   return W4_OK;
@@ -350,13 +355,12 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xn, 
     ProfScope ps(c, W4_K_DENSE, st);
     LCHK(c, 1, launch_gemm(c->mat(L.o), B, c->W<uint16_t>(c->wp.attn_o), qd, h, H, EPI_RESID, st));
   }
-  {
-    ProfScope ps(c, W4_K_DENSE, st);
-    LCHK(c, 1, launch_gemm(c->mat(L.router), B, h, H, c->W<float>(c->wp.rlogits), d.n_experts, EPI_F32_NORM, st,
-                           c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn));
-  }
   RouteOut r = c->route_out(ids_out);
-  LCHK(c, 1, launch_route(c->W<float>(c->wp.rlogits), B, d.n_experts, d.top_k, r, st));
+  {
+    const Mat R = c->mat(L.router);
+    LCHK(c, 1, launch_router(B, H, d.n_experts, d.top_k, d.group, h, c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn,
+                             R.tiles, R.scales, r, c->W<unsigned>(c->wp.ticket), st));
+  }
   {
     ProfScope ps(c, W4_K_MOE_GATEUP, st);
     LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), xn, H, r, c->W<uint16_t>(c->wp.act), st));

@@ -55,6 +55,13 @@ struct RouteOut {
 // Routing in one work-group: top-k softmax of fp32 logits [B][E], bucketing and 16-row units.  B <= 32.
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st);
 
+// MoE front end of a decode layer in one launch (one work-group per row, B <= 32):
+// xn = RMSNorm(h) * gamma, the router product, top-k softmax and the bucketing
+// (done by the last work-group to finish; ticket is zero before and after).
+hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
+                         uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
+                         unsigned* ticket, hipStream_t st);
+
 // Grouped expert GEMMs over the bucketed pairs (persistent, work list from route).
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
                              uint16_t* act, hipStream_t st);
@@ -72,8 +79,8 @@ hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const
 hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, hipStream_t st);
 
 struct KV {
-  uint16_t* K;   // [L][S][Hkv][cap][D]
-  uint16_t* VT;  // [L][S][Hkv][cap/64][D][64]
+  uint16_t* K;   // [L][S][Hkv][cap/64][64*D], MFMA operand order (w4_attn.hip)
+  uint16_t* VT;  // [L][S][Hkv][cap/64][64*D], MFMA operand order (w4_attn.hip)
   int S, Hkv, cap, D;
 };
 hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStream_t st);

@@ -51,8 +51,10 @@ def test_geometry_and_size_limits():
     assert L.w4_bank_bytes(d) > 0
     import dataclasses
     for bad in (dict(hidden=200), dict(head_dim=96), dict(group=16), dict(top_k=0), dict(n_experts=1, top_k=2),
-                dict(n_q_heads=3), dict(moe_inter=100)):
+                dict(n_q_heads=3), dict(moe_inter=100), dict(hidden=2176), dict(moe_inter=2304 + 128)):
         assert L.w4_bank_bytes(dataclasses.replace(d, **bad)) == 0, bad
+    for ok in (dict(hidden=1920), dict(hidden=4096), dict(moe_inter=2304)):   # <= 16 slices of 128 / 256
+        assert L.w4_bank_bytes(dataclasses.replace(d, **ok)) > 0, ok
     assert L.w4_arena_bytes(d, 33, 128) == 0
     assert L.w4_arena_bytes(d, 8, 100) == 0
     assert L.w4_arena_bytes(d, 8, 128) > 0
