@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libw4moe.so")
 
 W4_OK, W4_E_INVALID, W4_E_NO_SLOT, W4_E_CONTEXT_CAP, W4_E_BAD_SLOT, W4_E_NOT_READY, W4_E_HIP, W4_E_UNSUPPORTED = \
     0, -1, -2, -3, -4, -5, -6, -7
-W4_K_DENSE, W4_K_MOE_GATEUP, W4_K_MOE_DOWN, W4_K_ATTENTION = 1, 2, 3, 4
+W4_K_DENSE, W4_K_MOE_GATEUP, W4_K_MOE_DOWN, W4_K_ATTENTION, W4_K_ROUTER = 1, 2, 3, 4, 5
 (W4_T_QKV, W4_T_O, W4_T_ROUTER, W4_T_GATE, W4_T_UP, W4_T_DOWN, W4_T_EMBED, W4_T_LM_HEAD, W4_T_ATTN_NORM,
  W4_T_MOE_NORM, W4_T_FINAL_NORM) = range(11)
 

@@ -357,6 +357,7 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xn, 
   }
   RouteOut r = c->route_out(ids_out);
   {
+    ProfScope ps(c, W4_K_ROUTER, st);
     const Mat R = c->mat(L.router);
     LCHK(c, 1, launch_router(B, H, d.n_experts, d.top_k, d.group, h, c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn,
                              R.tiles, R.scales, r, c->W<unsigned>(c->wp.ticket), st));
@@ -715,7 +716,7 @@ const char* w4_last_error(const w4_ctx* c) { return c ? c->err.c_str() : "null c
 
 int w4_profile_begin(w4_ctx* c, int32_t kernel) {
   if (!c) return W4_E_INVALID;
-  if (kernel < W4_K_DENSE || kernel > W4_K_ATTENTION) return fail(c, W4_E_INVALID, "unknown kernel family");
+  if (kernel < W4_K_DENSE || kernel > W4_K_ROUTER) return fail(c, W4_E_INVALID, "unknown kernel family");
   c->prof_kernel = kernel;
   c->prof_used = 0;
   return W4_OK;

@@ -64,6 +64,7 @@ def lib():
         L.orc_moe.argtypes = [C.POINTER(_Model), C.c_int, C.c_int, _u16p, _f32p, _u16p, C.c_void_p, C.c_void_p]
         L.orc_layer_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
                                      _u16p, C.c_void_p, C.c_void_p]
+        L.orc_embed.argtypes = [C.POINTER(_Model), C.c_int, _i32p, _u16p]
         L.orc_decode_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, _i32p, _i32p, _i32p,
                                       C.c_void_p, _i32p, C.c_void_p, C.c_void_p]
         L.orc_attn_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
@@ -243,6 +244,14 @@ def moe(model: Model, layer: int, x: np.ndarray, logits: np.ndarray):
     w = np.empty((B, d.top_k), np.float32)
     lib().orc_moe(C.byref(model.m), layer, B, x, logits, y, ids.ctypes.data, w.ctypes.data)
     return y, ids, w
+
+
+def embed(model: Model, tokens) -> np.ndarray:
+    """h fp16 bits [B][hidden]: the dequantised embedding rows of tokens (step O1)."""
+    tokens = _c(tokens, np.int32)
+    h = np.empty((len(tokens), model.desc.hidden), np.uint16)
+    lib().orc_embed(C.byref(model.m), len(tokens), tokens, h)
+    return h
 
 
 def layer_step(model: Model, arena: Arena, layer: int, slots, positions, h: np.ndarray):

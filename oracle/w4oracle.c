@@ -412,6 +412,20 @@ EXPORT void orc_layer_step(const orc_model* m, orc_arena* a, int l, int B, const
               logits_out ? logits_out + (size_t)b * m->n_experts : NULL);
 }
 
+/* Embedding row of a token, dequantised and stored =>h (step O1). */
+static void embed_row(const orc_model* m, int token, uint16_t* h) {
+  const int H = m->hidden, g = m->group;
+  const uint8_t* er = m->emb_p + (size_t)token * (H / 2);
+  const uint16_t* es = m->emb_s + (size_t)token * (H / g);
+  for (int i = 0; i < H; i++) h[i] = orc_f2h((float)code_at(er, i) * HF(es[i / g]));
+}
+
+/* h [B][hidden] = the embedding rows of tokens[b]. */
+EXPORT void orc_embed(const orc_model* m, int B, const int32_t* tokens, uint16_t* h) {
+  h2f_init();
+  for (int b = 0; b < B; b++) embed_row(m, tokens[b], h + (size_t)b * m->hidden);
+}
+
 /* Whole decode step for B streams: embedding row of the token (dequantised
  * =>h), every layer, final RMSNorm, output projection =>h, greedy argmax
  * (ties to the lower id).  Greedy decoding per the batched-serving page,
@@ -425,9 +439,7 @@ EXPORT void orc_decode_step(const orc_model* m, orc_arena* a, int B, const int32
   uint16_t* hn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
   uint16_t* lg = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)V);
   for (int b = 0; b < B; b++) {
-    const uint8_t* er = m->emb_p + (size_t)tokens[b] * (H / 2);
-    const uint16_t* es = m->emb_s + (size_t)tokens[b] * (H / g);
-    for (int i = 0; i < H; i++) h[i] = orc_f2h((float)code_at(er, i) * HF(es[i / g]));
+    embed_row(m, tokens[b], h);
     for (int l = 0; l < m->n_layers; l++)
       layer_one(m, a, l, slots[b], positions[b], h,
                 ids_out ? ids_out + ((size_t)l * B + b) * k : NULL,
