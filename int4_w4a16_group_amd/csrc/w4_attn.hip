@@ -297,13 +297,15 @@ __global__ void __launch_bounds__(64) k_attn(AttnArgs a) {
   }
 }
 
-// One wave per (head, stream): combine the stream's chunks.  Lane c holds
+// One wave per (head, stream): combine the stream's chunks.  Output o is
+// [B][Hq*D], row-major (rows == 0) or an activation panel with that many rows.  Lane c holds
 // chunk c (c + 64, ... beyond 64 chunks); M and L are wave reductions with a
 // fixed tree, then every lane sums its columns over the chunks in order.
 // nchmax <= 256 (ctx_cap <= 16384, checked at context creation).
 __global__ void __launch_bounds__(64) k_attn_reduce(int Hq, int D, int nchmax, const int32_t* __restrict__ pos,
                                                     const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml, uint16_t* __restrict__ o) {
+                                                    const float* __restrict__ part_ml, uint16_t* __restrict__ o,
+                                                    int rows) {
   __shared__ float wgt[256];
   const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
   const int nch = (pos[b] + 1 + 63) / 64;
@@ -334,13 +336,15 @@ __global__ void __launch_bounds__(64) k_attn_reduce(int Hq, int D, int nchmax, c
   for (int d = lane; d < D; d += 64) {
     float acc = 0.f;
     for (int c = 0; c < nch; ++c) acc = acc + po[(size_t)c * D + d] * wgt[c];
-    o[((size_t)b * Hq + h) * D + d] = f2h(acc / L);
+    const int kk = h * D + d;  // column of the [B][Hq*D] output
+    const size_t off = rows ? ((size_t)(kk >> 3) * rows + b) * 8 + (kk & 7) : (size_t)b * Hq * D + kk;
+    o[off] = f2h(acc / L);
   }
 }
 
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
                             int max_pos, const uint16_t* q, float* part_o, float* part_ml, uint16_t* o,
-                            hipStream_t st, void* prof) {
+                            hipStream_t st, void* prof, int o_rows) {
   AttnArgs a;
   a.kv = kv;
   a.layer = layer;
@@ -360,7 +364,8 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   else
     hipLaunchKernelGGL(k_attn<64>, grid, dim3(64), 0, st, a);
   if (prof) prof_mark(prof, st);
-  hipLaunchKernelGGL(k_attn_reduce, dim3(Hq, B), dim3(64), 0, st, Hq, kv.D, a.nchmax, pos, part_o, part_ml, o);
+  hipLaunchKernelGGL(k_attn_reduce, dim3(Hq, B), dim3(64), 0, st, Hq, kv.D, a.nchmax, pos, part_o, part_ml, o,
+                     o_rows);
   return hipGetLastError();
 }
 

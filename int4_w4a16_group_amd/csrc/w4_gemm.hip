@@ -179,6 +179,21 @@ __device__ __forceinline__ void load_x(XRegs<MT, NCH * 4>& x, RowPtr rowptr, int
   }
 }
 
+// A-operand rows from an activation panel: element (row b, column k) of a
+// [rows][K] activation at ((k / 8) * rows + b) * 8 + k % 8, so the 4-lane
+// groups of every operand load read 64 contiguous bytes (rows is a multiple
+// of 16; rows past the batch hold stale values, which only reach output rows
+// that are never stored: an MFMA output row depends on its own A row only).
+template <int MT, int NCH>
+__device__ __forceinline__ void load_x_panel(XRegs<MT, NCH * 4>& x, const uint16_t* __restrict__ xp, int rows,
+                                             int kbase, int lane) {
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < NCH * 4; ++ks)
+      x.a[mt][ks] = ld_h8(xp + ((size_t)((kbase >> 3) + 4 * ks + (lane >> 4)) * rows + 16 * mt + (lane & 15)) * 8);
+}
+
 // Sum the waves' partial tiles (red: [NW][MT][64 lanes][4]) in wave order and
 // hand each output (row, col-in-tile, value) to epi.  Consecutive threads take
 // consecutive columns.
@@ -210,14 +225,10 @@ struct DenseArgs {
   int ldx, B;
   void* y;
   int ldy;
-  // RMSNorm prologue (NORM kernels): x is the raw row, multiplied by
-  // 1/sqrt(mean(x^2) + eps) * gamma before the product; work-group 0 writes it to xn.
-  const uint16_t* gamma;
-  float eps;
-  uint16_t* xn;
+  int xrows;  // XP kernels: x is a panel with this many rows (see load_x_panel)
 };
 
-template <int MT, int NCH, int G, int EPI, int LB, bool NORM>
+template <int MT, int NCH, int G, int EPI, int LB, bool XP>
 __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   extern __shared__ float red[];  // two buffers of [NW][MT][64][4]
   constexpr int NS = NCH * 128 / G;
@@ -227,49 +238,11 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   const int G0 = gridDim.x;
   if ((int)blockIdx.x >= a.ntiles) return;
   XRegs<MT, NCH * 4> x;
-  load_x<MT, NCH>(x, [&](int row) -> const uint16_t* { return row < a.B ? a.x + (size_t)row * a.ldx : nullptr; },
-                  kbase, lane);
-  if (NORM) {
-    // The NW slices cover K: per-row sum of squares of each slice (lane values,
-    // then the 4 lanes of a row), then over slices in slice order.
-    __shared__ float s_ss[16 * 32];
-    __shared__ float s_r[32];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float ss = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NCH * 4; ++ks)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ss = ss + (float)x.a[mt][ks][j] * (float)x.a[mt][ks][j];
-      ss = ss + __shfl_xor(ss, 16, 64);
-      ss = ss + __shfl_xor(ss, 32, 64);
-      if (lane < 16) s_ss[w * 32 + mt * 16 + lane] = ss;
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < a.B) {
-      float ss = s_ss[threadIdx.x];
-      for (int ww = 1; ww < NW; ++ww) ss = ss + s_ss[ww * 32 + threadIdx.x];
-      s_r[threadIdx.x] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int row = mt * 16 + (lane & 15);
-      if (row < a.B) {
-        const float r = s_r[row];
-#pragma unroll
-        for (int ks = 0; ks < NCH * 4; ++ks) {
-          const int k0 = kbase + ks * 32 + 8 * (lane >> 4);
-          const h8 gm = ld_h8(a.gamma + k0);
-          h8 v = x.a[mt][ks];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = (_Float16)(((float)v[j] * r) * (float)gm[j]);
-          x.a[mt][ks] = v;
-          if (blockIdx.x == 0) *reinterpret_cast<h8*>(a.xn + (size_t)row * a.K + k0) = v;
-        }
-      }
-    }
-  }
+  if (XP)
+    load_x_panel<MT, NCH>(x, a.x, a.xrows, kbase, lane);
+  else
+    load_x<MT, NCH>(x, [&](int row) -> const uint16_t* { return row < a.B ? a.x + (size_t)row * a.ldx : nullptr; },
+                    kbase, lane);
   const DqConst dk;
   int buf = 0;
   auto run = [&](const Stage<NCH, G>& st, int t, bool valid) {
@@ -320,46 +293,46 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
 typedef void (*DenseKernel)(DenseArgs);
 
 // LB: launch bound; 512 threads (<= 8 waves) leaves up to 256 VGPRs per lane.
-template <int MT, int NCH, int G, int LB>
+template <int MT, int NCH, int G, int LB, bool XP>
 static DenseKernel pick_epi(int epi) {
   switch (epi) {
-    case EPI_F16: return k_gemm_dense<MT, NCH, G, EPI_F16, LB, false>;
-    case EPI_F32: return k_gemm_dense<MT, NCH, G, EPI_F32, LB, false>;
-    case EPI_F32_NORM: return k_gemm_dense<MT, NCH, G, EPI_F32, LB, true>;
-    default: return k_gemm_dense<MT, NCH, G, EPI_RESID, LB, false>;
+    case EPI_F16: return k_gemm_dense<MT, NCH, G, EPI_F16, LB, XP>;
+    case EPI_F32: return k_gemm_dense<MT, NCH, G, EPI_F32, LB, XP>;
+    default: return k_gemm_dense<MT, NCH, G, EPI_RESID, LB, XP>;
   }
 }
-template <int MT, int NCH, int LB>
+template <int MT, int NCH, int LB, bool XP>
 static DenseKernel pick_g_lb(int g, int epi) {
   switch (g) {
-    case 32: return pick_epi<MT, NCH, 32, LB>(epi);
-    case 64: return pick_epi<MT, NCH, 64, LB>(epi);
-    default: return pick_epi<MT, NCH, 128, LB>(epi);
+    case 32: return pick_epi<MT, NCH, 32, LB, XP>(epi);
+    case 64: return pick_epi<MT, NCH, 64, LB, XP>(epi);
+    default: return pick_epi<MT, NCH, 128, LB, XP>(epi);
   }
 }
-template <int MT, int NCH>
+template <int MT, int NCH, bool XP>
 static DenseKernel pick_g(int g, int epi, int nw) {
-  return nw <= 8 ? pick_g_lb<MT, NCH, 512>(g, epi) : pick_g_lb<MT, NCH, 1024>(g, epi);
+  return nw <= 8 ? pick_g_lb<MT, NCH, 512, XP>(g, epi) : pick_g_lb<MT, NCH, 1024, XP>(g, epi);
+}
+template <bool XP>
+static DenseKernel pick(int MT, int nch, int g, int epi, int nw) {
+  if (MT == 1) return nch == 2 ? pick_g<1, 2, XP>(g, epi, nw) : pick_g<1, 1, XP>(g, epi, nw);
+  return nch == 2 ? pick_g<2, 2, XP>(g, epi, nw) : pick_g<2, 1, XP>(g, epi, nw);
 }
 
 // Slice width: 256 columns, or 128 when K is not a multiple of 256.
 static inline int nch_for(int K) { return (K % 256 == 0) ? 2 : 1; }
 
-hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi,
-                       hipStream_t st, const uint16_t* gamma, float eps, uint16_t* xn) {
+hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi, hipStream_t st,
+                       int xrows) {
   const int nch = nch_for(w.K);
   const int NW = w.K / (nch * 128);
   const int MT = B > 16 ? 2 : 1;
-  DenseKernel k;
-  if (MT == 1)
-    k = nch == 2 ? pick_g<1, 2>(w.g, epi, NW) : pick_g<1, 1>(w.g, epi, NW);
-  else
-    k = nch == 2 ? pick_g<2, 2>(w.g, epi, NW) : pick_g<2, 1>(w.g, epi, NW);
+  const DenseKernel k = xrows > 0 ? pick<true>(MT, nch, w.g, epi, NW) : pick<false>(MT, nch, w.g, epi, NW);
   const int ntiles = w.ntiles();
   // enough work-groups to fill 256 CUs at ~16 waves each, each looping over tiles
   const int target = std::max(1, 4096 / NW);
   const int grid = std::min(ntiles, target);
-  DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy, gamma, eps, xn};
+  DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy, xrows};
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), 2 * NW * MT * 1024, st, a);
   return hipGetLastError();
 }

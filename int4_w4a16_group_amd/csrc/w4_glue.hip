@@ -11,6 +11,12 @@ namespace w4 {
 
 static constexpr int kNormThreads = 256;
 
+// Offset of element (row b, column k) of a [.][H] activation: row-major when
+// rows == 0, else the panel layout of the dense products (w4_internal.h).
+__device__ __forceinline__ size_t act_off(int b, int k, int H, int rows) {
+  return rows ? ((size_t)(k >> 3) * rows + b) * 8 + (k & 7) : (size_t)b * H + k;
+}
+
 // Block-wide sum with a fixed order (wave shuffles, then waves in order).
 __device__ __forceinline__ float block_sum(float v, float* sh) {
 #pragma unroll
@@ -27,7 +33,7 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
 // out = x * (1/sqrt(mean(x^2) + eps)) * gamma, row held in registers (H <= 16*256).
 template <int PER>
 __device__ __forceinline__ void norm_row(const float (&v)[PER], int H, const uint16_t* __restrict__ gamma, float eps,
-                                         uint16_t* __restrict__ out, float* sh) {
+                                         uint16_t* __restrict__ out, int b, int rows, float* sh) {
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -39,7 +45,7 @@ __device__ __forceinline__ void norm_row(const float (&v)[PER], int H, const uin
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = threadIdx.x + j * kNormThreads;
-    if (i < H) out[i] = f2h((v[j] * r) * h2f(gamma[i]));
+    if (i < H) out[act_off(b, i, H, rows)] = f2h((v[j] * r) * h2f(gamma[i]));
   }
 }
 
@@ -47,7 +53,7 @@ constexpr int kPer = 16;  // hidden <= 4096
 
 __global__ void __launch_bounds__(kNormThreads) k_rmsnorm(int H, const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ gamma, float eps,
-                                                          uint16_t* __restrict__ out) {
+                                                          uint16_t* __restrict__ out, int rows) {
   __shared__ float sh[16];
   const int b = blockIdx.x;
   float v[kPer];
@@ -56,12 +62,12 @@ __global__ void __launch_bounds__(kNormThreads) k_rmsnorm(int H, const uint16_t*
     const int i = threadIdx.x + j * kNormThreads;
     v[j] = i < H ? h2f(x[(size_t)b * H + i]) : 0.f;
   }
-  norm_row<kPer>(v, H, gamma, eps, out + (size_t)b * H, sh);
+  norm_row<kPer>(v, H, gamma, eps, out, b, rows, sh);
 }
 
 hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma, float eps, uint16_t* out,
-                          hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(kNormThreads), 0, st, H, x, gamma, eps, out);
+                          hipStream_t st, int out_rows) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(B), dim3(kNormThreads), 0, st, H, x, gamma, eps, out, out_rows);
   return hipGetLastError();
 }
 
@@ -71,7 +77,7 @@ __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, con
                                                         const uint8_t* __restrict__ emb_p,
                                                         const uint16_t* __restrict__ emb_s, uint16_t* __restrict__ h,
                                                         const uint16_t* __restrict__ gamma, float eps,
-                                                        uint16_t* __restrict__ xn) {
+                                                        uint16_t* __restrict__ xn, int rows) {
   __shared__ float sh[16];
   const int b = blockIdx.x;
   int t = tokens[b];
@@ -92,13 +98,14 @@ __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, con
       v[j] = h2f(hv);
     }
   }
-  norm_row<kPer>(v, H, gamma, eps, xn + (size_t)b * H, sh);
+  norm_row<kPer>(v, H, gamma, eps, xn, b, rows, sh);
 }
 
 hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const uint8_t* emb_p,
                         const uint16_t* emb_s, uint16_t* h, const uint16_t* gamma, float eps, uint16_t* xn,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(k_embed, dim3(B), dim3(kNormThreads), 0, st, H, V, g, tokens, emb_p, emb_s, h, gamma, eps, xn);
+                        hipStream_t st, int xn_rows) {
+  hipLaunchKernelGGL(k_embed, dim3(B), dim3(kNormThreads), 0, st, H, V, g, tokens, emb_p, emb_s, h, gamma, eps, xn,
+                     xn_rows);
   return hipGetLastError();
 }
 
@@ -111,7 +118,7 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
                                                           const int32_t* __restrict__ inv,
                                                           const uint16_t* __restrict__ y, uint16_t* __restrict__ h,
                                                           int resid, const uint16_t* __restrict__ gamma, float eps,
-                                                          uint16_t* __restrict__ xn) {
+                                                          uint16_t* __restrict__ xn, int rows) {
   __shared__ float sh[16];
   __shared__ int s_inv[16];
   __shared__ float s_w[16];
@@ -162,15 +169,15 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
     if (i < H) {
       const uint16_t o0 = f2h((v[2 * j] * rr) * h2f(gamma[i]));
       const uint16_t o1 = f2h((v[2 * j + 1] * rr) * h2f(gamma[i + 1]));
-      *reinterpret_cast<uint32_t*>(xn + (size_t)b * H + i) = (uint32_t)o0 | ((uint32_t)o1 << 16);
+      *reinterpret_cast<uint32_t*>(xn + act_off(b, i, H, rows)) = (uint32_t)o0 | ((uint32_t)o1 << 16);
     }
   }
 }
 
 hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* inv, const uint16_t* y, uint16_t* h,
-                          bool resid, const uint16_t* gamma, float eps, uint16_t* xn, hipStream_t st) {
+                          bool resid, const uint16_t* gamma, float eps, uint16_t* xn, hipStream_t st, int xn_rows) {
   hipLaunchKernelGGL(k_combine, dim3(B), dim3(kCombThreads), 0, st, H, k, w, inv, y, h, resid ? 1 : 0, gamma, eps,
-                     xn);
+                     xn, xn_rows);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ struct BankPlan {
 };
 
 struct WsPlan {
-  size_t h, xn, qkv, q, attn_o, part_o, part_ml, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+  size_t h, xn, xp, qkv, q, attn_o, part_o, part_ml, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
       used, n_used, units, n_units, act, y, logits, next, rows, table, total;
 };
 
@@ -133,9 +133,11 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   const size_t nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * D, nch = cap / 64;
   w.h = take(Bm * H * 2);
   w.xn = take(Bm * H * 2);
+  const size_t R = panel_rows(Bm);
+  w.xp = take(R * H * 2);
   w.qkv = take(Bm * nqkv * 2);
   w.q = take(Bm * Hq * D * 2);
-  w.attn_o = take(Bm * Hq * D * 2);
+  w.attn_o = take(R * Hq * D * 2);
   w.part_o = take(Bm * Hq * nch * D * 4);
   w.part_ml = take(Bm * Hq * nch * 2 * 4);
   w.rlogits = take(Bm * E * 4);
@@ -331,36 +333,39 @@ struct ProfScope {
   } while (0)
 
 // One decoder layer on rows whose slot/pos vectors are uploaded.  Input: h
-// (residual) and xn = RMSNorm_attn(h).  Output: h updated; if next_gamma,
-// xn = RMSNorm(h) * next_gamma.
-int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xn, int32_t* ids_out,
+// (residual, row-major) and xp = RMSNorm_attn(h) as an activation panel.
+// Output: h updated; if next_gamma, xp = RMSNorm(h) * next_gamma (panel).
+int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, int32_t* ids_out,
                const uint16_t* next_gamma, hipStream_t st) {
   const w4_model_desc& d = c->d;
   const LayerLoc& L = c->bp.layers[l];
   const int H = d.hidden, nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim, qd = d.n_q_heads * d.head_dim;
+  const int R = panel_rows(c->Bm);
   const int32_t* slot = c->W<int32_t>(c->wp.rows);
   const int32_t* pos = slot + c->Bm;
   KV kv = c->kv();
   uint16_t* qkv = c->W<uint16_t>(c->wp.qkv);
+  uint16_t* xn = c->W<uint16_t>(c->wp.xn);  // MoE input, row-major (gathered by stream)
+  uint16_t* o = c->W<uint16_t>(c->wp.attn_o);
   {
     ProfScope ps(c, W4_K_DENSE, st);
-    LCHK(c, 1, launch_gemm(c->mat(L.qkv), B, xn, H, qkv, nqkv, EPI_F16, st));
+    LCHK(c, 1, launch_gemm(c->mat(L.qkv), B, xp, H, qkv, nqkv, EPI_F16, st, R));
   }
   LCHK(c, 1, launch_rope_append(B, l, d.n_q_heads, kv, slot, pos, qkv, nqkv, c->W<float2>(c->wp.table),
                                 c->W<uint16_t>(c->wp.q), st));
   LCHK(c, 2, launch_attention(B, l, d.n_q_heads, kv, slot, pos, max_pos, c->W<uint16_t>(c->wp.q),
-                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), c->W<uint16_t>(c->wp.attn_o), st,
-                              c->prof_kernel == W4_K_ATTENTION ? c : nullptr));
+                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), o, st,
+                              c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
   {
     ProfScope ps(c, W4_K_DENSE, st);
-    LCHK(c, 1, launch_gemm(c->mat(L.o), B, c->W<uint16_t>(c->wp.attn_o), qd, h, H, EPI_RESID, st));
+    LCHK(c, 1, launch_gemm(c->mat(L.o), B, o, qd, h, H, EPI_RESID, st, R));
   }
   RouteOut r = c->route_out(ids_out);
   {
     ProfScope ps(c, W4_K_ROUTER, st);
-    const Mat R = c->mat(L.router);
+    const Mat Rm = c->mat(L.router);
     LCHK(c, 1, launch_router(B, H, d.n_experts, d.top_k, d.group, h, c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn,
-                             R.tiles, R.scales, r, c->W<unsigned>(c->wp.ticket), st));
+                             Rm.tiles, Rm.scales, r, c->W<unsigned>(c->wp.ticket), st));
   }
   {
     ProfScope ps(c, W4_K_MOE_GATEUP, st);
@@ -371,7 +376,7 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xn, 
     LCHK(c, 1, launch_moe_down(c->mat(L.down), c->W<uint16_t>(c->wp.act), r, c->W<uint16_t>(c->wp.y), st));
   }
   LCHK(c, 1, launch_combine(B, H, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), h, true, next_gamma, d.rms_eps,
-                            xn, st));
+                            xp, st, R));
   return W4_OK;
 }
 
@@ -558,20 +563,21 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
   rc = upload_rows(c, B, slots, st, &max_pos);
   if (rc) return rc;
   uint16_t* h = c->W<uint16_t>(c->wp.h);
-  uint16_t* xn = c->W<uint16_t>(c->wp.xn);
+  uint16_t* xp = c->W<uint16_t>(c->wp.xp);
+  const int R = panel_rows(c->Bm);
   LCHK(c, 1, launch_embed(B, d.hidden, d.vocab, d.group, tokens, c->Bk<uint8_t>(c->bp.emb_p),
-                          c->Bk<uint16_t>(c->bp.emb_s), h, c->Bk<uint16_t>(c->bp.layers[0].attn_norm), d.rms_eps, xn,
-                          st));
+                          c->Bk<uint16_t>(c->bp.emb_s), h, c->Bk<uint16_t>(c->bp.layers[0].attn_norm), d.rms_eps, xp,
+                          st, R));
   for (int l = 0; l < d.n_layers; ++l) {
     const uint16_t* ng = l + 1 < d.n_layers ? c->Bk<uint16_t>(c->bp.layers[l + 1].attn_norm)
                                             : c->Bk<uint16_t>(c->bp.final_norm);
-    rc = layer_body(c, l, B, max_pos, h, xn, route_ids ? route_ids + (size_t)l * B * d.top_k : nullptr, ng, st);
+    rc = layer_body(c, l, B, max_pos, h, xp, route_ids ? route_ids + (size_t)l * B * d.top_k : nullptr, ng, st);
     if (rc) return rc;
   }
   uint16_t* lg = logits ? static_cast<uint16_t*>(logits) : c->W<uint16_t>(c->wp.logits);
   {
     ProfScope ps(c, W4_K_DENSE, st);
-    LCHK(c, 1, launch_gemm(c->mat(c->bp.lm), B, xn, d.hidden, lg, d.vocab, EPI_F16, st));
+    LCHK(c, 1, launch_gemm(c->mat(c->bp.lm), B, xp, d.hidden, lg, d.vocab, EPI_F16, st, R));
   }
   LCHK(c, 1, launch_argmax(B, d.vocab, lg, next, st));
   for (int b = 0; b < B; ++b) c->pos[slots[b]]++;
@@ -693,9 +699,10 @@ int w4_layer_step(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, voi
   rc = upload_rows(c, B, slots, st, &max_pos);
   if (rc) return rc;
   uint16_t* hh = static_cast<uint16_t*>(h);
-  uint16_t* xn = c->W<uint16_t>(c->wp.xn);
-  LCHK(c, 1, launch_rmsnorm(B, c->d.hidden, hh, c->Bk<uint16_t>(c->bp.layers[layer].attn_norm), c->d.rms_eps, xn, st));
-  return layer_body(c, layer, B, max_pos, hh, xn, route_ids, nullptr, st);
+  uint16_t* xp = c->W<uint16_t>(c->wp.xp);
+  LCHK(c, 1, launch_rmsnorm(B, c->d.hidden, hh, c->Bk<uint16_t>(c->bp.layers[layer].attn_norm), c->d.rms_eps, xp, st,
+                            panel_rows(c->Bm)));
+  return layer_body(c, layer, B, max_pos, hh, xp, route_ids, nullptr, st);
 }
 
 const char* w4_status_string(int32_t s) {

@@ -30,14 +30,21 @@ struct Mat {
   int ntiles() const { return (N + 15) / 16; }
 };
 
-// EPI_F32_NORM: fp32 output of RMSNorm(x) * gamma . W^T (gamma, eps, xn given; x rows are raw).
-enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_RESID = 2, EPI_F32_NORM = 3 };
+enum Epi { EPI_F16 = 0, EPI_F32 = 1, EPI_RESID = 2 };
+
+// Activation panel: element (row b, column k) of a [rows][K] fp16 activation
+// at ((k / 8) * rows + b) * 8 + k % 8, rows = max streams rounded up to 16.
+// The dense products read their input from a panel in the decode step (every
+// MFMA operand load then reads 64 contiguous bytes per 4-lane group); the
+// per-stage entry points keep row-major activations (rows = 0 below).
+inline int panel_rows(int max_streams) { return (max_streams + 15) / 16 * 16; }
 
 // ---- launchers (kernels in *.hip); all return hipGetLastError() ----
 hipError_t launch_repack(const uint8_t* src_packed, const uint16_t* src_scales, int count, int N, int K,
                          int g, uint4* dst_tiles, uint16_t* dst_scales, hipStream_t st);
+// xrows > 0: x is a panel with xrows rows (ldx unused); else row-major with stride ldx.
 hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi,
-                       hipStream_t st, const uint16_t* gamma = nullptr, float eps = 0.f, uint16_t* xn = nullptr);
+                       hipStream_t st, int xrows = 0);
 
 struct RouteOut {
   int32_t* ids;          // [B][k]
@@ -68,14 +75,16 @@ hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x
 hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st);
 // h[b] = fp16(h[b] + fp16(sum_r w[b][r] * y[inv[b][r]]))  (resid), or out = fp16(sum ...) (no resid);
 // then optionally xn[b] = RMSNorm(h[b]) * gamma.
+// Normalised outputs (xn, out) go to a panel with that many rows when
+// xn_rows > 0, else row-major [B][H].
 hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* inv, const uint16_t* y,
                           uint16_t* h, bool resid, const uint16_t* gamma, float eps, uint16_t* xn,
-                          hipStream_t st);
+                          hipStream_t st, int xn_rows = 0);
 hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma, float eps, uint16_t* out,
-                          hipStream_t st);
+                          hipStream_t st, int out_rows = 0);
 hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const uint8_t* emb_p,
                         const uint16_t* emb_s, uint16_t* h, const uint16_t* gamma, float eps, uint16_t* xn,
-                        hipStream_t st);
+                        hipStream_t st, int xn_rows = 0);
 hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, hipStream_t st);
 
 struct KV {
@@ -97,7 +106,7 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
 // prof: when non-null, an event is recorded (prof_mark) right before and after the chunk pass.
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
                             int max_pos, const uint16_t* q, float* part_o, float* part_ml, uint16_t* o,
-                            hipStream_t st, void* prof = nullptr);
+                            hipStream_t st, void* prof = nullptr, int o_rows = 0);
 void prof_mark(void* ctx, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
 
