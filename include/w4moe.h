@@ -180,7 +180,7 @@ enum {
   W4_K_DENSE = 1,      /* dense W4A16 products: q/k/v, o, output projection */
   W4_K_MOE_GATEUP = 2, /* grouped expert gate/up + SwiGLU */
   W4_K_MOE_DOWN = 3,   /* grouped expert down */
-  W4_K_ATTENTION = 4,  /* split-KV attention (chunk pass; the chunk reduce is not included) */
+  W4_K_ATTENTION = 4,  /* split-KV decode attention (one launch, split combine included) */
   W4_K_ROUTER = 5      /* MoE front end: norm, router product, top-k, bucketing (one launch) */
 };
 /* Record a HIP event pair around every launch of one kernel family in the

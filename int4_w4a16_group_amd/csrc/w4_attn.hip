@@ -162,210 +162,294 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
 }
 
 // ------------------------------------------------------------------ attention
+// Work-group (split sp, kv head g, stream b) of four waves: wave w takes the
+// 64-position chunk c = 4 sp + w of stream b (positions 64c .. 64c+63, masked
+// beyond the stream's position p).  A stream has nch = p/64 + 1 chunks and
+// ns = ceil(nch/4) splits, functions of its own position only, so its result
+// is the same in any batch.  With z in log2 units (z = S log2(e) / sqrt(D)):
+//   chunk (one wave): S = Q K^T (MFMA); m_c = max z; P = 2^(z - m_c);
+//     l_c = sum P; O_c = P V (MFMA, P as fp16 hi + lo parts, fp32 accumulate);
+//   split (the work-group, chunks in order): M_s = max m_c, a_c = 2^(m_c - M_s),
+//     L_s = sum l_c a_c, O_s = sum O_c a_c;
+//   stream and head (the last work-group of (b, g) to finish, splits in
+//     order): M = max M_s, b_s = 2^(M_s - M), L = sum L_s b_s,
+//     o = sum O_s b_s / L.
+// Split partials are published with device-scope stores and counted with a
+// device-scope ticket per (b, g); the last work-group reads them back with
+// device-scope loads (no cache-wide fence is needed).
 struct AttnArgs {
   KV kv;
-  int layer, Hq, nchmax;
+  int layer, Hq, nsmax;
   const int32_t* slot;
   const int32_t* pos;
   const uint16_t* q;  // [B][Hq][D]
-  float* part_o;      // [B][Hq][nchmax][D]
-  float* part_ml;     // [B][Hq][nchmax][2]  (row max in log2 units, row sum)
-  float scale;        // log2(e) / sqrt(D): scores are kept in log2 units, p = 2^(z - max)
+  float* part_o;      // [B][Hq][nsmax][D]  split partials (unnormalised)
+  float* part_ml;     // [B][Hq][nsmax][2]  (M_s in log2 units, L_s)
+  unsigned* ticket;   // [B][Hkv], zero between launches
+  const int32_t* splits;  // work-group x -> (stream b << 16 | split): every split of every stream, no idle groups
+  uint16_t* o;        // [B][Hq*D]: row-major (o_rows == 0) or an activation panel with o_rows rows
+  int o_rows;
+  float scale;        // log2(e) / sqrt(D)
 };
 
+// Final combine over a stream's splits, in split order: thread -> (head h,
+// four consecutive d).  The partials of NB splits are requested at a time
+// (indices clamped within the last batch) before any is used; they are read
+// with device-scope loads because other work-groups wrote them in this launch.
+template <int D, int NB>
+__device__ void combine_splits(const AttnArgs& a, int b, int g, int G, int ns, int tid) {
+  for (int i = tid; i < G * D / 4; i += 256) {
+    const int h = i / (D / 4), d0 = (i - h * (D / 4)) * 4;
+    const size_t row = (size_t)b * a.Hq + g * G + h;
+    const float* ml = a.part_ml + row * a.nsmax * 2;
+    const float* po = a.part_o + row * a.nsmax * D + d0;
+    // M over every split first; when all splits fit one batch (ns <= NB) the
+    // batch loaded below gives it, with no separate pass.
+    float M = -INFINITY;
+    if (ns > NB) {
+      for (int s0 = 0; s0 < ns; s0 += NB) {
+        float mv[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          mv[j] = __hip_atomic_load(ml + 2 * min(s0 + j, ns - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) M = fmaxf(M, mv[j]);  // clamped duplicates do not change a max
+      }
+    }
+    float L = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += NB) {
+      float mv[NB], lv[NB], ov[NB][4];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int s2 = min(s0 + j, ns - 1);
+        mv[j] = __hip_atomic_load(ml + 2 * s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lv[j] = __hip_atomic_load(ml + 2 * s2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          ov[j][k] = __hip_atomic_load(po + (size_t)s2 * D + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (ns <= NB) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) M = fmaxf(M, mv[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (s0 + j < ns) {
+          const float bs = __builtin_amdgcn_exp2f(mv[j] - M);
+          L = L + lv[j] * bs;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[k] = acc[k] + ov[j][k] * bs;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int kk = (g * G + h) * D + d0 + k;  // column of the [B][Hq*D] output
+      const size_t off =
+          a.o_rows ? ((size_t)(kk >> 3) * a.o_rows + b) * 8 + (kk & 7) : (size_t)b * a.Hq * D + kk;
+      a.o[off] = f2h(acc[k] / L);
+    }
+  }
+}
+
 template <int D>
-__global__ void __launch_bounds__(64) k_attn(AttnArgs a) {
+__global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
   constexpr int KSQ = D / 32;  // k-steps of q.K
   constexpr int NDT = D / 16;  // output d-tiles
-  __shared__ float Pl[16][65];
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  __shared__ float Pl[4][16][65];
+  __shared__ float s_m[4][16], s_l[4][16];
+  __shared__ float s_a[4][16];
+  __shared__ int s_last;
+  extern __shared__ float Ob[];  // [4 waves][G][D]
+  const int bs_ = a.splits[blockIdx.x];
+  const int b = bs_ >> 16, sp = bs_ & 0xFFFF, g = blockIdx.y;
   const int p = a.pos[b];
-  if (c * 64 > p) return;
-  const int lane = threadIdx.x;
-  const int G = a.Hq / a.kv.Hkv;
-  const int s = a.slot[b];
-  const size_t base = kv_base(a.kv, a.layer, s, g);
-  const uint16_t* Kb = a.kv.K + base;
-  const uint16_t* Vb = a.kv.VT + base;
-  const int c0 = c * 64;
+  const int nch = p / 64 + 1, ns = attn_splits(p);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int Hkv = a.kv.Hkv, G = a.Hq / Hkv;
+  const int c = 4 * sp + w;
+  const bool live = c < nch;  // this wave's chunk holds positions <= p
   const int col = lane & 15, quad = lane >> 4;
-  const bool last = (c0 + 63 > p);
-
-  // K operands first (the scores need them first), then V, all in flight
-  // together; each load is 1 KB contiguous across the wave.
-  const uint16_t* Kc = Kb + (size_t)c * 64 * D + lane * 8;
-  const uint16_t* Vc = Vb + (size_t)c * 64 * D + lane * 8;
-  h8 kb[4][KSQ];
+  float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lrow[4] = {0.f, 0.f, 0.f, 0.f};
+  f4 oacc[NDT];
 #pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    const size_t base = kv_base(a.kv, a.layer, a.slot[b], g);
+    const int c0 = c * 64;
+    const bool last = (c0 + 63 > p);
+    // K operands first (the scores need them first), then V, all in flight
+    // together; each load is 1 KB contiguous across the wave.
+    const uint16_t* Kc = a.kv.K + base + (size_t)c * 64 * D + lane * 8;
+    const uint16_t* Vc = a.kv.VT + base + (size_t)c * 64 * D + lane * 8;
+    h8 kb[4][KSQ];
 #pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(Kc + (pt * KSQ + ks) * 512);
-  h8 vop[NDT][2];
+    for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
-  // Q operand: rows = the G query heads of kv head g (rows >= G are zero).
-  h8 qa[KSQ];
-  {
-    const uint16_t* qp = a.q + ((size_t)b * a.Hq + g * G + col) * D + 8 * quad;
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) qa[ks] = col < G ? ld_h8(qp + 32 * ks) : h8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-  // scores: lane holds S[head 4*quad + r][pos c0 + 16*pt + col]
-  f4 S[4];
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt) {
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(qa[ks], kb[pt][ks], acc);
-    S[pt] = acc;
-  }
-  float mrow[4], lrow[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const int pp = c0 + pt * 16 + col;
-      const float z = S[pt][r] * a.scale;
-      S[pt][r] = pp > p ? -INFINITY : z;
-      m = fmaxf(m, S[pt][r]);
-    }
-    m = row16_max(m);
-    float l = 0.f;
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const float e = __builtin_amdgcn_exp2f(S[pt][r] - m);
-      S[pt][r] = e;
-      l = l + e;
-    }
-    l = row16_sum(l);
-    mrow[r] = m;
-    lrow[r] = l;
-  }
-#pragma unroll
-  for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Pl[4 * quad + r][pt * 16 + col] = S[pt][r];
-  __syncthreads();
-  // P as the A operand (row = head col, k = positions 32ks + 8quad + j), hi + lo fp16.
-  h8 phi[2], plo[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float pv = Pl[col][32 * ks + 8 * quad + j];
-      const _Float16 hi = (_Float16)pv;
-      phi[ks][j] = hi;
-      plo[ks][j] = (_Float16)(pv - (float)hi);
-    }
-  if (last) {
+      for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(Kc + (pt * KSQ + ks) * 512);
+    h8 vop[NDT][2];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
+    // Q operand: rows = the G query heads of kv head g (rows >= G are zero).
+    h8 qa[KSQ];
+    {
+      const uint16_t* qp = a.q + ((size_t)b * a.Hq + g * G + col) * D + 8 * quad;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (c0 + 32 * ks + 8 * quad + j > p) vop[dt][ks][j] = (_Float16)0.0f;
-  }
-  float* po = a.part_o + (((size_t)b * a.Hq + g * G) * a.nchmax + c) * D;
+      for (int ks = 0; ks < KSQ; ++ks) qa[ks] = col < G ? ld_h8(qp + 32 * ks) : h8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    // scores: lane holds S[head 4*quad + r][pos c0 + 16*pt + col]
+    f4 S[4];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    f4 o = {0.f, 0.f, 0.f, 0.f};
+    for (int pt = 0; pt < 4; ++pt) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      o = mfma16x16x32(phi[ks], vop[dt][ks], o);
-      o = mfma16x16x32(plo[ks], vop[dt][ks], o);
+      for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(qa[ks], kb[pt][ks], acc);
+      S[pt] = acc;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int h = 4 * quad + r;
-      if (h < G) po[(size_t)h * a.nchmax * D + dt * 16 + col] = o[r];
+      float m = -INFINITY;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int pp = c0 + pt * 16 + col;
+        const float z = S[pt][r] * a.scale;
+        S[pt][r] = pp > p ? -INFINITY : z;
+        m = fmaxf(m, S[pt][r]);
+      }
+      m = row16_max(m);
+      float l = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const float e = __builtin_amdgcn_exp2f(S[pt][r] - m);
+        S[pt][r] = e;
+        l = l + e;
+      }
+      l = row16_sum(l);
+      mrow[r] = m;
+      lrow[r] = l;
+    }
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Pl[w][4 * quad + r][pt * 16 + col] = S[pt][r];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P is in LDS
+    __builtin_amdgcn_wave_barrier();
+    // P as the A operand (row = head col, k = positions 32ks + 8quad + j), hi + lo fp16.
+    h8 phi[2], plo[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pv = Pl[w][col][32 * ks + 8 * quad + j];
+        const _Float16 hi = (_Float16)pv;
+        phi[ks][j] = hi;
+        plo[ks][j] = (_Float16)(pv - (float)hi);
+      }
+    if (last) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c0 + 32 * ks + 8 * quad + j > p) vop[dt][ks][j] = (_Float16)0.0f;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      f4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        o = mfma16x16x32(phi[ks], vop[dt][ks], o);
+        o = mfma16x16x32(plo[ks], vop[dt][ks], o);
+      }
+      oacc[dt] = o;
     }
   }
+  // chunk results to LDS: heads h < G of this wave
+  float* ob = Ob + (size_t)w * G * D;
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * quad + r;
+      if (h < G) ob[h * D + dt * 16 + col] = oacc[dt][r];
+    }
   if (col == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int h = 4 * quad + r;
-      if (h < G) {
-        float* ml = a.part_ml + (((size_t)b * a.Hq + g * G + h) * a.nchmax + c) * 2;
-        ml[0] = mrow[r];
-        ml[1] = lrow[r];
-      }
+      s_m[w][4 * quad + r] = mrow[r];
+      s_l[w][4 * quad + r] = lrow[r];
     }
   }
-}
-
-// One wave per (head, stream): combine the stream's chunks.  Output o is
-// [B][Hq*D], row-major (rows == 0) or an activation panel with that many rows.  Lane c holds
-// chunk c (c + 64, ... beyond 64 chunks); M and L are wave reductions with a
-// fixed tree, then every lane sums its columns over the chunks in order.
-// nchmax <= 256 (ctx_cap <= 16384, checked at context creation).
-__global__ void __launch_bounds__(64) k_attn_reduce(int Hq, int D, int nchmax, const int32_t* __restrict__ pos,
-                                                    const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml, uint16_t* __restrict__ o,
-                                                    int rows) {
-  __shared__ float wgt[256];
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int nch = (pos[b] + 1 + 63) / 64;
-  const float* ml = part_ml + ((size_t)b * Hq + h) * nchmax * 2;
-  float mv[4], lv[4];
-  float M = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = lane + 64 * j;
-    mv[j] = c < nch ? ml[2 * c] : -INFINITY;
-    lv[j] = c < nch ? ml[2 * c + 1] : 0.f;
-    M = fmaxf(M, mv[j]);
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  float L = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = lane + 64 * j;
-    const float e = c < nch ? __builtin_amdgcn_exp2f(mv[j] - M) : 0.f;
-    if (c < nch) wgt[c] = e;
-    L = L + lv[j] * e;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) L = L + __shfl_xor(L, off, 64);
   __syncthreads();
-  const float* po = part_o + ((size_t)b * Hq + h) * nchmax * D;
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    for (int c = 0; c < nch; ++c) acc = acc + po[(size_t)c * D + d] * wgt[c];
-    const int kk = h * D + d;  // column of the [B][Hq*D] output
-    const size_t off = rows ? ((size_t)(kk >> 3) * rows + b) * 8 + (kk & 7) : (size_t)b * Hq * D + kk;
-    o[off] = f2h(acc / L);
+  // split combine, chunks (waves) in order
+  if (tid < G) {
+    float M = s_m[0][tid];
+    for (int ww = 1; ww < 4; ++ww) M = fmaxf(M, s_m[ww][tid]);
+    float L = 0.f;
+    for (int ww = 0; ww < 4; ++ww) {
+      const float al = s_m[ww][tid] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_m[ww][tid] - M);
+      s_a[ww][tid] = al;
+      L = L + s_l[ww][tid] * al;
+    }
+    float* ml = a.part_ml + (((size_t)b * a.Hq + g * G + tid) * a.nsmax + sp) * 2;
+    __hip_atomic_store(ml, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(ml + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += 256) {
+    const int h = i / D, d = i - h * D;
+    float v = Ob[(size_t)h * D + d] * s_a[0][h];
+    for (int ww = 1; ww < 4; ++ww) v = v + Ob[((size_t)ww * G + h) * D + d] * s_a[ww][h];
+    __hip_atomic_store(a.part_o + (((size_t)b * a.Hq + g * G + h) * a.nsmax + sp) * D + d, v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // every partial store complete before the ticket
+  __syncthreads();
+  unsigned* tk = a.ticket + (size_t)b * Hkv + g;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(ns - 1);
+  __syncthreads();
+  if (!s_last) return;
+  if (ns <= 2)
+    combine_splits<D, 2>(a, b, g, G, ns, tid);
+  else if (ns <= 4)
+    combine_splits<D, 4>(a, b, g, G, ns, tid);
+  else if (ns <= 8)
+    combine_splits<D, 8>(a, b, g, G, ns, tid);
+  else
+    combine_splits<D, 16>(a, b, g, G, ns, tid);
+  if (tid == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
-                            int max_pos, const uint16_t* q, float* part_o, float* part_ml, uint16_t* o,
-                            hipStream_t st, void* prof, int o_rows) {
+                            const int32_t* splits, int nsplits, const uint16_t* q, float* part_o, float* part_ml,
+                            unsigned* ticket, uint16_t* o, hipStream_t st, void* prof, int o_rows) {
+  (void)B;
   AttnArgs a;
   a.kv = kv;
   a.layer = layer;
   a.Hq = Hq;
-  a.nchmax = kv.cap / 64;
+  a.nsmax = attn_splits(kv.cap - 1);
   a.slot = slot;
   a.pos = pos;
   a.q = q;
   a.part_o = part_o;
   a.part_ml = part_ml;
+  a.ticket = ticket;
+  a.splits = splits;
+  a.o = o;
+  a.o_rows = o_rows;
   a.scale = (float)(1.4426950408889634 / sqrt((double)kv.D));
-  const int nch = (max_pos + 1 + 63) / 64;
-  dim3 grid(nch, kv.Hkv, B);
+  dim3 grid(nsplits, kv.Hkv);
+  const size_t shm = (size_t)4 * (Hq / kv.Hkv) * kv.D * sizeof(float);
   if (prof) prof_mark(prof, st);
   if (kv.D == 128)
-    hipLaunchKernelGGL(k_attn<128>, grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), shm, st, a);
   else
-    hipLaunchKernelGGL(k_attn<64>, grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), shm, st, a);
   if (prof) prof_mark(prof, st);
-  hipLaunchKernelGGL(k_attn_reduce, dim3(Hq, B), dim3(64), 0, st, Hq, kv.D, a.nchmax, pos, part_o, part_ml, o,
-                     o_rows);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ struct BankPlan {
 };
 
 struct WsPlan {
-  size_t h, xn, xp, qkv, q, attn_o, part_o, part_ml, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+  size_t h, xn, xp, qkv, q, attn_o, part_o, part_ml, aticket, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
       used, n_used, units, n_units, act, y, logits, next, rows, table, total;
 };
 
@@ -140,6 +140,7 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.attn_o = take(R * Hq * D * 2);
   w.part_o = take(Bm * Hq * nch * D * 4);
   w.part_ml = take(Bm * Hq * nch * 2 * 4);
+  w.aticket = take(Bm * d.n_kv_heads * 4);
   w.rlogits = take(Bm * E * 4);
   w.ticket = take(64);
   w.ids = take(Bm * k * 4);
@@ -157,7 +158,7 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.y = take(Bm * k * H * 2);
   w.logits = take((size_t)Bm * d.vocab * 2);
   w.next = take(Bm * 4);
-  w.rows = take(2 * Bm * 4);  // slot ids then positions of the current rows
+  w.rows = take((2 * Bm + (size_t)Bm * attn_splits(cap - 1)) * 4);  // slot ids, positions, attention split list
   w.table = take((size_t)cap * (D / 2) * 8);
   w.total = cur;
   return w;
@@ -178,6 +179,8 @@ struct w4_ctx {
   bool dev_ready = false, table_ready = false;
   int device = -1;
   int32_t* pinned = nullptr;
+  int nsplits = 0;  // attention splits of the rows last uploaded
+  size_t row_words() const { return 2 * (size_t)Bm + (size_t)Bm * attn_splits(cap - 1); }
   hipEvent_t ev[kRing] = {};
   bool ev_used[kRing] = {};
   int ring = 0;
@@ -260,7 +263,7 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
     HIPCHK(c, hipGetDeviceProperties(&prop, dev));
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
       return fail(c, W4_E_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", library built for gfx950");
-    HIPCHK(c, hipHostMalloc((void**)&c->pinned, sizeof(int32_t) * 2 * c->Bm * kRing, hipHostMallocDefault));
+    HIPCHK(c, hipHostMalloc((void**)&c->pinned, sizeof(int32_t) * c->row_words() * kRing, hipHostMallocDefault));
     for (int i = 0; i < kRing; ++i) HIPCHK(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
     c->device = dev;
     c->dev_ready = true;
@@ -268,7 +271,8 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
   if (!c->table_ready) {
     HIPCHK(c, launch_rope_table(c->cap, c->d.head_dim, (double)c->d.rope_theta, c->W<float2>(c->wp.table), st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.ticket), 0u, 16, st));
-    c->launches += 2;
+    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.aticket), 0u, (size_t)c->Bm * c->d.n_kv_heads, st));
+    c->launches += 3;
     c->table_ready = true;
   }
   return W4_OK;
@@ -298,16 +302,20 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
     HIPCHK(c, hipEventSynchronize(c->ev[i]));
     c->syncs++;
   }
-  int32_t* p = c->pinned + (size_t)i * 2 * c->Bm;
-  int mp = 0;
+  int32_t* p = c->pinned + (size_t)i * c->row_words();
+  int32_t* split = p + 2 * c->Bm;
+  int mp = 0, n = 0;
   for (int b = 0; b < B; ++b) {
+    const int pos = c->pos[slots[b]];
     p[b] = slots[b];
-    p[c->Bm + b] = c->pos[slots[b]];
-    mp = std::max(mp, c->pos[slots[b]]);
+    p[c->Bm + b] = pos;
+    mp = std::max(mp, pos);
+    for (int sp = 0; sp < attn_splits(pos); ++sp) split[n++] = (b << 16) | sp;
   }
-  HIPCHK(c, hipMemcpyAsync(c->W<int32_t>(c->wp.rows), p, sizeof(int32_t) * 2 * c->Bm, hipMemcpyHostToDevice, st));
+  HIPCHK(c, hipMemcpyAsync(c->W<int32_t>(c->wp.rows), p, sizeof(int32_t) * (2 * c->Bm + n), hipMemcpyHostToDevice, st));
   HIPCHK(c, hipEventRecord(c->ev[i], st));
   c->ev_used[i] = true;
+  c->nsplits = n;
   if (max_pos) *max_pos = mp;
   return W4_OK;
 }
@@ -353,9 +361,9 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
   }
   LCHK(c, 1, launch_rope_append(B, l, d.n_q_heads, kv, slot, pos, qkv, nqkv, c->W<float2>(c->wp.table),
                                 c->W<uint16_t>(c->wp.q), st));
-  LCHK(c, 2, launch_attention(B, l, d.n_q_heads, kv, slot, pos, max_pos, c->W<uint16_t>(c->wp.q),
-                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), o, st,
-                              c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
+  LCHK(c, 1, launch_attention(B, l, d.n_q_heads, kv, slot, pos, pos + c->Bm, c->nsplits, c->W<uint16_t>(c->wp.q),
+                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), c->W<unsigned>(c->wp.aticket), o,
+                              st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
   {
     ProfScope ps(c, W4_K_DENSE, st);
     LCHK(c, 1, launch_gemm(c->mat(L.o), B, o, qd, h, H, EPI_RESID, st, R));
@@ -679,8 +687,9 @@ int w4_attn_decode(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, co
   KV kv = c->kv();
   LCHK(c, 1, launch_append(B, layer, kv, slot, pos, static_cast<const uint16_t*>(k_new),
                            static_cast<const uint16_t*>(v_new), st));
-  LCHK(c, 2, launch_attention(B, layer, c->d.n_q_heads, kv, slot, pos, max_pos, static_cast<const uint16_t*>(q),
-                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), static_cast<uint16_t*>(o), st,
+  LCHK(c, 1, launch_attention(B, layer, c->d.n_q_heads, kv, slot, pos, pos + c->Bm, c->nsplits,
+                              static_cast<const uint16_t*>(q), c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
+                              c->W<unsigned>(c->wp.aticket), static_cast<uint16_t*>(o), st,
                               c->prof_kernel == W4_K_ATTENTION ? c : nullptr));
   return W4_OK;
 }

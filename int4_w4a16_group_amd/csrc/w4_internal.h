@@ -104,9 +104,16 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
                        hipStream_t st);
 // split-KV decode attention; part_o [B][Hq][nchmax][D] f32, part_ml [B][Hq][nchmax][2].
 // prof: when non-null, an event is recorded (prof_mark) right before and after the chunk pass.
+// Split-KV decode attention in one launch.  A stream at position p has
+// attn_splits(p) splits of 256 positions; splits [nsplits] lists (b << 16 |
+// split) for every split of every row (built on the host with the rows).  The
+// last work-group of each (stream, kv head) combines the splits; ticket
+// [B][Hkv] is zero before and after.  o: [B][Hq*D] row-major, or an
+// activation panel with o_rows rows.
+__host__ __device__ inline int attn_splits(int pos) { return (pos / 64 + 1 + 3) / 4; }
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
-                            int max_pos, const uint16_t* q, float* part_o, float* part_ml, uint16_t* o,
-                            hipStream_t st, void* prof = nullptr, int o_rows = 0);
+                            const int32_t* splits, int nsplits, const uint16_t* q, float* part_o, float* part_ml,
+                            unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0);
 void prof_mark(void* ctx, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
 
