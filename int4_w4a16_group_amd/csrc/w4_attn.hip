@@ -83,63 +83,6 @@ static __device__ __forceinline__ size_t v_off(int D, int p, int d) {
   return (size_t)(p >> 6) * 64 * D + (size_t)(((((d >> 4) * 2 + (q >> 5)) * 4 + ((q & 31) >> 3)) * 16 + (d & 15)) * 8 + (q & 7));
 }
 
-// Rotary on the q and k heads of qkv[b] (rotate-half pairs (i, i+D/2)), then
-// append k (rotated) and v at position pos[b] of slot[b]; rotated q -> q_out.
-__global__ void k_rope_append(int layer, int Hq, KV kv, const int32_t* __restrict__ slot,
-                              const int32_t* __restrict__ pos, const uint16_t* __restrict__ qkv, int ldqkv,
-                              const float2* __restrict__ table, uint16_t* __restrict__ q_out) {
-  const int b = blockIdx.x;
-  const int D = kv.D, half = D / 2, Hkv = kv.Hkv;
-  const int p = pos[b], s = slot[b];
-  const uint16_t* src = qkv + (size_t)b * ldqkv;
-  const int npairs = (Hq + Hkv) * half;
-  for (int idx = threadIdx.x; idx < npairs; idx += blockDim.x) {
-    const int h = idx / half, i = idx - h * half;
-    const float2 cs = table[(size_t)p * half + i];
-    const float a = h2f(src[h * D + i]), bb = h2f(src[h * D + i + half]);
-    const uint16_t o0 = f2h(a * cs.x - bb * cs.y);
-    const uint16_t o1 = f2h(a * cs.y + bb * cs.x);
-    if (h < Hq) {
-      q_out[((size_t)b * Hq + h) * D + i] = o0;
-      q_out[((size_t)b * Hq + h) * D + i + half] = o1;
-    } else {
-      uint16_t* kb = kv.K + kv_base(kv, layer, s, h - Hq);
-      kb[k_off(D, p, i)] = o0;
-      kb[k_off(D, p, i + half)] = o1;
-    }
-  }
-  const uint16_t* vsrc = src + (Hq + Hkv) * D;
-  for (int idx = threadIdx.x; idx < Hkv * D; idx += blockDim.x) {
-    const int g = idx / D, d = idx - g * D;
-    kv.VT[kv_base(kv, layer, s, g) + v_off(D, p, d)] = vsrc[idx];
-  }
-}
-
-hipError_t launch_rope_append(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
-                              const uint16_t* qkv, int ldqkv, const float2* table, uint16_t* q_out,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(k_rope_append, dim3(B), dim3(256), 0, st, layer, Hq, kv, slot, pos, qkv, ldqkv, table, q_out);
-  return hipGetLastError();
-}
-
-__global__ void k_append(int layer, KV kv, const int32_t* __restrict__ slot, const int32_t* __restrict__ pos,
-                         const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new) {
-  const int b = blockIdx.x;
-  const int p = pos[b], s = slot[b], D = kv.D;
-  for (int idx = threadIdx.x; idx < kv.Hkv * D; idx += blockDim.x) {
-    const int g = idx / D, d = idx - g * D;
-    const size_t base = kv_base(kv, layer, s, g);
-    kv.K[base + k_off(D, p, d)] = k_new[(size_t)b * kv.Hkv * D + idx];
-    kv.VT[base + v_off(D, p, d)] = v_new[(size_t)b * kv.Hkv * D + idx];
-  }
-}
-
-hipError_t launch_append(int B, int layer, const KV& kv, const int32_t* slot, const int32_t* pos,
-                         const uint16_t* k_new, const uint16_t* v_new, hipStream_t st) {
-  hipLaunchKernelGGL(k_append, dim3(B), dim3(256), 0, st, layer, kv, slot, pos, k_new, v_new);
-  return hipGetLastError();
-}
-
 // Seed a slot from canonical k, v [L][P][Hkv][D].  Block (pos chunk of 64, layer*Hkv + g).
 __global__ void k_seed(int P, int slot, KV kv, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v) {
   const int p0 = blockIdx.x * 64;
@@ -182,7 +125,14 @@ struct AttnArgs {
   int layer, Hq, nsmax;
   const int32_t* slot;
   const int32_t* pos;
-  const uint16_t* q;  // [B][Hq][D]
+  // this step's q, k, v of stream b: q at q + b*ldq ([Hq][D]), k and v at
+  // knew/vnew + b*ldkv ([Hkv][D]); rotated at the stream's position through
+  // table (cos, sin of p * theta^(-2i/D), [cap][D/2]) when table is not null
+  const uint16_t* q;
+  const uint16_t* knew;
+  const uint16_t* vnew;
+  int ldq, ldkv;
+  const float2* table;
   float* part_o;      // [B][Hq][nsmax][D]  split partials (unnormalised)
   float* part_ml;     // [B][Hq][nsmax][2]  (M_s in log2 units, L_s)
   unsigned* ticket;   // [B][Hkv], zero between launches
@@ -258,6 +208,7 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
   __shared__ float Pl[4][16][65];
   __shared__ float s_m[4][16], s_l[4][16];
   __shared__ float s_a[4][16];
+  __shared__ __align__(16) uint16_t s_k[4][D];
   __shared__ int s_last;
   extern __shared__ float Ob[];  // [4 waves][G][D]
   const int bs_ = a.splits[blockIdx.x];
@@ -291,12 +242,70 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
-    // Q operand: rows = the G query heads of kv head g (rows >= G are zero).
+    // The wave whose chunk holds position p: this step's k (rotated) and v go
+    // into the arena at p and replace what the loads above read there.
+    if (c == (p >> 6)) {
+      uint16_t* Ka = a.kv.K + base;
+      uint16_t* Va = a.kv.VT + base;
+      const uint16_t* kp = a.knew + (size_t)b * a.ldkv + g * D;
+      const uint16_t* vp = a.vnew + (size_t)b * a.ldkv + g * D;
+      if (lane < D / 2) {
+        const float x0 = h2f(kp[lane]), x1 = h2f(kp[lane + D / 2]);
+        uint16_t k0 = kp[lane], k1 = kp[lane + D / 2];
+        if (a.table) {
+          const float2 cs = a.table[(size_t)p * (D / 2) + lane];
+          k0 = f2h(x0 * cs.x - x1 * cs.y);
+          k1 = f2h(x0 * cs.y + x1 * cs.x);
+        }
+        s_k[w][lane] = k0;
+        s_k[w][lane + D / 2] = k1;
+        Ka[k_off(D, p, lane)] = k0;
+        Ka[k_off(D, p, lane + D / 2)] = k1;
+      }
+      for (int d = lane; d < D; d += 64) Va[v_off(D, p, d)] = vp[d];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): s_k written
+      __builtin_amdgcn_wave_barrier();
+      // K operand: position p is column p%16 of position tile (p%64)/16
+      const int ptp = (p & 63) >> 4, colp = p & 15;
+      h8 kf[KSQ];
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) kf[ks] = *reinterpret_cast<const h8*>(&s_k[w][32 * ks + 8 * quad]);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int ks = 0; ks < KSQ; ++ks)
+          if (pt == ptp && col == colp) kb[pt][ks] = kf[ks];
+      // V operand: position p is element p%8 of k-step (p%64)/32 in lane quad (p%32)/8
+      const int ksp = (p & 63) >> 5, qdp = (p & 31) >> 3, jp = p & 7;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const _Float16 vf = __builtin_bit_cast(_Float16, vp[16 * dt + col]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (ks == ksp && quad == qdp && j == jp) vop[dt][ks][j] = vf;
+      }
+    }
+    // Q operand: rows = the G query heads of kv head g (rows >= G are zero),
+    // rotated pairs (i, i + D/2) = k-steps (ks, ks + KSQ/2) of the same lane.
     h8 qa[KSQ];
     {
-      const uint16_t* qp = a.q + ((size_t)b * a.Hq + g * G + col) * D + 8 * quad;
+      const uint16_t* qp = a.q + (size_t)b * a.ldq + (g * G + col) * D + 8 * quad;
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) qa[ks] = col < G ? ld_h8(qp + 32 * ks) : h8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (a.table && col < G) {
+        const float2* tr = a.table + (size_t)p * (D / 2) + 8 * quad;
+#pragma unroll
+        for (int ks = 0; ks < KSQ / 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float2 cs = tr[32 * ks + j];
+            const float x0 = (float)qa[ks][j], x1 = (float)qa[ks + KSQ / 2][j];
+            qa[ks][j] = (_Float16)(x0 * cs.x - x1 * cs.y);
+            qa[ks + KSQ / 2][j] = (_Float16)(x0 * cs.y + x1 * cs.x);
+          }
+      }
     }
     // scores: lane holds S[head 4*quad + r][pos c0 + 16*pt + col]
     f4 S[4];
@@ -424,7 +433,8 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
 }
 
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
-                            const int32_t* splits, int nsplits, const uint16_t* q, float* part_o, float* part_ml,
+                            const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
+                            const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
                             unsigned* ticket, uint16_t* o, hipStream_t st, void* prof, int o_rows) {
   (void)B;
   AttnArgs a;
@@ -435,6 +445,11 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   a.slot = slot;
   a.pos = pos;
   a.q = q;
+  a.knew = knew;
+  a.vnew = vnew;
+  a.ldq = ldq;
+  a.ldkv = ldkv;
+  a.table = table;
   a.part_o = part_o;
   a.part_ml = part_ml;
   a.ticket = ticket;

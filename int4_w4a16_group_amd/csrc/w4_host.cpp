@@ -42,7 +42,7 @@ struct BankPlan {
 };
 
 struct WsPlan {
-  size_t h, xn, xp, qkv, q, attn_o, part_o, part_ml, aticket, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
       used, n_used, units, n_units, act, y, logits, next, rows, table, total;
 };
 
@@ -136,7 +136,6 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   const size_t R = panel_rows(Bm);
   w.xp = take(R * H * 2);
   w.qkv = take(Bm * nqkv * 2);
-  w.q = take(Bm * Hq * D * 2);
   w.attn_o = take(R * Hq * D * 2);
   w.part_o = take(Bm * Hq * nch * D * 4);
   w.part_ml = take(Bm * Hq * nch * 2 * 4);
@@ -359,11 +358,10 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
     ProfScope ps(c, W4_K_DENSE, st);
     LCHK(c, 1, launch_gemm(c->mat(L.qkv), B, xp, H, qkv, nqkv, EPI_F16, st, R));
   }
-  LCHK(c, 1, launch_rope_append(B, l, d.n_q_heads, kv, slot, pos, qkv, nqkv, c->W<float2>(c->wp.table),
-                                c->W<uint16_t>(c->wp.q), st));
-  LCHK(c, 1, launch_attention(B, l, d.n_q_heads, kv, slot, pos, pos + c->Bm, c->nsplits, c->W<uint16_t>(c->wp.q),
-                              c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml), c->W<unsigned>(c->wp.aticket), o,
-                              st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
+  LCHK(c, 1, launch_attention(B, l, d.n_q_heads, kv, slot, pos, pos + c->Bm, c->nsplits, qkv, nqkv,
+                              qkv + (size_t)d.n_q_heads * d.head_dim, qkv + (size_t)(d.n_q_heads + d.n_kv_heads) * d.head_dim,
+                              nqkv, c->W<float2>(c->wp.table), c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
+                              c->W<unsigned>(c->wp.aticket), o, st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
   {
     ProfScope ps(c, W4_K_DENSE, st);
     LCHK(c, 1, launch_gemm(c->mat(L.o), B, o, qd, h, H, EPI_RESID, st, R));
@@ -685,10 +683,10 @@ int w4_attn_decode(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, co
   const int32_t* slot = c->W<int32_t>(c->wp.rows);
   const int32_t* pos = slot + c->Bm;
   KV kv = c->kv();
-  LCHK(c, 1, launch_append(B, layer, kv, slot, pos, static_cast<const uint16_t*>(k_new),
-                           static_cast<const uint16_t*>(v_new), st));
-  LCHK(c, 1, launch_attention(B, layer, c->d.n_q_heads, kv, slot, pos, pos + c->Bm, c->nsplits,
-                              static_cast<const uint16_t*>(q), c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
+  const int Hq = c->d.n_q_heads, Hkv = c->d.n_kv_heads, D = c->d.head_dim;
+  LCHK(c, 1, launch_attention(B, layer, Hq, kv, slot, pos, pos + c->Bm, c->nsplits, static_cast<const uint16_t*>(q),
+                              Hq * D, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), Hkv * D,
+                              nullptr, c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
                               c->W<unsigned>(c->wp.aticket), static_cast<uint16_t*>(o), st,
                               c->prof_kernel == W4_K_ATTENTION ? c : nullptr));
   return W4_OK;

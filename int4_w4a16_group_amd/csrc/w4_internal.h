@@ -93,13 +93,6 @@ struct KV {
   int S, Hkv, cap, D;
 };
 hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStream_t st);
-// q/k rotary at each stream's position, K/V append into the arena; q_out [B][Hq][D].
-hipError_t launch_rope_append(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
-                              const uint16_t* qkv, int ldqkv, const float2* table, uint16_t* q_out,
-                              hipStream_t st);
-// plain K/V append (no rotary): k_new/v_new [B][Hkv][D].
-hipError_t launch_append(int B, int layer, const KV& kv, const int32_t* slot, const int32_t* pos,
-                         const uint16_t* k_new, const uint16_t* v_new, hipStream_t st);
 hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, const uint16_t* v,
                        hipStream_t st);
 // split-KV decode attention; part_o [B][Hq][nchmax][D] f32, part_ml [B][Hq][nchmax][2].
@@ -108,11 +101,14 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
 // attn_splits(p) splits of 256 positions; splits [nsplits] lists (b << 16 |
 // split) for every split of every row (built on the host with the rows).  The
 // last work-group of each (stream, kv head) combines the splits; ticket
-// [B][Hkv] is zero before and after.  o: [B][Hq*D] row-major, or an
-// activation panel with o_rows rows.
+// [B][Hkv] is zero before and after.  This step's q (row stride ldq) and k,
+// v (row stride ldkv) are rotated at each stream's position through table
+// when it is not null; k and v are appended to the arena at the position.
+// o: [B][Hq*D] row-major, or an activation panel with o_rows rows.
 __host__ __device__ inline int attn_splits(int pos) { return (pos / 64 + 1 + 3) / 4; }
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
-                            const int32_t* splits, int nsplits, const uint16_t* q, float* part_o, float* part_ml,
+                            const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
+                            const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
                             unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0);
 void prof_mark(void* ctx, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);

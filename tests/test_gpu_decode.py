@@ -159,7 +159,7 @@ def test_batch_invariants_bitwise(gpu, small_model):
     ref = [ref_run.step(slots, tokens)[0] for _ in range(3)]      # three steps, B = 4
     launches, syncs = L.w4_last_step_counts(ref_run.ctx.ctx)
     # per layer: q/k/v, rotary+append, attention chunks + reduce, o, norm+router, routing, gate/up, down, combine
-    assert syncs == 0 and launches == 1 + SMALL.n_layers * 8 + 2
+    assert syncs == 0 and launches == 1 + SMALL.n_layers * 7 + 2
     ref_run.ctx.close()
     # I7: each stream stepped alone (B = 1), in separate calls, gives the same bits
     run, slots = _fresh(gpu, mw, prompts)
