@@ -348,9 +348,8 @@ struct MoeArgs {
   size_t scale_stride;    // halves per expert
   const uint16_t* x;      // gate/up: rows by stream; down: rows by pair
   int ldx;
-  const int32_t* offsets;
-  const int32_t* pair_stream;
-  const int2* units;      // (expert, first row) of every 16-row unit, experts ascending
+  const int4* units;      // (expert, first pair, rows, 0) of every 16-row unit, experts ascending
+  const int32_t* unit_rows;  // [unit][16] stream of each row (gate/up input rows)
   const int32_t* n_units;
   uint16_t* out;          // [pairs][N]
 };
@@ -383,23 +382,23 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
     const int t0 = f - unit * T;
     const int t1 = min(T, t0 + (f_end - f));  // this work-group's tiles of this unit: [t0, t1)
     f += t1 - t0;
-    const int2 un = a.units[unit];
-    const int e = un.x, r0 = un.y;
-    const int off = a.offsets[e];
-    const int m = a.offsets[e + 1] - off;
+    // The unit's record and its rows' streams are independent loads; the
+    // input rows follow (rows past the unit's count repeat row 0; their
+    // outputs are not stored).
+    const int4 un = a.units[unit];
+    const int ur = GATEUP ? a.unit_rows[unit * 16 + (lane & 15)] : 0;
+    const int e = un.x, off = un.y, m = un.z;
     const uint4* T0 = a.t0 + a.tile_stride * e;
     const uint4* T1 = GATEUP ? a.t1 + a.tile_stride * e : nullptr;
     const uint16_t* S0 = a.s0 + a.scale_stride * e;
     const uint16_t* S1 = GATEUP ? a.s1 + a.scale_stride * e : nullptr;
     XRegs<1, NCH * 4> x;
-    load_x<1, NCH>(
-        x,
-        [&](int i) -> const uint16_t* {
-          if (r0 + i >= m) return nullptr;
-          const int row = GATEUP ? a.pair_stream[off + r0 + i] : off + r0 + i;
-          return a.x + (size_t)row * a.ldx;
-        },
-        kbase, lane);
+    {
+      const int i = lane & 15;
+      const uint16_t* xr = a.x + (size_t)(GATEUP ? ur : off + min(i, m - 1)) * a.ldx + kbase + 8 * (lane >> 4);
+#pragma unroll
+      for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
+    }
     auto run = [&](const Stage<NCH, G>& g0, const Stage<NCH, G>& g1, int t, bool valid) {
       float sv0[NS], sv1[NS];
       g0.scales_f32(sv0);
@@ -424,17 +423,17 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
             vg = vg + rb[ww * 256 + idx];
             vu = vu + red1[ww * 256 + idx];
           }
-          const int row = r0 + i, n = t * 16 + j;
-          if (valid && row < m && n < a.N) {
+          const int n = t * 16 + j;
+          if (valid && i < m && n < a.N) {
             const float gt = h2f(f2h(vg)), up = h2f(f2h(vu));
             const float silu = gt / (1.0f + expf(-gt));
-            a.out[(size_t)(off + row) * a.N + n] = f2h(silu * up);
+            a.out[(size_t)(off + i) * a.N + n] = f2h(silu * up);
           }
         }
       } else {
         reduce_tile<1>(rb, NW, [&](int i, int j, float v) {
-          const int row = r0 + i, n = t * 16 + j;
-          if (valid && row < m && n < a.N) a.out[(size_t)(off + row) * a.N + n] = f2h(v);
+          const int n = t * 16 + j;
+          if (valid && i < m && n < a.N) a.out[(size_t)(off + i) * a.N + n] = f2h(v);
         });
       }
       buf ^= 1;
@@ -512,9 +511,8 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   a.scale_stride = (size_t)m0.Np() * (m0.K / m0.g);
   a.x = x;
   a.ldx = ldx;
-  a.offsets = r.offsets;
-  a.pair_stream = r.pair_stream;
   a.units = r.units;
+  a.unit_rows = r.unit_rows;
   a.n_units = r.n_units;
   a.out = out;
   MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);

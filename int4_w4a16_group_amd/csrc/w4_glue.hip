@@ -188,6 +188,7 @@ hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* in
 // 16-row work units of the grouped GEMMs.  All of it is per-row arithmetic
 // with fixed orders, so a row's routing never depends on the other rows.
 constexpr int kRouteMaxE = 256;
+constexpr int kRouteMaxUnits = kRouteMaxE + 32 * 16 / 16 + 1;  // used experts + B*k/16 (B <= 32, k <= 16)
 
 // Order-preserving key of a logit: larger float -> larger unsigned; NaN
 // ranks as -inf and -0 as +0 (they compare equal as floats).
@@ -282,6 +283,95 @@ __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane
   (void)s_lv;
 }
 
+// Exclusive prefix sum over the wave of small non-negative values (< 2^BITS),
+// and the wave total, from one ballot per bit.
+template <int BITS>
+__device__ __forceinline__ int wave_excl_sum(int v, int lane, int* total) {
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int ex = 0, tot = 0;
+#pragma unroll
+  for (int bit = 0; bit < BITS; ++bit) {
+    const unsigned long long m = __ballot((v >> bit) & 1);
+    ex += __popcll(m & lt) << bit;
+    tot += __popcll(m) << bit;
+  }
+  *total = tot;
+  return ex;
+}
+
+// Bucketing of B rows whose expert ids are in s_ids [B*k] and stream masks
+// in s_mask [E] (bit b set when row b chose the expert): exclusive scans over
+// experts (wave bit-sliced prefix sums, waves in order; needs >= 4 waves),
+// the pairs ordered by (expert, stream), and the 16-row work units of the
+// grouped products: units[u] = (expert, first pair, rows), unit_rows[u][i] =
+// the stream of the unit's row i (rows past the unit's count repeat row 0).
+struct BucketLds {
+  unsigned* mask;  // [E]
+  int* off;        // [E] first pair of the expert
+  int* ubase;      // [E] first unit of the expert
+  int* tot;        // [12]
+  int* urows;      // [(E + B*k/16 + 1) * 16]
+};
+__device__ void bucket_core(int E, int k, int B, const int* s_ids, const BucketLds& L, const RouteOut& o) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int P = B * k;
+  int c = 0, u = 0, nu = 0, ec = 0, eu = 0, en = 0;
+  const int e = tid;
+  if (w < 4) {  // experts 64w .. 64w+63
+    c = e < E ? __popc(L.mask[e]) : 0;
+    u = c > 0;
+    nu = (c + 15) >> 4;
+    int tc, tu, tn;
+    ec = wave_excl_sum<6>(c, lane, &tc);
+    eu = wave_excl_sum<1>(u, lane, &tu);
+    en = wave_excl_sum<2>(nu, lane, &tn);
+    if (lane == 0) {
+      L.tot[3 * w] = tc;
+      L.tot[3 * w + 1] = tu;
+      L.tot[3 * w + 2] = tn;
+    }
+  }
+  __syncthreads();
+  if (w < 4) {
+    for (int ww = 0; ww < w; ++ww) {
+      ec += L.tot[3 * ww];
+      eu += L.tot[3 * ww + 1];
+      en += L.tot[3 * ww + 2];
+    }
+    if (e < E) {
+      L.off[e] = ec;
+      L.ubase[e] = en;
+      if (o.counts) o.counts[e] = c;
+      if (o.offsets) o.offsets[e] = ec;
+      if (u) o.used[eu] = e;
+      for (int j = 0; j < nu; ++j) o.units[en + j] = make_int4(e, ec + 16 * j, min(16, c - 16 * j), 0);
+    }
+    if (e == E - 1) {
+      if (o.offsets) o.offsets[E] = ec + c;
+      *o.n_used = eu + u;
+      *o.n_units = en + nu;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < P; i += blockDim.x) {
+    const int b = i / k, ex = s_ids[i];
+    const int r = __popc(L.mask[ex] & ((1u << b) - 1u));  // row of the pair within its expert
+    const int pos = L.off[ex] + r;
+    if (o.pair_stream) o.pair_stream[pos] = b;
+    if (o.pair_rank) o.pair_rank[pos] = i - b * k;
+    o.inv[i] = pos;
+    L.urows[(L.ubase[ex] + (r >> 4)) * 16 + (r & 15)] = b;
+  }
+  __syncthreads();
+  if (e < E && w < 4 && c > 0) {  // pad the expert's last unit with its first row
+    const int ul = en + nu - 1, ml = c - 16 * (nu - 1);
+    for (int i = ml; i < 16; ++i) L.urows[ul * 16 + i] = L.urows[ul * 16];
+  }
+  __syncthreads();
+  const int nun = L.tot[2] + L.tot[5] + L.tot[8] + L.tot[11];  // units of all experts
+  for (int i = tid; i < nun * 16; i += blockDim.x) o.unit_rows[i] = L.urows[i];
+}
+
 // One work-group of 1024 threads: top-k softmax of every row (one wave per
 // row), then the (stream, expert) bucketing and the 16-row work units of the
 // grouped GEMMs.
@@ -290,6 +380,9 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
   __shared__ int s_ids[32 * 16];
   __shared__ unsigned s_mask[kRouteMaxE];
   __shared__ int s_off[kRouteMaxE];
+  __shared__ int s_ub[kRouteMaxE];
+  __shared__ int s_tot[12];
+  __shared__ int s_ur[kRouteMaxUnits * 16];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0u;
   for (int i = threadIdx.x; i < B * E; i += blockDim.x) s_lg[i] = logits[i];
@@ -304,49 +397,7 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
       topk_row<4>(s_lg + b * E, E, k, lane, o.ids, o.w, s_ids, nullptr, s_mask, b);
   }
   __syncthreads();
-  if (w == 0) {  // exclusive scans over experts: offsets, used experts, 16-row units
-    int base = 0, ubase = 0, nbase = 0;
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      const int e = e0 + lane;
-      const int c = e < E ? __popc(s_mask[e]) : 0;
-      const int u = c > 0;
-      const int nu = (c + 15) >> 4;
-      int inc = c, uinc = u, ninc = nu;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int tt = __shfl_up(inc, d, 64), tu = __shfl_up(uinc, d, 64), tn = __shfl_up(ninc, d, 64);
-        if (lane >= d) {
-          inc += tt;
-          uinc += tu;
-          ninc += tn;
-        }
-      }
-      if (e < E) {
-        s_off[e] = base + inc - c;
-        if (o.counts) o.counts[e] = c;
-        if (o.offsets) o.offsets[e] = base + inc - c;
-        if (u) o.used[ubase + uinc - 1] = e;
-        for (int j = 0; j < nu; ++j) o.units[nbase + ninc - nu + j] = make_int2(e, 16 * j);
-      }
-      base += __shfl(inc, 63, 64);
-      ubase += __shfl(uinc, 63, 64);
-      nbase += __shfl(ninc, 63, 64);
-    }
-    if (lane == 0) {
-      if (o.offsets) o.offsets[E] = base;
-      *o.n_used = ubase;
-      *o.n_units = nbase;
-    }
-  }
-  __syncthreads();
-  const int P = B * k;
-  for (int i = threadIdx.x; i < P; i += blockDim.x) {
-    const int b = i / k, e = s_ids[i];
-    const int pos = s_off[e] + __popc(s_mask[e] & ((1u << b) - 1u));
-    if (o.pair_stream) o.pair_stream[pos] = b;
-    if (o.pair_rank) o.pair_rank[pos] = i - b * k;
-    o.inv[i] = pos;
-  }
+  bucket_core(E, k, B, s_ids, BucketLds{s_mask, s_off, s_ub, s_tot, s_ur}, o);
 }
 
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st) {
@@ -377,83 +428,6 @@ struct RouterArgs {
   unsigned* ticket;        // zero between launches
 };
 
-// Exclusive prefix sum over the wave of small non-negative values (< 2^BITS),
-// and the wave total, from one ballot per bit.
-template <int BITS>
-__device__ __forceinline__ int wave_excl_sum(int v, int lane, int* total) {
-  const unsigned long long lt = (1ull << lane) - 1ull;
-  int ex = 0, tot = 0;
-#pragma unroll
-  for (int bit = 0; bit < BITS; ++bit) {
-    const unsigned long long m = __ballot((v >> bit) & 1);
-    ex += __popcll(m & lt) << bit;
-    tot += __popcll(m) << bit;
-  }
-  *total = tot;
-  return ex;
-}
-
-// Bucketing of all B rows by the last work-group: per-expert stream masks,
-// exclusive scans over experts (wave bit-sliced prefix sums, then waves in
-// order), the 16-row work units, and the pair scatter.
-__device__ void bucket_rows(const RouterArgs& a, unsigned* s_mask, int* s_off, int* s_tot, int* s_ids) {
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int E = a.E, k = a.k, P = a.B * a.k;
-  const RouteOut& o = a.o;
-  if (tid < E) s_mask[tid] = 0u;
-  __syncthreads();
-  for (int i = tid; i < P; i += blockDim.x) {
-    const int e = __hip_atomic_load(&o.ids[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_ids[i] = e;
-    atomicOr(&s_mask[e], 1u << (i / k));
-  }
-  __syncthreads();
-  int c = 0, u = 0, nu = 0, ec = 0, eu = 0, en = 0;
-  const int e = tid;
-  if (w < 4) {  // experts 64w .. 64w+63
-    c = e < E ? __popc(s_mask[e]) : 0;
-    u = c > 0;
-    nu = (c + 15) >> 4;
-    int tc, tu, tn;
-    ec = wave_excl_sum<6>(c, lane, &tc);
-    eu = wave_excl_sum<1>(u, lane, &tu);
-    en = wave_excl_sum<2>(nu, lane, &tn);
-    if (lane == 0) {
-      s_tot[3 * w] = tc;
-      s_tot[3 * w + 1] = tu;
-      s_tot[3 * w + 2] = tn;
-    }
-  }
-  __syncthreads();
-  if (w < 4) {
-    for (int ww = 0; ww < w; ++ww) {
-      ec += s_tot[3 * ww];
-      eu += s_tot[3 * ww + 1];
-      en += s_tot[3 * ww + 2];
-    }
-    if (e < E) {
-      s_off[e] = ec;
-      if (o.counts) o.counts[e] = c;
-      if (o.offsets) o.offsets[e] = ec;
-      if (u) o.used[eu] = e;
-      for (int j = 0; j < nu; ++j) o.units[en + j] = make_int2(e, 16 * j);
-    }
-    if (e == E - 1) {
-      if (o.offsets) o.offsets[E] = ec + c;
-      *o.n_used = eu + u;
-      *o.n_units = en + nu;
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < P; i += blockDim.x) {
-    const int b = i / k, ex = s_ids[i];
-    const int pos = s_off[ex] + __popc(s_mask[ex] & ((1u << b) - 1u));
-    if (o.pair_stream) o.pair_stream[pos] = b;
-    if (o.pair_rank) o.pair_rank[pos] = i - b * k;
-    o.inv[i] = pos;
-  }
-}
-
 template <int G>
 __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   constexpr int SPG = G / 32;   // k-steps per group
@@ -470,6 +444,8 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   __shared__ int s_off[kRouteMaxE];
   __shared__ int s_tot[12];
   __shared__ int s_ids[32 * 16];
+  __shared__ int s_ub[kRouteMaxE];
+  __shared__ int s_ur[kRouteMaxUnits * 16];
   __shared__ int s_last;
   const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int H = a.H, E = a.E, k = a.k;
@@ -629,7 +605,15 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
              (unsigned)(gridDim.x - 1);
   __syncthreads();
   if (!s_last) return;
-  bucket_rows(a, s_mask, s_off, s_tot, s_ids);
+  if (tid < E) s_mask[tid] = 0u;
+  __syncthreads();
+  for (int i = tid; i < a.B * k; i += blockDim.x) {
+    const int ex = __hip_atomic_load(&a.o.ids[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ids[i] = ex;
+    atomicOr(&s_mask[ex], 1u << (i / k));
+  }
+  __syncthreads();
+  bucket_core(E, k, a.B, s_ids, BucketLds{s_mask, s_off, s_ub, s_tot, s_ur}, a.o);
   if (tid == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

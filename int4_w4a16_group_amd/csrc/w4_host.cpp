@@ -43,7 +43,7 @@ struct BankPlan {
 
 struct WsPlan {
   size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
-      used, n_used, units, n_units, act, y, logits, next, rows, table, total;
+      used, n_used, units, unit_rows, n_units, act, y, logits, next, rows, table, total;
 };
 
 bool geometry_ok(const w4_model_desc* d, std::string* why) {
@@ -151,7 +151,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.inv = take(Bm * k * 4);
   w.used = take(E * 4);
   w.n_used = take(4);
-  w.units = take((E + Bm * k / 16 + 1) * 8);
+  w.units = take((E + Bm * k / 16 + 1) * 16);
+  w.unit_rows = take((E + Bm * k / 16 + 1) * 16 * 4);
   w.n_units = take(4);
   w.act = take(Bm * k * I * 2);
   w.y = take(Bm * k * H * 2);
@@ -235,7 +236,8 @@ struct w4_ctx {
     r.inv = W<int32_t>(wp.inv);
     r.used = W<int32_t>(wp.used);
     r.n_used = W<int32_t>(wp.n_used);
-    r.units = W<int2>(wp.units);
+    r.units = W<int4>(wp.units);
+    r.unit_rows = W<int32_t>(wp.unit_rows);
     r.n_units = W<int32_t>(wp.n_units);
     return r;
   }

@@ -56,7 +56,8 @@ struct RouteOut {
   int32_t* inv;          // [B][k] position of pair (b, r) in expert order
   int32_t* used;         // [E] used experts, ascending
   int32_t* n_used;       // [1]
-  int2* units;           // [E + B*k/16] (expert, first row) per 16-row unit of each used expert
+  int4* units;           // [E + B*k/16 + 1] per 16-row unit of each used expert: (expert, first pair, rows, 0)
+  int32_t* unit_rows;    // [same][16] stream of each unit row (rows past the count repeat row 0)
   int32_t* n_units;      // [1]
 };
 // Routing in one work-group: top-k softmax of fp32 logits [B][E], bucketing and 16-row units.  B <= 32.
