@@ -354,103 +354,149 @@ struct MoeArgs {
   uint16_t* out;          // [pairs][N]
 };
 
+// s_setprio takes an immediate: level 0..3.
+__device__ __forceinline__ void set_prio_level(int l) {
+  if (l >= 3)
+    __builtin_amdgcn_s_setprio(3);
+  else if (l == 2)
+    __builtin_amdgcn_s_setprio(2);
+  else if (l == 1)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Persistent grouped GEMM.  The work is the flattened list of (unit, column
 // tile) items, unit = 16 rows of one used expert (the routing kernel builds
 // the unit list on the device); work-group i takes items
 // [i*total/grid, (i+1)*total/grid), so every work-group gets the same share
 // whatever the routing.  Its NW waves own the K slices (as in the dense
-// product); the x slice of the current unit stays in registers; tiles go
-// through two register stages, the next tile's loads in flight while the
-// current one is multiplied and reduced.  The arithmetic of an output does
-// not depend on which work-group computes it.
+// product); the x slice of the current unit stays in registers.  Items go
+// through two register stages in pairs, the next item's loads in flight
+// while the current one is multiplied and reduced; the prefetch runs across
+// unit boundaries (the x slice of a new unit is loaded after the last
+// multiply of the previous one, with its first tiles already in flight).
+// The arithmetic of an output does not depend on which work-group computes
+// it.
 template <int NCH, int G, bool GATEUP, int LB>
 __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
-  extern __shared__ float red[];  // two buffers of [GATEUP ? 2 : 1][NW][64][4]
+  // dynamic LDS: two buffers of [GATEUP ? 2 : 1][NW][64][4] partials, then
+  // the unit records of this work-group's range
+  extern __shared__ float red[];
   constexpr int NS = NCH * 128 / G;
   const int NW = blockDim.x >> 6;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int T = a.ntiles;
-  const long long total = (long long)(*a.n_units) * T;
+  const int nu = *a.n_units;
+  const long long total = (long long)nu * T;
   const int f_begin = (int)(blockIdx.x * total / gridDim.x);
   const int f_end = (int)((blockIdx.x + 1) * total / gridDim.x);
+  if (f_begin >= f_end) return;
+  const int last = f_end - 1;
   const int kbase = w * NCH * 128;
   const int bufsz = (GATEUP ? 2 : 1) * NW * 256;
+  const int i16 = lane & 15;
   const DqConst dk;
-  int buf = 0;
-  for (int f = f_begin; f < f_end;) {
-    const int unit = f / T;
-    const int t0 = f - unit * T;
-    const int t1 = min(T, t0 + (f_end - f));  // this work-group's tiles of this unit: [t0, t1)
-    f += t1 - t0;
-    // The unit's record and its rows' streams are independent loads; the
-    // input rows follow (rows past the unit's count repeat row 0; their
-    // outputs are not stored).
-    const int4 un = a.units[unit];
-    const int ur = GATEUP ? a.unit_rows[unit * 16 + (lane & 15)] : 0;
-    const int e = un.x, off = un.y, m = un.z;
-    const uint4* T0 = a.t0 + a.tile_stride * e;
-    const uint4* T1 = GATEUP ? a.t1 + a.tile_stride * e : nullptr;
-    const uint16_t* S0 = a.s0 + a.scale_stride * e;
-    const uint16_t* S1 = GATEUP ? a.s1 + a.scale_stride * e : nullptr;
-    XRegs<1, NCH * 4> x;
-    {
-      const int i = lane & 15;
-      const uint16_t* xr = a.x + (size_t)(GATEUP ? ur : off + min(i, m - 1)) * a.ldx + kbase + 8 * (lane >> 4);
+  // Unit records are read from LDS inside the loop: a record loaded from
+  // global memory there is a vector load (the kernel's stores might alias
+  // it), and a wait for it would also wait for the tile loads in flight.
+  int4* lrec = reinterpret_cast<int4*>(red + 2 * bufsz);
+  const int u_first = f_begin / T, nr = last / T - u_first + 1;
+  for (int i = threadIdx.x; i < nr; i += blockDim.x) lrec[i] = a.units[u_first + i];
+  __syncthreads();
+
+  // item f's tile into a stage (past the range: the WG's last tile again)
+  auto stage_load = [&](Stage<NCH, G>& g0, Stage<NCH, G>& g1, int f) {
+    const int fc = min(f, last), u = __builtin_amdgcn_readfirstlane(fc / T), t = fc - u * T;
+    const int e = lrec[u - u_first].x;
+    g0.load(a.t0 + a.tile_stride * e, a.s0 + a.scale_stride * e, a.K, t, w, lane);
+    if (GATEUP) g1.load(a.t1 + a.tile_stride * e, a.s1 + a.scale_stride * e, a.K, t, w, lane);
+  };
+  // x slice of unit u (rows past the unit's count repeat row 0; their
+  // outputs are not stored)
+  // (gate/up: the next unit's row index is loaded a unit ahead, so a switch
+  // does not wait for it)
+  XRegs<1, NCH * 4> x;
+  int xu = -1, nrow = 0;
+  auto load_x = [&](int uv, int grow) {
+    const int u = __builtin_amdgcn_readfirstlane(uv);
+    const int4 un = lrec[u - u_first];
+    const int row = GATEUP ? grow : un.y + min(i16, un.z - 1);
+    const uint16_t* xr = a.x + (size_t)row * a.ldx + kbase + 8 * (lane >> 4);
 #pragma unroll
-      for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
+    for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
+    xu = u;
+    if (GATEUP) nrow = a.unit_rows[min(u + 1, nu - 1) * 16 + i16];
+  };
+
+  int buf = 0;
+  auto run = [&](const Stage<NCH, G>& g0, const Stage<NCH, G>& g1, int f, bool valid) {
+    const int u = __builtin_amdgcn_readfirstlane(min(f, last) / T), t = min(f, last) - u * T;
+    const int4 un = lrec[u - u_first];
+    const int off = un.y, m = un.z;
+    float sv0[NS], sv1[NS];
+    g0.scales_f32(sv0);
+    f4 acc0[1] = {f4{0.f, 0.f, 0.f, 0.f}}, acc1[1] = {f4{0.f, 0.f, 0.f, 0.f}};
+    tile_mac<1, NCH, G>(x, g0.w, sv0, acc0, dk);
+    if (GATEUP) {
+      g1.scales_f32(sv1);
+      tile_mac<1, NCH, G>(x, g1.w, sv1, acc1, dk);
     }
-    auto run = [&](const Stage<NCH, G>& g0, const Stage<NCH, G>& g1, int t, bool valid) {
-      float sv0[NS], sv1[NS];
-      g0.scales_f32(sv0);
-      f4 acc0[1] = {f4{0.f, 0.f, 0.f, 0.f}}, acc1[1] = {f4{0.f, 0.f, 0.f, 0.f}};
-      tile_mac<1, NCH, G>(x, g0.w, sv0, acc0, dk);
-      if (GATEUP) {
-        g1.scales_f32(sv1);
-        tile_mac<1, NCH, G>(x, g1.w, sv1, acc1, dk);
-      }
-      float* rb = red + buf * bufsz;
-      f4* r4 = reinterpret_cast<f4*>(rb);
-      r4[w * 64 + lane] = acc0[0];
-      if (GATEUP) r4[(NW + w) * 64 + lane] = acc1[0];
-      __syncthreads();  // this tile's partials visible; the other buffer's readers are done
-      if (GATEUP) {
-        const float* red1 = rb + NW * 256;
-        for (int o = threadIdx.x; o < 256; o += blockDim.x) {
-          const int i = o >> 4, j = o & 15;
-          const int idx = ((i >> 2) * 16 + j) * 4 + (i & 3);
-          float vg = rb[idx], vu = red1[idx];
-          for (int ww = 1; ww < NW; ++ww) {
-            vg = vg + rb[ww * 256 + idx];
-            vu = vu + red1[ww * 256 + idx];
-          }
-          const int n = t * 16 + j;
-          if (valid && i < m && n < a.N) {
-            const float gt = h2f(f2h(vg)), up = h2f(f2h(vu));
-            const float silu = gt / (1.0f + expf(-gt));
-            a.out[(size_t)(off + i) * a.N + n] = f2h(silu * up);
-          }
+    float* rb = red + buf * bufsz;
+    f4* r4 = reinterpret_cast<f4*>(rb);
+    r4[w * 64 + lane] = acc0[0];
+    if (GATEUP) r4[(NW + w) * 64 + lane] = acc1[0];
+    __syncthreads();  // this tile's partials visible; the other buffer's readers are done
+    if (GATEUP) {
+      // lanes l and l^32 of a wave sum the gate and the up partials of one
+      // output (slices in order, every read issued before the adds)
+      constexpr int NB = LB / 64;  // >= NW
+      for (int ob = 0; ob < 256; ob += NW * 32) {  // uniform trip count
+        const int o = ob + w * 32 + (lane & 31), pp = lane >> 5;
+        const int oc = min(o, 255);
+        const int i = oc >> 4, j = oc & 15;
+        const float* p = rb + pp * NW * 256 + ((i >> 2) * 16 + j) * 4 + (i & 3);
+        float r[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) r[k] = p[min(k, NW - 1) * 256];
+        float v = r[0];
+#pragma unroll
+        for (int k = 1; k < NB; ++k) v = k < NW ? v + r[k] : v;
+        const float vu = __shfl_xor(v, 32, 64);
+        const int n = t * 16 + j;
+        if (pp == 0 && o < 256 && valid && i < m && n < a.N) {
+          const float gt = h2f(f2h(v)), up = h2f(f2h(vu));
+          const float silu = gt / (1.0f + expf(-gt));
+          a.out[(size_t)(off + i) * a.N + n] = f2h(silu * up);
         }
-      } else {
-        reduce_tile<1>(rb, NW, [&](int i, int j, float v) {
-          const int n = t * 16 + j;
-          if (valid && i < m && n < a.N) a.out[(size_t)(off + i) * a.N + n] = f2h(v);
-        });
       }
-      buf ^= 1;
-    };
-    // tiles t0 .. t1-1 in pairs; loads unconditional, indices clamped to t1-1
-    Stage<NCH, G> a0, a1, b0, b1;
-    a0.load(T0, S0, a.K, t0, w, lane);
-    if (GATEUP) a1.load(T1, S1, a.K, t0, w, lane);
-    for (int t = t0; t < t1; t += 2) {
-      const int tb = min(t + 1, t1 - 1), tn = min(t + 2, t1 - 1);
-      b0.load(T0, S0, a.K, tb, w, lane);
-      if (GATEUP) b1.load(T1, S1, a.K, tb, w, lane);
-      run(a0, a1, t, true);
-      a0.load(T0, S0, a.K, tn, w, lane);
-      if (GATEUP) a1.load(T1, S1, a.K, tn, w, lane);
-      run(b0, b1, t + 1, t + 1 < t1);
+    } else {
+      reduce_tile<1>(rb, NW, [&](int i, int j, float v) {
+        const int n = t * 16 + j;
+        if (valid && i < m && n < a.N) a.out[(size_t)(off + i) * a.N + n] = f2h(v);
+      });
     }
+    buf ^= 1;
+  };
+
+  // Items in pairs through stages a and b.  A new unit's x is loaded after
+  // the previous multiply and before the next prefetch: the multiply that
+  // needs it waits for its own stage, issued earlier, in any case.
+  Stage<NCH, G> a0, a1, b0, b1;
+  stage_load(a0, a1, f_begin);
+  load_x(f_begin / T, GATEUP ? a.unit_rows[(f_begin / T) * 16 + i16] : 0);
+  stage_load(b0, b1, f_begin + 1);
+  for (int f = f_begin; f < f_end; f += 2) {
+    // Issue priority by remaining work: the waves of the work-group with
+    // more tiles left win the compute unit's arbitration, so a work-group
+    // that falls behind the one sharing its compute unit catches up.
+    set_prio_level((4 * (f_end - f)) / (f_end - f_begin + 1));
+    run(a0, a1, f, true);
+    if (f + 1 < f_end && (f + 1) / T != xu) load_x((f + 1) / T, nrow);
+    stage_load(a0, a1, f + 2);
+    run(b0, b1, f + 1, f + 1 < f_end);
+    if (f + 2 < f_end && (f + 2) / T != xu) load_x((f + 2) / T, nrow);
+    stage_load(b0, b1, f + 3);
   }
 }
 
@@ -516,7 +562,7 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   a.n_units = r.n_units;
   a.out = out;
   MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);
-  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024;
+  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)kMaxUnits * 16;
   const int grid = resident_grid(k, NW * 64, shm);
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), shm, st, a);
   return hipGetLastError();

@@ -187,8 +187,6 @@ hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* in
 // MFMA, top-k softmax routing, and the (stream, expert) bucketing with the
 // 16-row work units of the grouped GEMMs.  All of it is per-row arithmetic
 // with fixed orders, so a row's routing never depends on the other rows.
-constexpr int kRouteMaxE = 256;
-constexpr int kRouteMaxUnits = kRouteMaxE + 32 * 16 / 16 + 1;  // used experts + B*k/16 (B <= 32, k <= 16)
 
 // Order-preserving key of a logit: larger float -> larger unsigned; NaN
 // ranks as -inf and -0 as +0 (they compare equal as floats).
@@ -382,7 +380,7 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
   __shared__ int s_off[kRouteMaxE];
   __shared__ int s_ub[kRouteMaxE];
   __shared__ int s_tot[12];
-  __shared__ int s_ur[kRouteMaxUnits * 16];
+  __shared__ int s_ur[kMaxUnits * 16];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int e = threadIdx.x; e < E; e += blockDim.x) s_mask[e] = 0u;
   for (int i = threadIdx.x; i < B * E; i += blockDim.x) s_lg[i] = logits[i];
@@ -445,7 +443,7 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   __shared__ int s_tot[12];
   __shared__ int s_ids[32 * 16];
   __shared__ int s_ub[kRouteMaxE];
-  __shared__ int s_ur[kRouteMaxUnits * 16];
+  __shared__ int s_ur[kMaxUnits * 16];
   __shared__ int s_last;
   const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int H = a.H, E = a.E, k = a.k;

@@ -46,6 +46,11 @@ hipError_t launch_repack(const uint8_t* src_packed, const uint16_t* src_scales, 
 hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi,
                        hipStream_t st, int xrows = 0);
 
+// Routing limits: experts, and 16-row units of the grouped products (used
+// experts + B*k/16 with B <= 32, k <= 16).
+constexpr int kRouteMaxE = 256;
+constexpr int kMaxUnits = kRouteMaxE + 32 * 16 / 16 + 1;
+
 struct RouteOut {
   int32_t* ids;          // [B][k]
   float* w;              // [B][k]
