@@ -202,7 +202,7 @@ __device__ void combine_splits(const AttnArgs& a, int b, int g, int G, int ns, i
 }
 
 template <int D>
-__global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
+__global__ void __launch_bounds__(256, 3) k_attn(AttnArgs a) {
   constexpr int KSQ = D / 32;  // k-steps of q.K
   constexpr int NDT = D / 16;  // output d-tiles
   __shared__ float Pl[4][16][65];
@@ -228,8 +228,10 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     const size_t base = kv_base(a.kv, a.layer, a.slot[b], g);
     const int c0 = c * 64;
     const bool last = (c0 + 63 > p);
-    // K operands first (the scores need them first), then V, all in flight
-    // together; each load is 1 KB contiguous across the wave.
+    // K operands now; V once the scores are issued, into the registers K
+    // held (this keeps the wave under 168 registers: three work-groups per
+    // compute unit, so a whole decode batch fits one round of work-groups).
+    // Each load is 1 KB contiguous across the wave.
     const uint16_t* Kc = a.kv.K + base + (size_t)c * 64 * D + lane * 8;
     const uint16_t* Vc = a.kv.VT + base + (size_t)c * 64 * D + lane * 8;
     h8 kb[4][KSQ];
@@ -237,14 +239,10 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
     for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(Kc + (pt * KSQ + ks) * 512);
-    h8 vop[NDT][2];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
+    const bool own = c == (p >> 6);  // this wave's chunk holds position p
     // The wave whose chunk holds position p: this step's k (rotated) and v go
     // into the arena at p and replace what the loads above read there.
-    if (c == (p >> 6)) {
+    if (own) {
       uint16_t* Ka = a.kv.K + base;
       uint16_t* Va = a.kv.VT + base;
       const uint16_t* kp = a.knew + (size_t)b * a.ldkv + g * D;
@@ -275,17 +273,6 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KSQ; ++ks)
           if (pt == ptp && col == colp) kb[pt][ks] = kf[ks];
-      // V operand: position p is element p%8 of k-step (p%64)/32 in lane quad (p%32)/8
-      const int ksp = (p & 63) >> 5, qdp = (p & 31) >> 3, jp = p & 7;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const _Float16 vf = __builtin_bit_cast(_Float16, vp[16 * dt + col]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (ks == ksp && quad == qdp && j == jp) vop[dt][ks][j] = vf;
-      }
     }
     // Q operand: rows = the G query heads of kv head g (rows >= G are zero),
     // rotated pairs (i, i + D/2) = k-steps (ks, ks + KSQ/2) of the same lane.
@@ -315,6 +302,26 @@ __global__ void __launch_bounds__(256) k_attn(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(qa[ks], kb[pt][ks], acc);
       S[pt] = acc;
+    }
+    h8 vop[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
+    if (own) {
+      // V operand: position p is element p%8 of k-step (p%64)/32 in lane quad
+      // (p%32)/8 (the arena already holds it; the loads above may not see it)
+      const uint16_t* vp = a.vnew + (size_t)b * a.ldkv + g * D;
+      const int ksp = (p & 63) >> 5, qdp = (p & 31) >> 3, jp = p & 7;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const _Float16 vf = __builtin_bit_cast(_Float16, vp[16 * dt + col]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (ks == ksp && quad == qdp && j == jp) vop[dt][ks][j] = vf;
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
