@@ -629,47 +629,112 @@ hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, c
 
 // ------------------------------------------------------------------ argmax
 // Largest fp16 logit per row, ties to the lower id (NaN never wins).
-__global__ void __launch_bounds__(1024) k_argmax(int V, const uint16_t* __restrict__ logits, int32_t* __restrict__ next) {
-  __shared__ float sv[16];
-  __shared__ int si[16];
-  const int b = blockIdx.x;
+// Greedy next token: argmax of each logits row (larger value first, then
+// the lower index; NaN never wins; a row of NaN gives 0).  Work-group
+// (split s, row b) scans V/8 consecutive entries with 16-byte loads (four in
+// flight per thread) and publishes its best with device-scope stores; the
+// last of a row's eight work-groups (per-row ticket, zero before and after)
+// combines them.  The result is the same as one scan of the row.
+constexpr int kArgmaxSplits = 8;
+__device__ __forceinline__ bool am_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+template <bool VEC>
+__global__ void __launch_bounds__(256) k_argmax(int V, const uint16_t* __restrict__ logits, int32_t* __restrict__ next,
+                                                float* part_v, int32_t* part_i, unsigned* ticket) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ int s_last;
+  const int sp = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const uint16_t* row = logits + (size_t)b * V;
+  const int per = ((V + kArgmaxSplits - 1) / kArgmaxSplits + 7) & ~7;
+  const int lo = sp * per, hi = min(V, lo + per);
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += blockDim.x) {
-    const float x = h2f(row[i]);
-    if (x > bv || (x == bv && i < bi)) {
-      bv = x;
-      bi = i;
+  if (VEC) {  // V % 8 == 0: rows and slices are 16-byte aligned
+    for (int base = lo + 8 * tid; base < hi; base += 4 * 8 * 256) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint4*>(row + min(base + u * 8 * 256, hi - 8));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i0 = base + u * 8 * 256;
+        if (i0 < hi) {
+          const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = h2f((uint16_t)(wd[j >> 1] >> (16 * (j & 1))));
+            if (am_better(x, i0 + j, bv, bi)) {
+              bv = x;
+              bi = i0 + j;
+            }
+          }
+        }
+      }
+    }
+  } else {
+    for (int i = lo + tid; i < hi; i += 256) {
+      const float x = h2f(row[i]);
+      if (am_better(x, i, bv, bi)) {
+        bv = x;
+        bi = i;
+      }
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float ov = __shfl_xor(bv, off, 64);
     const int oi = __shfl_xor(bi, off, 64);
-    if (ov > bv || (ov == bv && oi < bi)) {
+    if (am_better(ov, oi, bv, bi)) {
       bv = ov;
       bi = oi;
     }
   }
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  const int w = tid >> 6;
+  if ((tid & 63) == 0) {
     sv[w] = bv;
     si[w] = bi;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int j = 1; j < (int)(blockDim.x >> 6); ++j)
-      if (sv[j] > bv || (sv[j] == bv && si[j] < bi)) {
+  if (tid == 0) {
+    for (int j = 1; j < 4; ++j)
+      if (am_better(sv[j], si[j], bv, bi)) {
         bv = sv[j];
         bi = si[j];
       }
-    next[b] = bi == 0x7fffffff ? 0 : bi;
+    __hip_atomic_store(part_v + b * kArgmaxSplits + sp, bv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(part_i + b * kArgmaxSplits + sp, bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // partial stored before the ticket
+    s_last = __hip_atomic_fetch_add(ticket + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(kArgmaxSplits - 1);
   }
+  __syncthreads();
+  if (!s_last || tid != 0) return;
+  float pv[kArgmaxSplits];
+  int pi[kArgmaxSplits];
+#pragma unroll
+  for (int j = 0; j < kArgmaxSplits; ++j) {
+    pv[j] = __hip_atomic_load(part_v + b * kArgmaxSplits + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pi[j] = __hip_atomic_load(part_i + b * kArgmaxSplits + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  bv = pv[0];
+  bi = pi[0];
+#pragma unroll
+  for (int j = 1; j < kArgmaxSplits; ++j)
+    if (am_better(pv[j], pi[j], bv, bi)) {
+      bv = pv[j];
+      bi = pi[j];
+    }
+  next[b] = bi == 0x7fffffff ? 0 : bi;
+  __hip_atomic_store(ticket + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, hipStream_t st) {
-  hipLaunchKernelGGL(k_argmax, dim3(B), dim3(1024), 0, st, V, logits, next);
+hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, float* part_v, int32_t* part_i,
+                         unsigned* ticket, hipStream_t st) {
+  const dim3 grid(kArgmaxSplits, B);
+  if (V % 8 == 0)
+    hipLaunchKernelGGL(k_argmax<true>, grid, dim3(256), 0, st, V, logits, next, part_v, part_i, ticket);
+  else
+    hipLaunchKernelGGL(k_argmax<false>, grid, dim3(256), 0, st, V, logits, next, part_v, part_i, ticket);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ struct BankPlan {
 };
 
 struct WsPlan {
-  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
       used, n_used, units, unit_rows, n_units, act, y, logits, next, rows, table, total;
 };
 
@@ -140,6 +140,9 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.part_o = take(Bm * Hq * nch * D * 4);
   w.part_ml = take(Bm * Hq * nch * 2 * 4);
   w.aticket = take(Bm * d.n_kv_heads * 4);
+  w.amax_v = take(Bm * 8 * 4);
+  w.amax_i = take(Bm * 8 * 4);
+  w.amax_ticket = take(Bm * 4);
   w.rlogits = take(Bm * E * 4);
   w.ticket = take(64);
   w.ids = take(Bm * k * 4);
@@ -273,7 +276,8 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
     HIPCHK(c, launch_rope_table(c->cap, c->d.head_dim, (double)c->d.rope_theta, c->W<float2>(c->wp.table), st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.ticket), 0u, 16, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.aticket), 0u, (size_t)c->Bm * c->d.n_kv_heads, st));
-    c->launches += 3;
+    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.amax_ticket), 0u, (size_t)c->Bm, st));
+    c->launches += 4;
     c->table_ready = true;
   }
   return W4_OK;
@@ -587,7 +591,8 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
     ProfScope ps(c, W4_K_DENSE, st);
     LCHK(c, 1, launch_gemm(c->mat(c->bp.lm), B, xp, d.hidden, lg, d.vocab, EPI_F16, st, R));
   }
-  LCHK(c, 1, launch_argmax(B, d.vocab, lg, next, st));
+  LCHK(c, 1, launch_argmax(B, d.vocab, lg, next, c->W<float>(c->wp.amax_v), c->W<int32_t>(c->wp.amax_i),
+                            c->W<unsigned>(c->wp.amax_ticket), st));
   for (int b = 0; b < B; ++b) c->pos[slots[b]]++;
   c->last_launches = c->launches - l0;
   c->last_syncs = c->syncs - s0;

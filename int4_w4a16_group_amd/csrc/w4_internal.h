@@ -91,7 +91,10 @@ hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma
 hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const uint8_t* emb_p,
                         const uint16_t* emb_s, uint16_t* h, const uint16_t* gamma, float eps, uint16_t* xn,
                         hipStream_t st, int xn_rows = 0);
-hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, hipStream_t st);
+// next[b] = argmax of logits row b (ties to the lower index); part_v/part_i
+// [B][8] hold the split partials, ticket [B] is zero before and after.
+hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, float* part_v, int32_t* part_i,
+                         unsigned* ticket, hipStream_t st);
 
 struct KV {
   uint16_t* K;   // [L][S][Hkv][cap/64][64*D], MFMA operand order (w4_attn.hip)
