@@ -123,12 +123,19 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
   __shared__ int s_inv[16];
   __shared__ float s_w[16];
   const int b = blockIdx.x;
+  constexpr int PER = 2;  // H <= 4096 = 2 columns x 2 x 1024 threads
+  // the residual row does not depend on the routing: requested first
+  uint32_t hres[PER] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = 2 * (threadIdx.x + j * kCombThreads);
+    if (resid && i < H) hres[j] = *reinterpret_cast<const uint32_t*>(h + (size_t)b * H + i);
+  }
   if (threadIdx.x < k) {
     s_inv[threadIdx.x] = inv[b * k + threadIdx.x];
     s_w[threadIdx.x] = w[b * k + threadIdx.x];
   }
   __syncthreads();
-  constexpr int PER = 2;  // H <= 4096 = 2 columns x 2 x 1024 threads
   float v[2 * PER];
   float ss = 0.f;
 #pragma unroll
@@ -150,7 +157,7 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
       uint16_t m0 = f2h(a0), m1 = f2h(a1);
       uint32_t* hp = reinterpret_cast<uint32_t*>(h + (size_t)b * H + i);
       if (resid) {
-        const uint32_t hv = *hp;
+        const uint32_t hv = hres[j];
         m0 = f2h(h2f((uint16_t)(hv & 0xFFFFu)) + h2f(m0));
         m1 = f2h(h2f((uint16_t)(hv >> 16)) + h2f(m1));
       }
