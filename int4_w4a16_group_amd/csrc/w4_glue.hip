@@ -4,6 +4,8 @@
 // work-group with a fixed reduction order, so a row's result never depends on
 // the other rows ("Batched-concurrent 4-bit serving on Apple Silicon",
 // section 3: per-stream glue runs at per-stream offsets).
+#include <algorithm>
+
 #include "w4_device.h"
 #include "w4_internal.h"
 
@@ -431,6 +433,9 @@ struct RouterArgs {
   int H, E, k, B;
   RouteOut o;
   unsigned* ticket;        // zero between launches
+  const uint8_t* pf;       // work-groups B .. B+npf-1 touch this span (touch_lines)
+  size_t pf_lines;
+  int npf;
 };
 
 template <int G>
@@ -453,8 +458,12 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   __shared__ int s_ur[kMaxUnits * 16];
   __shared__ int s_last;
   const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if (b >= a.B) {
+    touch_lines(a.pf, a.pf_lines, b - a.B, a.npf);
+    return;
+  }
   const int H = a.H, E = a.E, k = a.k;
-  const int NC = H >> 7, NT = (E + 15) >> 4, NU = NT * NC;
+  const int NC = H >> 7, NT = (E + 15) >> 4;
 
   // The row and gain are requested first (their wait comes first); then this wave's
   // first batch of weights, whose latency overlaps the norm.  Wave w owns the
@@ -607,7 +616,7 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   __syncthreads();
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(gridDim.x - 1);
+             (unsigned)(a.B - 1);
   __syncthreads();
   if (!s_last) return;
   if (tid < E) s_mask[tid] = 0u;
@@ -622,14 +631,21 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   if (tid == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+int touch_groups(size_t bytes, int threads) {
+  const size_t lines = bytes / 128;
+  return (int)std::min(lines, std::max<size_t>(256, (lines + threads - 1) / threads));
+}
+
 hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
                          uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
-                         unsigned* ticket, hipStream_t st) {
-  RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket};
+                         unsigned* ticket, hipStream_t st, const void* pf, size_t pf_bytes) {
+  const int npf = pf ? touch_groups(pf_bytes, 1024) : 0;
+  RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket, static_cast<const uint8_t*>(pf),
+               pf_bytes / 128, npf};
   switch (g) {
-    case 32: hipLaunchKernelGGL(k_router<32>, dim3(B), dim3(1024), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(k_router<64>, dim3(B), dim3(1024), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_router<128>, dim3(B), dim3(1024), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(k_router<32>, dim3(B + npf), dim3(1024), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_router<64>, dim3(B + npf), dim3(1024), 0, st, a); break;
+    default: hipLaunchKernelGGL(k_router<128>, dim3(B + npf), dim3(1024), 0, st, a); break;
   }
   return hipGetLastError();
 }

@@ -71,9 +71,15 @@ hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut
 // MoE front end of a decode layer in one launch (one work-group per row, B <= 32):
 // xn = RMSNorm(h) * gamma, the router product, top-k softmax and the bucketing
 // (done by the last work-group to finish; ticket is zero before and after).
+// pf, pf_bytes: a span of the bank touched by spare work-groups of the launch
+// (touch_lines below); null for none.
 hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
                          uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
-                         unsigned* ticket, hipStream_t st);
+                         unsigned* ticket, hipStream_t st, const void* pf = nullptr, size_t pf_bytes = 0);
+// Spare work-groups for touching a span of that many bytes with threads-wide
+// work-groups: about one per compute unit, each touching at most one line
+// per thread.
+int touch_groups(size_t bytes, int threads);
 
 // Grouped expert GEMMs over the bucketed pairs (persistent, work list from route).
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
@@ -120,6 +126,19 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
                             unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0);
 void prof_mark(void* ctx, hipStream_t st);
+
+// Touch line j + nj*t (128 bytes each) of a span, t = the thread, so that the
+// memory-side cache holds the span for a launch that reads it soon after.
+// Run by spare work-groups of a launch that leaves most compute units idle:
+// one compute unit fetches only a small share of the chip's bandwidth, so
+// the span is spread over many work-groups.
+__device__ __forceinline__ void touch_lines(const uint8_t* span, size_t lines, size_t j, size_t nj) {
+  const size_t li = j + nj * threadIdx.x;
+  if (li < lines) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(span + (li << 7));
+    asm volatile("" ::"v"(v));
+  }
+}
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
 
 }  // namespace w4
