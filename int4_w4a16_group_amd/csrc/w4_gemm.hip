@@ -355,6 +355,7 @@ struct MoeArgs {
   const int4* units;      // (expert, first pair, rows, 0) of every 16-row unit, experts ascending
   const int32_t* unit_rows;  // [unit][16] stream of each row (gate/up input rows)
   const int32_t* n_units;
+  int units_cap;          // records allocated in units, at most 2 per thread
   uint16_t* out;          // [pairs][N]
   int ncu;                // compute units
   int dshare;             // range weight skew in 1/1000 (see k_moe)
@@ -393,6 +394,11 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   const int NW = blockDim.x >> 6;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int T = a.ntiles;
+  // Every allocated unit record is requested together with the unit count
+  // (records past the count are stale and never used), so the work range and
+  // its records arrive in one round trip.
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int4 rec0 = a.units[min(tid, a.units_cap - 1)], rec1 = a.units[min(tid + nth, a.units_cap - 1)];
   const int nu = *a.n_units;
   const long long total = (long long)nu * T;
   // Ranges by weight: the first work-group dispatched to each compute unit
@@ -422,14 +428,14 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // global memory there is a vector load (the kernel's stores might alias
   // it), and a wait for it would also wait for the tile loads in flight.
   int4* lrec = reinterpret_cast<int4*>(red + 2 * bufsz);
-  const int u_first = f_begin / T, nr = last / T - u_first + 1;
-  for (int i = threadIdx.x; i < nr; i += blockDim.x) lrec[i] = a.units[u_first + i];
+  if (tid < a.units_cap) lrec[tid] = rec0;
+  if (tid + nth < a.units_cap) lrec[tid + nth] = rec1;
   __syncthreads();
 
   // item f's tile into a stage (past the range: the WG's last tile again)
   auto stage_load = [&](Stage<NCH, G>& g0, Stage<NCH, G>& g1, int f) {
     const int fc = min(f, last), u = __builtin_amdgcn_readfirstlane(fc / T), t = fc - u * T;
-    const int e = lrec[u - u_first].x;
+    const int e = lrec[u].x;
     g0.load(a.t0 + a.tile_stride * e, a.s0 + a.scale_stride * e, a.K, t, w, lane);
     if (GATEUP) g1.load(a.t1 + a.tile_stride * e, a.s1 + a.scale_stride * e, a.K, t, w, lane);
   };
@@ -441,7 +447,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   int xu = -1, nrow = 0;
   auto load_x = [&](int uv, int grow) {
     const int u = __builtin_amdgcn_readfirstlane(uv);
-    const int4 un = lrec[u - u_first];
+    const int4 un = lrec[u];
     const int row = GATEUP ? grow : un.y + min(i16, un.z - 1);
     const uint16_t* xr = a.x + (size_t)row * a.ldx + kbase + 8 * (lane >> 4);
 #pragma unroll
@@ -453,7 +459,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   int buf = 0;
   auto run = [&](const Stage<NCH, G>& g0, const Stage<NCH, G>& g1, int f, bool valid) {
     const int u = __builtin_amdgcn_readfirstlane(min(f, last) / T), t = min(f, last) - u * T;
-    const int4 un = lrec[u - u_first];
+    const int4 un = lrec[u];
     const int off = un.y, m = un.z;
     float sv0[NS], sv1[NS];
     g0.scales_f32(sv0);
@@ -596,10 +602,12 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   a.units = r.units;
   a.unit_rows = r.unit_rows;
   a.n_units = r.n_units;
+  a.units_cap = r.units_cap;
   a.out = out;
   a.ncu = cu_count();
   a.dshare = gateup ? 75 : 0;  // measured: gate/up 38.5 us at 60-120 against 40.0 at 0
   MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);
+  if (r.units_cap > kMaxUnits || r.units_cap > 2 * NW * 64) return hipErrorInvalidValue;
   const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)kMaxUnits * 16;
   const int grid = resident_grid(k, NW * 64, shm);
   hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), shm, st, a);

@@ -242,6 +242,7 @@ struct w4_ctx {
     r.units = W<int4>(wp.units);
     r.unit_rows = W<int32_t>(wp.unit_rows);
     r.n_units = W<int32_t>(wp.n_units);
+    r.units_cap = d.n_experts + Bm * d.top_k / 16 + 1;
     return r;
   }
 };

@@ -64,6 +64,7 @@ struct RouteOut {
   int4* units;           // [E + B*k/16 + 1] per 16-row unit of each used expert: (expert, first pair, rows, 0)
   int32_t* unit_rows;    // [same][16] stream of each unit row (rows past the count repeat row 0)
   int32_t* n_units;      // [1]
+  int units_cap;         // records allocated in units (>= any n_units)
 };
 // Routing in one work-group: top-k softmax of fp32 logits [B][E], bucketing and 16-row units.  B <= 32.
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st);
