@@ -136,7 +136,8 @@ struct AttnArgs {
   float* part_o;      // [B][Hq][nsmax][D]  split partials (unnormalised)
   float* part_ml;     // [B][Hq][nsmax][2]  (M_s in log2 units, L_s)
   unsigned* ticket;   // [B][Hkv], zero between launches
-  const int32_t* splits;  // work-group x -> (stream b << 16 | split): every split of every stream, no idle groups
+  const int32_t* splits;  // work-group x -> (stream b << 16 | split << 8 | kv head): every split of every
+                          // stream for every kv head, no idle groups
   uint16_t* o;        // [B][Hq*D]: row-major (o_rows == 0) or an activation panel with o_rows rows
   int o_rows;
   float scale;        // log2(e) / sqrt(D)
@@ -212,7 +213,7 @@ __global__ void __launch_bounds__(256, 3) k_attn(AttnArgs a) {
   __shared__ int s_last;
   extern __shared__ float Ob[];  // [4 waves][G][D]
   const int bs_ = a.splits[blockIdx.x];
-  const int b = bs_ >> 16, sp = bs_ & 0xFFFF, g = blockIdx.y;
+  const int b = bs_ >> 16, sp = (bs_ >> 8) & 0xFF, g = bs_ & 0xFF;
   const int p = a.pos[b];
   const int nch = p / 64 + 1, ns = attn_splits(p);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -464,7 +465,7 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   a.o = o;
   a.o_rows = o_rows;
   a.scale = (float)(1.4426950408889634 / sqrt((double)kv.D));
-  dim3 grid(nsplits, kv.Hkv);
+  dim3 grid(nsplits);
   const size_t shm = (size_t)4 * (Hq / kv.Hkv) * kv.D * sizeof(float);
   if (prof) prof_mark(prof, st);
   if (kv.D == 128)

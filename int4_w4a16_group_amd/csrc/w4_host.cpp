@@ -161,7 +161,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.y = take(Bm * k * H * 2);
   w.logits = take((size_t)Bm * d.vocab * 2);
   w.next = take(Bm * 4);
-  w.rows = take((2 * Bm + (size_t)Bm * attn_splits(cap - 1)) * 4);  // slot ids, positions, attention split list
+  // slot ids, positions, attention work list (every split of every row, per kv head)
+  w.rows = take((2 * Bm + (size_t)Bm * attn_splits(cap - 1) * d.n_kv_heads) * 4);
   w.table = take((size_t)cap * (D / 2) * 8);
   w.total = cur;
   return w;
@@ -183,7 +184,7 @@ struct w4_ctx {
   int device = -1;
   int32_t* pinned = nullptr;
   int nsplits = 0;  // attention splits of the rows last uploaded
-  size_t row_words() const { return 2 * (size_t)Bm + (size_t)Bm * attn_splits(cap - 1); }
+  size_t row_words() const { return 2 * (size_t)Bm + (size_t)Bm * attn_splits(cap - 1) * d.n_kv_heads; }
   hipEvent_t ev[kRing] = {};
   bool ev_used[kRing] = {};
   int ring = 0;
@@ -316,8 +317,19 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
     p[b] = slots[b];
     p[c->Bm + b] = pos;
     mp = std::max(mp, pos);
-    for (int sp = 0; sp < attn_splits(pos); ++sp) split[n++] = (b << 16) | sp;
   }
+  // Attention work list (stream b << 16 | split << 8 | kv head), the splits
+  // with the most 64-position chunks first: work-groups are dispatched in
+  // list order, so the short tail splits are the ones that double up on a
+  // compute unit.  The order does not change any result.
+  const int W = 4;  // chunks per split (attn_splits)
+  for (int cnt = W; cnt >= 1; --cnt)
+    for (int b = 0; b < B; ++b) {
+      const int nch = c->pos[slots[b]] / 64 + 1, ns = attn_splits(c->pos[slots[b]]);
+      for (int sp = 0; sp < ns; ++sp)
+        if (std::min(W, nch - W * sp) == cnt)
+          for (int g = 0; g < c->d.n_kv_heads; ++g) split[n++] = (b << 16) | (sp << 8) | g;
+    }
   HIPCHK(c, hipMemcpyAsync(c->W<int32_t>(c->wp.rows), p, sizeof(int32_t) * (2 * c->Bm + n), hipMemcpyHostToDevice, st));
   HIPCHK(c, hipEventRecord(c->ev[i], st));
   c->ev_used[i] = true;

@@ -115,7 +115,8 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
 // prof: when non-null, an event is recorded (prof_mark) right before and after the chunk pass.
 // Split-KV decode attention in one launch.  A stream at position p has
 // attn_splits(p) splits of 256 positions; splits [nsplits] lists (b << 16 |
-// split) for every split of every row (built on the host with the rows).  The
+// split << 8 | kv head) for every split of every row and kv head (built on
+// the host with the rows), one work-group each.  The
 // last work-group of each (stream, kv head) combines the splits; ticket
 // [B][Hkv] is zero before and after.  This step's q (row stride ldq) and k,
 // v (row stride ldkv) are rotated at each stream's position through table
