@@ -438,7 +438,7 @@ struct RouterArgs {
   int npf;
 };
 
-template <int G>
+template <int G, bool VS>
 __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   constexpr int SPG = G / 32;   // k-steps per group
   constexpr int NGC = 128 / G;  // groups per 128-column chunk
@@ -465,11 +465,12 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   const int H = a.H, E = a.E, k = a.k;
   const int NC = H >> 7, NT = (E + 15) >> 4;
 
-  // The row and gain are requested first (their wait comes first); then this wave's
-  // first batch of weights, whose latency overlaps the norm.  Wave w owns the
-  // 128-column chunks c = w, w + 16, ... and, for each, the router tiles in
-  // batches of eight; every load of a batch is issued before any is used
-  // (tile indices clamped, results of clamped tiles dropped).
+  // The row and gain are requested first (their wait comes first); then this
+  // wave's first batch of weights, whose latency overlaps the norm.  Wave w
+  // owns expert tile t = w / WPT and a contiguous range of cpr 128-column
+  // chunks, taken in batches of eight; every load of a batch is issued before
+  // any is used (indices clamped, results of clamped chunks dropped).  With
+  // VS the eight chunks' scales of the lane's expert are one 16-byte load.
   const int i0 = 4 * tid;
   uint2 hraw = make_uint2(0u, 0u), graw = make_uint2(0u, 0u);
   if (i0 < H) {
@@ -477,20 +478,35 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
     graw = *reinterpret_cast<const uint2*>(a.gamma + i0);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep these two loads ahead of the weight loads
+  int NTp = 1;
+  while (NTp < NT) NTp <<= 1;
+  const int WPT = 16 / NTp, cpr = (NC + WPT - 1) / WPT;
+  const int wt = w / WPT, tc = min(wt, NT - 1);
+  const int c0 = (w % WPT) * cpr, c1 = min(NC, c0 + cpr);
   uint4 wv[8];
   uint16_t sr[8][NGC];
-  auto load_batch = [&](int c, int t0) {
+  auto load_batch = [&](int cb) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int t = min(t0 + i, NT - 1);
-      wv[i] = a.tiles[((size_t)t * NC + c) * 64 + lane];
+      const int c = min(cb + i, NC - 1);
+      wv[i] = a.tiles[((size_t)tc * NC + c) * 64 + lane];
+    }
+    const uint16_t* srow = a.scales + (size_t)(16 * tc + (lane & 15)) * (H / G);
+    if (VS) {
+      const uint4 v = *reinterpret_cast<const uint4*>(srow + min(cb, H / G - 8));
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < NGC; ++j) sr[i][j] = a.scales[(size_t)(16 * t + (lane & 15)) * (H / G) + c * NGC + j];
+      for (int i = 0; i < 8; ++i) sr[i][0] = (uint16_t)(u[i / 2] >> (16 * (i & 1)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NGC; ++j) sr[i][j] = srow[min(cb + i, NC - 1) * NGC + j];
     }
   };
   // Unconditional (chunk clamped): a load under a branch would make every
   // later wait on the row count the weight loads too.
-  load_batch(min(w, NC - 1), 0);
+  load_batch(min(c0, NC - 1));
   __builtin_amdgcn_sched_barrier(0);
 
   // 1. RMSNorm of the row: 4 columns per thread, fixed-order block sum.
@@ -523,13 +539,17 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
 
   // 2. Chunk partials P[t][c] (stored at unit t * NC + c).  Every A-operand
   // row is the normalised row, so D row 0 (lanes 0..15, element 0) is the
-  // result; the A operand of a chunk is read from LDS once.
+  // result; the A operand of a chunk is read from LDS (a broadcast read).
   const DqConst dk;
-  auto run_batch = [&](int c, int t0, const h8 (&xa)[4]) {
+  for (int cb = c0; cb < c1; cb += 8) {
+    if (cb != c0) load_batch(cb);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int t = t0 + i;
-      if (t < NT) {
+      const int c = cb + i;
+      if (wt < NT && c < c1) {
+        h8 xa[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const h8*>(s_x + 128 * c + 32 * s + 8 * (lane >> 4));
         const uint32_t wd[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
         f4 acc = {0.f, 0.f, 0.f, 0.f}, part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -546,17 +566,8 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
         // live stops the compiler from reusing a destination register of an
         // MFMA still in flight for the next operand.
         asm volatile("" ::"v"(acc));
-        if (lane < 16) s_part[(t * NC + c) * 16 + lane] = acc[0];
+        if (lane < 16) s_part[(wt * NC + c) * 16 + lane] = acc[0];
       }
-    }
-  };
-  for (int c = w; c < NC; c += 16) {
-    h8 xa[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const h8*>(s_x + 128 * c + 32 * s + 8 * (lane >> 4));
-    for (int t0 = 0; t0 < NT; t0 += 8) {
-      if (c != w || t0 != 0) load_batch(c, t0);
-      run_batch(c, t0, xa);
     }
   }
   __syncthreads();
@@ -642,10 +653,22 @@ hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, c
   const int npf = pf ? touch_groups(pf_bytes, 1024) : 0;
   RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket, static_cast<const uint8_t*>(pf),
                pf_bytes / 128, npf};
+  // chunk ranges as in the kernel: the eight scales of a batch are one
+  // aligned 16-byte load when g = 128 and ranges and scale rows are multiples of 8
+  const int NC = H / 128, NT = (E + 15) / 16;
+  int NTp = 1;
+  while (NTp < NT) NTp <<= 1;
+  const int cpr = (NC + 16 / NTp - 1) / (16 / NTp);
+  const bool vs = g == 128 && NC % 8 == 0 && cpr % 8 == 0;
   switch (g) {
-    case 32: hipLaunchKernelGGL(k_router<32>, dim3(B + npf), dim3(1024), 0, st, a); break;
-    case 64: hipLaunchKernelGGL(k_router<64>, dim3(B + npf), dim3(1024), 0, st, a); break;
-    default: hipLaunchKernelGGL(k_router<128>, dim3(B + npf), dim3(1024), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_router<32, false>), dim3(B + npf), dim3(1024), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_router<64, false>), dim3(B + npf), dim3(1024), 0, st, a); break;
+    default:
+      if (vs)
+        hipLaunchKernelGGL((k_router<128, true>), dim3(B + npf), dim3(1024), 0, st, a);
+      else
+        hipLaunchKernelGGL((k_router<128, false>), dim3(B + npf), dim3(1024), 0, st, a);
+      break;
   }
   return hipGetLastError();
 }
