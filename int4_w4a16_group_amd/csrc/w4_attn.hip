@@ -283,16 +283,21 @@ __global__ void __launch_bounds__(256, 3) k_attn(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) qa[ks] = col < G ? ld_h8(qp + 32 * ks) : h8{0, 0, 0, 0, 0, 0, 0, 0};
       if (a.table && col < G) {
-        const float2* tr = a.table + (size_t)p * (D / 2) + 8 * quad;
+        // 16-byte loads (two (cos, sin) pairs each): the row is 16-byte aligned
+        const float4* tr = reinterpret_cast<const float4*>(a.table + (size_t)p * (D / 2) + 8 * quad);
 #pragma unroll
-        for (int ks = 0; ks < KSQ / 2; ++ks)
+        for (int ks = 0; ks < KSQ / 2; ++ks) {
+          float4 t4[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) t4[jj] = tr[16 * ks + jj];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            const float2 cs = tr[32 * ks + j];
+            const float2 cs = (j & 1) ? make_float2(t4[j / 2].z, t4[j / 2].w) : make_float2(t4[j / 2].x, t4[j / 2].y);
             const float x0 = (float)qa[ks][j], x1 = (float)qa[ks + KSQ / 2][j];
             qa[ks][j] = (_Float16)(x0 * cs.x - x1 * cs.y);
             qa[ks + KSQ / 2][j] = (_Float16)(x0 * cs.y + x1 * cs.x);
           }
+        }
       }
     }
     // scores: lane holds S[head 4*quad + r][pos c0 + 16*pt + col]

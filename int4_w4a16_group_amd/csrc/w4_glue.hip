@@ -113,8 +113,9 @@ hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const
 
 // moe = fp16(sum_r w_r * y_r) in rank order; resid: h = fp16(h + moe), else h = moe.
 // Then (gamma != null) xn = RMSNorm(h) * gamma.  One work-group per row; each
-// thread owns column pairs, so every rank's row is read as coalesced half2.
-constexpr int kCombThreads = 1024;
+// thread owns runs of eight columns, so every load and store is 16 bytes (few
+// memory instructions per compute unit: this launch is latency-bound).
+constexpr int kCombThreads = 256;
 
 __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const float* __restrict__ w,
                                                           const int32_t* __restrict__ inv,
@@ -125,48 +126,58 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
   __shared__ int s_inv[16];
   __shared__ float s_w[16];
   const int b = blockIdx.x;
-  constexpr int PER = 2;  // H <= 4096 = 2 columns x 2 x 1024 threads
+  constexpr int PER = 2;  // H <= 4096 = 8 columns x 2 x 256 threads
+  auto half_of = [](const uint4& q, int e) -> float {
+    const uint32_t u = e < 2 ? q.x : e < 4 ? q.y : e < 6 ? q.z : q.w;
+    return h2f((uint16_t)(u >> (16 * (e & 1))));
+  };
   // the residual row does not depend on the routing: requested first
-  uint32_t hres[PER] = {0u, 0u};
+  uint4 hres[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = 2 * (threadIdx.x + j * kCombThreads);
-    if (resid && i < H) hres[j] = *reinterpret_cast<const uint32_t*>(h + (size_t)b * H + i);
+    const int i = 8 * (threadIdx.x + j * kCombThreads);
+    hres[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (resid && i < H) hres[j] = *reinterpret_cast<const uint4*>(h + (size_t)b * H + i);
   }
   if (threadIdx.x < k) {
     s_inv[threadIdx.x] = inv[b * k + threadIdx.x];
     s_w[threadIdx.x] = w[b * k + threadIdx.x];
   }
   __syncthreads();
-  float v[2 * PER];
+  float v[8 * PER];
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = 2 * (threadIdx.x + j * kCombThreads);
-    v[2 * j] = v[2 * j + 1] = 0.f;
+    const int i = 8 * (threadIdx.x + j * kCombThreads);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * j + e] = 0.f;
     if (i < H) {
-      uint32_t yr[16];
+      uint4 yr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (r < k) yr[r] = *reinterpret_cast<const uint32_t*>(y + (size_t)s_inv[r] * H + i);
-      float a0 = 0.f, a1 = 0.f;
+        if (r < k) yr[r] = *reinterpret_cast<const uint4*>(y + (size_t)s_inv[r] * H + i);
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (r < k) {
-          a0 = a0 + s_w[r] * h2f((uint16_t)(yr[r] & 0xFFFFu));
-          a1 = a1 + s_w[r] * h2f((uint16_t)(yr[r] >> 16));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = acc[e] + s_w[r] * half_of(yr[r], e);
         }
-      uint16_t m0 = f2h(a0), m1 = f2h(a1);
-      uint32_t* hp = reinterpret_cast<uint32_t*>(h + (size_t)b * H + i);
-      if (resid) {
-        const uint32_t hv = hres[j];
-        m0 = f2h(h2f((uint16_t)(hv & 0xFFFFu)) + h2f(m0));
-        m1 = f2h(h2f((uint16_t)(hv >> 16)) + h2f(m1));
+      uint32_t out[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint16_t m0 = f2h(acc[e]), m1 = f2h(acc[e + 1]);
+        if (resid) {
+          m0 = f2h(half_of(hres[j], e) + h2f(m0));
+          m1 = f2h(half_of(hres[j], e + 1) + h2f(m1));
+        }
+        out[e / 2] = (uint32_t)m0 | ((uint32_t)m1 << 16);
+        v[8 * j + e] = h2f(m0);
+        v[8 * j + e + 1] = h2f(m1);
       }
-      *hp = (uint32_t)m0 | ((uint32_t)m1 << 16);
-      v[2 * j] = h2f(m0);
-      v[2 * j + 1] = h2f(m1);
-      ss = ss + (v[2 * j] * v[2 * j] + v[2 * j + 1] * v[2 * j + 1]);
+      *reinterpret_cast<uint4*>(h + (size_t)b * H + i) = make_uint4(out[0], out[1], out[2], out[3]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = ss + v[8 * j + e] * v[8 * j + e];
     }
   }
   if (!gamma) return;
@@ -174,11 +185,17 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
   const float rr = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int i = 2 * (threadIdx.x + j * kCombThreads);
+    const int i = 8 * (threadIdx.x + j * kCombThreads);
     if (i < H) {
-      const uint16_t o0 = f2h((v[2 * j] * rr) * h2f(gamma[i]));
-      const uint16_t o1 = f2h((v[2 * j + 1] * rr) * h2f(gamma[i + 1]));
-      *reinterpret_cast<uint32_t*>(xn + act_off(b, i, H, rows)) = (uint32_t)o0 | ((uint32_t)o1 << 16);
+      const uint4 gv = *reinterpret_cast<const uint4*>(gamma + i);
+      uint32_t out[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint16_t o0 = f2h((v[8 * j + e] * rr) * half_of(gv, e));
+        const uint16_t o1 = f2h((v[8 * j + e + 1] * rr) * half_of(gv, e + 1));
+        out[e / 2] = (uint32_t)o0 | ((uint32_t)o1 << 16);
+      }
+      *reinterpret_cast<uint4*>(xn + act_off(b, i, H, rows)) = make_uint4(out[0], out[1], out[2], out[3]);
     }
   }
 }
