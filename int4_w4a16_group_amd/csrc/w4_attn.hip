@@ -202,8 +202,11 @@ __device__ void combine_splits(const AttnArgs& a, int b, int g, int G, int ns, i
   }
 }
 
-template <int D>
-__global__ void __launch_bounds__(256, 3) k_attn(AttnArgs a) {
+// VE: the V operands are requested together with K (one memory round trip
+// less; about 226 registers, for a work list that fits one work-group per
+// compute unit); otherwise after the scores, into the registers K held.
+template <int D, bool VE>
+__global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
   constexpr int KSQ = D / 32;  // k-steps of q.K
   constexpr int NDT = D / 16;  // output d-tiles
   __shared__ float Pl[4][16][65];
@@ -240,6 +243,14 @@ __global__ void __launch_bounds__(256, 3) k_attn(AttnArgs a) {
     for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
       for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(Kc + (pt * KSQ + ks) * 512);
+    h8 vop[NDT][2];
+    auto load_v = [&]() {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
+    };
+    if (VE) load_v();
     const bool own = c == (p >> 6);  // this wave's chunk holds position p
     // The wave whose chunk holds position p: this step's k (rotated) and v go
     // into the arena at p and replace what the loads above read there.
@@ -309,11 +320,7 @@ __global__ void __launch_bounds__(256, 3) k_attn(AttnArgs a) {
       for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(qa[ks], kb[pt][ks], acc);
       S[pt] = acc;
     }
-    h8 vop[NDT][2];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
+    if (!VE) load_v();
     if (own) {
       // V operand: position p is element p%8 of k-step (p%64)/32 in lane quad
       // (p%32)/8 (the arena already holds it; the loads above may not see it)
@@ -473,10 +480,21 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   dim3 grid(nsplits);
   const size_t shm = (size_t)4 * (Hq / kv.Hkv) * kv.D * sizeof(float);
   if (prof) prof_mark(prof, st);
-  if (kv.D == 128)
-    hipLaunchKernelGGL(k_attn<128>, grid, dim3(256), shm, st, a);
-  else
-    hipLaunchKernelGGL(k_attn<64>, grid, dim3(256), shm, st, a);
+  // measured on the 48-layer model: V with K is faster while the work list
+  // fits one work-group per compute unit; beyond that the smaller register
+  // footprint (three work-groups per unit) wins
+  const bool ve = nsplits <= 128;
+  if (kv.D == 128) {
+    if (ve)
+      hipLaunchKernelGGL((k_attn<128, true>), grid, dim3(256), shm, st, a);
+    else
+      hipLaunchKernelGGL((k_attn<128, false>), grid, dim3(256), shm, st, a);
+  } else {
+    if (ve)
+      hipLaunchKernelGGL((k_attn<64, true>), grid, dim3(256), shm, st, a);
+    else
+      hipLaunchKernelGGL((k_attn<64, false>), grid, dim3(256), shm, st, a);
+  }
   if (prof) prof_mark(prof, st);
   return hipGetLastError();
 }
