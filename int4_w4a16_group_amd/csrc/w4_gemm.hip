@@ -182,16 +182,19 @@ __device__ __forceinline__ void load_x(XRegs<MT, NCH * 4>& x, RowPtr rowptr, int
 // A-operand rows from an activation panel: element (row b, column k) of a
 // [rows][K] activation at ((k / 8) * rows + b) * 8 + k % 8, so the 4-lane
 // groups of every operand load read 64 contiguous bytes (rows is a multiple
-// of 16; rows past the batch hold stale values, which only reach output rows
-// that are never stored: an MFMA output row depends on its own A row only).
+// of 16).  Tile rows past the batch read row B-1 again: lanes that share an
+// address cost the load unit one access, and those rows only reach output
+// rows that are never stored (an MFMA output row depends on its own A row).
 template <int MT, int NCH>
 __device__ __forceinline__ void load_x_panel(XRegs<MT, NCH * 4>& x, const uint16_t* __restrict__ xp, int rows,
-                                             int kbase, int lane) {
+                                             int B, int kbase, int lane) {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = min(16 * mt + (lane & 15), B - 1);
 #pragma unroll
     for (int ks = 0; ks < NCH * 4; ++ks)
-      x.a[mt][ks] = ld_h8(xp + ((size_t)((kbase >> 3) + 4 * ks + (lane >> 4)) * rows + 16 * mt + (lane & 15)) * 8);
+      x.a[mt][ks] = ld_h8(xp + ((size_t)((kbase >> 3) + 4 * ks + (lane >> 4)) * rows + row) * 8);
+  }
 }
 
 // Sum the waves' partial tiles (red: [NW][MT][64 lanes][4]) in wave order and
@@ -239,7 +242,7 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   if ((int)blockIdx.x >= a.ntiles) return;
   XRegs<MT, NCH * 4> x;
   if (XP)
-    load_x_panel<MT, NCH>(x, a.x, a.xrows, kbase, lane);
+    load_x_panel<MT, NCH>(x, a.x, a.xrows, a.B, kbase, lane);
   else
     load_x<MT, NCH>(x, [&](int row) -> const uint16_t* { return row < a.B ? a.x + (size_t)row * a.ldx : nullptr; },
                     kbase, lane);
