@@ -74,7 +74,9 @@ hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma
 }
 
 // h[b] = fp16(code * scale) of the token's embedding row (token ids outside
-// [0, V) read row 0); xn[b] = RMSNorm(h[b]).
+// [0, V) read row 0); xn[b] = RMSNorm(h[b]).  Each thread owns runs of eight
+// columns: one 4-byte load of their codes, one scale (g is a multiple of 8),
+// 16-byte stores.
 __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, const int32_t* __restrict__ tokens,
                                                         const uint8_t* __restrict__ emb_p,
                                                         const uint16_t* __restrict__ emb_s, uint16_t* __restrict__ h,
@@ -86,21 +88,53 @@ __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, con
   if (t < 0 || t >= V) t = 0;
   const uint8_t* row = emb_p + (size_t)t * (H / 2);
   const uint16_t* srow = emb_s + (size_t)t * (H / g);
-  float v[kPer];
+  constexpr int PER = 2;  // H <= 4096 = 8 columns x 2 x 256 threads
+  float v[8 * PER];
+  float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int i = threadIdx.x + j * kNormThreads;
-    v[j] = 0.f;
+  for (int j = 0; j < PER; ++j) {
+    const int i = 8 * (threadIdx.x + j * kNormThreads);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[8 * j + e] = 0.f;
     if (i < H) {
-      const unsigned byte = row[i >> 1];
-      const unsigned nib = (i & 1) ? (byte >> 4) : (byte & 15u);
-      const int q = (int)nib - ((nib & 8u) ? 16 : 0);
-      const uint16_t hv = f2h((float)q * h2f(srow[i / g]));
-      h[(size_t)b * H + i] = hv;
-      v[j] = h2f(hv);
+      const uint32_t pk = *reinterpret_cast<const uint32_t*>(row + i / 2);  // element i+e in nibble e
+      const float sc = h2f(srow[i / g]);
+      uint32_t out[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        uint16_t hv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const unsigned nib = (pk >> (4 * (e + u))) & 15u;
+          const int q = (int)nib - ((nib & 8u) ? 16 : 0);
+          hv[u] = f2h((float)q * sc);
+          v[8 * j + e + u] = h2f(hv[u]);
+        }
+        out[e / 2] = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+      }
+      *reinterpret_cast<uint4*>(h + (size_t)b * H + i) = make_uint4(out[0], out[1], out[2], out[3]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss = ss + v[8 * j + e] * v[8 * j + e];
     }
   }
-  norm_row<kPer>(v, H, gamma, eps, xn, b, rows, sh);
+  ss = block_sum(ss, sh);
+  const float rr = 1.0f / sqrtf(ss / (float)H + eps);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = 8 * (threadIdx.x + j * kNormThreads);
+    if (i < H) {
+      const uint4 gv = *reinterpret_cast<const uint4*>(gamma + i);
+      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint32_t out[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint16_t o0 = f2h((v[8 * j + e] * rr) * h2f((uint16_t)(gw[e / 2] & 0xFFFFu)));
+        const uint16_t o1 = f2h((v[8 * j + e + 1] * rr) * h2f((uint16_t)(gw[e / 2] >> 16)));
+        out[e / 2] = (uint32_t)o0 | ((uint32_t)o1 << 16);
+      }
+      *reinterpret_cast<uint4*>(xn + act_off(b, i, H, rows)) = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+  }
 }
 
 hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const uint8_t* emb_p,
