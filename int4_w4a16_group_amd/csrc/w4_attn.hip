@@ -479,23 +479,22 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   a.scale = (float)(1.4426950408889634 / sqrt((double)kv.D));
   dim3 grid(nsplits);
   const size_t shm = (size_t)4 * (Hq / kv.Hkv) * kv.D * sizeof(float);
-  if (prof) prof_mark(prof, st);
+  if (prof) prof_arm(prof);
   // measured on the 48-layer model: V with K is faster while the work list
   // fits one work-group per compute unit; beyond that the smaller register
   // footprint (three work-groups per unit) wins
   const bool ve = nsplits <= 128;
   if (kv.D == 128) {
     if (ve)
-      hipLaunchKernelGGL((k_attn<128, true>), grid, dim3(256), shm, st, a);
+      w4_launch(k_attn<128, true>, grid, dim3(256), shm, st, a);
     else
-      hipLaunchKernelGGL((k_attn<128, false>), grid, dim3(256), shm, st, a);
+      w4_launch(k_attn<128, false>, grid, dim3(256), shm, st, a);
   } else {
     if (ve)
-      hipLaunchKernelGGL((k_attn<64, true>), grid, dim3(256), shm, st, a);
+      w4_launch(k_attn<64, true>, grid, dim3(256), shm, st, a);
     else
-      hipLaunchKernelGGL((k_attn<64, false>), grid, dim3(256), shm, st, a);
+      w4_launch(k_attn<64, false>, grid, dim3(256), shm, st, a);
   }
-  if (prof) prof_mark(prof, st);
   return hipGetLastError();
 }
 

@@ -340,7 +340,7 @@ hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y,
   int grid = std::min(ntiles, target);
   if (NW <= 8 && ntiles >= 256 && ntiles <= 1024) grid = (ntiles + 1) / 2;
   DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy, xrows};
-  hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), 2 * NW * MT * 1024, st, a);
+  w4_launch(k, dim3(grid), dim3(NW * 64), 2 * NW * MT * 1024, st, a);
   return hipGetLastError();
 }
 
@@ -613,7 +613,7 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   if (r.units_cap > kMaxUnits || r.units_cap > 2 * NW * 64) return hipErrorInvalidValue;
   const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)kMaxUnits * 16;
   const int grid = resident_grid(k, NW * 64, shm);
-  hipLaunchKernelGGL(k, dim3(grid), dim3(NW * 64), shm, st, a);
+  w4_launch(k, dim3(grid), dim3(NW * 64), (uint32_t)shm, st, a);
   return hipGetLastError();
 }
 

@@ -712,13 +712,13 @@ hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, c
   const int cpr = (NC + 16 / NTp - 1) / (16 / NTp);
   const bool vs = g == 128 && NC % 8 == 0 && cpr % 8 == 0;
   switch (g) {
-    case 32: hipLaunchKernelGGL((k_router<32, false>), dim3(B + npf), dim3(1024), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_router<64, false>), dim3(B + npf), dim3(1024), 0, st, a); break;
+    case 32: w4_launch(k_router<32, false>, dim3(B + npf), dim3(1024), 0, st, a); break;
+    case 64: w4_launch(k_router<64, false>, dim3(B + npf), dim3(1024), 0, st, a); break;
     default:
       if (vs)
-        hipLaunchKernelGGL((k_router<128, true>), dim3(B + npf), dim3(1024), 0, st, a);
+        w4_launch(k_router<128, true>, dim3(B + npf), dim3(1024), 0, st, a);
       else
-        hipLaunchKernelGGL((k_router<128, false>), dim3(B + npf), dim3(1024), 0, st, a);
+        w4_launch(k_router<128, false>, dim3(B + npf), dim3(1024), 0, st, a);
       break;
   }
   return hipGetLastError();

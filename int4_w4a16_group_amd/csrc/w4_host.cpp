@@ -195,13 +195,16 @@ struct w4_ctx {
   int prof_kernel = 0;
   std::vector<hipEvent_t> prof_ev;  // pool, used in (start, stop) pairs
   size_t prof_used = 0;
-  void prof_record(hipStream_t st) {
-    if (prof_used == prof_ev.size()) {
+  // arm the next launch with the pool's next (start, stop) pair
+  void prof_arm() {
+    while (prof_ev.size() < prof_used + 2) {
       hipEvent_t e;
       if (hipEventCreate(&e) != hipSuccess) return;
       prof_ev.push_back(e);
     }
-    (void)hipEventRecord(prof_ev[prof_used++], st);
+    g_launch_ev.start = prof_ev[prof_used];
+    g_launch_ev.stop = prof_ev[prof_used + 1];
+    prof_used += 2;
   }
 
   template <class T>
@@ -338,17 +341,13 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
   return W4_OK;
 }
 
-// Event pair around one launch of the profiled kernel family.
+// Times the one launch in its scope when it belongs to the profiled kernel
+// family (events recorded with that launch's dispatch, see w4_launch).
 struct ProfScope {
-  w4_ctx* c;
-  hipStream_t st;
-  bool on;
-  ProfScope(w4_ctx* c_, int kernel, hipStream_t st_) : c(c_), st(st_), on(c_->prof_kernel == kernel) {
-    if (on) c->prof_record(st);
+  ProfScope(w4_ctx* c, int kernel, hipStream_t) {
+    if (c->prof_kernel == kernel) c->prof_arm();
   }
-  ~ProfScope() {
-    if (on) c->prof_record(st);
-  }
+  ~ProfScope() { g_launch_ev = LaunchEvents{}; }
 };
 
 #define LCHK(ctx, n, expr)                                                                      \
@@ -420,7 +419,8 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
 }  // namespace
 
 namespace w4 {
-void prof_mark(void* ctx, hipStream_t st) { static_cast<w4_ctx*>(ctx)->prof_record(st); }
+thread_local LaunchEvents g_launch_ev;
+void prof_arm(void* ctx) { static_cast<w4_ctx*>(ctx)->prof_arm(); }
 }  // namespace w4
 
 // =========================================================================== C ABI

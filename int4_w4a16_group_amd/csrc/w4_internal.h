@@ -2,6 +2,7 @@
 // the w4moe library.  Nothing here is part of the public C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -112,7 +113,7 @@ hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStr
 hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, const uint16_t* v,
                        hipStream_t st);
 // split-KV decode attention; part_o [B][Hq][nchmax][D] f32, part_ml [B][Hq][nchmax][2].
-// prof: when non-null, an event is recorded (prof_mark) right before and after the chunk pass.
+// prof: when non-null, the launch is timed (prof_arm).
 // Split-KV decode attention in one launch.  A stream at position p has
 // attn_splits(p) splits of 256 positions; splits [nsplits] lists (b << 16 |
 // split << 8 | kv head) for every split of every row and kv head (built on
@@ -127,7 +128,25 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
                             const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
                             unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0);
-void prof_mark(void* ctx, hipStream_t st);
+// Kernel timing: the host arms a (start, stop) event pair for the next
+// launch of the profiled kernel family (prof_arm, from the context's pool);
+// that launch records them with its own dispatch (hipExtLaunchKernelGGL), so
+// the elapsed time is the kernel's alone, without the gap before it.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_ev;
+void prof_arm(void* ctx);
+template <typename F, typename... Args>
+inline void w4_launch(F kernel, const dim3& grid, const dim3& block, uint32_t shm, hipStream_t st, Args... args) {
+  if (g_launch_ev.start) {
+    const LaunchEvents e = g_launch_ev;
+    g_launch_ev = LaunchEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, st, e.start, e.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shm, st, args...);
+  }
+}
 
 // Touch line j + nj*t (128 bytes each) of a span, t = the thread, so that the
 // memory-side cache holds the span for a launch that reads it soon after.
