@@ -221,7 +221,8 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
   const int nch = p / 64 + 1, ns = attn_splits(p);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int Hkv = a.kv.Hkv, G = a.Hq / Hkv;
-  const int c = 4 * sp + w;
+  const int c = kAttnSplitChunks * sp + w;
+  static_assert(kAttnSplitChunks == 4, "one wave per chunk in a four-wave work-group");
   const bool live = c < nch;  // this wave's chunk holds positions <= p
   const int col = lane & 15, quad = lane >> 4;
   float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lrow[4] = {0.f, 0.f, 0.f, 0.f};

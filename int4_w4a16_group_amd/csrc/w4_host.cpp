@@ -325,7 +325,7 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
   // with the most 64-position chunks first: work-groups are dispatched in
   // list order, so the short tail splits are the ones that double up on a
   // compute unit.  The order does not change any result.
-  const int W = 4;  // chunks per split (attn_splits)
+  const int W = kAttnSplitChunks;
   for (int cnt = W; cnt >= 1; --cnt)
     for (int b = 0; b < B; ++b) {
       const int nch = c->pos[slots[b]] / 64 + 1, ns = attn_splits(c->pos[slots[b]]);

@@ -123,7 +123,10 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
 // v (row stride ldkv) are rotated at each stream's position through table
 // when it is not null; k and v are appended to the arena at the position.
 // o: [B][Hq*D] row-major, or an activation panel with o_rows rows.
-__host__ __device__ inline int attn_splits(int pos) { return (pos / 64 + 1 + 3) / 4; }
+constexpr int kAttnSplitChunks = 4;  // 64-position chunks per split = waves per attention work-group
+__host__ __device__ inline int attn_splits(int pos) {
+  return (pos / 64 + kAttnSplitChunks) / kAttnSplitChunks;
+}
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
                             const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
