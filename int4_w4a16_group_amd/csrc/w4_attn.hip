@@ -143,6 +143,18 @@ struct AttnArgs {
   float scale;        // log2(e) / sqrt(D)
 };
 
+// A float pair through one 8-byte device-scope access (partials written and
+// read by different work-groups of the same launch).
+__device__ __forceinline__ float2 ld_pair(const float* p) {
+  const uint64_t u =
+      __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+__device__ __forceinline__ void st_pair(float* p, float x, float y) {
+  const uint64_t u = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Final combine over a stream's splits, in split order: thread -> (head h,
 // four consecutive d).  The partials of NB splits are requested at a time
 // (indices clamped within the last batch) before any is used; they are read
@@ -173,11 +185,14 @@ __device__ void combine_splits(const AttnArgs& a, int b, int g, int G, int ns, i
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int s2 = min(s0 + j, ns - 1);
-        mv[j] = __hip_atomic_load(ml + 2 * s2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        lv[j] = __hip_atomic_load(ml + 2 * s2 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          ov[j][k] = __hip_atomic_load(po + (size_t)s2 * D + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float2 m_l = ld_pair(ml + 2 * s2);
+        mv[j] = m_l.x;
+        lv[j] = m_l.y;
+        const float2 o01 = ld_pair(po + (size_t)s2 * D), o23 = ld_pair(po + (size_t)s2 * D + 2);
+        ov[j][0] = o01.x;
+        ov[j][1] = o01.y;
+        ov[j][2] = o23.x;
+        ov[j][3] = o23.y;
       }
       if (ns <= NB) {
 #pragma unroll
@@ -424,16 +439,17 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
       L = L + s_l[ww][tid] * al;
     }
     float* ml = a.part_ml + (((size_t)b * a.Hq + g * G + tid) * a.nsmax + sp) * 2;
-    __hip_atomic_store(ml, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(ml + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_pair(ml, M, L);
   }
   __syncthreads();
-  for (int i = tid; i < G * D; i += 256) {
+  for (int i = 2 * tid; i < G * D; i += 512) {  // column pairs (d, d + 1)
     const int h = i / D, d = i - h * D;
-    float v = Ob[(size_t)h * D + d] * s_a[0][h];
-    for (int ww = 1; ww < 4; ++ww) v = v + Ob[((size_t)ww * G + h) * D + d] * s_a[ww][h];
-    __hip_atomic_store(a.part_o + (((size_t)b * a.Hq + g * G + h) * a.nsmax + sp) * D + d, v, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    float v0 = Ob[(size_t)h * D + d] * s_a[0][h], v1 = Ob[(size_t)h * D + d + 1] * s_a[0][h];
+    for (int ww = 1; ww < 4; ++ww) {
+      v0 = v0 + Ob[((size_t)ww * G + h) * D + d] * s_a[ww][h];
+      v1 = v1 + Ob[((size_t)ww * G + h) * D + d + 1] * s_a[ww][h];
+    }
+    st_pair(a.part_o + (((size_t)b * a.Hq + g * G + h) * a.nsmax + sp) * D + d, v0, v1);
   }
   __builtin_amdgcn_s_waitcnt(0);  // every partial store complete before the ticket
   __syncthreads();
