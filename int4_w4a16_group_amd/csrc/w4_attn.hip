@@ -207,13 +207,15 @@ __device__ void combine_splits(const AttnArgs& a, int b, int g, int G, int ns, i
           for (int k = 0; k < 4; ++k) acc[k] = acc[k] + ov[j][k] * bs;
         }
     }
+    // columns kk .. kk+3 of the [B][Hq*D] output (kk % 4 == 0): consecutive in
+    // the row and within one 8-column block of a panel, so one 8-byte store
+    const int kk = (g * G + h) * D + d0;
+    const size_t off = a.o_rows ? ((size_t)(kk >> 3) * a.o_rows + b) * 8 + (kk & 7) : (size_t)b * a.Hq * D + kk;
+    uint16_t r[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int kk = (g * G + h) * D + d0 + k;  // column of the [B][Hq*D] output
-      const size_t off =
-          a.o_rows ? ((size_t)(kk >> 3) * a.o_rows + b) * 8 + (kk & 7) : (size_t)b * a.Hq * D + kk;
-      a.o[off] = f2h(acc[k] / L);
-    }
+    for (int k = 0; k < 4; ++k) r[k] = f2h(acc[k] / L);
+    *reinterpret_cast<uint2*>(a.o + off) =
+        make_uint2((uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16));
   }
 }
 
