@@ -22,7 +22,7 @@ FLAGS = [
 
 def build(force: bool = True, jobs: int = 4) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    deps = srcs + [os.path.join(CSRC, h) for h in ("w4_internal.h", "w4_device.h")] + \
+    deps = srcs + [os.path.join(CSRC, h) for h in ("w4_internal.h", "w4_device.h", "w4_tile.h")] + \
         [os.path.join(ROOT, "include", "w4moe.h")]
     if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(os.path.getmtime(d) for d in deps):
         return LIB

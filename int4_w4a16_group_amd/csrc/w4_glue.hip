@@ -8,6 +8,7 @@
 
 #include "w4_device.h"
 #include "w4_internal.h"
+#include "w4_tile.h"
 
 namespace w4 {
 
@@ -484,12 +485,68 @@ struct RouterArgs {
   int H, E, k, B;
   RouteOut o;
   unsigned* ticket;        // zero between launches
-  const uint8_t* pf;       // work-groups B .. B+npf-1 touch this span (touch_lines)
+  const uint8_t* pf;       // work-groups nd+B .. nd+B+npf-1 touch this span (touch_lines)
   size_t pf_lines;
   int npf;
+  // fused output projection (nd > 0): work-groups 0 .. nd-1 compute h += o * Wo^T, one 16-column
+  // tile each, publish h with device-scope stores and count themselves in done (zero before and after)
+  int nd;
+  unsigned* done;
+  uint16_t* hw;            // = h, written by the projection's work-groups
+  const uint16_t* ox;      // attention output, an activation panel with oxrows rows
+  int oxrows;
+  const uint4* otiles;     // Wo bank tiles, K = oK
+  const uint16_t* oscales;
+  int oK;
 };
 
-template <int G, bool VS>
+// One tile of the output projection inside the router launch (16 waves, one
+// 256-column K slice each): the same arithmetic as the dense product's
+// residual epilogue, with h published by 4-byte device-scope stores of
+// column pairs, then a count in a.done.
+template <int MT, int G>
+__device__ __forceinline__ void oproj_tile(const RouterArgs& a, float* red) {
+  constexpr int NCH = 2, NS = NCH * 128 / G;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, t = blockIdx.x;
+  const int kbase = w * NCH * 128;
+  XRegs<MT, NCH * 4> x;
+  load_x_panel<MT, NCH>(x, a.ox, a.oxrows, a.B, kbase, lane);
+  Stage<NCH, G> st;
+  st.load(a.otiles, a.oscales, a.oK, t, w, lane);
+  float sv[NS];
+  st.scales_f32(sv);
+  f4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  const DqConst dk;
+  tile_mac<MT, NCH, G>(x, st.w, sv, acc, dk);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(red)[(w * MT + mt) * 64 + lane] = acc[mt];
+  __syncthreads();
+  const int H = a.H;
+  // every call is made by whole waves (one output per thread), so lanes j and
+  // j ^ 1 (adjacent columns of one row) pair up for one 4-byte store
+  reduce_tile<MT>(red, 16, [&](int row, int j, float v) {
+    const int n = t * 16 + j;
+    uint16_t* hp = a.hw + (size_t)min(row, a.B - 1) * H + n;
+    const uint16_t nv = f2h(h2f(*hp) + h2f(f2h(v)));
+    const uint32_t nb = __shfl_xor((uint32_t)nv, 1, 64);
+    if (row < a.B && (j & 1) == 0)
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(hp), (uint32_t)nv | (nb << 16), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  });
+  __builtin_amdgcn_s_waitcnt(0);  // every store complete before the count
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// FMT = 0: the router alone.  FMT = 1, 2: fused with the output projection
+// (16-row tiles of the batch): the router work-groups take the indices after
+// the projection's, so those are resident or done when a router work-group
+// starts (work-groups are dispatched in index order) and the wait below ends.
+// A router work-group requests its weights first, then waits (bounded) for
+// the count, then reads its row of h with device-scope loads.
+template <int G, bool VS, int FMT>
 __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   constexpr int SPG = G / 32;   // k-steps per group
   constexpr int NGC = 128 / G;  // groups per 128-column chunk
@@ -508,7 +565,15 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   __shared__ int s_ub[kRouteMaxE];
   __shared__ int s_ur[kMaxUnits * 16];
   __shared__ int s_last;
-  const int b = blockIdx.x, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  extern __shared__ float red[];  // projection partials (FMT > 0)
+  const int nd = FMT ? a.nd : 0;
+  if constexpr (FMT > 0) {
+    if ((int)blockIdx.x < nd) {
+      oproj_tile<FMT, G>(a, red);
+      return;
+    }
+  }
+  const int b = blockIdx.x - nd, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   if (b >= a.B) {
     touch_lines(a.pf, a.pf_lines, b - a.B, a.npf);
     return;
@@ -524,7 +589,7 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   // VS the eight chunks' scales of the lane's expert are one 16-byte load.
   const int i0 = 4 * tid;
   uint2 hraw = make_uint2(0u, 0u), graw = make_uint2(0u, 0u);
-  if (i0 < H) {
+  if (!FMT && i0 < H) {
     hraw = *reinterpret_cast<const uint2*>(a.h + (size_t)b * H + i0);
     graw = *reinterpret_cast<const uint2*>(a.gamma + i0);
   }
@@ -559,6 +624,20 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   // later wait on the row count the weight loads too.
   load_batch(min(c0, NC - 1));
   __builtin_amdgcn_sched_barrier(0);
+  if (FMT) {
+    if (tid == 0) {
+      unsigned it = 0;
+      while (__hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)nd && ++it < (1u << 16))
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __syncthreads();
+    if (i0 < H) {
+      const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.h + (size_t)b * H + i0),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hraw = make_uint2((uint32_t)u, (uint32_t)(u >> 32));
+      graw = *reinterpret_cast<const uint2*>(a.gamma + i0);
+    }
+  }
 
   // 1. RMSNorm of the row: 4 columns per thread, fixed-order block sum.
   {
@@ -690,7 +769,10 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   }
   __syncthreads();
   bucket_core(E, k, a.B, s_ids, BucketLds{s_mask, s_off, s_ub, s_tot, s_ur}, a.o);
-  if (tid == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (FMT) __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 int touch_groups(size_t bytes, int threads) {
@@ -700,7 +782,8 @@ int touch_groups(size_t bytes, int threads) {
 
 hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
                          uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
-                         unsigned* ticket, hipStream_t st, const void* pf, size_t pf_bytes) {
+                         unsigned* ticket, hipStream_t st, const void* pf, size_t pf_bytes, const Mat* oproj,
+                         const uint16_t* o_panel, int o_rows, unsigned* done) {
   const int npf = pf ? touch_groups(pf_bytes, 1024) : 0;
   RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket, static_cast<const uint8_t*>(pf),
                pf_bytes / 128, npf};
@@ -711,14 +794,36 @@ hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, c
   while (NTp < NT) NTp <<= 1;
   const int cpr = (NC + 16 / NTp - 1) / (16 / NTp);
   const bool vs = g == 128 && NC % 8 == 0 && cpr % 8 == 0;
+  if (oproj) {
+    // fused output projection: g = 128 and K = 16 slices of 256 (the 16 waves)
+    if (g != 128 || oproj->K != 16 * 256 || oproj->N != H || !done || !o_panel) return hipErrorInvalidValue;
+    a.nd = oproj->ntiles();
+    a.done = done;
+    a.hw = const_cast<uint16_t*>(h);
+    a.ox = o_panel;
+    a.oxrows = o_rows;
+    a.otiles = oproj->tiles;
+    a.oscales = oproj->scales;
+    a.oK = oproj->K;
+    const int MT = B > 16 ? 2 : 1;
+    const dim3 grid(a.nd + B + npf);
+    const uint32_t shm = 16 * MT * 1024;
+    if (MT == 2)
+      vs ? w4_launch(k_router<128, true, 2>, grid, dim3(1024), shm, st, a)
+         : w4_launch(k_router<128, false, 2>, grid, dim3(1024), shm, st, a);
+    else
+      vs ? w4_launch(k_router<128, true, 1>, grid, dim3(1024), shm, st, a)
+         : w4_launch(k_router<128, false, 1>, grid, dim3(1024), shm, st, a);
+    return hipGetLastError();
+  }
   switch (g) {
-    case 32: w4_launch(k_router<32, false>, dim3(B + npf), dim3(1024), 0, st, a); break;
-    case 64: w4_launch(k_router<64, false>, dim3(B + npf), dim3(1024), 0, st, a); break;
+    case 32: w4_launch(k_router<32, false, 0>, dim3(B + npf), dim3(1024), 0, st, a); break;
+    case 64: w4_launch(k_router<64, false, 0>, dim3(B + npf), dim3(1024), 0, st, a); break;
     default:
       if (vs)
-        w4_launch(k_router<128, true>, dim3(B + npf), dim3(1024), 0, st, a);
+        w4_launch(k_router<128, true, 0>, dim3(B + npf), dim3(1024), 0, st, a);
       else
-        w4_launch(k_router<128, false>, dim3(B + npf), dim3(1024), 0, st, a);
+        w4_launch(k_router<128, false, 0>, dim3(B + npf), dim3(1024), 0, st, a);
       break;
   }
   return hipGetLastError();
