@@ -751,23 +751,34 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
     __hip_atomic_store(&a.o.ids[b * k + tid], s_te[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.o.w[b * k + tid] = s_ex[tid] / sum;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-
-  // 4. Ticket: the last work-group to arrive buckets every row.
-  __syncthreads();
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (unsigned)(a.B - 1);
-  __syncthreads();
-  if (!s_last) return;
-  if (tid < E) s_mask[tid] = 0u;
-  __syncthreads();
-  for (int i = tid; i < a.B * k; i += blockDim.x) {
-    const int ex = __hip_atomic_load(&a.o.ids[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_ids[i] = ex;
-    atomicOr(&s_mask[ex], 1u << (i / k));
+  // 4. Ticket: the last work-group to arrive buckets every row.  A batch of
+  // one row has one work-group: it buckets its own ids from LDS, with no
+  // ticket and no round trip through memory (the ticket stays zero).
+  if (a.B == 1) {
+    if (tid < E) s_mask[tid] = 0u;
+    __syncthreads();
+    if (tid < k) {
+      s_ids[tid] = s_te[tid];
+      atomicOr(&s_mask[s_te[tid]], 1u);
+    }
+    __syncthreads();
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (unsigned)(a.B - 1);
+    __syncthreads();
+    if (!s_last) return;
+    if (tid < E) s_mask[tid] = 0u;
+    __syncthreads();
+    for (int i = tid; i < a.B * k; i += blockDim.x) {
+      const int ex = __hip_atomic_load(&a.o.ids[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ids[i] = ex;
+      atomicOr(&s_mask[ex], 1u << (i / k));
+    }
+    __syncthreads();
   }
-  __syncthreads();
   bucket_core(E, k, a.B, s_ids, BucketLds{s_mask, s_off, s_ub, s_tot, s_ur}, a.o);
   if (tid == 0) {
     __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
