@@ -154,8 +154,7 @@ def main():
         launches, syncs = L.w4_last_step_counts(ctx.ctx)
         r = routes.cpu().numpy()
         U = np.array([[len(np.unique(r[i, l])) for l in range(d.n_layers)] for i in range(args.steps)])
-        fused = launches == 1 + 6 * d.n_layers + 2  # 6 launches per layer: o projection inside the router
-        byt = step_bytes(d, B, U, pos0, args.steps, fused)
+        byt = step_bytes(d, B, U, pos0, args.steps)
         ms = dt / args.steps * 1e3
         # host time of one w4_decode_step call while the pinned ring still has
         # room (the first calls; later ones also wait for the GPU)
@@ -179,7 +178,7 @@ def main():
                 kms, n = L.w4_profile_end(ctx.ctx)
                 r2 = routes2.cpu().numpy()
                 U2 = np.array([[len(np.unique(r2[i, l])) for l in range(d.n_layers)] for i in range(args.steps)])
-                b2 = step_bytes(d, B, U2, pos1, args.steps, fused)
+                b2 = step_bytes(d, B, U2, pos1, args.steps)
                 kt[name] = dict(ms_total=kms, launches=n, avg_us=kms / max(n, 1) * 1e3,
                                 GBps=b2[name] * args.steps / (kms * 1e-3) / 1e9 if kms > 0 else None,
                                 bytes_per_launch=b2[name] * args.steps / max(n, 1))
@@ -230,10 +229,9 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def step_bytes(d, B, U, pos0, steps, fused=False):
+def step_bytes(d, B, U, pos0, steps):
     """Algorithmic bytes per step (averaged over the timed steps), by kernel family.
-    U[i][l]: unique experts of layer l at step i; pos0: positions at the first step.
-    fused: the output projection runs inside the router launch (its bytes count there)."""
+    U[i][l]: unique experts of layer l at step i; pos0: positions at the first step."""
     H, I, k, E, V, g = d.hidden, d.moe_inter, d.top_k, d.n_experts, d.vocab, d.group
     q = d.n_q_heads * d.head_dim
     nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim
@@ -244,10 +242,6 @@ def step_bytes(d, B, U, pos0, steps, fused=False):
     dense_io = B * (H * 2 + nqkv * 2 + q * 2 + H * 2 * 2)
     dense = d.n_layers * (dense_w + dense_io) + wb(V, H) + B * (H * 2 + V * 2)
     router = d.n_layers * (wb(E, H) + B * (H * 2 * 2 + k * 8))
-    if fused:
-        oproj = d.n_layers * (wb(H, q) + B * (q * 2 + H * 2 * 2))
-        dense -= oproj
-        router += oproj
     Um = U.mean(axis=0)                                   # per layer, averaged over steps
     gateup = float(np.sum(Um * 2 * wb(I, H)) + d.n_layers * B * k * (H * 2 + I * 2))
     down = float(np.sum(Um * wb(H, I)) + d.n_layers * B * k * (I * 2 + H * 2))

@@ -8,7 +8,6 @@
 
 #include "w4_device.h"
 #include "w4_internal.h"
-#include "w4_tile.h"
 
 namespace w4 {
 
@@ -465,15 +464,24 @@ hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut
 }
 
 // ------------------------------------------------------------------ router
-// The whole MoE front end of a decode layer in one launch.  Work-group b
-// (1024 threads) owns stream row b:
-//   xn = RMSNorm(h[b]) * gamma (fp16; written out for the expert GEMMs);
+// The whole MoE front end of a decode layer in one launch.  Work-group
+// (b, t) (1024 threads) owns stream row b and the 16 experts of tile t:
+//   xn = RMSNorm(h[b]) * gamma (fp16; every tile's work-group computes it,
+//     tile 0's writes it out for the expert GEMMs);
 //   logits[e] = sum over 128-column chunks c, in chunk order, of
-//     P[e][c] = sum over the chunk's groups of fma(scale, MFMA chain, .) from 0;
-//   top-k softmax of the row (ranked by logit, ties to the lower id).
-// Then each work-group takes a ticket; the last one buckets all rows.  Every
-// order above depends on the geometry only, never on B or on the other rows.
-constexpr int kRouterMaxUnits = 16 * 32;  // (E <= 256) / 16 tiles x (H <= 4096) / 128 chunks
+//     P[e][c] = sum over the chunk's groups of fma(scale, MFMA chain, .) from 0,
+//     published with device-scope stores;
+// the last of the row's work-groups to take the row's ticket reads the row's
+// logits back and takes its top-k softmax (ranked by logit, ties to the lower
+// id).  Then each row's last work-group takes the launch ticket; the last one
+// buckets all rows.  Every order above depends on the geometry only, never
+// on B or on the other rows.
+//
+// One work-group per (row, tile) rather than per row: a compute unit keeps
+// only so many misses in flight, so one work-group streaming the whole 128 KB
+// bank took about 9 us; a 16 KB tile arrives in a fraction of that, and the
+// exchange of the logits costs less than it saves.
+constexpr int kRouterMaxChunks = 32;  // H <= 4096
 
 struct RouterArgs {
   const uint16_t* h;       // [B][H] residual rows
@@ -485,73 +493,19 @@ struct RouterArgs {
   int H, E, k, B;
   RouteOut o;
   unsigned* ticket;        // zero between launches
-  const uint8_t* pf;       // work-groups nd+B .. nd+B+npf-1 touch this span (touch_lines)
+  float* lg;               // [B][E] logits, exchanged between a row's work-groups
+  unsigned* rticket;       // [B] row tickets, zero between launches
+  const uint8_t* pf;       // work-groups B*NT .. B*NT+npf-1 touch this span (touch_lines)
   size_t pf_lines;
   int npf;
-  // fused output projection (nd > 0): work-groups 0 .. nd-1 compute h += o * Wo^T, one 16-column
-  // tile each, publish h with device-scope stores and count themselves in done (zero before and after)
-  int nd;
-  unsigned* done;
-  uint16_t* hw;            // = h, written by the projection's work-groups
-  const uint16_t* ox;      // attention output, an activation panel with oxrows rows
-  int oxrows;
-  const uint4* otiles;     // Wo bank tiles, K = oK
-  const uint16_t* oscales;
-  int oK;
 };
 
-// One tile of the output projection inside the router launch (16 waves, one
-// 256-column K slice each): the same arithmetic as the dense product's
-// residual epilogue, with h published by 4-byte device-scope stores of
-// column pairs, then a count in a.done.
-template <int MT, int G>
-__device__ __forceinline__ void oproj_tile(const RouterArgs& a, float* red) {
-  constexpr int NCH = 2, NS = NCH * 128 / G;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, t = blockIdx.x;
-  const int kbase = w * NCH * 128;
-  XRegs<MT, NCH * 4> x;
-  load_x_panel<MT, NCH>(x, a.ox, a.oxrows, a.B, kbase, lane);
-  Stage<NCH, G> st;
-  st.load(a.otiles, a.oscales, a.oK, t, w, lane);
-  float sv[NS];
-  st.scales_f32(sv);
-  f4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
-  const DqConst dk;
-  tile_mac<MT, NCH, G>(x, st.w, sv, acc, dk);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(red)[(w * MT + mt) * 64 + lane] = acc[mt];
-  __syncthreads();
-  const int H = a.H;
-  // every call is made by whole waves (one output per thread), so lanes j and
-  // j ^ 1 (adjacent columns of one row) pair up for one 4-byte store
-  reduce_tile<MT>(red, 16, [&](int row, int j, float v) {
-    const int n = t * 16 + j;
-    uint16_t* hp = a.hw + (size_t)min(row, a.B - 1) * H + n;
-    const uint16_t nv = f2h(h2f(*hp) + h2f(f2h(v)));
-    const uint32_t nb = __shfl_xor((uint32_t)nv, 1, 64);
-    if (row < a.B && (j & 1) == 0)
-      __hip_atomic_store(reinterpret_cast<uint32_t*>(hp), (uint32_t)nv | (nb << 16), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  });
-  __builtin_amdgcn_s_waitcnt(0);  // every store complete before the count
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// FMT = 0: the router alone.  FMT = 1, 2: fused with the output projection
-// (16-row tiles of the batch): the router work-groups take the indices after
-// the projection's, so those are resident or done when a router work-group
-// starts (work-groups are dispatched in index order) and the wait below ends.
-// A router work-group requests its weights first, then waits (bounded) for
-// the count, then reads its row of h with device-scope loads.
-template <int G, bool VS, int FMT>
+template <int G>
 __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   constexpr int SPG = G / 32;   // k-steps per group
   constexpr int NGC = 128 / G;  // groups per 128-column chunk
   __shared__ __align__(16) uint16_t s_x[4096];
-  __shared__ float s_part[kRouterMaxUnits * 16];
+  __shared__ float s_part[kRouterMaxChunks * 16];
   __shared__ float s_lg[kRouteMaxE];
   __shared__ float sh[16];
   __shared__ __align__(16) uint32_t s_key[kRouteMaxE];
@@ -565,79 +519,37 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   __shared__ int s_ub[kRouteMaxE];
   __shared__ int s_ur[kMaxUnits * 16];
   __shared__ int s_last;
-  extern __shared__ float red[];  // projection partials (FMT > 0)
-  const int nd = FMT ? a.nd : 0;
-  if constexpr (FMT > 0) {
-    if ((int)blockIdx.x < nd) {
-      oproj_tile<FMT, G>(a, red);
-      return;
-    }
-  }
-  const int b = blockIdx.x - nd, tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  if (b >= a.B) {
-    touch_lines(a.pf, a.pf_lines, b - a.B, a.npf);
-    return;
-  }
   const int H = a.H, E = a.E, k = a.k;
   const int NC = H >> 7, NT = (E + 15) >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if ((int)blockIdx.x >= a.B * NT) {
+    touch_lines(a.pf, a.pf_lines, blockIdx.x - a.B * NT, a.npf);
+    return;
+  }
+  const int b = blockIdx.x / NT, t = blockIdx.x - b * NT;
 
-  // The row and gain are requested first (their wait comes first); then this
-  // wave's first batch of weights, whose latency overlaps the norm.  Wave w
-  // owns expert tile t = w / WPT and a contiguous range of cpr 128-column
-  // chunks, taken in batches of eight; every load of a batch is issued before
-  // any is used (indices clamped, results of clamped chunks dropped).  With
-  // VS the eight chunks' scales of the lane's expert are one 16-byte load.
+  // The row and gain are requested first (their wait comes first); then the
+  // weights and scales of this wave's first chunk (wave w takes chunks w,
+  // w + 16, ...), whose latency overlaps the norm.
   const int i0 = 4 * tid;
   uint2 hraw = make_uint2(0u, 0u), graw = make_uint2(0u, 0u);
-  if (!FMT && i0 < H) {
+  if (i0 < H) {
     hraw = *reinterpret_cast<const uint2*>(a.h + (size_t)b * H + i0);
     graw = *reinterpret_cast<const uint2*>(a.gamma + i0);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep these two loads ahead of the weight loads
-  int NTp = 1;
-  while (NTp < NT) NTp <<= 1;
-  const int WPT = 16 / NTp, cpr = (NC + WPT - 1) / WPT;
-  const int wt = w / WPT, tc = min(wt, NT - 1);
-  const int c0 = (w % WPT) * cpr, c1 = min(NC, c0 + cpr);
-  uint4 wv[8];
-  uint16_t sr[8][NGC];
-  auto load_batch = [&](int cb) {
+  uint4 wv;
+  uint16_t sr[NGC];
+  const uint16_t* srow = a.scales + (size_t)(16 * t + (lane & 15)) * (H / G);
+  auto load_chunk = [&](int c) {
+    wv = a.tiles[((size_t)t * NC + c) * 64 + lane];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = min(cb + i, NC - 1);
-      wv[i] = a.tiles[((size_t)tc * NC + c) * 64 + lane];
-    }
-    const uint16_t* srow = a.scales + (size_t)(16 * tc + (lane & 15)) * (H / G);
-    if (VS) {
-      const uint4 v = *reinterpret_cast<const uint4*>(srow + min(cb, H / G - 8));
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sr[i][0] = (uint16_t)(u[i / 2] >> (16 * (i & 1)));
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < NGC; ++j) sr[i][j] = srow[min(cb + i, NC - 1) * NGC + j];
-    }
+    for (int j = 0; j < NGC; ++j) sr[j] = srow[c * NGC + j];
   };
   // Unconditional (chunk clamped): a load under a branch would make every
   // later wait on the row count the weight loads too.
-  load_batch(min(c0, NC - 1));
+  load_chunk(min(w, NC - 1));
   __builtin_amdgcn_sched_barrier(0);
-  if (FMT) {
-    if (tid == 0) {
-      unsigned it = 0;
-      while (__hip_atomic_load(a.done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)nd && ++it < (1u << 16))
-        __builtin_amdgcn_s_sleep(1);
-    }
-    __syncthreads();
-    if (i0 < H) {
-      const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(a.h + (size_t)b * H + i0),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      hraw = make_uint2((uint32_t)u, (uint32_t)(u >> 32));
-      graw = *reinterpret_cast<const uint2*>(a.gamma + i0);
-    }
-  }
 
   // 1. RMSNorm of the row: 4 columns per thread, fixed-order block sum.
   {
@@ -654,62 +566,69 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
       ss = ss + v[3] * v[3];
     }
     ss = block_sum(ss, sh);
-    const float r = 1.0f / sqrtf(ss / (float)H + a.eps);
+    const float rs = 1.0f / sqrtf(ss / (float)H + a.eps);
     if (i0 < H) {
-      const uint16_t o0 = f2h((v[0] * r) * h2f((uint16_t)(graw.x & 0xFFFFu)));
-      const uint16_t o1 = f2h((v[1] * r) * h2f((uint16_t)(graw.x >> 16)));
-      const uint16_t o2 = f2h((v[2] * r) * h2f((uint16_t)(graw.y & 0xFFFFu)));
-      const uint16_t o3 = f2h((v[3] * r) * h2f((uint16_t)(graw.y >> 16)));
+      const uint16_t o0 = f2h((v[0] * rs) * h2f((uint16_t)(graw.x & 0xFFFFu)));
+      const uint16_t o1 = f2h((v[1] * rs) * h2f((uint16_t)(graw.x >> 16)));
+      const uint16_t o2 = f2h((v[2] * rs) * h2f((uint16_t)(graw.y & 0xFFFFu)));
+      const uint16_t o3 = f2h((v[3] * rs) * h2f((uint16_t)(graw.y >> 16)));
       const uint2 packed = make_uint2((uint32_t)o0 | ((uint32_t)o1 << 16), (uint32_t)o2 | ((uint32_t)o3 << 16));
       *reinterpret_cast<uint2*>(s_x + i0) = packed;
-      *reinterpret_cast<uint2*>(a.xn + (size_t)b * H + i0) = packed;
+      if (t == 0) *reinterpret_cast<uint2*>(a.xn + (size_t)b * H + i0) = packed;
     }
   }
   __syncthreads();
 
-  // 2. Chunk partials P[t][c] (stored at unit t * NC + c).  Every A-operand
-  // row is the normalised row, so D row 0 (lanes 0..15, element 0) is the
-  // result; the A operand of a chunk is read from LDS (a broadcast read).
+  // 2. Chunk partials P[c] of the tile's 16 experts.  Every A-operand row is
+  // the normalised row, so D row 0 (lanes 0..15, element 0) is the result;
+  // the A operand of a chunk is read from LDS (a broadcast read).
   const DqConst dk;
-  for (int cb = c0; cb < c1; cb += 8) {
-    if (cb != c0) load_batch(cb);
+  for (int c = w; c < NC; c += 16) {
+    if (c != w) load_chunk(c);
+    h8 xa[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = cb + i;
-      if (wt < NT && c < c1) {
-        h8 xa[4];
+    for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const h8*>(s_x + 128 * c + 32 * s + 8 * (lane >> 4));
+    const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+    f4 acc = {0.f, 0.f, 0.f, 0.f}, part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xa[s] = *reinterpret_cast<const h8*>(s_x + 128 * c + 32 * s + 8 * (lane >> 4));
-        const uint32_t wd[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
-        f4 acc = {0.f, 0.f, 0.f, 0.f}, part = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4; ++s) {
+      if (s % SPG == 0) part = f4{0.f, 0.f, 0.f, 0.f};
+      part = mfma16x16x32(xa[s], dq8(wd[s], dk), part);
+      if ((s + 1) % SPG == 0) {
+        const float sc = h2f(sr[s / SPG]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s % SPG == 0) part = f4{0.f, 0.f, 0.f, 0.f};
-          part = mfma16x16x32(xa[s], dq8(wd[s], dk), part);
-          if ((s + 1) % SPG == 0) {
-            const float sc = h2f(sr[i][s / SPG]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, part[r], acc[r]);
-          }
-        }
-        // All four rows are equal; keeping every element of the MFMA results
-        // live stops the compiler from reusing a destination register of an
-        // MFMA still in flight for the next operand.
-        asm volatile("" ::"v"(acc));
-        if (lane < 16) s_part[(wt * NC + c) * 16 + lane] = acc[0];
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(sc, part[q], acc[q]);
       }
     }
-  }
-  __syncthreads();
-  if (tid < E) {
-    const int t = tid >> 4, col = tid & 15;
-    float l = s_part[(t * NC) * 16 + col];
-    for (int c = 1; c < NC; ++c) l = l + s_part[(t * NC + c) * 16 + col];
-    s_lg[tid] = l;
+    // All four rows are equal; keeping every element of the MFMA results
+    // live stops the compiler from reusing a destination register of an
+    // MFMA still in flight for the next operand.
+    asm volatile("" ::"v"(acc));
+    if (lane < 16) s_part[c * 16 + lane] = acc[0];
   }
   __syncthreads();
 
-  // 3. Top-k of the row by rank counting: rank(e) = #{e' : key e' > key e, or
+  // 3. The tile's logits to memory; the row's last work-group reads all back.
+  if (tid < 16 && 16 * t + tid < E) {
+    float l = s_part[tid];
+    for (int c = 1; c < NC; ++c) l = l + s_part[c * 16 + tid];
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(a.lg) + (size_t)b * E + 16 * t + tid, __float_as_uint(l),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the stores complete before the row ticket
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(a.rticket + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(NT - 1);
+  __syncthreads();
+  if (!s_last) return;
+  if (tid < E)
+    s_lg[tid] = __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(a.lg) + (size_t)b * E + tid,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (tid == 0) __hip_atomic_store(a.rticket + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+
+  // 4. Top-k of the row by rank counting: rank(e) = #{e' : key e' > key e, or
   // equal keys and e' < e} (NaN ranks as -inf); thread (e, part) counts over
   // one part of the experts, integer LDS adds combine the parts.  The experts
   // of rank < k are the top-k in rank order.
@@ -745,15 +664,15 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   if (tid < k) {
     float sum = 0.f;
     for (int r = 0; r < k; ++r) sum = sum + s_ex[r];
-    // ids are read by the last work-group within this launch: device-scope
+    // ids are read by the last row within this launch: device-scope
     // atomic stores, complete (vmcnt 0) before the ticket is taken.  The
     // other outputs are read by later launches only.
     __hip_atomic_store(&a.o.ids[b * k + tid], s_te[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     a.o.w[b * k + tid] = s_ex[tid] / sum;
   }
-  // 4. Ticket: the last work-group to arrive buckets every row.  A batch of
-  // one row has one work-group: it buckets its own ids from LDS, with no
-  // ticket and no round trip through memory (the ticket stays zero).
+  // 5. Launch ticket: the last row to arrive buckets every row.  With one
+  // row, its last work-group buckets the row's ids straight from LDS, with
+  // no launch ticket and no round trip through memory (the ticket stays zero).
   if (a.B == 1) {
     if (tid < E) s_mask[tid] = 0u;
     __syncthreads();
@@ -780,10 +699,7 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
     __syncthreads();
   }
   bucket_core(E, k, a.B, s_ids, BucketLds{s_mask, s_off, s_ub, s_tot, s_ur}, a.o);
-  if (tid == 0) {
-    __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (FMT) __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 int touch_groups(size_t bytes, int threads) {
@@ -793,49 +709,17 @@ int touch_groups(size_t bytes, int threads) {
 
 hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
                          uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
-                         unsigned* ticket, hipStream_t st, const void* pf, size_t pf_bytes, const Mat* oproj,
-                         const uint16_t* o_panel, int o_rows, unsigned* done) {
+                         unsigned* ticket, float* lg, unsigned* rticket, hipStream_t st, const void* pf,
+                         size_t pf_bytes) {
+  if (H % 128 != 0 || H / 128 > kRouterMaxChunks || E > kRouteMaxE || !lg || !rticket) return hipErrorInvalidValue;
   const int npf = pf ? touch_groups(pf_bytes, 1024) : 0;
-  RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket, static_cast<const uint8_t*>(pf),
-               pf_bytes / 128, npf};
-  // chunk ranges as in the kernel: the eight scales of a batch are one
-  // aligned 16-byte load when g = 128 and ranges and scale rows are multiples of 8
-  const int NC = H / 128, NT = (E + 15) / 16;
-  int NTp = 1;
-  while (NTp < NT) NTp <<= 1;
-  const int cpr = (NC + 16 / NTp - 1) / (16 / NTp);
-  const bool vs = g == 128 && NC % 8 == 0 && cpr % 8 == 0;
-  if (oproj) {
-    // fused output projection: g = 128 and K = 16 slices of 256 (the 16 waves)
-    if (g != 128 || oproj->K != 16 * 256 || oproj->N != H || !done || !o_panel) return hipErrorInvalidValue;
-    a.nd = oproj->ntiles();
-    a.done = done;
-    a.hw = const_cast<uint16_t*>(h);
-    a.ox = o_panel;
-    a.oxrows = o_rows;
-    a.otiles = oproj->tiles;
-    a.oscales = oproj->scales;
-    a.oK = oproj->K;
-    const int MT = B > 16 ? 2 : 1;
-    const dim3 grid(a.nd + B + npf);
-    const uint32_t shm = 16 * MT * 1024;
-    if (MT == 2)
-      vs ? w4_launch(k_router<128, true, 2>, grid, dim3(1024), shm, st, a)
-         : w4_launch(k_router<128, false, 2>, grid, dim3(1024), shm, st, a);
-    else
-      vs ? w4_launch(k_router<128, true, 1>, grid, dim3(1024), shm, st, a)
-         : w4_launch(k_router<128, false, 1>, grid, dim3(1024), shm, st, a);
-    return hipGetLastError();
-  }
+  const RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket, lg, rticket,
+                     static_cast<const uint8_t*>(pf), pf_bytes / 128, npf};
+  const dim3 grid(B * ((E + 15) / 16) + npf);
   switch (g) {
-    case 32: w4_launch(k_router<32, false, 0>, dim3(B + npf), dim3(1024), 0, st, a); break;
-    case 64: w4_launch(k_router<64, false, 0>, dim3(B + npf), dim3(1024), 0, st, a); break;
-    default:
-      if (vs)
-        w4_launch(k_router<128, true, 0>, dim3(B + npf), dim3(1024), 0, st, a);
-      else
-        w4_launch(k_router<128, false, 0>, dim3(B + npf), dim3(1024), 0, st, a);
-      break;
+    case 32: w4_launch(k_router<32>, grid, dim3(1024), 0, st, a); break;
+    case 64: w4_launch(k_router<64>, grid, dim3(1024), 0, st, a); break;
+    default: w4_launch(k_router<128>, grid, dim3(1024), 0, st, a); break;
   }
   return hipGetLastError();
 }

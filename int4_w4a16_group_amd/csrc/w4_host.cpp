@@ -42,7 +42,7 @@ struct BankPlan {
 };
 
 struct WsPlan {
-  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, odone, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, rlg, rticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
       used, n_used, units, unit_rows, n_units, act, y, logits, next, rows, table, total;
 };
 
@@ -145,7 +145,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.amax_ticket = take(Bm * 4);
   w.rlogits = take(Bm * E * 4);
   w.ticket = take(64);
-  w.odone = take(64);
+  w.rlg = take(Bm * E * 4);
+  w.rticket = take(Bm * 4);
   w.ids = take(Bm * k * 4);
   w.w = take(Bm * k * 4);
   w.counts = take(E * 4);
@@ -281,9 +282,9 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
   if (!c->table_ready) {
     HIPCHK(c, launch_rope_table(c->cap, c->d.head_dim, (double)c->d.rope_theta, c->W<float2>(c->wp.table), st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.ticket), 0u, 16, st));
-    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.odone), 0u, 16, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.aticket), 0u, (size_t)c->Bm * c->d.n_kv_heads, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.amax_ticket), 0u, (size_t)c->Bm, st));
+    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.rticket), 0u, (size_t)c->Bm, st));
     c->launches += 5;
     c->table_ready = true;
   }
@@ -394,25 +395,17 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
                               qkv + (size_t)d.n_q_heads * d.head_dim, qkv + (size_t)(d.n_q_heads + d.n_kv_heads) * d.head_dim,
                               nqkv, c->W<float2>(c->wp.table), c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
                               c->W<unsigned>(c->wp.aticket), o, st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
-  // With g = 128 and an output projection of K = 4096 (16 slices of 256, the
-  // router work-group's 16 waves), the projection runs inside the router
-  // launch at B <= 8, so the router's weight requests overlap it (see
-  // k_router).  Measured on the 48-layer model: +3.5% tok/s at B = 1, +1.5% at
-  // B = 4; at B = 32 the separate launches were 1% faster.  The arithmetic is
-  // the same either way.
-  const Mat Om = c->mat(L.o);
-  const bool fuse = d.group == 128 && Om.K == 16 * 256 && B <= 8;
-  if (!fuse) {
+  {
     ProfScope ps(c, W4_K_DENSE, st);
-    LCHK(c, 1, launch_gemm(Om, B, o, qd, h, H, EPI_RESID, st, R));
+    LCHK(c, 1, launch_gemm(c->mat(L.o), B, o, qd, h, H, EPI_RESID, st, R));
   }
   RouteOut r = c->route_out(ids_out);
   {
     ProfScope ps(c, W4_K_ROUTER, st);
     const Mat Rm = c->mat(L.router);
     LCHK(c, 1, launch_router(B, H, d.n_experts, d.top_k, d.group, h, c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn,
-                             Rm.tiles, Rm.scales, r, c->W<unsigned>(c->wp.ticket), st, next_span, next_bytes,
-                             fuse ? &Om : nullptr, o, R, c->W<unsigned>(c->wp.odone)));
+                             Rm.tiles, Rm.scales, r, c->W<unsigned>(c->wp.ticket), c->W<float>(c->wp.rlg),
+                             c->W<unsigned>(c->wp.rticket), st, next_span, next_bytes));
   }
   {
     ProfScope ps(c, W4_K_MOE_GATEUP, st);

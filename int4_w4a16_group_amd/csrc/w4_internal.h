@@ -70,18 +70,16 @@ struct RouteOut {
 // Routing in one work-group: top-k softmax of fp32 logits [B][E], bucketing and 16-row units.  B <= 32.
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st);
 
-// MoE front end of a decode layer in one launch (one work-group per row, B <= 32):
-// xn = RMSNorm(h) * gamma, the router product, top-k softmax and the bucketing
-// (done by the last work-group to finish; ticket is zero before and after).
+// MoE front end of a decode layer in one launch (one work-group per row and
+// 16-expert tile, B <= 32): xn = RMSNorm(h) * gamma, the router product, top-k
+// softmax and the bucketing.  lg [B][E]: the logits exchanged between a row's
+// work-groups; rticket [B] and ticket: counters, zero before and after.
 // pf, pf_bytes: a span of the bank touched by spare work-groups of the launch
-// (touch_lines below); null for none.  oproj: the output projection run in
-// the same launch first (h += o * Wo^T, o an activation panel with o_rows
-// rows; g = 128 and K = 4096 only; done: a counter, zero before and after).
+// (touch_lines below); null for none.
 hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
                          uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
-                         unsigned* ticket, hipStream_t st, const void* pf = nullptr, size_t pf_bytes = 0,
-                         const Mat* oproj = nullptr, const uint16_t* o_panel = nullptr, int o_rows = 0,
-                         unsigned* done = nullptr);
+                         unsigned* ticket, float* lg, unsigned* rticket, hipStream_t st, const void* pf = nullptr,
+                         size_t pf_bytes = 0);
 // Spare work-groups for touching a span of that many bytes with threads-wide
 // work-groups: about one per compute unit, each touching at most one line
 // per thread.
