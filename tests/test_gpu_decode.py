@@ -72,6 +72,52 @@ def test_tiny_layer_two_steps(gpu):
         ctx.close()
 
 
+# Router geometries beyond the tiny and full models: the router runs one
+# work-group per (row, 16-expert tile), each wave taking 128-column chunks
+# w, w + 16, ...  H = 4096 gives two chunks per wave, 40 experts three tiles
+# (the last one partial), g = 64 two scale groups per chunk; H = 1024 leaves
+# half the waves without a chunk, 24 experts give two tiles.
+ROUTER_SHAPES = {
+    "h4096_e40_g64": dataclasses.replace(inputs.TINY, hidden=4096, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                                n_experts=40, top_k=4, moe_inter=256, group=64),
+    "h1024_e24_g128": dataclasses.replace(inputs.TINY, hidden=1024, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                                                 n_experts=24, top_k=3, moe_inter=128, group=128),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTER_SHAPES))
+def test_layer_router_geometries(gpu, name):
+    d = ROUTER_SHAPES[name]
+    positions = [1, 9, 30, 64, 100]
+    B, n_slots, cap = len(positions), 8, 128
+    mw = inputs.make_model(d, 3, with_vocab=False)
+    ctx = Context(d, n_slots, cap)
+    om = oracle.Model(mw)
+    oa = oracle.Arena(d, n_slots, cap)
+    try:
+        ctx.load_model(mw)
+        slots = []
+        for b, p in enumerate(positions):
+            k, v = inputs.prefix_kv(3, b, d.n_layers, p, d.n_kv_heads, d.head_dim)
+            s = ctx.join(p, 4, k, v)
+            oa.seed(s, k, v)
+            slots.append(s)
+        h = inputs.normal_f16(inputs.rng(3, inputs.T_X, d.hidden), (B, d.hidden))
+        hd = to_dev(h, gpu)
+        ids = torch.empty((B, d.top_k), dtype=torch.int32, device=gpu)
+        L.w4_layer_step(ctx.ctx, 0, slots, hd, ids, ctx.stream)
+        rh, rids, rlg = oracle.layer_step(om, oa, 0, slots, positions, h)
+        gh, gids = to_host(hd), to_host(ids)
+        for b in range(B):
+            if set(gids[b]) != set(rids[b]):
+                assert near_tie(rlg[b], d.top_k), f"{name}: routing differs at row {b}"
+                pytest.skip("routing near-tie")
+        assert np.array_equal(gids, rids), name
+        assert_normwise(f16v(gh), f16v(rh), TOL, name)
+    finally:
+        ctx.close()
+
+
 # ------------------------------------------------------------------ whole step
 SMALL = dataclasses.replace(inputs.TINY, n_layers=3, vocab=500, top_k=2)
 
