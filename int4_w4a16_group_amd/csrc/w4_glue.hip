@@ -89,6 +89,13 @@ __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, con
   const uint8_t* row = emb_p + (size_t)t * (H / 2);
   const uint16_t* srow = emb_s + (size_t)t * (H / g);
   constexpr int PER = 2;  // H <= 4096 = 8 columns x 2 x 256 threads
+  // the norm's gain is requested with the codes, not after the sum
+  uint4 gv[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = 8 * (threadIdx.x + j * kNormThreads);
+    gv[j] = i < H ? *reinterpret_cast<const uint4*>(gamma + i) : make_uint4(0u, 0u, 0u, 0u);
+  }
   float v[8 * PER];
   float ss = 0.f;
 #pragma unroll
@@ -123,8 +130,7 @@ __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, con
   for (int j = 0; j < PER; ++j) {
     const int i = 8 * (threadIdx.x + j * kNormThreads);
     if (i < H) {
-      const uint4 gv = *reinterpret_cast<const uint4*>(gamma + i);
-      const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+      const uint32_t gw[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
       uint32_t out[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -165,13 +171,16 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
     const uint32_t u = e < 2 ? q.x : e < 4 ? q.y : e < 6 ? q.z : q.w;
     return h2f((uint16_t)(u >> (16 * (e & 1))));
   };
-  // the residual row does not depend on the routing: requested first
-  uint4 hres[PER];
+  // the residual row and the norm's gain do not depend on the routing:
+  // requested first, so the gain is not a memory round trip after the sum
+  uint4 hres[PER], gv[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = 8 * (threadIdx.x + j * kCombThreads);
     hres[j] = make_uint4(0u, 0u, 0u, 0u);
+    gv[j] = make_uint4(0u, 0u, 0u, 0u);
     if (resid && i < H) hres[j] = *reinterpret_cast<const uint4*>(h + (size_t)b * H + i);
+    if (gamma && i < H) gv[j] = *reinterpret_cast<const uint4*>(gamma + i);
   }
   if (threadIdx.x < k) {
     s_inv[threadIdx.x] = inv[b * k + threadIdx.x];
@@ -221,12 +230,11 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
   for (int j = 0; j < PER; ++j) {
     const int i = 8 * (threadIdx.x + j * kCombThreads);
     if (i < H) {
-      const uint4 gv = *reinterpret_cast<const uint4*>(gamma + i);
       uint32_t out[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const uint16_t o0 = f2h((v[8 * j + e] * rr) * half_of(gv, e));
-        const uint16_t o1 = f2h((v[8 * j + e + 1] * rr) * half_of(gv, e + 1));
+        const uint16_t o0 = f2h((v[8 * j + e] * rr) * half_of(gv[j], e));
+        const uint16_t o1 = f2h((v[8 * j + e + 1] * rr) * half_of(gv[j], e + 1));
         out[e / 2] = (uint32_t)o0 | ((uint32_t)o1 << 16);
       }
       *reinterpret_cast<uint4*>(xn + act_off(b, i, H, rows)) = make_uint4(out[0], out[1], out[2], out[3]);
