@@ -250,11 +250,11 @@ hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* in
 }
 
 // ------------------------------------------------------------------ routing
-// One work-group of 1024 threads does the whole MoE front end for B <= 32
-// rows: (optional) RMSNorm of the block input, the fp32 router product on
-// MFMA, top-k softmax routing, and the (stream, expert) bucketing with the
-// 16-row work units of the grouped GEMMs.  All of it is per-row arithmetic
-// with fixed orders, so a row's routing never depends on the other rows.
+// Top-k softmax routing and the (stream, expert) bucketing with the 16-row
+// work units of the grouped GEMMs, shared by the routing primitive (k_route,
+// from given logits) and the decode router (k_router).  All of it is per-row
+// arithmetic with fixed orders, so a row's routing never depends on the
+// other rows.
 
 // Order-preserving key of a logit: larger float -> larger unsigned; NaN
 // ranks as -inf and -0 as +0 (they compare equal as floats).
