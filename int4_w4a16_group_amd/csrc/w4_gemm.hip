@@ -157,6 +157,73 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   }
 }
 
+// The residual product with K = 16 slices of 256 (the output projection at
+// K = 4096) over two 8-wave work-groups per 16-column tile, so that 2x as many
+// compute units share the activation panel reads.  Work-group 2t takes slices
+// 0..7 of tile t, sums its waves' partials in wave order and publishes that
+// sum (device-scope stores, then a flag); work-group 2t+1 takes slices 8..15,
+// waits (bounded) for the flag and continues the same in-order sum over its
+// own waves.  The result is r0 + r1 + ... + r15 summed left to right, the
+// one-work-group form's sum bit for bit.  The second work-group has the higher
+// index, so the first is resident or done when it waits.
+template <int MT, int G>
+__global__ void __launch_bounds__(512) k_gemm_resid_split(DenseArgs a, float* part, unsigned* flag) {
+  extern __shared__ float red[];  // [8 waves][MT][64][4]
+  constexpr int NCH = 2, NS = NCH * 128 / G;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x >> 1, half = blockIdx.x & 1;
+  if (t >= a.ntiles) return;
+  const int ws = half * 8 + w;  // this wave's K slice
+  XRegs<MT, NCH * 4> x;
+  load_x_panel<MT, NCH>(x, a.x, a.xrows, a.B, ws * NCH * 128, lane);
+  Stage<NCH, G> st;
+  st.load(a.tiles, a.scales, a.K, t, ws, lane);
+  float sv[NS];
+  st.scales_f32(sv);
+  f4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  const DqConst dk;
+  tile_mac<MT, NCH, G>(x, st.w, sv, acc, dk);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(red)[(w * MT + mt) * 64 + lane] = acc[mt];
+  __syncthreads();
+  uint32_t* pt = reinterpret_cast<uint32_t*>(part) + (size_t)t * MT * 256;
+  if (half == 0) {
+    // output (row, j) is entry row * 16 + j of the tile's published sum
+    reduce_tile<MT>(red, 8, [&](int row, int j, float v) {
+      __hip_atomic_store(pt + row * 16 + j, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    });
+    __builtin_amdgcn_s_waitcnt(0);  // every store complete before the flag
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(flag + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    unsigned it = 0;
+    while (__hip_atomic_load(flag + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u && ++it < (1u << 16))
+      __builtin_amdgcn_s_sleep(1);
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < MT * 256; o += blockDim.x) {
+    const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
+    const int idx = mt * 256 + ((i >> 2) * 16 + j) * 4 + (i & 3);  // as in reduce_tile
+    float p[8];
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) p[ww] = red[ww * MT * 256 + idx];
+    float v = __uint_as_float(__hip_atomic_load(pt + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) v = v + p[ww];
+    const int row = mt * 16 + i, n = t * 16 + j;
+    if (row < a.B && n < a.N) {
+      uint16_t* h = reinterpret_cast<uint16_t*>(a.y) + (size_t)row * a.ldy + n;
+      *h = f2h(h2f(*h) + h2f(f2h(v)));
+    }
+  }
+  __syncthreads();  // every read of the published sum done before the reset
+  if (threadIdx.x == 0) __hip_atomic_store(flag + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 typedef void (*DenseKernel)(DenseArgs);
 
 // LB: launch bound; 512 threads (<= 8 waves) leaves up to 256 VGPRs per lane.
@@ -478,6 +545,30 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)kMaxUnits * 16;
   const int grid = resident_grid(k, NW * 64, shm);
   w4_launch(k, dim3(grid), dim3(NW * 64), (uint32_t)shm, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int xrows, uint16_t* h, int ldh,
+                                  float* part, unsigned* flag, hipStream_t st) {
+  if (w.K != 16 * 256 || w.ntiles() > kSplitMaxTiles || xrows < 1 || !part || !flag) return hipErrorInvalidValue;
+  const int MT = B > 16 ? 2 : 1;
+  DenseArgs a{w.tiles, w.scales, w.N, w.K, w.ntiles(), xp, 0, B, h, ldh, xrows};
+  const dim3 grid(2 * w.ntiles());
+  const uint32_t shm = 8 * MT * 1024;
+  switch (w.g) {
+    case 32:
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 32>, grid, dim3(512), shm, st, a, part, flag)
+              : w4_launch(k_gemm_resid_split<1, 32>, grid, dim3(512), shm, st, a, part, flag);
+      break;
+    case 64:
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 64>, grid, dim3(512), shm, st, a, part, flag)
+              : w4_launch(k_gemm_resid_split<1, 64>, grid, dim3(512), shm, st, a, part, flag);
+      break;
+    default:
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 128>, grid, dim3(512), shm, st, a, part, flag)
+              : w4_launch(k_gemm_resid_split<1, 128>, grid, dim3(512), shm, st, a, part, flag);
+      break;
+  }
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ struct BankPlan {
 };
 
 struct WsPlan {
-  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, rlg, rticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, rlg, rticket, spart, sflag, ids, w, counts, offsets, pair_stream, pair_rank, inv,
       used, n_used, units, unit_rows, n_units, act, y, logits, next, rows, table, total;
 };
 
@@ -147,6 +147,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.ticket = take(64);
   w.rlg = take(Bm * E * 4);
   w.rticket = take(Bm * 4);
+  w.spart = take((size_t)kSplitMaxTiles * 512 * 4);
+  w.sflag = take((size_t)kSplitMaxTiles * 4);
   w.ids = take(Bm * k * 4);
   w.w = take(Bm * k * 4);
   w.counts = take(E * 4);
@@ -285,7 +287,8 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.aticket), 0u, (size_t)c->Bm * c->d.n_kv_heads, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.amax_ticket), 0u, (size_t)c->Bm, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.rticket), 0u, (size_t)c->Bm, st));
-    c->launches += 5;
+    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.sflag), 0u, (size_t)kSplitMaxTiles, st));
+    c->launches += 6;
     c->table_ready = true;
   }
   return W4_OK;
@@ -395,9 +398,17 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
                               qkv + (size_t)d.n_q_heads * d.head_dim, qkv + (size_t)(d.n_q_heads + d.n_kv_heads) * d.head_dim,
                               nqkv, c->W<float2>(c->wp.table), c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
                               c->W<unsigned>(c->wp.aticket), o, st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
+  // Above 16 rows (a 32-row tile) the output projection at K = 4096 runs as
+  // two work-groups per tile (same sums, bit for bit; see
+  // launch_gemm_resid_split).  Measured on the 48-layer model: +0.4% tok/s at
+  // B = 32; at B <= 8 the flag wait cost more than the spread saved (-1..2%).
   {
     ProfScope ps(c, W4_K_DENSE, st);
-    LCHK(c, 1, launch_gemm(c->mat(L.o), B, o, qd, h, H, EPI_RESID, st, R));
+    const Mat Om = c->mat(L.o);
+    if (B > 16 && Om.K == 16 * 256 && Om.ntiles() <= kSplitMaxTiles)
+      LCHK(c, 1, launch_gemm_resid_split(Om, B, o, R, h, H, c->W<float>(c->wp.spart), c->W<unsigned>(c->wp.sflag), st));
+    else
+      LCHK(c, 1, launch_gemm(Om, B, o, qd, h, H, EPI_RESID, st, R));
   }
   RouteOut r = c->route_out(ids_out);
   {

@@ -85,6 +85,14 @@ hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, c
 // per thread.
 int touch_groups(size_t bytes, int threads);
 
+// h += x * W^T (fp16 residual epilogue) for K = 4096 with the K slices split
+// over two work-groups per tile (bit-identical to launch_gemm's EPI_RESID);
+// xp an activation panel with xrows rows; part [ntiles][512] fp32 and flag
+// [ntiles] (zero before and after) are scratch.  ntiles <= kSplitMaxTiles.
+constexpr int kSplitMaxTiles = 256;
+hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int xrows, uint16_t* h, int ldh,
+                                  float* part, unsigned* flag, hipStream_t st);
+
 // Grouped expert GEMMs over the bucketed pairs (persistent, work list from route).
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
                              uint16_t* act, hipStream_t st);
