@@ -112,6 +112,8 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
                     kbase, lane);
   const DqConst dk;
   int buf = 0;
+  uint16_t hpre = 0;  // see the single-tile case below
+  bool pre = false;
   auto run = [&](const Stage<NCH, G>& st, int t, bool valid) {
     float sv[NS];
     st.scales_f32(sv);
@@ -132,7 +134,8 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
           reinterpret_cast<uint16_t*>(a.y)[(size_t)row * a.ldy + n] = f2h(v);
         } else {
           uint16_t* h = reinterpret_cast<uint16_t*>(a.y) + (size_t)row * a.ldy + n;
-          *h = f2h(h2f(*h) + h2f(f2h(v)));
+          const uint16_t hold = pre ? hpre : *h;
+          *h = f2h(h2f(hold) + h2f(f2h(v)));
         }
       }
     });
@@ -145,6 +148,16 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   Stage<NCH, G> sa, sb;
   sa.load(a.tiles, a.scales, a.K, blockIdx.x, w, lane);
   if (n == 1) {
+    // Residual epilogue of a single tile with one output per thread: the
+    // thread's h value is requested now, with the operands, instead of after
+    // the reduction (the thread that reads an element is its only writer).
+    if (EPI == EPI_RESID && (int)blockDim.x >= MT * 256) {
+      const int o = threadIdx.x;
+      const int row = (o >> 8) * 16 + ((o >> 4) & 15), col = (int)blockIdx.x * 16 + (o & 15);
+      if (o < MT * 256 && row < a.B && col < a.N)
+        hpre = reinterpret_cast<const uint16_t*>(a.y)[(size_t)row * a.ldy + col];
+      pre = true;
+    }
     run(sa, blockIdx.x, true);
     return;
   }
