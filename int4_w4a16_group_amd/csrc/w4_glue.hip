@@ -506,7 +506,30 @@ struct RouterArgs {
   const uint8_t* pf;       // work-groups B*NT .. B*NT+npf-1 touch this span (touch_lines)
   size_t pf_lines;
   int npf;
+  // and the live KV chunks of layer kvl for the rows (slot, pos as in the
+  // attention), when kv.K is not null
+  KV kv;
+  int kvl;
+  const int32_t* slot;
+  const int32_t* pos;
 };
+
+// Spare work-group j of the router launch: the live 64-position chunks of
+// every (row, kv head) of layer a.kvl, K and V, npf / (2 B Hkv) work-groups
+// per span, one 4-byte load per 128-byte line.
+__device__ __forceinline__ void touch_kv(const RouterArgs& a, int j) {
+  const int ns = 2 * a.B * a.kv.Hkv, wps = a.npf / ns;
+  if (j >= ns * wps) return;
+  const int s = j / wps, q = j - s * wps;
+  const int bg = s >> 1, b = bg / a.kv.Hkv, g = bg - b * a.kv.Hkv;
+  const size_t base = (((size_t)a.kvl * a.kv.S + a.slot[b]) * a.kv.Hkv + g) * (size_t)a.kv.cap * a.kv.D;
+  const uint8_t* span = reinterpret_cast<const uint8_t*>(((s & 1) ? a.kv.VT : a.kv.K) + base);
+  const size_t lines = (size_t)(a.pos[b] / 64 + 1) * 64 * a.kv.D * 2 / 128;
+  for (size_t li = (size_t)q * blockDim.x + threadIdx.x; li < lines; li += (size_t)wps * blockDim.x) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(span + (li << 7));
+    asm volatile("" ::"v"(v));
+  }
+}
 
 template <int G>
 __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
@@ -532,6 +555,7 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   if ((int)blockIdx.x >= a.B * NT) {
     touch_lines(a.pf, a.pf_lines, blockIdx.x - a.B * NT, a.npf);
+    if (a.kv.K) touch_kv(a, blockIdx.x - a.B * NT);
     return;
   }
   const int b = blockIdx.x / NT, t = blockIdx.x - b * NT;
@@ -718,11 +742,18 @@ int touch_groups(size_t bytes, int threads) {
 hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
                          uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
                          unsigned* ticket, float* lg, unsigned* rticket, hipStream_t st, const void* pf,
-                         size_t pf_bytes) {
+                         size_t pf_bytes, const KV* kv_next, int kv_layer, const int32_t* slot, const int32_t* pos) {
   if (H % 128 != 0 || H / 128 > kRouterMaxChunks || E > kRouteMaxE || !lg || !rticket) return hipErrorInvalidValue;
   const int npf = pf ? touch_groups(pf_bytes, 1024) : 0;
-  const RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket, lg, rticket,
-                     static_cast<const uint8_t*>(pf), pf_bytes / 128, npf};
+  RouterArgs a{h, gamma, eps, xn, tiles, scales, H, E, k, B, o, ticket, lg, rticket,
+               static_cast<const uint8_t*>(pf), pf_bytes / 128, npf};
+  a.kv = KV{};
+  if (kv_next && npf > 0 && slot && pos) {
+    a.kv = *kv_next;
+    a.kvl = kv_layer;
+    a.slot = slot;
+    a.pos = pos;
+  }
   const dim3 grid(B * ((E + 15) / 16) + npf);
   switch (g) {
     case 32: w4_launch(k_router<32>, grid, dim3(1024), 0, st, a); break;

@@ -386,7 +386,11 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
   // q/k/v, o and router weights (contiguous in the bank), so that those
   // latency-bound launches find them in the memory-side cache.  Measured on
   // the 48-layer model: q/k/v and o 0.5 us faster each at B <= 8; at B = 32
-  // the expert and KV traffic in between evicts the span again.
+  // the expert and KV traffic in between evicts the span again.  With one
+  // row they also touch that row's live KV chunks of the next layer: its
+  // attention 11.2 -> 10.4 us, +2% tok/s; with 2..8 rows the larger touch
+  // lengthened the router launch by about as much as the attention gained
+  // (B = 2: -0.8%, 3: +1.3%, 4: -0.4%, 8: -1.7%).
   const uint8_t* next_span = nullptr;
   size_t next_bytes = 0;
   if (l + 1 < d.n_layers && B <= 8) {
@@ -416,7 +420,8 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
     const Mat Rm = c->mat(L.router);
     LCHK(c, 1, launch_router(B, H, d.n_experts, d.top_k, d.group, h, c->Bk<uint16_t>(L.moe_norm), d.rms_eps, xn,
                              Rm.tiles, Rm.scales, r, c->W<unsigned>(c->wp.ticket), c->W<float>(c->wp.rlg),
-                             c->W<unsigned>(c->wp.rticket), st, next_span, next_bytes));
+                             c->W<unsigned>(c->wp.rticket), st, next_span, next_bytes,
+                             next_span && B == 1 ? &kv : nullptr, l + 1, slot, pos));
   }
   {
     ProfScope ps(c, W4_K_MOE_GATEUP, st);

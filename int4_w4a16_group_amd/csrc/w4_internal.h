@@ -79,7 +79,8 @@ hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut
 hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
                          uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
                          unsigned* ticket, float* lg, unsigned* rticket, hipStream_t st, const void* pf = nullptr,
-                         size_t pf_bytes = 0);
+                         size_t pf_bytes = 0, const struct KV* kv_next = nullptr, int kv_layer = 0,
+                         const int32_t* slot = nullptr, const int32_t* pos = nullptr);
 // Spare work-groups for touching a span of that many bytes with threads-wide
 // work-groups: about one per compute unit, each touching at most one line
 // per thread.
