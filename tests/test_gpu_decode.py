@@ -118,6 +118,45 @@ def test_layer_router_geometries(gpu, name):
         ctx.close()
 
 
+# The output projection at K = 4096 above 16 rows runs as two work-groups per
+# tile (the second continues the first's in-order sum); 32 query heads x 128
+# give K = 4096, B = 20 rows a 32-row tile, and g = 32 / 64 the scale groups
+# the full model does not use.
+@pytest.mark.parametrize("g", [32, 64])
+def test_layer_split_output_projection(gpu, g):
+    d = dataclasses.replace(inputs.TINY, hidden=512, n_q_heads=32, n_kv_heads=4, head_dim=128, n_experts=8,
+                            top_k=2, moe_inter=128, group=g)
+    B, n_slots, cap = 20, 24, 128
+    positions = [(7 * b + 3) % 120 for b in range(B)]
+    mw = inputs.make_model(d, 5, with_vocab=False)
+    ctx = Context(d, n_slots, cap)
+    om = oracle.Model(mw)
+    oa = oracle.Arena(d, n_slots, cap)
+    try:
+        ctx.load_model(mw)
+        slots = []
+        for b, p in enumerate(positions):
+            k, v = inputs.prefix_kv(5, b, d.n_layers, p, d.n_kv_heads, d.head_dim)
+            s = ctx.join(p, 4, k, v)
+            if p:
+                oa.seed(s, k, v)
+            slots.append(s)
+        h = inputs.normal_f16(inputs.rng(5, inputs.T_X, g), (B, d.hidden))
+        hd = to_dev(h, gpu)
+        ids = torch.empty((B, d.top_k), dtype=torch.int32, device=gpu)
+        L.w4_layer_step(ctx.ctx, 0, slots, hd, ids, ctx.stream)
+        rh, rids, rlg = oracle.layer_step(om, oa, 0, slots, positions, h)
+        gh, gids = to_host(hd), to_host(ids)
+        for b in range(B):
+            if set(gids[b]) != set(rids[b]):
+                assert near_tie(rlg[b], d.top_k), f"g={g}: routing differs at row {b}"
+                pytest.skip("routing near-tie")
+        assert np.array_equal(gids, rids)
+        assert_normwise(f16v(gh), f16v(rh), TOL, f"g={g}")
+    finally:
+        ctx.close()
+
+
 # ------------------------------------------------------------------ whole step
 SMALL = dataclasses.replace(inputs.TINY, n_layers=3, vocab=500, top_k=2)
 
