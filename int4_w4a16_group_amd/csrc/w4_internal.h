@@ -70,17 +70,6 @@ struct RouteOut {
 // Routing in one work-group: top-k softmax of fp32 logits [B][E], bucketing and 16-row units.  B <= 32.
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st);
 
-// MoE front end of a decode layer in one launch (one work-group per row and
-// 16-expert tile, B <= 32): xn = RMSNorm(h) * gamma, the router product, top-k
-// softmax and the bucketing.  lg [B][E]: the logits exchanged between a row's
-// work-groups; rticket [B] and ticket: counters, zero before and after.
-// pf, pf_bytes: a span of the bank touched by spare work-groups of the launch
-// (touch_lines below); null for none.
-hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
-                         uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
-                         unsigned* ticket, float* lg, unsigned* rticket, hipStream_t st, const void* pf = nullptr,
-                         size_t pf_bytes = 0, const struct KV* kv_next = nullptr, int kv_layer = 0,
-                         const int32_t* slot = nullptr, const int32_t* pos = nullptr);
 // Spare work-groups for touching a span of that many bytes with threads-wide
 // work-groups: about one per compute unit, each touching at most one line
 // per thread.
@@ -120,6 +109,18 @@ struct KV {
   uint16_t* VT;  // [L][S][Hkv][cap/64][64*D], MFMA operand order (w4_attn.hip)
   int S, Hkv, cap, D;
 };
+// MoE front end of a decode layer in one launch (one work-group per row and
+// 16-expert tile, B <= 32): xn = RMSNorm(h) * gamma, the router product, top-k
+// softmax and the bucketing.  lg [B][E]: the logits exchanged between a row's
+// work-groups; rticket [B] and ticket: counters, zero before and after.
+// pf, pf_bytes: a span of the bank touched by spare work-groups of the launch
+// (touch_lines below); null for none.  kv_next (with slot, pos as in the
+// attention): that KV's live chunks of layer kv_layer are touched too.
+hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, const uint16_t* gamma, float eps,
+                         uint16_t* xn, const uint4* tiles, const uint16_t* scales, const RouteOut& o,
+                         unsigned* ticket, float* lg, unsigned* rticket, hipStream_t st, const void* pf = nullptr,
+                         size_t pf_bytes = 0, const KV* kv_next = nullptr, int kv_layer = 0,
+                         const int32_t* slot = nullptr, const int32_t* pos = nullptr);
 hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStream_t st);
 hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, const uint16_t* v,
                        hipStream_t st);
