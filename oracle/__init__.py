@@ -60,13 +60,15 @@ def lib():
         L.orc_rope.argtypes = [C.c_int, C.c_int, C.c_int, C.c_double, _u16p, _u16p]
         L.orc_attention.argtypes = [C.c_int] * 4 + [_u16p, C.c_void_p, C.c_void_p, C.c_int64, _u16p]
         L.orc_topk_softmax.argtypes = [C.c_int, C.c_int, _f32p, _i32p, _f32p]
+        L.orc_route_weights.argtypes = [C.c_int, _f32p, _i32p, _f32p]
         L.orc_bucket.argtypes = [C.c_int] * 3 + [_i32p] * 5
-        L.orc_moe.argtypes = [C.POINTER(_Model), C.c_int, C.c_int, _u16p, _f32p, _u16p, C.c_void_p, C.c_void_p]
+        L.orc_moe.argtypes = [C.POINTER(_Model), C.c_int, C.c_int, _u16p, _f32p, C.c_void_p, _u16p, C.c_void_p,
+                              C.c_void_p]
         L.orc_layer_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
-                                     _u16p, C.c_void_p, C.c_void_p]
+                                     _u16p, C.c_void_p, C.c_void_p, C.c_void_p]
         L.orc_embed.argtypes = [C.POINTER(_Model), C.c_int, _i32p, _u16p]
         L.orc_decode_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, _i32p, _i32p, _i32p,
-                                      C.c_void_p, _i32p, C.c_void_p, C.c_void_p]
+                                      C.c_void_p, C.c_void_p, _i32p, C.c_void_p, C.c_void_p]
         L.orc_attn_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
                                     _u16p, _u16p, _u16p, _u16p]
         L.orc_threads.restype = C.c_int
@@ -163,6 +165,45 @@ def topk_softmax(logits: np.ndarray, k: int):
     return ids, w
 
 
+def route_weights(logits: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Softmax weights of ranked selections: logits f32 [B,E], ids int32 [B,k] -> w f32 [B,k]."""
+    logits = _c(logits, np.float32)
+    ids = _c(ids, np.int32)
+    B, k = ids.shape
+    w = np.empty((B, k), np.float32)
+    for b in range(B):
+        lib().orc_route_weights(k, logits[b], ids[b], w[b])
+    return w
+
+
+def route_ok(ids, logits, tol) -> bool:
+    """Whether ranked expert ids are a top-k of the logits up to the tolerance
+    (the acceptance rule for a routing decision taken elsewhere before the
+    oracle replays it): k distinct experts; every selected logit >= every
+    unselected one - t, and each rank's logit >= the next rank's - t, with
+    t = tol * max|logits|.  Where all gaps around the top k exceed t, only the
+    exact top-k in rank order passes."""
+    ids = [int(i) for i in np.asarray(ids).ravel()]
+    lg = np.asarray(logits, dtype=np.float64)
+    if len(set(ids)) != len(ids) or min(ids) < 0 or max(ids) >= len(lg):
+        return False
+    t = tol * np.max(np.abs(lg))
+    sel = lg[ids]
+    rest = np.delete(lg, ids)
+    if rest.size and sel.min() < rest.max() - t:
+        return False
+    return bool(np.all(sel[:-1] >= sel[1:] - t))
+
+
+def _force(force, shape):
+    """Forced ranked expert ids (int32, C order) or None."""
+    if force is None:
+        return None
+    f = _c(force, np.int32)
+    assert f.shape == shape, (f.shape, shape)
+    return f
+
+
 def bucket(ids: np.ndarray, E: int):
     ids = _c(ids, np.int32)
     B, k = ids.shape
@@ -234,15 +275,18 @@ class Arena:
         self.v[:, slot, :p] = v
 
 
-def moe(model: Model, layer: int, x: np.ndarray, logits: np.ndarray):
+def moe(model: Model, layer: int, x: np.ndarray, logits: np.ndarray, force=None):
+    """force: ranked expert ids [B, top_k] replacing the top-k of the logits (a replayed
+    routing decision), or None."""
     x = _c(x, np.uint16)
     logits = _c(logits, np.float32)
     B = x.shape[0]
     d = model.desc
+    f = _force(force, (B, d.top_k))
     y = np.empty_like(x)
     ids = np.empty((B, d.top_k), np.int32)
     w = np.empty((B, d.top_k), np.float32)
-    lib().orc_moe(C.byref(model.m), layer, B, x, logits, y, ids.ctypes.data, w.ctypes.data)
+    lib().orc_moe(C.byref(model.m), layer, B, x, logits, _ptr(f), y, ids.ctypes.data, w.ctypes.data)
     return y, ids, w
 
 
@@ -254,30 +298,35 @@ def embed(model: Model, tokens) -> np.ndarray:
     return h
 
 
-def layer_step(model: Model, arena: Arena, layer: int, slots, positions, h: np.ndarray):
+def layer_step(model: Model, arena: Arena, layer: int, slots, positions, h: np.ndarray, force=None):
+    """force: ranked expert ids [B, top_k] replacing the router's top-k, or None."""
     h = _c(h, np.uint16).copy()
     slots = _c(slots, np.int32)
     positions = _c(positions, np.int32)
     d = model.desc
     B = h.shape[0]
+    f = _force(force, (B, d.top_k))
     ids = np.empty((B, d.top_k), np.int32)
     lg = np.empty((B, d.n_experts), np.float32)
-    lib().orc_layer_step(C.byref(model.m), C.byref(arena.a), layer, B, slots, positions, h,
+    lib().orc_layer_step(C.byref(model.m), C.byref(arena.a), layer, B, slots, positions, h, _ptr(f),
                          ids.ctypes.data, lg.ctypes.data)
     return h, ids, lg
 
 
-def decode_step(model: Model, arena: Arena, slots, positions, tokens, want_logits=True, want_router=False):
+def decode_step(model: Model, arena: Arena, slots, positions, tokens, want_logits=True, want_router=False,
+                force=None):
+    """force: ranked expert ids [n_layers, B, top_k] replacing every layer's top-k, or None."""
     slots = _c(slots, np.int32)
     positions = _c(positions, np.int32)
     tokens = _c(tokens, np.int32)
     d = model.desc
     B = len(slots)
+    f = _force(force, (d.n_layers, B, d.top_k))
     logits = np.empty((B, d.vocab), np.uint16) if want_logits else None
     nxt = np.empty(B, np.int32)
     ids = np.empty((d.n_layers, B, d.top_k), np.int32)
     rl = np.empty((d.n_layers, B, d.n_experts), np.float32) if want_router else None
-    lib().orc_decode_step(C.byref(model.m), C.byref(arena.a), B, slots, positions, tokens,
+    lib().orc_decode_step(C.byref(model.m), C.byref(arena.a), B, slots, positions, tokens, _ptr(f),
                           _ptr(logits), nxt, ids.ctypes.data, _ptr(rl))
     return logits, nxt, ids, rl
 

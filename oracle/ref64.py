@@ -84,6 +84,13 @@ def topk_softmax(logits: np.ndarray, k: int):
     return ids, w / w.sum()
 
 
+def forced_weights(logits: np.ndarray, ids) -> np.ndarray:
+    """Softmax over the logits of a given ranked selection (a replayed routing decision)."""
+    sel = np.asarray(logits, dtype=np.float64)[np.asarray(ids)]
+    w = np.exp(sel - sel.max())
+    return w / w.sum()
+
+
 def expert_mlp(x: np.ndarray, gate, up, down, group) -> np.ndarray:
     """One SwiGLU expert on a float64 row x (already fp16-valued)."""
     g = f16(gemm(x[None], gate.packed, gate.scales, group)[0])
@@ -108,9 +115,10 @@ def moe(x: np.ndarray, ids, w, lw, group) -> np.ndarray:
     return f16(acc)
 
 
-def layer(desc, lw, kcache, vcache, pos: int, h: np.ndarray):
+def layer(desc, lw, kcache, vcache, pos: int, h: np.ndarray, force_ids=None):
     """One decoder layer for one stream.  kcache / vcache: float64 [cap, Hkv, D]
-    holding positions 0..pos-1 (updated in place at pos).  h float64 [H]."""
+    holding positions 0..pos-1 (updated in place at pos).  h float64 [H].
+    force_ids: ranked expert ids used instead of the router's top-k, or None."""
     d = desc
     nq, nkv = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
     xn = rmsnorm(h, from_bits(lw.attn_norm), d.rms_eps)
@@ -123,18 +131,23 @@ def layer(desc, lw, kcache, vcache, pos: int, h: np.ndarray):
     h = f16(h + f16(gemm(att[None], lw.o.packed, lw.o.scales, d.group)[0]))
     xn2 = rmsnorm(h, from_bits(lw.moe_norm), d.rms_eps)
     logits = gemm(xn2[None], lw.router.packed, lw.router.scales, d.group)[0]
-    ids, w = topk_softmax(logits, d.top_k)
+    if force_ids is None:
+        ids, w = topk_softmax(logits, d.top_k)
+    else:
+        ids = np.asarray(force_ids)
+        w = forced_weights(logits, ids)
     h = f16(h + moe(xn2, ids, w, lw, d.group))
     return h, ids, logits
 
 
-def decode(desc, mw, kcaches, vcaches, pos: int, token: int):
-    """Whole decode step for one stream; caches: per-layer float64 [cap, Hkv, D]."""
+def decode(desc, mw, kcaches, vcaches, pos: int, token: int, force_ids=None):
+    """Whole decode step for one stream; caches: per-layer float64 [cap, Hkv, D].
+    force_ids: per layer ranked expert ids replacing the top-k, or None."""
     d = desc
     emb = dequant(mw.embed.packed[token], mw.embed.scales[token], d.group)
     h = f16(emb)
     for l, lw in enumerate(mw.layers):
-        h, _, _ = layer(d, lw, kcaches[l], vcaches[l], pos, h)
+        h, _, _ = layer(d, lw, kcaches[l], vcaches[l], pos, h, None if force_ids is None else force_ids[l])
     hn = rmsnorm(h, from_bits(mw.final_norm), d.rms_eps)
     logits = f16(gemm(hn[None], mw.lm_head.packed, mw.lm_head.scales, d.group)[0])
     return logits, int(np.argmax(logits))

@@ -5,11 +5,12 @@
  * and this file shares no code, header or table with it.
  *
  * What it computes is the plain per-stream transformer decode step with
- * dequantised weights.  The pages ("Batched-concurrent 4-bit serving on
- * Apple Silicon", section 3) state that the batched GEMM row math is
- * row-independent and per-stream glue runs at per-stream offsets, so a batch
- * of B streams has exactly the result of B separate single-stream steps; the
- * oracle therefore loops over streams one at a time and never batches.
+ * dequantised weights.  In the batched design ("Batched-concurrent 4-bit
+ * serving on Apple Silicon", section 3) no row of a batched product depends
+ * on another row, and the per-stream steps each work on their own stream's
+ * data, so a batch of B streams gives exactly what B separate single-stream
+ * steps give; the oracle therefore takes the streams one at a time and never
+ * batches.
  *
  * Precision (workload definition): int4 group dequant w = q * s, exact in
  * fp32; every dot product accumulates in fp32, sequentially over k; values are
@@ -218,6 +219,18 @@ EXPORT void orc_attention(int Hq, int Hkv, int D, int npos, const uint16_t* q, c
 /* r = 0..k-1) and weighted by the softmax over the k selected logits:       */
 /*   w_r = exp(l_r - l_0) / sum_r' exp(l_r' - l_0).                          */
 /* ------------------------------------------------------------------------ */
+/* Weights of a ranked selection ids[0..k-1]: the softmax over the selected
+ * logits, w_r = exp(l_{ids r} - l_{ids 0}) / sum_r' exp(l_{ids r'} - l_{ids 0}),
+ * summed in rank order. */
+EXPORT void orc_route_weights(int k, const float* logits, const int32_t* ids, float* w) {
+  float sum = 0.0f;
+  for (int r = 0; r < k; r++) {
+    w[r] = expf(logits[ids[r]] - logits[ids[0]]);
+    sum = sum + w[r];
+  }
+  for (int r = 0; r < k; r++) w[r] = w[r] / sum;
+}
+
 EXPORT void orc_topk_softmax(int E, int k, const float* logits, int32_t* ids, float* w) {
   unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
   for (int r = 0; r < k; r++) {
@@ -229,13 +242,23 @@ EXPORT void orc_topk_softmax(int E, int k, const float* logits, int32_t* ids, fl
     taken[best] = 1;
     ids[r] = best;
   }
-  float sum = 0.0f;
-  for (int r = 0; r < k; r++) {
-    w[r] = expf(logits[ids[r]] - logits[ids[0]]);
-    sum = sum + w[r];
-  }
-  for (int r = 0; r < k; r++) w[r] = w[r] / sum;
+  orc_route_weights(k, logits, ids, w);
   free(taken);
+}
+
+/* Routing of one stream: the top-k of its logits, or, when force is not
+ * NULL, the ranked expert ids given there (weighted by the softmax over those
+ * experts' logits, as above).  The forced form replays a routing decision
+ * taken elsewhere at a near-tie of the k-th and (k+1)-th logits, where either
+ * choice is a correct top-k within the tolerance; with force equal to this
+ * function's own top-k it changes nothing. */
+static void route_one(int E, int k, const float* logits, const int32_t* force, int32_t* ids, float* w) {
+  if (force) {
+    memcpy(ids, force, sizeof(int32_t) * (size_t)k);
+    orc_route_weights(k, logits, ids, w);
+  } else {
+    orc_topk_softmax(E, k, logits, ids, w);
+  }
 }
 
 /* (stream, expert) bucketing: the B*k (stream, rank) pairs ordered by expert,
@@ -333,15 +356,16 @@ static void moe_one(const orc_model* m, int l, const uint16_t* xn, const int32_t
 
 /* MoE block for B streams given router logits (config of the grouped-expert
  * layer): per stream, top-k softmax then the SwiGLU experts; no residual.
- * x fp16 [B][H] (the post-norm input), logits f32 [B][E] -> y fp16 [B][H].   */
+ * x fp16 [B][H] (the post-norm input), logits f32 [B][E] -> y fp16 [B][H].
+ * force [B][k]: ranked expert ids to use instead of the top-k, or NULL.      */
 EXPORT void orc_moe(const orc_model* m, int l, int B, const uint16_t* x, const float* logits,
-                    uint16_t* y, int32_t* ids_out, float* w_out) {
+                    const int32_t* force, uint16_t* y, int32_t* ids_out, float* w_out) {
   h2f_init();
   int k = m->top_k, E = m->n_experts, H = m->hidden;
   for (int b = 0; b < B; b++) {
     int32_t ids[256];
     float w[256];
-    orc_topk_softmax(E, k, logits + (size_t)b * E, ids, w);
+    route_one(E, k, logits + (size_t)b * E, force ? force + (size_t)b * k : NULL, ids, w);
     if (ids_out) memcpy(ids_out + (size_t)b * k, ids, sizeof(int32_t) * k);
     if (w_out) memcpy(w_out + (size_t)b * k, w, sizeof(float) * k);
     moe_one(m, l, x + (size_t)b * H, ids, w, y + (size_t)b * H);
@@ -362,9 +386,10 @@ static size_t arena_off(const orc_model* m, const orc_arena* a, int l, int slot,
 
 /* One decoder layer for one stream at position p (p keys already cached in
  * its slot; the new key is written at p, attention covers 0..p).
- * h: fp16 [H] residual stream, updated in place. */
+ * h: fp16 [H] residual stream, updated in place.  force: ranked expert ids
+ * [k] replacing the top-k (see route_one), or NULL. */
 static void layer_one(const orc_model* m, orc_arena* a, int l, int slot, int p, uint16_t* h,
-                      int32_t* ids_out, float* logits_out) {
+                      const int32_t* force, int32_t* ids_out, float* logits_out) {
   int H = m->hidden, Hq = m->n_q, Hkv = m->n_kv, D = m->head_dim, g = m->group;
   int nq = Hq * D, nkv = Hkv * D, nqkv = nq + 2 * nkv, E = m->n_experts, k = m->top_k;
   uint16_t* xn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
@@ -389,7 +414,7 @@ static void layer_one(const orc_model* m, orc_arena* a, int l, int slot, int p, 
   orc_w4_gemm(1, E, H, g, xn, m->r_p[l], m->r_s[l], NULL, lg);   /* router logits stay fp32 */
   int32_t ids[256];
   float w[256];
-  orc_topk_softmax(E, k, lg, ids, w);
+  route_one(E, k, lg, force, ids, w);
   if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * k);
   if (logits_out) memcpy(logits_out, lg, sizeof(float) * E);
   moe_one(m, l, xn, ids, w, proj);
@@ -402,13 +427,15 @@ static void layer_one(const orc_model* m, orc_arena* a, int l, int slot, int p, 
 }
 
 /* One layer for B streams (slots[b], positions[b]); h fp16 [B][H] in/out.
- * ids_out [B][k] and logits_out [B][E] (router) optional. */
+ * force [B][k] ranked expert ids replacing the top-k, or NULL; ids_out [B][k]
+ * and logits_out [B][E] (router) optional. */
 EXPORT void orc_layer_step(const orc_model* m, orc_arena* a, int l, int B, const int32_t* slots,
-                           const int32_t* positions, uint16_t* h, int32_t* ids_out, float* logits_out) {
+                           const int32_t* positions, uint16_t* h, const int32_t* force, int32_t* ids_out,
+                           float* logits_out) {
   h2f_init();
   for (int b = 0; b < B; b++)
     layer_one(m, a, l, slots[b], positions[b], h + (size_t)b * m->hidden,
-              ids_out ? ids_out + (size_t)b * m->top_k : NULL,
+              force ? force + (size_t)b * m->top_k : NULL, ids_out ? ids_out + (size_t)b * m->top_k : NULL,
               logits_out ? logits_out + (size_t)b * m->n_experts : NULL);
 }
 
@@ -429,10 +456,11 @@ EXPORT void orc_embed(const orc_model* m, int B, const int32_t* tokens, uint16_t
 /* Whole decode step for B streams: embedding row of the token (dequantised
  * =>h), every layer, final RMSNorm, output projection =>h, greedy argmax
  * (ties to the lower id).  Greedy decoding per the batched-serving page,
- * section 3.  logits fp16 [B][V] (optional), next [B], ids_out [L][B][k]. */
+ * section 3.  logits fp16 [B][V] (optional), next [B], ids_out [L][B][k];
+ * force [L][B][k]: ranked expert ids replacing every layer's top-k, or NULL. */
 EXPORT void orc_decode_step(const orc_model* m, orc_arena* a, int B, const int32_t* slots,
-                            const int32_t* positions, const int32_t* tokens, uint16_t* logits,
-                            int32_t* next, int32_t* ids_out, float* router_out) {
+                            const int32_t* positions, const int32_t* tokens, const int32_t* force,
+                            uint16_t* logits, int32_t* next, int32_t* ids_out, float* router_out) {
   h2f_init();
   int H = m->hidden, V = m->vocab, g = m->group, k = m->top_k, E = m->n_experts;
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
@@ -441,7 +469,7 @@ EXPORT void orc_decode_step(const orc_model* m, orc_arena* a, int B, const int32
   for (int b = 0; b < B; b++) {
     embed_row(m, tokens[b], h);
     for (int l = 0; l < m->n_layers; l++)
-      layer_one(m, a, l, slots[b], positions[b], h,
+      layer_one(m, a, l, slots[b], positions[b], h, force ? force + ((size_t)l * B + b) * k : NULL,
                 ids_out ? ids_out + ((size_t)l * B + b) * k : NULL,
                 router_out ? router_out + ((size_t)l * B + b) * E : NULL);
     orc_rmsnorm(H, h, m->final_norm, m->rms_eps, hn);
@@ -459,7 +487,10 @@ EXPORT void orc_decode_step(const orc_model* m, orc_arena* a, int B, const int32
 
 /* Attention-only step (slot-indexed GQA decode with a KV append), B streams:
  * q [B][Hq][D], k_new/v_new [B][Hkv][D] are written at positions[b] of
- * slots[b] in layer l, then attention over 0..positions[b] -> o [B][Hq][D]. */
+ * slots[b] in layer l, then attention over 0..positions[b] (positions[b] + 1
+ * keys) -> o [B][Hq][D].  The slot is the stream's stable KV home ("Per-stream
+ * KV-slot isolation for parallel low-bit decode on Apple Silicon", section 1):
+ * nothing outside (layer l, slots[b], positions[b]) is written. */
 EXPORT void orc_attn_step(const orc_model* m, orc_arena* a, int l, int B, const int32_t* slots,
                           const int32_t* positions, const uint16_t* q, const uint16_t* k_new,
                           const uint16_t* v_new, uint16_t* o) {

@@ -14,7 +14,7 @@ from int4_w4a16_group_amd import _lib as L
 from int4_w4a16_group_amd import inputs
 from int4_w4a16_group_amd.engine import Context
 from tests.gpu_util import empty_f16, to_dev, to_host
-from tests.util import assert_normwise, f16v
+from tests.util import assert_normwise, f16v, route_ok
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
@@ -93,13 +93,12 @@ def test_moe_router_computed_on_device(moe_ctx, gpu):
     ctx, om = moe_ctx
     x = inputs.normal_f16(inputs.rng(4, 4), (6, MOE.hidden))
     y, ids = gpu_moe(ctx, x, None, gpu)
-    lw_r = om  # oracle router logits from the same weights
     mw_layer = inputs.make_layer(MOE, 0, 0)
     rl = oracle.w4_gemm(x, mw_layer.router.packed, mw_layer.router.scales, MOE.group, out="f32")
-    ry, rids, _ = oracle.moe(lw_r, 0, x, rl)
+    # the oracle replays the GPU's routing once it is accepted as a top-k of the
+    # oracle's logits (exactly the top-k unless the k-th and (k+1)-th are within
+    # the tolerance), so every row is compared
+    ry, rids, _ = oracle.moe(om, 0, x, rl, force=ids)
     for b in range(6):
-        s = np.sort(rl[b])[::-1]
-        if set(ids[b]) != set(rids[b]):
-            assert s[7] - s[8] <= TOL * np.abs(rl[b]).max(), "routing differs without a near-tie"
-            continue
+        assert route_ok(ids[b], rl[b], TOL), f"row {b}: routing differs beyond a near-tie"
         assert_normwise(f16v(y[b]), f16v(ry[b]), TOL, f"router-on-device row {b}")
