@@ -74,6 +74,12 @@ def main():
     ap.add_argument("--profile", choices=("on", "off"), default="on", help="HIP-event kernel timing passes")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 512 MiB device-to-device copy first (a known-size reference for HBM counters)")
+    ap.add_argument("--read-ceiling", choices=("on", "off"), default="on",
+                    help="measure the HBM streaming-read ceiling with the library's read probe (4 GiB, 16-byte loads)")
+    ap.add_argument("--ragged", choices=("on", "off"), default="on",
+                    help="continuous-batching leg: 256 steps, arrivals p=0.5, prompts U{1..2048}, lives U{16..512}")
+    ap.add_argument("--cpu-single-steps", type=int, default=2,
+                    help="decode steps of one stream in the oracle's single-thread sample")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
@@ -97,6 +103,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         log("calibration copy: 512 MiB read + 512 MiB written")
+    ceiling = read_ceiling(dev, L) if args.read_ceiling == "on" else None
     d = inputs.FULL
     batches = [int(b) for b in args.batches.split(",")]
     Bmax, cap = 32, 4096
@@ -141,16 +148,21 @@ def main():
             tok, nxt = nxt, tok
         routes = torch.empty((args.steps, d.n_layers, B, d.top_k), dtype=torch.int32, device=dev)
         pos0 = np.array([ctx.position(s) for s in sl])
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         enq = []
         for i in range(args.steps):
+            evs[i].record(ctx.stream)
             t1 = time.perf_counter()
             L.w4_decode_step(ctx.ctx, sl, tok, None, nxt, routes[i], ctx.stream)
             enq.append(time.perf_counter() - t1)
             tok, nxt = nxt, tok
+        evs[-1].record(ctx.stream)
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
+        # per-step times between events recorded on the step's stream (back-to-back steps)
+        step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
         launches, syncs = L.w4_last_step_counts(ctx.ctx)
         r = routes.cpu().numpy()
         U = np.array([[len(np.unique(r[i, l])) for l in range(d.n_layers)] for i in range(args.steps)])
@@ -159,7 +171,9 @@ def main():
         # host time of one w4_decode_step call while the pinned ring still has
         # room (the first calls; later ones also wait for the GPU)
         host_ms = float(np.median(enq[:min(len(enq), 6)])) * 1e3
-        entry = dict(tok_s=B * args.steps / dt, ms_per_step=ms, host_enqueue_ms_per_step=host_ms,
+        entry = dict(tok_s=B * args.steps / dt, ms_per_step=ms,
+                     step_ms_median=float(np.median(step_ms)), step_ms_min=float(step_ms.min()),
+                     step_ms_max=float(step_ms.max()), host_enqueue_ms_per_step=host_ms,
                      launches_per_step=launches, syncs_per_step=syncs,
                      unique_experts_per_layer=float(U.mean()),
                      algorithmic_GB_per_step=byt["total"] / 1e9,
@@ -192,6 +206,12 @@ def main():
         log(f"B={B}: {entry['tok_s']:.0f} tok/s, {ms:.3f} ms/step, U={entry['unique_experts_per_layer']:.1f}"
             + (f", weight stream {entry['weight_stream_GBps']:.0f} GB/s" if "weight_stream_GBps" in entry else ""))
 
+    ragged = None
+    if args.ragged == "on":
+        for s in slots:
+            ctx.release(s)
+        ragged = ragged_leg(args, d, ctx, dev, L)
+
     Bh = max(batches)
     head = sweep[Bh]
     roof = None
@@ -222,11 +242,119 @@ def main():
         "weight_stream_GBps": head.get("weight_stream_GBps"),
         "weight_stream_frac": head.get("weight_stream_frac"),
         "roofline": roof,
+        "hbm_read_ceiling": ceiling,
+        "ragged": ragged,
         "cpu_baseline": cpu,
         "parity_first_step": parity,
     }
     ctx.close()
     print(json.dumps(out), flush=True)
+
+
+def read_ceiling(dev, L):
+    """HBM streaming-read ceiling: the library's read probe (16-byte loads, one
+    pass) over 4 GiB, far beyond the 256 MB memory-side cache, at a few grid
+    sizes; the best of three passes each, timed with events on the stream."""
+    import torch
+    nbytes = 4 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    res = {}
+    st = torch.cuda.current_stream(dev)
+    for per_cu in (4, 8, 16):
+        grid = 256 * per_cu
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+        best = None
+        for _ in range(4):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            L.w4_read_probe(src, nbytes, sink, grid, st)
+            b.record(st)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        res[str(grid)] = nbytes / (best * 1e-3) / 1e9
+    del src
+    top = max(res.values())
+    log(f"HBM read ceiling (probe): {top:.0f} GB/s ({res})")
+    return dict(GBps=top, frac_of_peak=top / PEAK_HBM_GBPS, bytes=nbytes, by_grid=res,
+                kernel="w4_read_probe: one pass of 16-byte loads, 256-thread work-groups")
+
+
+def ragged_leg(args, d, ctx, dev, L):
+    """Continuous batching on the full model: the schedule of the full-size
+    ragged test (32 slots x 4096; a request arrives with probability 0.5 per
+    step, FIFO; prompts ~ U{1..2048} with seeded K/V; lives ~ U{16..512};
+    finished slots released and reused), 256 steps.  Every admitted stream's
+    prompt K/V is staged in device memory first; the timed region is the whole
+    schedule: joins (seed copies), decode steps with each stream's next id fed
+    back on the device, releases.  Aggregate tok/s = tokens decoded / time."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    from int4_w4a16_group_amd import inputs
+    seed, n_steps, Bmax = args.seed + 1, 256, 32
+    per_step, info = inputs.ragged_schedule(seed, n_steps, Bmax, 0.5, 2048, 16, 512)
+    admitted = sorted({s for a in per_step for s in a})
+    with ThreadPoolExecutor(16) as ex:
+        kv_host = list(ex.map(lambda s: inputs.prefix_kv(seed, s, d.n_layers, info[s][0], d.n_kv_heads, d.head_dim),
+                              admitted))
+    kv_dev = {s: tuple(torch.from_numpy(a.view(np.int16)).to(dev) for a in kv)
+              for s, kv in zip(admitted, kv_host)}
+    del kv_host
+    ids = {s: i for i, s in enumerate(admitted)}
+    tok_all = torch.tensor([inputs.first_token(seed, s, d.vocab) for s in admitted], dtype=torch.int32, device=dev)
+    act_idx = [torch.tensor([ids[s] for s in a], dtype=torch.int64, device=dev) for a in per_step]
+    nxt = torch.empty(Bmax, dtype=torch.int32, device=dev)
+    per = d.n_layers * Bmax * d.top_k
+    routes = torch.empty((n_steps, per), dtype=torch.int32, device=dev)   # step i: [n_layers][B_i][top_k]
+    slot_of, reused, freed = {}, 0, set()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for step, active in enumerate(per_step):
+        for s in active:
+            if s not in slot_of:
+                sl = L.w4_slot_alloc(ctx.ctx, info[s][0], info[s][1])
+                L.w4_slot_seed(ctx.ctx, sl, kv_dev[s][0], kv_dev[s][1], ctx.stream)
+                slot_of[s] = sl
+                reused += sl in freed
+        B = len(active)
+        tok = tok_all.index_select(0, act_idx[step])
+        L.w4_decode_step(ctx.ctx, [slot_of[s] for s in active], tok, None, nxt[:B],
+                         routes[step, :d.n_layers * B * d.top_k], ctx.stream)
+        tok_all.index_copy_(0, act_idx[step], nxt[:B])
+        nxt_active = per_step[step + 1] if step + 1 < n_steps else []
+        for s in active:
+            if s not in nxt_active:
+                L.w4_slot_release(ctx.ctx, slot_of[s])
+                freed.add(slot_of[s])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    L.w4_check_errors(ctx.ctx)
+    sizes = np.array([len(a) for a in per_step])
+    r = routes.cpu().numpy()
+    U = np.array([[len(np.unique(r[i, :d.n_layers * sizes[i] * d.top_k].reshape(d.n_layers, sizes[i], d.top_k)[l]))
+                   for l in range(d.n_layers)] for i in range(n_steps)])
+    out = dict(tok_s=float(sizes.sum() / dt), steps=n_steps, tokens=int(sizes.sum()), seconds=dt,
+               mean_B=float(sizes.mean()), min_B=int(sizes.min()), max_B=int(sizes.max()),
+               B_changes=int(np.sum(sizes[1:] != sizes[:-1])), joins=len(admitted), slot_reuses=reused,
+               unique_experts_per_layer=float(U.mean()),
+               schedule="32 slots x 4096, arrivals p=0.5 FIFO, prompts U{1..2048}, lives U{16..512}, seed 1")
+    log(f"ragged: {out['tok_s']:.0f} tok/s over {n_steps} steps, mean B {out['mean_B']:.1f} "
+        f"({out['min_B']}..{out['max_B']}, {out['B_changes']} changes), {len(admitted)} joins, {reused} slot reuses")
+    del kv_dev
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def step_bytes(d, B, U, pos0, steps):
@@ -292,9 +420,26 @@ def cpu_leg(args, d, mw, ctx, slots, prompts, kvs, first, dev, L):
         pos = pos + 1
     dt = time.perf_counter() - t0
     ntok = nS * args.cpu_steps
-    cpu = dict(value=ntok / dt, unit="tok/s", cores=oracle.threads(), kind="oracle",
+    nthreads = oracle.threads()
+    # the same oracle on one thread: the first stream, a few steps
+    single = None
+    if args.cpu_single_steps > 0:
+        oracle.set_threads(1)
+        oa1 = fresh_arena()
+        tk = first[:1].copy()
+        p1 = np.array(prompts[:1], np.int32)
+        t1 = time.perf_counter()
+        for step in range(args.cpu_single_steps):
+            _, tk, _, _ = oracle.decode_step(om, oa1, [0], p1, tk)
+            p1 = p1 + 1
+        single = dict(value=args.cpu_single_steps / (time.perf_counter() - t1), unit="tok/s", cores=1,
+                      sample=f"first stream, {args.cpu_single_steps} greedy decode steps")
+        oracle.set_threads(nthreads)
+    cpu = dict(value=ntok / dt, unit="tok/s", cores=nthreads, kind="oracle", cpu_model=cpu_model(),
+               host_cpus=os.cpu_count(),
                sample=f"first {nS} streams of the B=32 workload, {args.cpu_steps} greedy decode steps each "
-                      f"({ntok} token-steps, full 48-layer model), plain C oracle with OpenMP over outputs")
+                      f"({ntok} token-steps, full 48-layer model), plain C oracle with OpenMP over outputs",
+               single_thread=single)
 
     # parity: layer-wise teacher-forced first step of the same streams
     oa = fresh_arena()

@@ -48,6 +48,9 @@ _SIGS = {
     "w4_slot_release": (C.c_int, [_vp, _i32]),
     "w4_slot_position": (C.c_int, [_vp, _i32, C.POINTER(_i32)]),
     "w4_slots_advance": (C.c_int, [_vp, _i32, C.POINTER(_i32)]),
+    "w4_slot_read_kv": (C.c_int, [_vp, _i32, _vp, _vp, _vp]),
+    "w4_check_errors": (C.c_int, [_vp]),
+    "w4_read_probe": (C.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "w4_decode_step": (C.c_int, [_vp, _i32, C.POINTER(_i32), _vp, _vp, _vp, _vp, _vp]),
     "w4_gemm": (C.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "w4_route": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -177,6 +180,18 @@ def w4_slot_position(ctx, slot: int) -> int:
 def w4_slots_advance(ctx, slots):
     arr, n = _i32arr(slots)
     return _check(ctx, lib().w4_slots_advance(ctx, n, arr))
+
+
+def w4_slot_read_kv(ctx, slot: int, k, v, stream=None):
+    return _check(ctx, lib().w4_slot_read_kv(ctx, slot, _p(k), _p(v), _s(stream)))
+
+
+def w4_read_probe(src, nbytes: int, sink, grid: int, stream=None):
+    return _check(None, lib().w4_read_probe(_p(src), nbytes, _p(sink), grid, _s(stream)))
+
+
+def w4_check_errors(ctx):
+    return _check(ctx, lib().w4_check_errors(ctx))
 
 
 def w4_decode_step(ctx, slots, tokens, logits, next_ids, route_ids=None, stream=None):

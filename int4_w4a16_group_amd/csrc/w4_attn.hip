@@ -104,6 +104,27 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
   return hipGetLastError();
 }
 
+// The inverse of k_seed: positions 0..P-1 of a slot -> canonical k, v [L][P][Hkv][D].
+__global__ void k_read_kv(int P, int slot, KV kv, uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
+  const int p0 = blockIdx.x * 64;
+  const int l = blockIdx.y / kv.Hkv, g = blockIdx.y - l * kv.Hkv;
+  const int D = kv.D;
+  const size_t base = kv_base(kv, l, slot, g);
+  const int np = min(64, P - p0);
+  for (int idx = threadIdx.x; idx < np * D; idx += blockDim.x) {
+    const int pp = idx / D, d = idx - pp * D;
+    const size_t dst = (((size_t)l * P + p0 + pp) * kv.Hkv + g) * D + d;
+    k[dst] = kv.K[base + k_off(D, p0 + pp, d)];
+    v[dst] = kv.VT[base + v_off(D, p0 + pp, d)];
+  }
+}
+
+hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uint16_t* v, hipStream_t st) {
+  if (P <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_read_kv, dim3((P + 63) / 64, L * kv.Hkv), dim3(256), 0, st, P, slot, kv, k, v);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ attention
 // Work-group (split sp, kv head g, stream b) of four waves: wave w takes the
 // 64-position chunk c = 4 sp + w of stream b (positions 64c .. 64c+63, masked

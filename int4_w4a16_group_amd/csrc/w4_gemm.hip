@@ -172,16 +172,17 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
 
 // The residual product with K = 16 slices of 256 (the output projection at
 // K = 4096) over two 8-wave work-groups per 16-column tile, so that 2x as many
-// compute units share the activation panel reads.  Work-group 2t takes slices
-// 0..7 of tile t, sums its waves' partials in wave order and publishes that
-// sum (device-scope stores, then a flag); work-group 2t+1 takes slices 8..15,
-// waits (bounded) for the flag and continues the same in-order sum over its
-// own waves.  The result is r0 + r1 + ... + r15 summed left to right, the
-// one-work-group form's sum bit for bit.  The second work-group has the higher
-// index, so the first is resident or done when it waits.
+// compute units share the activation panel reads.  Work-group 2t + u takes
+// slices 8u .. 8u+7 of tile t and sums its waves' partials in slice order
+// (run u); both publish their run sums with device-scope stores and take the
+// tile's ticket, and the one that arrives second adds run 0 + run 1 and
+// applies the residual epilogue: the order of the one-work-group form
+// (reduce_tile), bit for bit.  Neither work-group waits for the other.
+// part: [ntiles][2][MT * 256] fp32; ticket [ntiles], zero before and after.
 template <int MT, int G>
-__global__ void __launch_bounds__(512) k_gemm_resid_split(DenseArgs a, float* part, unsigned* flag) {
+__global__ void __launch_bounds__(512) k_gemm_resid_split(DenseArgs a, float* part, unsigned* ticket) {
   extern __shared__ float red[];  // [8 waves][MT][64][4]
+  __shared__ int s_last;
   constexpr int NCH = 2, NS = NCH * 128 / G;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x >> 1, half = blockIdx.x & 1;
@@ -201,40 +202,36 @@ __global__ void __launch_bounds__(512) k_gemm_resid_split(DenseArgs a, float* pa
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(red)[(w * MT + mt) * 64 + lane] = acc[mt];
   __syncthreads();
-  uint32_t* pt = reinterpret_cast<uint32_t*>(part) + (size_t)t * MT * 256;
-  if (half == 0) {
-    // output (row, j) is entry row * 16 + j of the tile's published sum
-    reduce_tile<MT>(red, 8, [&](int row, int j, float v) {
-      __hip_atomic_store(pt + row * 16 + j, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    });
-    __builtin_amdgcn_s_waitcnt(0);  // every store complete before the flag
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_store(flag + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
-  if (threadIdx.x == 0) {
-    unsigned it = 0;
-    while (__hip_atomic_load(flag + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u && ++it < (1u << 16))
-      __builtin_amdgcn_s_sleep(1);
-  }
-  __syncthreads();
-  for (int o = threadIdx.x; o < MT * 256; o += blockDim.x) {
-    const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
-    const int idx = mt * 256 + ((i >> 2) * 16 + j) * 4 + (i & 3);  // as in reduce_tile
+  // one output per thread (MT * 256 <= 512 threads): this half's run sum
+  const int o = threadIdx.x;
+  const bool has = o < MT * 256;
+  float run = 0.f;
+  uint32_t* mine = reinterpret_cast<uint32_t*>(part) + ((size_t)t * 2 + half) * MT * 256;
+  if (has) {
+    const int idx = tile_out_idx(o);
     float p[8];
 #pragma unroll
     for (int ww = 0; ww < 8; ++ww) p[ww] = red[ww * MT * 256 + idx];
-    float v = __uint_as_float(__hip_atomic_load(pt + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-#pragma unroll
-    for (int ww = 0; ww < 8; ++ww) v = v + p[ww];
-    const int row = mt * 16 + i, n = t * 16 + j;
+    run = run_sum(p, 8);
+    __hip_atomic_store(mine + o, __float_as_uint(run), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the run sums stored before the ticket
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(ticket + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 1u;
+  __syncthreads();
+  if (!s_last) return;
+  if (has) {
+    const uint32_t* other = reinterpret_cast<const uint32_t*>(part) + ((size_t)t * 2 + (half ^ 1)) * MT * 256;
+    const float r2 = __uint_as_float(__hip_atomic_load(other + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const float v = half == 0 ? run + r2 : r2 + run;  // run 0 + run 1
+    const int row = ((o >> 8) << 4) + ((o >> 4) & 15), n = t * 16 + (o & 15);
     if (row < a.B && n < a.N) {
       uint16_t* h = reinterpret_cast<uint16_t*>(a.y) + (size_t)row * a.ldy + n;
       *h = f2h(h2f(*h) + h2f(f2h(v)));
     }
   }
-  __syncthreads();  // every read of the published sum done before the reset
-  if (threadIdx.x == 0) __hip_atomic_store(flag + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(ticket + t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 typedef void (*DenseKernel)(DenseArgs);
@@ -562,24 +559,24 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
 }
 
 hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int xrows, uint16_t* h, int ldh,
-                                  float* part, unsigned* flag, hipStream_t st) {
-  if (w.K != 16 * 256 || w.ntiles() > kSplitMaxTiles || xrows < 1 || !part || !flag) return hipErrorInvalidValue;
+                                  float* part, unsigned* ticket, hipStream_t st) {
+  if (w.K != 16 * 256 || w.ntiles() > kSplitMaxTiles || xrows < 1 || !part || !ticket) return hipErrorInvalidValue;
   const int MT = B > 16 ? 2 : 1;
   DenseArgs a{w.tiles, w.scales, w.N, w.K, w.ntiles(), xp, 0, B, h, ldh, xrows};
   const dim3 grid(2 * w.ntiles());
   const uint32_t shm = 8 * MT * 1024;
   switch (w.g) {
     case 32:
-      MT == 2 ? w4_launch(k_gemm_resid_split<2, 32>, grid, dim3(512), shm, st, a, part, flag)
-              : w4_launch(k_gemm_resid_split<1, 32>, grid, dim3(512), shm, st, a, part, flag);
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 32>, grid, dim3(512), shm, st, a, part, ticket)
+              : w4_launch(k_gemm_resid_split<1, 32>, grid, dim3(512), shm, st, a, part, ticket);
       break;
     case 64:
-      MT == 2 ? w4_launch(k_gemm_resid_split<2, 64>, grid, dim3(512), shm, st, a, part, flag)
-              : w4_launch(k_gemm_resid_split<1, 64>, grid, dim3(512), shm, st, a, part, flag);
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 64>, grid, dim3(512), shm, st, a, part, ticket)
+              : w4_launch(k_gemm_resid_split<1, 64>, grid, dim3(512), shm, st, a, part, ticket);
       break;
     default:
-      MT == 2 ? w4_launch(k_gemm_resid_split<2, 128>, grid, dim3(512), shm, st, a, part, flag)
-              : w4_launch(k_gemm_resid_split<1, 128>, grid, dim3(512), shm, st, a, part, flag);
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 128>, grid, dim3(512), shm, st, a, part, ticket)
+              : w4_launch(k_gemm_resid_split<1, 128>, grid, dim3(512), shm, st, a, part, ticket);
       break;
   }
   return hipGetLastError();

@@ -2,8 +2,8 @@
 // top-k softmax routing with (stream, expert) bucketing, expert combine with
 // the residual, and greedy argmax.  Each stream's row is handled by its own
 // work-group with a fixed reduction order, so a row's result never depends on
-// the other rows ("Batched-concurrent 4-bit serving on Apple Silicon",
-// section 3: per-stream glue runs at per-stream offsets).
+// the other rows (the batched design of "Batched-concurrent 4-bit serving on
+// Apple Silicon", section 3, keeps each stream's own steps on its own data).
 #include <algorithm>
 
 #include "w4_device.h"
@@ -73,19 +73,22 @@ hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma
   return hipGetLastError();
 }
 
-// h[b] = fp16(code * scale) of the token's embedding row (token ids outside
-// [0, V) read row 0); xn[b] = RMSNorm(h[b]).  Each thread owns runs of eight
-// columns: one 4-byte load of their codes, one scale (g is a multiple of 8),
-// 16-byte stores.
+// h[b] = fp16(code * scale) of the token's embedding row; xn[b] =
+// RMSNorm(h[b]).  bad[b] = 1 when the token id is outside [0, V) (the row is
+// then all zeros and the host reports the step as invalid), else 0.  Each
+// thread owns runs of eight columns: one 4-byte load of their codes, one scale
+// (g is a multiple of 8), 16-byte stores.
 __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, const int32_t* __restrict__ tokens,
                                                         const uint8_t* __restrict__ emb_p,
                                                         const uint16_t* __restrict__ emb_s, uint16_t* __restrict__ h,
                                                         const uint16_t* __restrict__ gamma, float eps,
-                                                        uint16_t* __restrict__ xn, int rows) {
+                                                        uint16_t* __restrict__ xn, int rows, int32_t* __restrict__ bad) {
   __shared__ float sh[16];
   const int b = blockIdx.x;
   int t = tokens[b];
-  if (t < 0 || t >= V) t = 0;
+  const bool invalid = t < 0 || t >= V;
+  if (threadIdx.x == 0) bad[b] = invalid ? 1 : 0;
+  if (invalid) t = 0;  // in bounds; every value below is replaced by zero
   const uint8_t* row = emb_p + (size_t)t * (H / 2);
   const uint16_t* srow = emb_s + (size_t)t * (H / g);
   constexpr int PER = 2;  // H <= 4096 = 8 columns x 2 x 256 threads
@@ -104,8 +107,8 @@ __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, con
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[8 * j + e] = 0.f;
     if (i < H) {
-      const uint32_t pk = *reinterpret_cast<const uint32_t*>(row + i / 2);  // element i+e in nibble e
-      const float sc = h2f(srow[i / g]);
+      const uint32_t pk = invalid ? 0u : *reinterpret_cast<const uint32_t*>(row + i / 2);  // element i+e in nibble e
+      const float sc = invalid ? 0.f : h2f(srow[i / g]);
       uint32_t out[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -145,9 +148,9 @@ __global__ void __launch_bounds__(kNormThreads) k_embed(int H, int V, int g, con
 
 hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const uint8_t* emb_p,
                         const uint16_t* emb_s, uint16_t* h, const uint16_t* gamma, float eps, uint16_t* xn,
-                        hipStream_t st, int xn_rows) {
+                        int32_t* bad, hipStream_t st, int xn_rows) {
   hipLaunchKernelGGL(k_embed, dim3(B), dim3(kNormThreads), 0, st, H, V, g, tokens, emb_p, emb_s, h, gamma, eps, xn,
-                     xn_rows);
+                     xn_rows, bad);
   return hipGetLastError();
 }
 
@@ -871,6 +874,33 @@ hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, fl
     hipLaunchKernelGGL(k_argmax<true>, grid, dim3(256), 0, st, V, logits, next, part_v, part_i, ticket);
   else
     hipLaunchKernelGGL(k_argmax<false>, grid, dim3(256), 0, st, V, logits, next, part_v, part_i, ticket);
+  return hipGetLastError();
+}
+
+// Streaming-read probe: every 16-byte chunk of src is loaded once (four
+// loads in flight per thread, consecutive lanes on consecutive chunks), the
+// words are folded into one value per thread, and a work-group stores it only
+// if it equals a constant no real data hits, so the loads stay and almost no
+// bytes are written.  Measures the HBM read ceiling with the load width the
+// weight kernels use.
+__global__ void __launch_bounds__(256) k_read_probe(const uint4* __restrict__ src, size_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= (a.x ^ a.y ^ a.z ^ a.w) + (b.x ^ b.y ^ b.z ^ b.w) + (c.x ^ c.y ^ c.z ^ c.w) + (d.x ^ d.y ^ d.z ^ d.w);
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {
+  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(src), bytes / 16, sink);
   return hipGetLastError();
 }
 

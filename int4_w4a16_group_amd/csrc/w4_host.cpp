@@ -42,7 +42,7 @@ struct BankPlan {
 };
 
 struct WsPlan {
-  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, rlg, rticket, spart, sflag, ids, w, counts, offsets, pair_stream, pair_rank, inv,
+  size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, rlg, rticket, spart, sticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
       used, n_used, units, unit_rows, n_units, act, y, logits, next, rows, table, total;
 };
 
@@ -147,8 +147,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.ticket = take(64);
   w.rlg = take(Bm * E * 4);
   w.rticket = take(Bm * 4);
-  w.spart = take((size_t)kSplitMaxTiles * 512 * 4);
-  w.sflag = take((size_t)kSplitMaxTiles * 4);
+  w.spart = take((size_t)kSplitMaxTiles * 2 * 512 * 4);
+  w.sticket = take((size_t)kSplitMaxTiles * 4);
   w.ids = take(Bm * k * 4);
   w.w = take(Bm * k * 4);
   w.counts = take(E * 4);
@@ -187,11 +187,19 @@ struct w4_ctx {
   bool dev_ready = false, table_ready = false;
   int device = -1;
   int32_t* pinned = nullptr;
+  // per ring entry, the step's invalid-token flags [Bm]: host-mapped, coherent
+  // memory that the embedding kernel writes through flags_dev (no copy)
+  int32_t* flags = nullptr;
+  int32_t* flags_dev = nullptr;
   int nsplits = 0;  // attention splits of the rows last uploaded
   size_t row_words() const { return 2 * (size_t)Bm + (size_t)Bm * attn_splits(cap - 1) * d.n_kv_heads; }
-  hipEvent_t ev[kRing] = {};
+  hipEvent_t ev[kRing] = {};      // the entry's upload has been read
+  hipEvent_t ev_err[kRing] = {};  // the entry's invalid-token flags have arrived
   bool ev_used[kRing] = {};
-  int ring = 0;
+  bool err_pending[kRing] = {};
+  int err_rows[kRing] = {};
+  int ring = 0, cur = 0;  // next entry; entry of the last upload
+  std::string sticky;     // an invalid token seen in an earlier step, not yet reported
   std::string err;
   int launches = 0, syncs = 0;
   int last_launches = 0, last_syncs = 0;
@@ -277,7 +285,13 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
       return fail(c, W4_E_UNSUPPORTED, std::string("device is ") + prop.gcnArchName + ", library built for gfx950");
     HIPCHK(c, hipHostMalloc((void**)&c->pinned, sizeof(int32_t) * c->row_words() * kRing, hipHostMallocDefault));
-    for (int i = 0; i < kRing; ++i) HIPCHK(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
+    HIPCHK(c, hipHostMalloc((void**)&c->flags, sizeof(int32_t) * c->Bm * kRing,
+                            hipHostMallocMapped | hipHostMallocCoherent));
+    HIPCHK(c, hipHostGetDevicePointer((void**)&c->flags_dev, c->flags, 0));
+    for (int i = 0; i < kRing; ++i) {
+      HIPCHK(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
+      HIPCHK(c, hipEventCreateWithFlags(&c->ev_err[i], hipEventDisableTiming));
+    }
     c->device = dev;
     c->dev_ready = true;
   }
@@ -287,7 +301,7 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.aticket), 0u, (size_t)c->Bm * c->d.n_kv_heads, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.amax_ticket), 0u, (size_t)c->Bm, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.rticket), 0u, (size_t)c->Bm, st));
-    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.sflag), 0u, (size_t)kSplitMaxTiles, st));
+    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.sticket), 0u, (size_t)kSplitMaxTiles, st));
     c->launches += 6;
     c->table_ready = true;
   }
@@ -310,6 +324,37 @@ int check_rows(w4_ctx* c, int32_t B, const int32_t* slots) {
   return W4_OK;
 }
 
+// Invalid-token flags of ring entry i (a finished step) -> the sticky report.
+void take_flags(w4_ctx* c, int i) {
+  const int32_t* f = c->flags + (size_t)i * c->Bm;
+  for (int b = 0; b < c->err_rows[i]; ++b)
+    if (f[b] && c->sticky.empty())
+      c->sticky = "a token id outside [0, vocab) was given to row " + std::to_string(b) +
+                  " of an earlier decode step (its embedding row was taken as zero)";
+  c->err_pending[i] = false;
+}
+
+// Collect the flags of every step that has finished (wait: every enqueued
+// step), then report and clear an invalid token seen since the last report.
+int poll_errors(w4_ctx* c, bool wait) {
+  for (int i = 0; i < kRing; ++i) {
+    if (!c->err_pending[i]) continue;
+    const hipError_t q = hipEventQuery(c->ev_err[i]);
+    if (q == hipErrorNotReady && !wait) continue;
+    if (q == hipErrorNotReady) {
+      HIPCHK(c, hipEventSynchronize(c->ev_err[i]));
+      c->syncs++;
+    } else if (q != hipSuccess) {
+      return fail(c, W4_E_HIP, std::string("hipEventQuery: ") + hipGetErrorString(q));
+    }
+    take_flags(c, i);
+  }
+  if (c->sticky.empty()) return W4_OK;
+  const std::string m = c->sticky;
+  c->sticky.clear();
+  return fail(c, W4_E_INVALID, m);
+}
+
 // Slot ids and positions of the rows -> workspace, through a pinned ring.
 int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int* max_pos) {
   const int i = c->ring;
@@ -318,6 +363,14 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
     HIPCHK(c, hipEventSynchronize(c->ev[i]));
     c->syncs++;
   }
+  if (c->err_pending[i]) {  // the entry's flags are overwritten by this step: collect them first
+    if (hipEventQuery(c->ev_err[i]) == hipErrorNotReady) {
+      HIPCHK(c, hipEventSynchronize(c->ev_err[i]));
+      c->syncs++;
+    }
+    take_flags(c, i);
+  }
+  c->cur = i;
   int32_t* p = c->pinned + (size_t)i * c->row_words();
   int32_t* split = p + 2 * c->Bm;
   int mp = 0, n = 0;
@@ -404,13 +457,13 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
                               c->W<unsigned>(c->wp.aticket), o, st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
   // Above 16 rows (a 32-row tile) the output projection at K = 4096 runs as
   // two work-groups per tile (same sums, bit for bit; see
-  // launch_gemm_resid_split).  Measured on the 48-layer model: +0.4% tok/s at
-  // B = 32; at B <= 8 the flag wait cost more than the spread saved (-1..2%).
+  // launch_gemm_resid_split).  Measured on the 48-layer model with the earlier
+  // flag-wait form: +0.4% tok/s at B = 32, -1..2% at B <= 8.
   {
     ProfScope ps(c, W4_K_DENSE, st);
     const Mat Om = c->mat(L.o);
     if (B > 16 && Om.K == 16 * 256 && Om.ntiles() <= kSplitMaxTiles)
-      LCHK(c, 1, launch_gemm_resid_split(Om, B, o, R, h, H, c->W<float>(c->wp.spart), c->W<unsigned>(c->wp.sflag), st));
+      LCHK(c, 1, launch_gemm_resid_split(Om, B, o, R, h, H, c->W<float>(c->wp.spart), c->W<unsigned>(c->wp.sticket), st));
     else
       LCHK(c, 1, launch_gemm(Om, B, o, qd, h, H, EPI_RESID, st, R));
   }
@@ -470,6 +523,20 @@ int w4_create(const w4_model_desc* d, int32_t max_streams, int32_t cap, void* ar
     std::fprintf(stderr, "w4_create: %s\n", why.c_str());
     return W4_E_INVALID;
   }
+  // The grouped expert products keep every 16-row unit record of a launch in
+  // two records per thread: E + max_streams * top_k / 16 + 1 records must fit
+  // in 2 * 64 * (waves of the product), for K = hidden (gate/up) and
+  // K = moe_inter (down), waves = K / 256 (K / 128 when K % 256 != 0).
+  for (int K : {d->hidden, d->moe_inter}) {
+    const int nw = K / ((K % 256 == 0) ? 256 : 128);
+    const int units_cap = d->n_experts + max_streams * d->top_k / 16 + 1;
+    if (units_cap > 2 * 64 * nw || units_cap > kMaxUnits) {
+      std::fprintf(stderr, "w4_create: %d experts with max_streams %d and top_k %d need %d expert work units, more "
+                   "than the %d that a product over K = %d holds\n", d->n_experts, max_streams, d->top_k, units_cap,
+                   2 * 64 * nw, K);
+      return W4_E_UNSUPPORTED;
+    }
+  }
   if (!arena_dev || !bank_dev || !ws_dev) return W4_E_INVALID;
   if (((uintptr_t)arena_dev | (uintptr_t)bank_dev | (uintptr_t)ws_dev) % kAlign) return W4_E_INVALID;
   w4_ctx* c = new w4_ctx;
@@ -493,9 +560,12 @@ void w4_destroy(w4_ctx* c) {
   if (!c) return;
   for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
   if (c->dev_ready) {
-    for (int i = 0; i < kRing; ++i)
+    for (int i = 0; i < kRing; ++i) {
       if (c->ev[i]) (void)hipEventSynchronize(c->ev[i]), (void)hipEventDestroy(c->ev[i]);
+      if (c->ev_err[i]) (void)hipEventSynchronize(c->ev_err[i]), (void)hipEventDestroy(c->ev_err[i]);
+    }
     if (c->pinned) (void)hipHostFree(c->pinned);
+    if (c->flags) (void)hipHostFree(c->flags);
   }
   delete c;
 }
@@ -581,6 +651,19 @@ int w4_slot_seed(w4_ctx* c, int32_t slot, const void* k, const void* v, void* st
   return W4_OK;
 }
 
+int w4_slot_read_kv(w4_ctx* c, int32_t slot, void* k, void* v, void* stream) {
+  if (!c) return W4_E_INVALID;
+  if (slot < 0 || slot >= c->Bm || !c->live[slot]) return fail(c, W4_E_BAD_SLOT, "slot is not live");
+  if (c->need_seed[slot]) return fail(c, W4_E_NOT_READY, "slot has an unseeded prompt");
+  if (!k || !v) return fail(c, W4_E_INVALID, "null K/V");
+  hipStream_t st = (hipStream_t)stream;
+  int rc = ensure_device(c, st);
+  if (rc) return rc;
+  LCHK(c, 1, launch_read_kv(c->d.n_layers, c->pos[slot], slot, c->kv(), static_cast<uint16_t*>(k),
+                            static_cast<uint16_t*>(v), st));
+  return W4_OK;
+}
+
 int w4_slot_release(w4_ctx* c, int32_t slot) {
   if (!c) return W4_E_INVALID;
   if (slot < 0 || slot >= c->Bm || !c->live[slot]) return fail(c, W4_E_BAD_SLOT, "slot is not live");
@@ -614,6 +697,8 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
   hipStream_t st = (hipStream_t)stream;
   rc = ensure_device(c, st);
   if (rc) return rc;
+  rc = poll_errors(c, false);
+  if (rc) return rc;
   const int l0 = c->launches, s0 = c->syncs;
   const w4_model_desc& d = c->d;
   int max_pos = 0;
@@ -624,7 +709,7 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
   const int R = panel_rows(c->Bm);
   LCHK(c, 1, launch_embed(B, d.hidden, d.vocab, d.group, tokens, c->Bk<uint8_t>(c->bp.emb_p),
                           c->Bk<uint16_t>(c->bp.emb_s), h, c->Bk<uint16_t>(c->bp.layers[0].attn_norm), d.rms_eps, xp,
-                          st, R));
+                          c->flags_dev + (size_t)c->cur * c->Bm, st, R));
   for (int l = 0; l < d.n_layers; ++l) {
     const uint16_t* ng = l + 1 < d.n_layers ? c->Bk<uint16_t>(c->bp.layers[l + 1].attn_norm)
                                             : c->Bk<uint16_t>(c->bp.final_norm);
@@ -638,6 +723,14 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
   }
   LCHK(c, 1, launch_argmax(B, d.vocab, lg, next, c->W<float>(c->wp.amax_v), c->W<int32_t>(c->wp.amax_i),
                             c->W<unsigned>(c->wp.amax_ticket), st));
+  // the embedding wrote the step's invalid-token flags into its ring entry;
+  // a later call reads them once this event has passed (see poll_errors)
+  {
+    const int i = c->cur;
+    HIPCHK(c, hipEventRecord(c->ev_err[i], st));
+    c->err_pending[i] = true;
+    c->err_rows[i] = B;
+  }
   for (int b = 0; b < B; ++b) c->pos[slots[b]]++;
   c->last_launches = c->launches - l0;
   c->last_syncs = c->syncs - s0;
@@ -729,6 +822,8 @@ int w4_attn_decode(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, co
   hipStream_t st = (hipStream_t)stream;
   rc = ensure_device(c, st);
   if (rc) return rc;
+  rc = poll_errors(c, false);
+  if (rc) return rc;
   int max_pos = 0;
   rc = upload_rows(c, B, slots, st, &max_pos);
   if (rc) return rc;
@@ -753,6 +848,8 @@ int w4_layer_step(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, voi
   if (!h) return fail(c, W4_E_INVALID, "null h");
   hipStream_t st = (hipStream_t)stream;
   rc = ensure_device(c, st);
+  if (rc) return rc;
+  rc = poll_errors(c, false);
   if (rc) return rc;
   int max_pos = 0;
   rc = upload_rows(c, B, slots, st, &max_pos);
@@ -803,6 +900,20 @@ int w4_profile_end(w4_ctx* c, double* total_ms, int32_t* launches) {
   if (total_ms) *total_ms = ms;
   if (launches) *launches = (int32_t)n;
   return W4_OK;
+}
+
+int w4_read_probe(const void* src, size_t bytes, void* sink, int32_t grid, void* stream) {
+  if (!src || !sink || grid < 1 || grid > (1 << 20) || bytes == 0 || bytes % 16 ||
+      ((uintptr_t)src % 16) != 0)
+    return W4_E_INVALID;
+  hipError_t e = launch_read_probe(src, bytes, static_cast<uint32_t*>(sink), grid, (hipStream_t)stream);
+  return e == hipSuccess ? W4_OK : W4_E_HIP;
+}
+
+int w4_check_errors(w4_ctx* c) {
+  if (!c) return W4_E_INVALID;
+  if (!c->dev_ready) return W4_OK;
+  return poll_errors(c, true);
 }
 
 int w4_last_step_counts(const w4_ctx* c, int32_t* launches, int32_t* syncs) {

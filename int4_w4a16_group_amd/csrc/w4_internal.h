@@ -77,11 +77,11 @@ int touch_groups(size_t bytes, int threads);
 
 // h += x * W^T (fp16 residual epilogue) for K = 4096 with the K slices split
 // over two work-groups per tile (bit-identical to launch_gemm's EPI_RESID);
-// xp an activation panel with xrows rows; part [ntiles][512] fp32 and flag
-// [ntiles] (zero before and after) are scratch.  ntiles <= kSplitMaxTiles.
+// xp an activation panel with xrows rows; part [ntiles][2][512] fp32 and
+// ticket [ntiles] (zero before and after) are scratch.  ntiles <= kSplitMaxTiles.
 constexpr int kSplitMaxTiles = 256;
 hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int xrows, uint16_t* h, int ldh,
-                                  float* part, unsigned* flag, hipStream_t st);
+                                  float* part, unsigned* ticket, hipStream_t st);
 
 // Grouped expert GEMMs over the bucketed pairs (persistent, work list from route).
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
@@ -96,9 +96,10 @@ hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* in
                           hipStream_t st, int xn_rows = 0);
 hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma, float eps, uint16_t* out,
                           hipStream_t st, int out_rows = 0);
+// bad [B]: 1 where the token id is outside [0, V) (that row is zero), else 0.
 hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const uint8_t* emb_p,
                         const uint16_t* emb_s, uint16_t* h, const uint16_t* gamma, float eps, uint16_t* xn,
-                        hipStream_t st, int xn_rows = 0);
+                        int32_t* bad, hipStream_t st, int xn_rows = 0);
 // next[b] = argmax of logits row b (ties to the lower index); part_v/part_i
 // [B][8] hold the split partials, ticket [B] is zero before and after.
 hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, float* part_v, int32_t* part_i,
@@ -124,6 +125,8 @@ hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, c
 hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStream_t st);
 hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, const uint16_t* v,
                        hipStream_t st);
+// positions 0..P-1 of a slot -> canonical k, v [L][P][Hkv][D]
+hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uint16_t* v, hipStream_t st);
 // split-KV decode attention; part_o [B][Hq][nchmax][D] f32, part_ml [B][Hq][nchmax][2].
 // prof: when non-null, the launch is timed (prof_arm).
 // Split-KV decode attention in one launch.  A stream at position p has
@@ -176,5 +179,7 @@ __device__ __forceinline__ void touch_lines(const uint8_t* span, size_t lines, s
   }
 }
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
+// Streaming-read probe (diagnostic): src[bytes] read once with 16-byte loads; sink [grid] words.
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 
 }  // namespace w4

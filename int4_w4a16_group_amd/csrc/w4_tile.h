@@ -123,25 +123,44 @@ __device__ __forceinline__ void load_x_panel(XRegs<MT, NCH * 4>& x, const uint16
   }
 }
 
-// Sum the waves' partial tiles (red: [NW][MT][64 lanes][4]) in wave order and
-// hand each output (row, col-in-tile, value) to epi.  Consecutive threads take
-// consecutive columns.
-// All NW (<= 16) reads are issued before the in-order sum; slots w >= NW
-// re-read the last slice and are not added.
+// Index in a [.][MT][64 lanes][4] partial tile of output o = (mt, row i,
+// column j) of the tile (the MFMA result layout: lane (i/4)*16 + j, element i%4).
+__device__ __forceinline__ int tile_out_idx(int o) {
+  const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
+  return mt * 256 + ((i >> 2) * 16 + j) * 4 + (i & 3);
+}
+
+// Sum of the K-slice partials w0 .. w1-1 (< w0 + 8) of one output, in slice
+// order; p: the partials of slices w0 .. w0+7 (entries past w1 not added).
+__device__ __forceinline__ float run_sum(const float (&p)[8], int n) {
+  float v = p[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) v = w < n ? v + p[w] : v;
+  return v;
+}
+
+// Sum the waves' partial tiles (red: [NW][MT][64 lanes][4]) and hand each
+// output (row, col-in-tile, value) to epi.  Order of the sum, a function of
+// the slice count only: slices in order in runs of eight, then the run sums
+// in order -- ((p0 + ... + p7) + (p8 + ... + p15)) for 16 slices.  (The split
+// output projection computes each run in its own work-group and adds the two
+// run sums the same way.)  Consecutive threads take consecutive columns.  All
+// NW (<= 16) reads are issued before the sums; slots w >= NW re-read the last
+// slice and are not added.
 template <int MT, class EpiF>
 __device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) {
   const int nt = blockDim.x;
   for (int o = threadIdx.x; o < MT * 256; o += nt) {
-    const int mt = o >> 8, i = (o >> 4) & 15, j = o & 15;
-    const int ln = (i >> 2) * 16 + j, r = i & 3;
-    const int idx = mt * 256 + ln * 4 + r;
-    float p[16];
+    const int idx = tile_out_idx(o);
+    float p0[8], p1[8];
 #pragma unroll
-    for (int w = 0; w < 16; ++w) p[w] = red[min(w, NW - 1) * MT * 256 + idx];
-    float v = p[0];
-#pragma unroll
-    for (int w = 1; w < 16; ++w) v = w < NW ? v + p[w] : v;
-    epi(mt * 16 + i, j, v);
+    for (int w = 0; w < 8; ++w) {
+      p0[w] = red[min(w, NW - 1) * MT * 256 + idx];
+      p1[w] = red[min(w + 8, NW - 1) * MT * 256 + idx];
+    }
+    float v = run_sum(p0, NW);
+    if (NW > 8) v = v + run_sum(p1, NW - 8);
+    epi(((o >> 8) << 4) + ((o >> 4) & 15), o & 15, v);
   }
 }
 

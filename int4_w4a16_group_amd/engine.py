@@ -89,3 +89,15 @@ class Context:
 
     def position(self, slot: int) -> int:
         return L.w4_slot_position(self.ctx, slot)
+
+    def read_kv(self, slot: int):
+        """The K/V a slot holds at positions 0..p-1 as host arrays, canonical
+        [n_layers][p][n_kv][head_dim] fp16 bits (the inverse of seeding)."""
+        d = self.desc
+        p = self.position(slot)
+        shape = (d.n_layers, p, d.n_kv_heads, d.head_dim)
+        k = torch.empty(shape, dtype=torch.int16, device=self.device)
+        v = torch.empty(shape, dtype=torch.int16, device=self.device)
+        L.w4_slot_read_kv(self.ctx, slot, k, v, self.stream)
+        torch.cuda.current_stream(self.device).synchronize()
+        return k.cpu().numpy().view(np.uint16), v.cpu().numpy().view(np.uint16)

@@ -72,6 +72,7 @@ def lib():
         L.orc_attn_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
                                     _u16p, _u16p, _u16p, _u16p]
         L.orc_threads.restype = C.c_int
+        L.orc_set_threads.argtypes = [C.c_int]
         L.orc_init()
         _lib = L
     return _lib
@@ -88,6 +89,10 @@ def _ptr(a):
 
 def threads() -> int:
     return lib().orc_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- primitives

@@ -40,6 +40,15 @@ EXPORT int orc_threads(void) {
 #endif
 }
 
+/* Set the threads of the parallel loops (n >= 1; no effect without OpenMP). */
+EXPORT void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* IEEE 754 binary16 <-> binary32, round to nearest, ties to even.           */
 /* ------------------------------------------------------------------------ */

@@ -150,3 +150,36 @@ def test_no_vendor_blas_linked():
     out = subprocess.run(["ldd", L.LIB_PATH], capture_output=True, text=True).stdout
     for name in ("rocblas", "hipblas", "hipblaslt", "miopen", "libtorch"):
         assert name not in out.lower(), name
+
+
+def test_create_rejects_geometry_the_grouped_products_cannot_hold():
+    """n_experts + max_streams * top_k / 16 + 1 expert work units must fit the
+    grouped products' records (2 * 64 per 256 columns of K): with hidden 256 a
+    128-expert model does not fit, and w4_create says so before any device work."""
+    import dataclasses
+    d = dataclasses.replace(inputs.TINY, n_experts=128, top_k=8)
+    assert L.w4_bank_bytes(d) > 0                               # the geometry itself is valid
+    with pytest.raises(L.W4Error) as e:
+        L.w4_create(d, 32, 128, FAKE, 2 * FAKE, 3 * FAKE)
+    assert e.value.status == L.W4_E_UNSUPPORTED
+    ok = dataclasses.replace(d, hidden=512, moe_inter=512)      # 2 * 64 * 2 = 256 >= 128 + 16 + 1
+    L.w4_destroy(L.w4_create(ok, 32, 128, FAKE, 2 * FAKE, 3 * FAKE))
+
+
+def test_read_kv_and_error_check_argument_checks():
+    c = make_ctx()
+    try:
+        assert L.w4_check_errors(c) == L.W4_OK                 # nothing enqueued yet
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slot_read_kv(c, 1, FAKE, FAKE)                # not live
+        assert e.value.status == L.W4_E_BAD_SLOT
+        s = L.w4_slot_alloc(c, 5, 1)
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slot_read_kv(c, s, FAKE, FAKE)                # prompt not seeded
+        assert e.value.status == L.W4_E_NOT_READY
+        t = L.w4_slot_alloc(c, 0, 1)
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slot_read_kv(c, t, 0, FAKE)                   # null destination
+        assert e.value.status == L.W4_E_INVALID
+    finally:
+        L.w4_destroy(c)

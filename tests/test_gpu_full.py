@@ -119,3 +119,136 @@ def test_full_size_rows_bit_identical_across_batches(full, gpu):
     release_all(f, slots)
     for i, r in enumerate(rows):
         assert np.array_equal(lg8[i], lg32[r]), f"stream {r}: permuted B=8 differs from B=32"
+
+
+# ------------------------------------------------------------------ continuous batching at full size
+def _layerwise_check(f, gpu, slots, rows, tokens, what):
+    """Teacher-forced layer-wise parity of one decode step for the rows listed
+    (indices into slots; the GPU layer runs every row of slots, so its
+    attention and routing see the whole batch): the oracle's arena is loaded
+    with the K/V the GPU holds for those slots (prompt and generated
+    positions), every GPU layer gets the oracle's input state, the oracle
+    replays the GPU's routing once it is accepted as a top-k within the
+    tolerance, and the output projection gets the oracle's final normalised
+    state.  Positions do not move."""
+    mw, ctx = f["mw"], f["ctx"]
+    B = len(slots)
+    pos = np.array([ctx.position(slots[r]) for r in rows], np.int32)
+    cap = int((pos.max() + 1 + 63) // 64 * 64)
+    om = oracle.Model(mw)
+    oa = oracle.Arena(D, len(rows), cap)
+    for j, r in enumerate(rows):
+        k, v = ctx.read_kv(slots[r])
+        oa.seed(j, k, v)
+    h_all = oracle.embed(om, tokens)                # every row of the batch, so the GPU layer sees B rows
+    h = h_all[rows]
+    worst = 0.0
+    for l in range(D.n_layers):
+        g_all = h_all.copy()
+        g_all[rows] = h
+        hd = to_dev(g_all, gpu)
+        ids = torch.empty((B, D.top_k), dtype=torch.int32, device=gpu)
+        L.w4_layer_step(ctx.ctx, l, slots, hd, ids, ctx.stream)
+        gh, gids = to_host(hd)[rows], to_host(ids)[rows]
+        rh, _, rlg = oracle.layer_step(om, oa, l, list(range(len(rows))), pos, h, force=gids)
+        for j in range(len(rows)):
+            assert route_ok(gids[j], rlg[j], TOL), f"{what}: layer {l} row {rows[j]}: routing beyond a near-tie"
+        a, r = gh.view(np.float16).astype(np.float64), rh.view(np.float16).astype(np.float64)
+        err = np.max(np.abs(a - r), 1) / np.max(np.abs(r), 1)
+        worst = max(worst, float(err.max()))
+        assert err.max() <= TOL, f"{what}: layer {l}: normwise {err.max():.2e}"
+        h = rh
+    xn = oracle.rmsnorm(h, mw.final_norm, D.rms_eps)
+    olg = oracle.w4_gemm(xn, mw.lm_head.packed, mw.lm_head.scales, D.group)
+    glg = torch.empty((len(rows), D.vocab), dtype=torch.int16, device=gpu)
+    L.w4_gemm(ctx.ctx, 0, L.W4_T_LM_HEAD, 0, len(rows), to_dev(xn, gpu), glg, ctx.stream)
+    g_, o_ = to_host(glg).view(np.float16).astype(np.float64), olg.view(np.float16).astype(np.float64)
+    err = np.max(np.abs(g_ - o_), 1) / np.max(np.abs(o_), 1)
+    assert err.max() <= TOL, f"{what}: output projection normwise {err.max():.2e}"
+    return worst
+
+
+def test_ragged_join_finish_full_model(full, gpu):
+    """Continuous batching on the 48-layer model: 32 slots x 4096, a request
+    arrives with probability 0.5 per step (FIFO), prompts ~ U{1..2048} with
+    seeded K/V, lives ~ U{16..512} decode steps, finished slots are released and
+    reused, 256 greedy steps with each stream's next id fed back.  Checked:
+    layer-wise oracle parity on two sampled steps (one near B = 32, one with
+    8..16 rows), and three sampled streams decoded alone, on a fresh context
+    holding only that stream, give the same logits bit for bit at every step."""
+    from concurrent.futures import ThreadPoolExecutor
+    f = full
+    mw, ctx = f["mw"], f["ctx"]
+    seed, n_steps = 1, 256
+    per_step, info = inputs.ragged_schedule(seed, n_steps, NS, 0.5, 2048, 16, 512)
+    sizes = [len(a) for a in per_step]
+    changes = sum(1 for i in range(1, n_steps) if sizes[i] != sizes[i - 1])
+    assert min(sizes) == 1 and max(sizes) == NS and changes >= 10, (min(sizes), max(sizes), changes)
+    admitted = sorted({sid for a in per_step for sid in a})
+    with ThreadPoolExecutor(16) as ex:
+        kvs = dict(zip(admitted, ex.map(lambda s: inputs.prefix_kv(seed, s, D.n_layers, info[s][0], D.n_kv_heads,
+                                                                  D.head_dim), admitted)))
+    join_step = {s: info[s][2] for s in admitted}
+    # sampled streams: the first (live for the whole run), the first and the last
+    # to join after a slot was freed (each takes a freed slot)
+    reusers = [s for s in admitted if join_step[s] > min(join_step[t] + info[t][1] for t in admitted)]
+    sample = sorted({admitted[0], reusers[0], reusers[-1]})
+    assert len(sample) == 3
+    full_step = next(i for i, n in enumerate(sizes) if n == NS)
+    mid_step = next(i for i, n in enumerate(sizes) if 8 <= n <= 16 and i > 2)
+    slot_of, live, freed, reused = {}, set(), set(), 0
+    tok = {s: inputs.first_token(seed, s, D.vocab) for s in admitted}
+    fed = {s: [] for s in sample}
+    got = {s: [] for s in sample}
+    lg = torch.empty((NS, D.vocab), dtype=torch.int16, device=gpu)
+    nx = torch.empty(NS, dtype=torch.int32, device=gpu)
+    parity = {}
+    try:
+        for step, active in enumerate(per_step):
+            for s in active:
+                if s not in slot_of:
+                    plen, life, _ = info[s]
+                    slot_of[s] = ctx.join(plen, life, *kvs.pop(s))
+                    reused += slot_of[s] in freed
+                    live.add(slot_of[s])
+            slots = [slot_of[s] for s in active]
+            tokens = np.array([tok[s] for s in active], np.int32)
+            if step in (full_step, mid_step):
+                rows = list(range(len(active))) if step == mid_step else list(range(0, len(active), 4))
+                parity[step] = _layerwise_check(f, gpu, slots, rows, tokens, f"step {step} (B={len(active)})")
+            B = len(active)
+            L.w4_decode_step(ctx.ctx, slots, torch.from_numpy(tokens).to(gpu), lg[:B], nx[:B], None, ctx.stream)
+            nxt = to_host(nx[:B])
+            for j, s in enumerate(active):
+                if s in fed:
+                    fed[s].append(int(tokens[j]))
+                    got[s].append(lg[j].clone())
+                tok[s] = int(nxt[j])
+            nxt_active = per_step[step + 1] if step + 1 < n_steps else []
+            for s in active:
+                if s not in nxt_active:
+                    ctx.release(slot_of[s])
+                    live.discard(slot_of[s])
+                    freed.add(slot_of[s])
+        assert reused > 0, "no freed slot was reused"
+        assert not live
+        assert L.w4_check_errors(ctx.ctx) == L.W4_OK
+    finally:
+        for sl in live:
+            ctx.release(sl)
+    assert set(parity) == {full_step, mid_step}
+    # each sampled stream alone on a fresh context with one slot: same bits at every step
+    solo = Context(D, 1, CAP, gpu)
+    try:
+        solo.load_model(mw)
+        for s in sample:
+            plen, life, _ = info[s]
+            k, v = inputs.prefix_kv(seed, s, D.n_layers, plen, D.n_kv_heads, D.head_dim)
+            sl = solo.join(plen, life, k, v)
+            for t, tk in enumerate(fed[s]):
+                L.w4_decode_step(solo.ctx, [sl], torch.tensor([tk], dtype=torch.int32, device=gpu), lg[:1], nx[:1],
+                                 None, solo.stream)
+                assert torch.equal(lg[0], got[s][t]), f"stream {s} step {t}: alone differs from the ragged batch"
+            solo.release(sl)
+    finally:
+        solo.close()
