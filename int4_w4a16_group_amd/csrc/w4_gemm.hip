@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) reinterpret_cast<f4*>(rb)[(w * MT + mt) * 64 + lane] = acc[mt];
     __syncthreads();  // partials of this tile visible; the other buffer's readers are done
-    reduce_tile<MT>(rb, NW, [&](int row, int j, float v) {
+    reduce_tile<MT, LB / 64>(rb, NW, [&](int row, int j, float v) {
       const int n = t * 16 + j;
       if (valid && row < a.B && n < a.N) {
         if (EPI == EPI_F32) {
@@ -442,7 +442,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
         }
       }
     } else {
-      reduce_tile<1>(rb, NW, [&](int i, int j, float v) {
+      reduce_tile<1, LB / 64>(rb, NW, [&](int i, int j, float v) {
         const int n = t * 16 + j;
         if (valid && i < m && n < a.N) a.out[(size_t)(off + i) * a.N + n] = f2h(v);
       });

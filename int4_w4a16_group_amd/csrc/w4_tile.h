@@ -139,27 +139,33 @@ __device__ __forceinline__ float run_sum(const float (&p)[8], int n) {
   return v;
 }
 
-// Sum the waves' partial tiles (red: [NW][MT][64 lanes][4]) and hand each
-// output (row, col-in-tile, value) to epi.  Order of the sum, a function of
-// the slice count only: slices in order in runs of eight, then the run sums
-// in order -- ((p0 + ... + p7) + (p8 + ... + p15)) for 16 slices.  (The split
-// output projection computes each run in its own work-group and adds the two
-// run sums the same way.)  Consecutive threads take consecutive columns.  All
-// NW (<= 16) reads are issued before the sums; slots w >= NW re-read the last
-// slice and are not added.
-template <int MT, class EpiF>
+// Sum the waves' partial tiles (red: [NW][MT][64 lanes][4], NW <= NWMAX <=
+// 16) and hand each output (row, col-in-tile, value) to epi.  Order of the
+// sum, a function of the slice count only: slices in order in runs of eight,
+// then the run sums in order -- ((p0 + ... + p7) + (p8 + ... + p15)) for 16
+// slices, one plain in-order chain for up to 8.  (The split output projection
+// computes each run in its own work-group and adds the two run sums the same
+// way.)  Consecutive threads take consecutive columns.  All NWMAX reads are
+// issued before the sums; slots w >= NW re-read the last slice and are not
+// added (selects, no branch, so the reads are never held back).
+template <int MT, int NWMAX, class EpiF>
 __device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) {
+  static_assert(NWMAX >= 1 && NWMAX <= 16, "at most 16 slices");
   const int nt = blockDim.x;
   for (int o = threadIdx.x; o < MT * 256; o += nt) {
     const int idx = tile_out_idx(o);
-    float p0[8], p1[8];
+    float p[NWMAX];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      p0[w] = red[min(w, NW - 1) * MT * 256 + idx];
-      p1[w] = red[min(w + 8, NW - 1) * MT * 256 + idx];
+    for (int w = 0; w < NWMAX; ++w) p[w] = red[min(w, NW - 1) * MT * 256 + idx];
+    float v = p[0];
+#pragma unroll
+    for (int w = 1; w < (NWMAX < 8 ? NWMAX : 8); ++w) v = w < NW ? v + p[w] : v;
+    if constexpr (NWMAX > 8) {
+      float u = p[8];
+#pragma unroll
+      for (int w = 9; w < NWMAX; ++w) u = w < NW ? u + p[w] : u;
+      v = NW > 8 ? v + u : v;
     }
-    float v = run_sum(p0, NW);
-    if (NW > 8) v = v + run_sum(p1, NW - 8);
     epi(((o >> 8) << 4) + ((o >> 4) & 15), o & 15, v);
   }
 }
