@@ -205,8 +205,24 @@ int w4_attn_decode(w4_ctx* ctx, int32_t layer, int32_t B, const int32_t* slots_h
 int w4_layer_step(w4_ctx* ctx, int32_t layer, int32_t B, const int32_t* slots_host, void* h_dev,
                   int32_t* route_ids_dev, void* stream);
 
+/* ---- allocation-free routing (no context) ----
+ * For callers that cannot allocate device memory or hold a context (code
+ * under HIP graph capture, tight serving loops): the routing and bucketing of
+ * w4_route, with the same arguments and results, for B <= 32 rows of
+ * n_experts <= 256 logits and top_k <= 16.  Its scratch is a 32 KiB
+ * file-scope device array (one per GPU, held until the process ends), so it
+ * allocates nothing; calls that overlap on one GPU share that array and race,
+ * so serialise them (one stream, or events).  W4_E_UNSUPPORTED beyond those
+ * sizes, W4_E_INVALID for null logits, ids or w; the message is
+ * w4_last_error(NULL). */
+int w4_route_noalloc(int32_t B, int32_t n_experts, int32_t top_k, const float* logits_dev, int32_t* ids_dev,
+                     float* w_dev, int32_t* counts_dev, int32_t* offsets_dev, int32_t* pair_stream_dev,
+                     int32_t* pair_rank_dev, void* stream);
+
 /* ---- diagnostics ---- */
 const char* w4_status_string(int32_t status);
+/* Message of the context's last failure; with NULL, that of the last failed
+ * context-free call on this thread. */
 const char* w4_last_error(const w4_ctx* ctx);
 /* Kernel launches and host-device synchronisations issued by the last
  * w4_decode_step (the batched-serving page, sections 3 and 4, counts GPU

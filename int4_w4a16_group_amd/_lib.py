@@ -51,6 +51,7 @@ _SIGS = {
     "w4_slot_read_kv": (C.c_int, [_vp, _i32, _vp, _vp, _vp]),
     "w4_check_errors": (C.c_int, [_vp]),
     "w4_read_probe": (C.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "w4_route_noalloc": (C.c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "w4_decode_step": (C.c_int, [_vp, _i32, C.POINTER(_i32), _vp, _vp, _vp, _vp, _vp]),
     "w4_gemm": (C.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
     "w4_route": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -119,7 +120,7 @@ def desc_of(d) -> w4_model_desc:
 
 def _check(ctx, rc):
     if rc != W4_OK:
-        msg = lib().w4_last_error(ctx).decode() if ctx else ""
+        msg = lib().w4_last_error(ctx).decode()
         raise W4Error(rc, f"{lib().w4_status_string(rc).decode()}: {msg}")
     return rc
 
@@ -188,6 +189,12 @@ def w4_slot_read_kv(ctx, slot: int, k, v, stream=None):
 
 def w4_read_probe(src, nbytes: int, sink, grid: int, stream=None):
     return _check(None, lib().w4_read_probe(_p(src), nbytes, _p(sink), grid, _s(stream)))
+
+
+def w4_route_noalloc(B: int, n_experts: int, top_k: int, logits, ids, w, counts=None, offsets=None,
+                     pair_stream=None, pair_rank=None, stream=None):
+    return _check(None, lib().w4_route_noalloc(B, n_experts, top_k, _p(logits), _p(ids), _p(w), _p(counts),
+                                               _p(offsets), _p(pair_stream), _p(pair_rank), _s(stream)))
 
 
 def w4_check_errors(ctx):

@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4moe.so")
-SOURCES = ["w4_gemm.hip", "w4_attn.hip", "w4_glue.hip", "w4_host.cpp"]
+SOURCES = ["w4_gemm.hip", "w4_attn.hip", "w4_glue.hip", "w4_noalloc.hip", "w4_host.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -875,7 +875,7 @@ const char* w4_status_string(int32_t s) {
   }
 }
 
-const char* w4_last_error(const w4_ctx* c) { return c ? c->err.c_str() : "null context"; }
+const char* w4_last_error(const w4_ctx* c) { return c ? c->err.c_str() : w4::g_free_err.c_str(); }
 
 int w4_profile_begin(w4_ctx* c, int32_t kernel) {
   if (!c) return W4_E_INVALID;

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <string>
+
 #include "w4moe.h"
 
 namespace w4 {
@@ -179,6 +181,8 @@ __device__ __forceinline__ void touch_lines(const uint8_t* span, size_t lines, s
   }
 }
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
+// Message of the last failed context-free entry point on this thread.
+extern thread_local std::string g_free_err;
 // Streaming-read probe (diagnostic): src[bytes] read once with 16-byte loads; sink [grid] words.
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 
