@@ -134,6 +134,19 @@ int w4_slot_position(const w4_ctx* ctx, int32_t slot, int32_t* pos_out);
 /* Advance the positions of n distinct live slots by one (used with the
  * per-layer entry points, which do not move positions). */
 int w4_slots_advance(w4_ctx* ctx, int32_t n, const int32_t* slots_host);
+/* Sampling of a live slot's next tokens (beyond the pages' greedy decoding;
+ * the batched-serving page, section 5, names non-greedy sampling as not
+ * validated there).  temperature 0 (the default after w4_slot_alloc) is
+ * greedy; otherwise: rank ids by (logit descending, id ascending), keep the
+ * first top_k (1..64), weight rank r by exp((l_r - l_0) / temperature), keep
+ * the shortest prefix whose running sum reaches top_p (0 < top_p <= 1) of the
+ * total, and invert that prefix's running sums at a draw u in [0, 1): u is
+ * the top 24 bits of output number p of the SplitMix64 generator started at
+ * seed, p the slot's position when the token is decoded.  So a stream's
+ * tokens depend on its own seed and positions only, never on the batch.
+ * W4_E_BAD_SLOT / W4_E_INVALID on a bad slot or parameter. */
+int w4_slot_set_sampling(w4_ctx* ctx, int32_t slot, uint64_t seed, float temperature, int32_t top_k,
+                         float top_p);
 /* Diagnostic, the inverse of w4_slot_seed: the K/V a live, seeded slot holds
  * at positions 0 .. p-1 (p = its current position) -> k_dev, v_dev, each
  * canonical [n_layers][p][n_kv][head_dim] fp16 (post-rotary keys), caller-
@@ -142,12 +155,13 @@ int w4_slot_read_kv(w4_ctx* ctx, int32_t slot, void* k_dev, void* v_dev, void* s
 
 /* One decode step for B streams ("Batched-concurrent 4-bit serving ...",
  * section 1: all layers and the output projection of the B streams in one
- * submission; section 3: greedy decoding).  Row b is the stream in
+ * submission; section 3: greedy decoding, or each slot's sampling as set by
+ * w4_slot_set_sampling).  Row b is the stream in
  * slots_host[b] at its current position p_b.  tokens_dev int32 [B] input ids
  * (an id outside [0, vocab) gives a zero embedding row and a sticky
  * W4_E_INVALID from the next enqueueing call or w4_check_errors).  Writes the
  * new K/V at p_b of each slot, returns fp16 logits [B][vocab] (logits_dev may
- * be NULL) and the greedy next ids int32 [B] (ties to the lower id).
+ * be NULL) and the next ids int32 [B] (greedy: ties to the lower id).
  * route_ids_dev: optional int32 [n_layers][B][top_k] expert ids per rank.
  * On success every listed slot's position advances by one.  A row's result
  * is bit-identical whatever the other rows, their order and the slot ids

@@ -49,6 +49,7 @@ _SIGS = {
     "w4_slot_position": (C.c_int, [_vp, _i32, C.POINTER(_i32)]),
     "w4_slots_advance": (C.c_int, [_vp, _i32, C.POINTER(_i32)]),
     "w4_slot_read_kv": (C.c_int, [_vp, _i32, _vp, _vp, _vp]),
+    "w4_slot_set_sampling": (C.c_int, [_vp, _i32, C.c_uint64, C.c_float, _i32, C.c_float]),
     "w4_check_errors": (C.c_int, [_vp]),
     "w4_read_probe": (C.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "w4_route_noalloc": (C.c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -181,6 +182,10 @@ def w4_slot_position(ctx, slot: int) -> int:
 def w4_slots_advance(ctx, slots):
     arr, n = _i32arr(slots)
     return _check(ctx, lib().w4_slots_advance(ctx, n, arr))
+
+
+def w4_slot_set_sampling(ctx, slot: int, seed: int, temperature: float, top_k: int, top_p: float):
+    return _check(ctx, lib().w4_slot_set_sampling(ctx, slot, seed & (2**64 - 1), temperature, top_k, top_p))
 
 
 def w4_slot_read_kv(ctx, slot: int, k, v, stream=None):

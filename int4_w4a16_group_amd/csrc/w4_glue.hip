@@ -877,6 +877,195 @@ hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, fl
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ sampling
+// Next token of each row by temperature / top-k / top-p sampling with a
+// counter-based draw, one 1024-thread work-group per row.  Steps (the same as
+// the CPU reference's):
+//   1. rank ids by (logit descending, id ascending), NaN as -inf, -0 as +0, and
+//      keep the first k = min(top_k, V): the k-th largest 16-bit ordered key is
+//      found by two 256-bin histogram passes (high byte, then the low byte
+//      within the bin that holds it); every id with a larger key is kept, and
+//      of the ids with that key the lowest ones (a block scan over contiguous
+//      id ranges, in id order) fill the remaining places;
+//   2. temperature 0 or k = 1: the first rank (greedy);
+//   3. e_r = exp((l_r - l_0) * (1/T)), c_r = e_0 + ... + e_r in rank order;
+//   4. nucleus: the shortest prefix 0..m with c_m >= top_p * c_{k-1};
+//   5. u = (z >> 40) * 2^-24 with z the output number pos of SplitMix64
+//      started at the row's seed; the first rank r <= m with u * c_m < c_r.
+// The draw depends on the stream's seed and position only, so a stream's
+// samples are the same in any batch.
+constexpr int kSampleThreads = 1024;
+
+__device__ __forceinline__ uint32_t sample_key(uint16_t h) {
+  if ((h & 0x7C00u) == 0x7C00u && (h & 0x03FFu)) h = 0xFC00u;  // NaN -> -inf
+  if (h == 0x8000u) h = 0;                                      // -0 -> +0
+  return (h & 0x8000u) ? (~(uint32_t)h & 0xFFFFu) : ((uint32_t)h | 0x8000u);
+}
+__device__ __forceinline__ float key_value(uint32_t key) {
+  const uint16_t h = (key & 0x8000u) ? (uint16_t)(key & 0x7FFFu) : (uint16_t)(~key & 0xFFFFu);
+  return h2f(h);
+}
+// SplitMix64 (Steele, Lea and Flood 2014; Vigna's splitmix64.c): output
+// number pos of the generator started at seed.
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t pos) {
+  uint64_t z = seed + (pos + 1ull) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Exclusive scan over the work-group (1024 threads) of a small count.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    base += i < w ? sh[i] : 0;
+    tot += sh[i];
+  }
+  *total = tot;
+  return base + incl - v;
+}
+
+__global__ void __launch_bounds__(kSampleThreads) k_sample(int V, const uint16_t* __restrict__ logits,
+                                                           const int32_t* __restrict__ params,
+                                                           const int32_t* __restrict__ pos,
+                                                           int32_t* __restrict__ next) {
+  __shared__ int hist[256];
+  __shared__ int s_scan[16];
+  __shared__ uint32_t c_key[kSampleMaxK];
+  __shared__ int c_id[kSampleMaxK];
+  __shared__ float r_val[kSampleMaxK];
+  __shared__ int r_id[kSampleMaxK];
+  __shared__ int s_b1, s_above, s_thr, s_cgt;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const uint16_t* row = logits + (size_t)b * V;
+  const int32_t* pr = params + (size_t)b * kSampleParams;
+  const float temp = __int_as_float(pr[0]), top_p = __int_as_float(pr[2]);
+  const int k = min(max(pr[1], 1), V);
+  const uint64_t seed = (uint64_t)(uint32_t)pr[3] | ((uint64_t)(uint32_t)pr[4] << 32);
+
+  // 1a. high-byte histogram, then the bin holding the k-th largest key
+  if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += kSampleThreads) atomicAdd(&hist[sample_key(row[i]) >> 8], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0, bin = 255;
+    for (; bin > 0 && acc + hist[bin] < k; --bin) acc += hist[bin];
+    s_b1 = bin;
+    s_above = acc;
+  }
+  __syncthreads();
+  const int b1 = s_b1;
+  // 1b. low-byte histogram within that bin: the k-th largest key itself
+  if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < V; i += kSampleThreads) {
+    const uint32_t key = sample_key(row[i]);
+    if ((int)(key >> 8) == b1) atomicAdd(&hist[key & 255u], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int acc = s_above, bin = 255;
+    for (; bin > 0 && acc + hist[bin] < k; --bin) acc += hist[bin];
+    s_thr = (b1 << 8) | bin;
+    s_cgt = acc;  // keys above the threshold key (< k)
+  }
+  __syncthreads();
+  const uint32_t thr = (uint32_t)s_thr;
+  const int cgt = s_cgt, need = k - cgt;
+  // 1c. candidates in id order: wave w owns the contiguous ids
+  // [w*per, (w+1)*per), its lanes reading consecutive ids (coalesced); in-wave
+  // order from ballots, across waves from a scan of the per-wave counts
+  const int lane = tid & 63, wv = tid >> 6;
+  const int per = (V + 15) / 16;
+  const int lo = min(wv * per, V), hi = min(lo + per, V);
+  int ngt = 0, neq = 0;
+  for (int i = lo + lane; i < hi; i += 64) {
+    const uint32_t key = sample_key(row[i]);
+    ngt += key > thr;
+    neq += key == thr;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    ngt += __shfl_xor(ngt, o, 64);
+    neq += __shfl_xor(neq, o, 64);
+  }
+  int tg = 0, te = 0;
+  // per-wave totals in lane 0 of each wave; the other lanes add zero
+  const int og = block_excl_scan(lane == 0 ? ngt : 0, s_scan, &tg);
+  const int oe = block_excl_scan(lane == 0 ? neq : 0, s_scan, &te);
+  int g = __shfl(og, 0, 64), e = __shfl(oe, 0, 64);
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int i0 = lo; i0 < hi; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t key = i < hi ? sample_key(row[i]) : 0u;
+    const bool isg = i < hi && key > thr, ise = i < hi && key == thr;
+    const unsigned long long mg = __ballot(isg), me = __ballot(ise);
+    if (isg) {
+      const int at = g + __popcll(mg & below);
+      c_key[at] = key;
+      c_id[at] = i;
+    }
+    if (ise) {
+      const int r = e + __popcll(me & below);
+      if (r < need) {
+        c_key[cgt + r] = key;
+        c_id[cgt + r] = i;
+      }
+    }
+    g += __popcll(mg);
+    e += __popcll(me);
+  }
+  __syncthreads();
+  // rank of each candidate: (key descending, id ascending)
+  if (tid < k) {
+    const uint32_t kk = c_key[tid];
+    const int ii = c_id[tid];
+    int r = 0;
+    for (int j = 0; j < k; ++j) r += (c_key[j] > kk || (c_key[j] == kk && c_id[j] < ii)) ? 1 : 0;
+    r_val[r] = key_value(kk);
+    r_id[r] = ii;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  int out = r_id[0];
+  if (temp > 0.0f && k > 1) {
+    const float inv_t = 1.0f / temp;
+    float c[kSampleMaxK];
+    float run = 0.0f;
+    const float l0 = r_val[0];
+    for (int r = 0; r < k; ++r) {
+      run = run + expf((r_val[r] - l0) * inv_t);
+      c[r] = run;
+    }
+    const float want = top_p * c[k - 1];
+    int m = 0;
+    while (m < k - 1 && c[m] < want) ++m;
+    const float u = (float)(uint32_t)(splitmix64_at(seed, (uint64_t)pos[b]) >> 40) * 0x1p-24f;
+    const float t = u * c[m];
+    int r = 0;
+    while (r < m && !(t < c[r])) ++r;
+    out = r_id[r];
+  }
+  next[b] = out;
+}
+
+hipError_t launch_sample(int B, int V, const uint16_t* logits, const int32_t* params, const int32_t* pos,
+                         int32_t* next, hipStream_t st) {
+  hipLaunchKernelGGL(k_sample, dim3(B), dim3(kSampleThreads), 0, st, V, logits, params, pos, next);
+  return hipGetLastError();
+}
+
 // Streaming-read probe: every 16-byte chunk of src is loaded once (four
 // loads in flight per thread, consecutive lanes on consecutive chunks), the
 // words are folded into one value per thread, and a work-group stores it only

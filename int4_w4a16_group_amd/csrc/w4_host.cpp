@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -121,6 +122,12 @@ BankPlan plan_bank(const w4_model_desc& d) {
   return p;
 }
 
+// Words uploaded with each step's rows: slot [Bm], position [Bm], sampling
+// parameters [Bm][kSampleParams], then the attention work list.
+size_t row_list_words(const w4_model_desc& d, int Bm, int cap) {
+  return (2 + (size_t)kSampleParams) * Bm + (size_t)Bm * attn_splits(cap - 1) * d.n_kv_heads;
+}
+
 WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   WsPlan w;
   size_t cur = 0;
@@ -165,14 +172,21 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.y = take(Bm * k * H * 2);
   w.logits = take((size_t)Bm * d.vocab * 2);
   w.next = take(Bm * 4);
-  // slot ids, positions, attention work list (every split of every row, per kv head)
-  w.rows = take((2 * Bm + (size_t)Bm * attn_splits(cap - 1) * d.n_kv_heads) * 4);
+  // slot ids, positions, sampling parameters, attention work list (every split
+  // of every row, per kv head): row_list_words
+  w.rows = take(row_list_words(d, Bm, cap) * 4);
   w.table = take((size_t)cap * (D / 2) * 8);
   w.total = cur;
   return w;
 }
 
 }  // namespace
+
+struct Sampling {  // per slot; temperature 0 = greedy
+  uint64_t seed = 0;
+  float temperature = 0.f, top_p = 1.f;
+  int32_t top_k = 1;
+};
 
 struct w4_ctx {
   w4_model_desc d{};
@@ -184,6 +198,8 @@ struct w4_ctx {
   WsPlan wp{};
   std::vector<int32_t> pos, prompt;
   std::vector<uint8_t> live, need_seed;
+  std::vector<Sampling> smp;
+  bool any_sampled = false;  // a row of the last upload samples
   bool dev_ready = false, table_ready = false;
   int device = -1;
   int32_t* pinned = nullptr;
@@ -192,7 +208,12 @@ struct w4_ctx {
   int32_t* flags = nullptr;
   int32_t* flags_dev = nullptr;
   int nsplits = 0;  // attention splits of the rows last uploaded
-  size_t row_words() const { return 2 * (size_t)Bm + (size_t)Bm * attn_splits(cap - 1) * d.n_kv_heads; }
+  // uploaded with each step's rows: slot [Bm], position [Bm], sampling
+  // parameters [Bm][kSampleParams], then the attention work list
+  size_t split_off() const { return (2 + (size_t)kSampleParams) * Bm; }
+  size_t row_words() const { return row_list_words(d, Bm, cap); }
+  const int32_t* dev_rows() { return reinterpret_cast<const int32_t*>(ws + wp.rows); }
+  const int32_t* dev_splits() { return dev_rows() + split_off(); }
   hipEvent_t ev[kRing] = {};      // the entry's upload has been read
   hipEvent_t ev_err[kRing] = {};  // the entry's invalid-token flags have arrived
   bool ev_used[kRing] = {};
@@ -372,12 +393,22 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
   }
   c->cur = i;
   int32_t* p = c->pinned + (size_t)i * c->row_words();
-  int32_t* split = p + 2 * c->Bm;
+  int32_t* split = p + c->split_off();
+  int32_t* prm = p + 2 * c->Bm;
+  bool sampled = false;
   int mp = 0, n = 0;
   for (int b = 0; b < B; ++b) {
     const int pos = c->pos[slots[b]];
     p[b] = slots[b];
     p[c->Bm + b] = pos;
+    const Sampling& sp = c->smp[slots[b]];
+    int32_t* q = prm + (size_t)b * kSampleParams;
+    std::memcpy(&q[0], &sp.temperature, 4);
+    q[1] = sp.top_k;
+    std::memcpy(&q[2], &sp.top_p, 4);
+    q[3] = (int32_t)(uint32_t)(sp.seed & 0xFFFFFFFFu);
+    q[4] = (int32_t)(uint32_t)(sp.seed >> 32);
+    sampled = sampled || sp.temperature > 0.f;
     mp = std::max(mp, pos);
   }
   // Attention work list (stream b << 16 | split << 8 | kv head), the splits
@@ -392,7 +423,10 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
         if (std::min(W, nch - W * sp) == cnt)
           for (int g = 0; g < c->d.n_kv_heads; ++g) split[n++] = (b << 16) | (sp << 8) | g;
     }
-  HIPCHK(c, hipMemcpyAsync(c->W<int32_t>(c->wp.rows), p, sizeof(int32_t) * (2 * c->Bm + n), hipMemcpyHostToDevice, st));
+  if (c->split_off() + n > c->row_words()) return fail(c, W4_E_INVALID, "row list exceeds its workspace region");
+  HIPCHK(c, hipMemcpyAsync(c->W<int32_t>(c->wp.rows), p, sizeof(int32_t) * (c->split_off() + n),
+                           hipMemcpyHostToDevice, st));
+  c->any_sampled = sampled;
   HIPCHK(c, hipEventRecord(c->ev[i], st));
   c->ev_used[i] = true;
   c->nsplits = n;
@@ -451,7 +485,7 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
     next_span = c->Bk<uint8_t>(Ln.attn_norm);
     next_bytes = Ln.gate.tiles - Ln.attn_norm;
   }
-  LCHK(c, 1, launch_attention(B, l, d.n_q_heads, kv, slot, pos, pos + c->Bm, c->nsplits, qkv, nqkv,
+  LCHK(c, 1, launch_attention(B, l, d.n_q_heads, kv, slot, pos, c->dev_splits(), c->nsplits, qkv, nqkv,
                               qkv + (size_t)d.n_q_heads * d.head_dim, qkv + (size_t)(d.n_q_heads + d.n_kv_heads) * d.head_dim,
                               nqkv, c->W<float2>(c->wp.table), c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
                               c->W<unsigned>(c->wp.aticket), o, st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
@@ -552,6 +586,7 @@ int w4_create(const w4_model_desc* d, int32_t max_streams, int32_t cap, void* ar
   c->prompt.assign(max_streams, 0);
   c->live.assign(max_streams, 0);
   c->need_seed.assign(max_streams, 0);
+  c->smp.assign(max_streams, Sampling{});
   *out = c;
   return W4_OK;
 }
@@ -630,6 +665,7 @@ int w4_slot_alloc(w4_ctx* c, int32_t prompt_len, int32_t max_new, int32_t* slot_
       c->pos[s] = 0;
       c->prompt[s] = prompt_len;
       c->need_seed[s] = prompt_len > 0;
+      c->smp[s] = Sampling{};  // greedy until set
       *slot_out = s;
       return W4_OK;
     }
@@ -648,6 +684,17 @@ int w4_slot_seed(w4_ctx* c, int32_t slot, const void* k, const void* v, void* st
                          static_cast<const uint16_t*>(v), st));
   c->need_seed[slot] = 0;
   c->pos[slot] = c->prompt[slot];
+  return W4_OK;
+}
+
+int w4_slot_set_sampling(w4_ctx* c, int32_t slot, uint64_t seed, float temperature, int32_t top_k, float top_p) {
+  if (!c) return W4_E_INVALID;
+  if (slot < 0 || slot >= c->Bm || !c->live[slot]) return fail(c, W4_E_BAD_SLOT, "slot is not live");
+  if (!(temperature >= 0.f) || !std::isfinite(temperature))
+    return fail(c, W4_E_INVALID, "temperature must be finite and >= 0");
+  if (top_k < 1 || top_k > kSampleMaxK) return fail(c, W4_E_INVALID, "top_k must be in [1, 64]");
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(c, W4_E_INVALID, "top_p must be in (0, 1]");
+  c->smp[slot] = Sampling{seed, temperature, top_p, top_k};
   return W4_OK;
 }
 
@@ -721,8 +768,15 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
     ProfScope ps(c, W4_K_DENSE, st);
     LCHK(c, 1, launch_gemm(c->mat(c->bp.lm), B, xp, d.hidden, lg, d.vocab, EPI_F16, st, R));
   }
-  LCHK(c, 1, launch_argmax(B, d.vocab, lg, next, c->W<float>(c->wp.amax_v), c->W<int32_t>(c->wp.amax_i),
-                            c->W<unsigned>(c->wp.amax_ticket), st));
+  // greedy rows only: the split argmax; any sampled row: the sampler for every
+  // row (a greedy row's id is the same either way: the first rank)
+  if (c->any_sampled) {
+    const int32_t* rows = c->dev_rows();
+    LCHK(c, 1, launch_sample(B, d.vocab, lg, rows + 2 * c->Bm, rows + c->Bm, next, st));
+  } else {
+    LCHK(c, 1, launch_argmax(B, d.vocab, lg, next, c->W<float>(c->wp.amax_v), c->W<int32_t>(c->wp.amax_i),
+                              c->W<unsigned>(c->wp.amax_ticket), st));
+  }
   // the embedding wrote the step's invalid-token flags into its ring entry;
   // a later call reads them once this event has passed (see poll_errors)
   {
@@ -831,7 +885,7 @@ int w4_attn_decode(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, co
   const int32_t* pos = slot + c->Bm;
   KV kv = c->kv();
   const int Hq = c->d.n_q_heads, Hkv = c->d.n_kv_heads, D = c->d.head_dim;
-  LCHK(c, 1, launch_attention(B, layer, Hq, kv, slot, pos, pos + c->Bm, c->nsplits, static_cast<const uint16_t*>(q),
+  LCHK(c, 1, launch_attention(B, layer, Hq, kv, slot, pos, c->dev_splits(), c->nsplits, static_cast<const uint16_t*>(q),
                               Hq * D, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), Hkv * D,
                               nullptr, c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
                               c->W<unsigned>(c->wp.aticket), static_cast<uint16_t*>(o), st,

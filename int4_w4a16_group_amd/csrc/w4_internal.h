@@ -106,6 +106,13 @@ hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const
 // [B][8] hold the split partials, ticket [B] is zero before and after.
 hipError_t launch_argmax(int B, int V, const uint16_t* logits, int32_t* next, float* part_v, int32_t* part_i,
                          unsigned* ticket, hipStream_t st);
+// Next token by temperature / top-k / top-p sampling (w4_glue.hip): params
+// [B][kSampleParams] = (temperature bits, top_k, top_p bits, seed low, seed
+// high) per row, pos [B] the row's position (the draw's counter).
+constexpr int kSampleMaxK = 64;
+constexpr int kSampleParams = 5;
+hipError_t launch_sample(int B, int V, const uint16_t* logits, const int32_t* params, const int32_t* pos,
+                         int32_t* next, hipStream_t st);
 
 struct KV {
   uint16_t* K;   // [L][S][Hkv][cap/64][64*D], MFMA operand order (w4_attn.hip)

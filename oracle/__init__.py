@@ -71,6 +71,12 @@ def lib():
                                       C.c_void_p, C.c_void_p, _i32p, C.c_void_p, C.c_void_p]
         L.orc_attn_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
                                     _u16p, _u16p, _u16p, _u16p]
+        L.orc_splitmix.restype = C.c_uint64
+        L.orc_splitmix.argtypes = [C.c_uint64, C.c_uint64]
+        L.orc_draw.restype = C.c_float
+        L.orc_draw.argtypes = [C.c_uint64, C.c_uint64]
+        L.orc_sample.restype = C.c_int32
+        L.orc_sample.argtypes = [C.c_int, _u16p, C.c_float, C.c_int, C.c_float, C.c_uint64, C.c_uint64]
         L.orc_threads.restype = C.c_int
         L.orc_set_threads.argtypes = [C.c_int]
         L.orc_init()
@@ -207,6 +213,23 @@ def _force(force, shape):
     f = _c(force, np.int32)
     assert f.shape == shape, (f.shape, shape)
     return f
+
+
+def splitmix(seed: int, pos: int) -> int:
+    """Output number pos of the SplitMix64 generator started at seed."""
+    return int(lib().orc_splitmix(seed & (2**64 - 1), pos))
+
+
+def draw(seed: int, pos: int) -> float:
+    """The sampler's uniform draw in [0, 1) for (seed, position)."""
+    return float(lib().orc_draw(seed & (2**64 - 1), pos))
+
+
+def sample(logits: np.ndarray, temperature: float, top_k: int, top_p: float, seed: int, pos: int) -> int:
+    """Next token from one fp16 logits row (bits [V]) by temperature / top-k / top-p sampling."""
+    row = _c(logits, np.uint16)
+    return int(lib().orc_sample(row.size, row, float(temperature), int(top_k), float(top_p),
+                                seed & (2**64 - 1), int(pos)))
 
 
 def bucket(ids: np.ndarray, E: int):

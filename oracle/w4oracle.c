@@ -494,6 +494,82 @@ EXPORT void orc_decode_step(const orc_model* m, orc_arena* a, int B, const int32
   free(lg);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Non-greedy sampling of the next token (beyond the pages' greedy decoding,  */
+/* which "Batched-concurrent 4-bit serving on Apple Silicon", section 5,      */
+/* names as not validated).  Readings: the usual temperature / top-k / top-p  */
+/* (nucleus) sampling, taken in this order:                                   */
+/*  1. rank every id by (logit descending, id ascending), NaN ranking as      */
+/*     -inf; keep the first top_k;                                            */
+/*  2. temperature 0, or top_k 1: the first id (greedy);                      */
+/*  3. weights e_r = exp((l_r - l_0) * (1/T)) over the kept ranks, running     */
+/*     sums c_r = e_0 + ... + e_r in rank order (fp32);                       */
+/*  4. nucleus: the shortest prefix 0..m with c_m >= top_p * c_{k-1};          */
+/*  5. the draw u in [0, 1): the first rank r <= m with u * c_m < c_r, else m. */
+/* The draw is counter-based, so a stream's samples depend only on its own    */
+/* seed and positions: u = (z >> 40) * 2^-24, z the output number pos of the  */
+/* SplitMix64 generator started at seed (Steele, Lea and Flood 2014; Vigna's  */
+/* splitmix64.c): z = seed + (pos + 1) * 0x9E3779B97F4A7C15, then            */
+/* z ^= z >> 30, z *= 0xBF58476D1CE4E5B9, z ^= z >> 27,                       */
+/* z *= 0x94D049BB133111EB, z ^= z >> 31.                                     */
+/* ------------------------------------------------------------------------ */
+EXPORT uint64_t orc_splitmix(uint64_t seed, uint64_t pos) {
+  uint64_t z = seed + (pos + 1u) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+EXPORT float orc_draw(uint64_t seed, uint64_t pos) {
+  return (float)(orc_splitmix(seed, pos) >> 40) * 0x1p-24f;
+}
+
+static float rank_value(uint16_t h) {
+  float v = HF(h);
+  return v != v ? -INFINITY : v;
+}
+
+EXPORT int32_t orc_sample(int V, const uint16_t* logits, float temperature, int top_k, float top_p,
+                          uint64_t seed, uint64_t pos) {
+  h2f_init();
+  int k = top_k < V ? top_k : V;
+  if (k < 1) k = 1; /* V >= 1 and top_k >= 1 by contract */
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  unsigned char* taken = (unsigned char*)calloc((size_t)V, 1);
+  for (int r = 0; r < k; r++) { /* selection in rank order: larger value, then lower id */
+    int best = -1;
+    for (int i = 0; i < V; i++) {
+      if (taken[i]) continue;
+      if (best < 0 || rank_value(logits[i]) > rank_value(logits[best])) best = i;
+    }
+    taken[best] = 1;
+    ids[r] = best;
+  }
+  int32_t out = ids[0];
+  if (temperature > 0.0f && k > 1) {
+    float inv_t = 1.0f / temperature;
+    float* c = (float*)malloc(sizeof(float) * (size_t)k);
+    float l0 = rank_value(logits[ids[0]]);
+    float run = 0.0f;
+    for (int r = 0; r < k; r++) {
+      float e = expf((rank_value(logits[ids[r]]) - l0) * inv_t);
+      run = run + e;
+      c[r] = run;
+    }
+    int m = 0;
+    float need = top_p * c[k - 1];
+    while (m < k - 1 && c[m] < need) m++;
+    float t = orc_draw(seed, pos) * c[m];
+    int r = 0;
+    while (r < m && !(t < c[r])) r++;
+    out = ids[r];
+    free(c);
+  }
+  free(ids);
+  free(taken);
+  return out;
+}
+
 /* Attention-only step (slot-indexed GQA decode with a KV append), B streams:
  * q [B][Hq][D], k_new/v_new [B][Hkv][D] are written at positions[b] of
  * slots[b] in layer l, then attention over 0..positions[b] (positions[b] + 1

@@ -183,3 +183,21 @@ def test_read_kv_and_error_check_argument_checks():
         assert e.value.status == L.W4_E_INVALID
     finally:
         L.w4_destroy(c)
+
+
+def test_sampling_parameters_are_validated():
+    c = make_ctx()
+    try:
+        with pytest.raises(L.W4Error) as e:
+            L.w4_slot_set_sampling(c, 0, 1, 0.7, 8, 0.9)               # slot not live
+        assert e.value.status == L.W4_E_BAD_SLOT
+        s = L.w4_slot_alloc(c, 0, 4)
+        for temp, k, p in ((-0.1, 8, 0.9), (float("nan"), 8, 0.9), (float("inf"), 8, 0.9), (0.7, 0, 0.9),
+                           (0.7, 65, 0.9), (0.7, 8, 0.0), (0.7, 8, 1.5)):
+            with pytest.raises(L.W4Error) as e:
+                L.w4_slot_set_sampling(c, s, 1, temp, k, p)
+            assert e.value.status == L.W4_E_INVALID, (temp, k, p)
+        L.w4_slot_set_sampling(c, s, 2**64 - 1, 0.7, 64, 1.0)
+        L.w4_slot_set_sampling(c, s, 0, 0.0, 1, 1.0)                   # back to greedy
+    finally:
+        L.w4_destroy(c)
