@@ -69,6 +69,8 @@ def lib():
         L.orc_embed.argtypes = [C.POINTER(_Model), C.c_int, _i32p, _u16p]
         L.orc_decode_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, _i32p, _i32p, _i32p,
                                       C.c_void_p, C.c_void_p, _i32p, C.c_void_p, C.c_void_p]
+        L.orc_prefill.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, C.c_void_p,
+                                  _u16p, _i32p, C.c_void_p]
         L.orc_attn_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
                                     _u16p, _u16p, _u16p, _u16p]
         L.orc_splitmix.restype = C.c_uint64
@@ -357,6 +359,22 @@ def decode_step(model: Model, arena: Arena, slots, positions, tokens, want_logit
     lib().orc_decode_step(C.byref(model.m), C.byref(arena.a), B, slots, positions, tokens, _ptr(f),
                           _ptr(logits), nxt, ids.ctypes.data, _ptr(rl))
     return logits, nxt, ids, rl
+
+
+def prefill(model: Model, arena: Arena, slot: int, tokens, force=None, want_ids=False):
+    """The prompt tokens through the model at positions 0..P-1 of the slot (its K/V
+    written there); returns the last token's fp16 logits [V], its greedy id and,
+    if asked, the expert ids [n_layers, P, top_k].  force: ranked expert ids
+    [n_layers, P, top_k] replacing every top-k, or None."""
+    tokens = _c(tokens, np.int32)
+    d = model.desc
+    P = len(tokens)
+    f = _force(force, (d.n_layers, P, d.top_k))
+    logits = np.empty(d.vocab, np.uint16)
+    nxt = np.empty(1, np.int32)
+    ids = np.empty((d.n_layers, P, d.top_k), np.int32) if want_ids else None
+    lib().orc_prefill(C.byref(model.m), C.byref(arena.a), int(slot), P, tokens, _ptr(f), logits, nxt, _ptr(ids))
+    return logits, int(nxt[0]), ids
 
 
 def attn_step(model: Model, arena: Arena, layer: int, slots, positions, q, k_new, v_new):

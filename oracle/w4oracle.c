@@ -494,6 +494,36 @@ EXPORT void orc_decode_step(const orc_model* m, orc_arena* a, int B, const int32
   free(lg);
 }
 
+/* Prefill of one joining stream ("Per-stream KV-slot isolation ...", section
+ * 1: a stream is seeded once, at join): its prompt tokens[0..P-1] go through
+ * the model at positions 0..P-1 of its slot, in order, each exactly as one
+ * decode step of that stream alone (the causal definition: token t attends
+ * to the K/V of tokens 0..t).  The slot then holds the prompt's K/V; the
+ * output is the last token's logits fp16 [V] (next-token distribution) and
+ * its greedy id.  force [L][P][k]: ranked expert ids replacing every top-k,
+ * or NULL; ids_out [L][P][k] optional. */
+EXPORT void orc_prefill(const orc_model* m, orc_arena* a, int slot, int P, const int32_t* tokens,
+                        const int32_t* force, uint16_t* logits, int32_t* next, int32_t* ids_out) {
+  h2f_init();
+  int H = m->hidden, V = m->vocab, g = m->group, k = m->top_k, L = m->n_layers;
+  uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+  uint16_t* hn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
+  for (int t = 0; t < P; t++) {
+    embed_row(m, tokens[t], h);
+    for (int l = 0; l < L; l++)
+      layer_one(m, a, l, slot, t, h, force ? force + ((size_t)l * P + t) * k : NULL,
+                ids_out ? ids_out + ((size_t)l * P + t) * k : NULL, NULL);
+  }
+  orc_rmsnorm(H, h, m->final_norm, m->rms_eps, hn);
+  orc_w4_gemm(1, V, H, g, hn, m->lm_p, m->lm_s, logits, NULL);
+  int best = 0;
+  for (int v = 1; v < V; v++)
+    if (HF(logits[v]) > HF(logits[best])) best = v;
+  *next = best;
+  free(h);
+  free(hn);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Non-greedy sampling of the next token (beyond the pages' greedy decoding,  */
 /* which "Batched-concurrent 4-bit serving on Apple Silicon", section 5,      */
