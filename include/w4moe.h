@@ -134,6 +134,26 @@ int w4_slot_position(const w4_ctx* ctx, int32_t slot, int32_t* pos_out);
 /* Advance the positions of n distinct live slots by one (used with the
  * per-layer entry points, which do not move positions). */
 int w4_slots_advance(w4_ctx* ctx, int32_t n, const int32_t* slots_host);
+/* Seed-at-join prefill ("Per-stream KV-slot isolation ...", section 1: a
+ * stream's KV is seeded once, at join), through the model itself: a slot
+ * allocated with prompt_len = P > 0 (and not yet seeded) gets the K/V of its
+ * prompt tokens_dev int32 [P] at positions 0..P-1, computed causally layer by
+ * layer over all P rows (the dense products as M = P row GEMMs, causal
+ * attention over the slot, the routed experts as one grouped product per
+ * layer), and its position becomes P.  Outputs: the last prompt token's fp16
+ * logits [vocab] (logits_dev may be NULL), the next token id int32 [1]
+ * (next_dev may be NULL; greedy, or the slot's sampling at draw counter P-1),
+ * and optionally the expert ids route_ids_dev int32 [n_layers][P][top_k].
+ * workspace_dev: caller-owned, 256-byte aligned, at least
+ * w4_prefill_workspace_bytes(desc, P, ctx_cap) bytes (ws_bytes gives its
+ * size).  Limits: P * top_k <= 16384 and n_experts * ceil(P / 32) * 4 +
+ * P * top_k <= 65536 (W4_E_UNSUPPORTED beyond).  An out-of-range token id is
+ * reported like the decode step's (sticky W4_E_INVALID).  The call replaces
+ * w4_slot_seed for that slot. */
+size_t w4_prefill_workspace_bytes(const w4_model_desc* desc, int32_t max_prompt, int32_t ctx_cap);
+int w4_slot_prefill(w4_ctx* ctx, int32_t slot, const int32_t* tokens_dev, void* workspace_dev, size_t ws_bytes,
+                    void* logits_dev, int32_t* next_dev, int32_t* route_ids_dev, void* stream);
+
 /* Sampling of a live slot's next tokens (beyond the pages' greedy decoding;
  * the batched-serving page, section 5, names non-greedy sampling as not
  * validated there).  temperature 0 (the default after w4_slot_alloc) is

@@ -50,6 +50,8 @@ _SIGS = {
     "w4_slots_advance": (C.c_int, [_vp, _i32, C.POINTER(_i32)]),
     "w4_slot_read_kv": (C.c_int, [_vp, _i32, _vp, _vp, _vp]),
     "w4_slot_set_sampling": (C.c_int, [_vp, _i32, C.c_uint64, C.c_float, _i32, C.c_float]),
+    "w4_prefill_workspace_bytes": (_sz, [C.POINTER(w4_model_desc), _i32, _i32]),
+    "w4_slot_prefill": (C.c_int, [_vp, _i32, _vp, _vp, _sz, _vp, _vp, _vp, _vp]),
     "w4_check_errors": (C.c_int, [_vp]),
     "w4_read_probe": (C.c_int, [_vp, _sz, _vp, _i32, _vp]),
     "w4_route_noalloc": (C.c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -182,6 +184,17 @@ def w4_slot_position(ctx, slot: int) -> int:
 def w4_slots_advance(ctx, slots):
     arr, n = _i32arr(slots)
     return _check(ctx, lib().w4_slots_advance(ctx, n, arr))
+
+
+def w4_prefill_workspace_bytes(desc, max_prompt: int, cap: int) -> int:
+    d = desc_of(desc)
+    return lib().w4_prefill_workspace_bytes(C.byref(d), max_prompt, cap)
+
+
+def w4_slot_prefill(ctx, slot: int, tokens, workspace, ws_bytes: int, logits=None, next_ids=None, route_ids=None,
+                    stream=None):
+    return _check(ctx, lib().w4_slot_prefill(ctx, slot, _p(tokens), _p(workspace), ws_bytes, _p(logits),
+                                             _p(next_ids), _p(route_ids), _s(stream)))
 
 
 def w4_slot_set_sampling(ctx, slot: int, seed: int, temperature: float, top_k: int, top_p: float):

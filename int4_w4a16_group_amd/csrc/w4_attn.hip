@@ -104,6 +104,30 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
   return hipGetLastError();
 }
 
+// Prefill of one layer: block (position i, kv head g); the key pair (t, t + D/2)
+// rotated at i with the same arithmetic as the decode step's append.
+__global__ void k_prefill_kv(int layer, int slot, KV kv, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                             int ld, const float2* __restrict__ table) {
+  const int i = blockIdx.x, g = blockIdx.y, D = kv.D, t = threadIdx.x;
+  if (t >= D / 2) return;
+  const size_t base = kv_base(kv, layer, slot, g);
+  const uint16_t* kp = k + (size_t)i * ld + g * D;
+  const uint16_t* vp = v + (size_t)i * ld + g * D;
+  const float x0 = h2f(kp[t]), x1 = h2f(kp[t + D / 2]);
+  const float2 cs = table[(size_t)i * (D / 2) + t];
+  kv.K[base + k_off(D, i, t)] = f2h(x0 * cs.x - x1 * cs.y);
+  kv.K[base + k_off(D, i, t + D / 2)] = f2h(x0 * cs.y + x1 * cs.x);
+  kv.VT[base + v_off(D, i, t)] = vp[t];
+  kv.VT[base + v_off(D, i, t + D / 2)] = vp[t + D / 2];
+}
+
+hipError_t launch_prefill_kv(int P, int layer, int slot, const KV& kv, const uint16_t* k, const uint16_t* v, int ld,
+                             const float2* table, hipStream_t st) {
+  if (P <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prefill_kv, dim3(P, kv.Hkv), dim3(64), 0, st, layer, slot, kv, k, v, ld, table);
+  return hipGetLastError();
+}
+
 // The inverse of k_seed: positions 0..P-1 of a slot -> canonical k, v [L][P][Hkv][D].
 __global__ void k_read_kv(int P, int slot, KV kv, uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
   const int p0 = blockIdx.x * 64;
@@ -290,7 +314,9 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
         for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
     };
     if (VE) load_v();
-    const bool own = c == (p >> 6);  // this wave's chunk holds position p
+    // this wave's chunk holds position p and the launch appends (knew given);
+    // a prefill launch finds every position's K/V in the arena already
+    const bool own = a.knew && c == (p >> 6);
     // The wave whose chunk holds position p: this step's k (rotated) and v go
     // into the arena at p and replace what the loads above read there.
     if (own) {

@@ -95,6 +95,9 @@ struct DenseArgs {
   int xrows;  // XP kernels: x is a panel with this many rows (see load_x_panel)
 };
 
+// Row blocks: work-group row blockIdx.y takes rows 16*MT*blockIdx.y .. +16*MT-1
+// of a row-major x (a panel has one block); an output row depends on its own
+// input row only, so the blocking never changes a result.
 template <int MT, int NCH, int G, int EPI, int LB, bool XP>
 __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   extern __shared__ float red[];  // two buffers of [NW][MT][64][4]
@@ -104,6 +107,15 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   const int kbase = w * NCH * 128;
   const int G0 = gridDim.x;
   if ((int)blockIdx.x >= a.ntiles) return;
+  const int rb = XP ? 0 : (int)blockIdx.y * MT * 16;
+  a.B = min(a.B - rb, MT * 16);  // rows of this block
+  if (!XP) {
+    a.x += (size_t)rb * a.ldx;
+    if (EPI == EPI_F32)
+      a.y = reinterpret_cast<float*>(a.y) + (size_t)rb * a.ldy;
+    else
+      a.y = reinterpret_cast<uint16_t*>(a.y) + (size_t)rb * a.ldy;
+  }
   XRegs<MT, NCH * 4> x;
   if (XP)
     load_x_panel<MT, NCH>(x, a.x, a.xrows, a.B, kbase, lane);
@@ -271,8 +283,10 @@ hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y,
   const int nch = nch_for(w.K);
   const int NW = w.K / (nch * 128);
   const int MT = B > 16 ? 2 : 1;
+  if (xrows > 0 && B > 32) return hipErrorInvalidValue;  // a panel holds at most 32 rows
   const DenseKernel k = xrows > 0 ? pick<true>(MT, nch, w.g, epi, NW) : pick<false>(MT, nch, w.g, epi, NW);
   const int ntiles = w.ntiles();
+  const int row_blocks = xrows > 0 ? 1 : (B + 31) / 32;  // 32-row blocks of a longer row-major x
   // enough work-groups to fill 256 CUs at ~16 waves each, each looping over
   // tiles; a mid-size product with at most 8 waves per tile takes two tiles
   // per work-group (the x slices in registers serve both: measured 6.2 us
@@ -281,7 +295,7 @@ hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y,
   int grid = std::min(ntiles, target);
   if (NW <= 8 && ntiles >= 256 && ntiles <= 1024) grid = (ntiles + 1) / 2;
   DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy, xrows};
-  w4_launch(k, dim3(grid), dim3(NW * 64), 2 * NW * MT * 1024, st, a);
+  w4_launch(k, dim3(grid, row_blocks), dim3(NW * 64), 2 * NW * MT * 1024, st, a);
   return hipGetLastError();
 }
 
@@ -374,6 +388,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   int4* lrec = reinterpret_cast<int4*>(red + 2 * bufsz);
   if (tid < a.units_cap) lrec[tid] = rec0;
   if (tid + nth < a.units_cap) lrec[tid + nth] = rec1;
+  for (int i = tid + 2 * nth; i < a.units_cap; i += nth) lrec[i] = a.units[i];  // prefill: more records
   __syncthreads();
 
   // item f's tile into a stage (past the range: the WG's last tile again)
@@ -551,8 +566,10 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   a.ncu = cu_count();
   a.dshare = gateup ? 75 : 0;  // measured: gate/up 38.5 us at 60-120 against 40.0 at 0
   MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);
-  if (r.units_cap > kMaxUnits || r.units_cap > 2 * NW * 64) return hipErrorInvalidValue;
-  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)kMaxUnits * 16;
+  if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
+  // the records of every unit in LDS (at most kMaxUnits in a decode step, whose
+  // launch shape is kept; a prefill can have more)
+  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)std::max(r.units_cap, kMaxUnits) * 16;
   const int grid = resident_grid(k, NW * 64, shm);
   w4_launch(k, dim3(grid), dim3(NW * 64), (uint32_t)shm, st, a);
   return hipGetLastError();

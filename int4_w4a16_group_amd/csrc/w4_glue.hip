@@ -271,10 +271,10 @@ __device__ __forceinline__ uint32_t sort_key(float v) {
 // Top-k of one row held by one wave (lane owns experts lane + 64j): ranks by
 // logit descending, ties to the lower id; w_r = exp(l_r - l_0) / sum, summed in
 // rank order.  Radix select of the k-th largest key over wave ballots, then
-// each selected expert's rank among the selected.
-template <int EPL>
-__device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane, int32_t* ids_out, float* w_out,
-                                         int32_t* s_ids, float* s_lv, unsigned* s_mask, int b) {
+// each selected expert's rank among the selected.  sel(e, rank, w) records one
+// selected expert (called by the lane that owns it).
+template <int EPL, class Sel>
+__device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane, Sel sel) {
   uint32_t key[EPL];
   bool valid[EPL];
 #pragma unroll
@@ -296,14 +296,14 @@ __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane
       need -= cnt;
   }
   // selected: key > T, plus the `need` lowest-index experts with key == T
-  bool sel[EPL];
+  bool sl[EPL];
   int before = 0;  // equal keys at lower indices in earlier slots
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const bool eq = valid[j] && key[j] == prefix;
     const unsigned long long m = __ballot(eq);
     const int below = before + __popcll(m & ((1ull << lane) - 1ull));
-    sel[j] = valid[j] && (key[j] > prefix || (eq && below < need));
+    sl[j] = valid[j] && (key[j] > prefix || (eq && below < need));
     before += __popcll(m);
   }
   // rank of each selected expert among the selected
@@ -312,7 +312,7 @@ __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane
   for (int j = 0; j < EPL; ++j) rank[j] = 0;
 #pragma unroll
   for (int j2 = 0; j2 < EPL; ++j2) {
-    unsigned long long m = __ballot(sel[j2]);
+    unsigned long long m = __ballot(sl[j2]);
     while (m) {
       const int L = __ffsll((long long)m) - 1;
       m &= m - 1;
@@ -321,7 +321,7 @@ __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane
 #pragma unroll
       for (int j = 0; j < EPL; ++j) {
         const int e = lane + 64 * j;
-        rank[j] += (sel[j] && (k2 > key[j] || (k2 == key[j] && e2 < e))) ? 1 : 0;
+        rank[j] += (sl[j] && (k2 > key[j] || (k2 == key[j] && e2 < e))) ? 1 : 0;
       }
     }
   }
@@ -331,7 +331,7 @@ __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane
     float v = 0.f;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
-      const unsigned long long m = __ballot(sel[j] && rank[j] == r);
+      const unsigned long long m = __ballot(sl[j] && rank[j] == r);
       if (m) v = __shfl(valid[j] ? lg[min(lane + 64 * j, E - 1)] : 0.f, __ffsll((long long)m) - 1, 64);
     }
     if (v != v) v = -INFINITY;
@@ -340,16 +340,12 @@ __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane
   }
 #pragma unroll
   for (int j = 0; j < EPL; ++j)
-    if (sel[j]) {
+    if (sl[j]) {
       const int e = lane + 64 * j;
       float v = lg[e];
       if (v != v) v = -INFINITY;
-      ids_out[b * k + rank[j]] = e;
-      w_out[b * k + rank[j]] = expf(v - l0) / sum;
-      s_ids[b * k + rank[j]] = e;
-      atomicOr(&s_mask[e], 1u << b);
+      sel(e, rank[j], expf(v - l0) / sum);
     }
-  (void)s_lv;
 }
 
 // Exclusive prefix sum over the wave of small non-negative values (< 2^BITS),
@@ -458,12 +454,18 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
   __syncthreads();
   // top-k per row, one wave per row
   for (int b = w; b < B; b += 16) {
+    auto sel = [&](int e, int r, float wt) {
+      o.ids[b * k + r] = e;
+      o.w[b * k + r] = wt;
+      s_ids[b * k + r] = e;
+      atomicOr(&s_mask[e], 1u << b);
+    };
     if (E <= 64)
-      topk_row<1>(s_lg + b * E, E, k, lane, o.ids, o.w, s_ids, nullptr, s_mask, b);
+      topk_row<1>(s_lg + b * E, E, k, lane, sel);
     else if (E <= 128)
-      topk_row<2>(s_lg + b * E, E, k, lane, o.ids, o.w, s_ids, nullptr, s_mask, b);
+      topk_row<2>(s_lg + b * E, E, k, lane, sel);
     else
-      topk_row<4>(s_lg + b * E, E, k, lane, o.ids, o.w, s_ids, nullptr, s_mask, b);
+      topk_row<4>(s_lg + b * E, E, k, lane, sel);
   }
   __syncthreads();
   bucket_core(E, k, B, s_ids, BucketLds{s_mask, s_off, s_ub, s_tot, s_ur}, o);
@@ -471,6 +473,104 @@ __global__ void __launch_bounds__(1024) k_route(const float* __restrict__ logits
 
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st) {
   hipLaunchKernelGGL(k_route, dim3(1), dim3(1024), 0, st, logits, B, E, k, o);
+  return hipGetLastError();
+}
+
+// Routing of the P rows of a prefill in one 1024-thread work-group, into the
+// same outputs as k_route: top-k softmax of each row (one wave per row, the
+// same arithmetic as k_route), then the bucketing by (expert, row): LDS holds
+// for every expert a P-bit mask of the rows that chose it and, per (row,
+// rank), the expert id as one byte; a pair's place within its expert is the
+// number of lower rows in that expert's mask (a prefix popcount), so the
+// pairs come out ordered by (expert, row) as in the decode step.
+__global__ void __launch_bounds__(1024) k_route_prefill(const float* __restrict__ logits, int P, int E, int k,
+                                                        RouteOut o) {
+  extern __shared__ uint32_t s_pm[];  // [E][W] row masks, then P*k expert bytes
+  __shared__ int s_cnt[kRouteMaxE], s_off[kRouteMaxE], s_ub[kRouteMaxE];
+  const int W = (P + 31) / 32;
+  uint8_t* s_e = reinterpret_cast<uint8_t*>(s_pm + (size_t)E * W);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < E * W; i += blockDim.x) s_pm[i] = 0u;
+  __syncthreads();
+  for (int b = w; b < P; b += 16) {
+    auto sel = [&](int e, int r, float wt) {
+      o.ids[b * k + r] = e;
+      o.w[b * k + r] = wt;
+      s_e[b * k + r] = (uint8_t)e;
+      atomicOr(&s_pm[e * W + (b >> 5)], 1u << (b & 31));
+    };
+    const float* lg = logits + (size_t)b * E;
+    if (E <= 64)
+      topk_row<1>(lg, E, k, lane, sel);
+    else if (E <= 128)
+      topk_row<2>(lg, E, k, lane, sel);
+    else
+      topk_row<4>(lg, E, k, lane, sel);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int c = 0;
+    for (int j = 0; j < W; ++j) c += __popc(s_pm[e * W + j]);
+    s_cnt[e] = c;
+  }
+  __syncthreads();
+  if (tid == 0) {  // exclusive scans over the experts, in expert order
+    int off = 0, ub = 0, nused = 0;
+    for (int e = 0; e < E; ++e) {
+      const int c = s_cnt[e];
+      s_off[e] = off;
+      s_ub[e] = ub;
+      if (o.counts) o.counts[e] = c;
+      if (o.offsets) o.offsets[e] = off;
+      if (c > 0) o.used[nused++] = e;
+      off += c;
+      ub += (c + 15) >> 4;
+    }
+    if (o.offsets) o.offsets[E] = off;
+    *o.n_used = nused;
+    *o.n_units = ub;
+  }
+  __syncthreads();
+  for (int i = tid; i < P * k; i += blockDim.x) {
+    const int b = i / k, e = s_e[i];
+    const uint32_t* m = s_pm + (size_t)e * W;
+    int r = __popc(m[b >> 5] & ((1u << (b & 31)) - 1u));
+    for (int j = 0; j < (b >> 5); ++j) r += __popc(m[j]);
+    const int pos = s_off[e] + r;
+    if (o.pair_stream) o.pair_stream[pos] = b;
+    if (o.pair_rank) o.pair_rank[pos] = i - b * k;
+    o.inv[i] = pos;
+    o.unit_rows[(s_ub[e] + (r >> 4)) * 16 + (r & 15)] = b;
+  }
+  // unit records; rows past a unit's count repeat its first row (the row of
+  // rank 16 u within the expert: found from the mask)
+  for (int e = tid; e < E; e += blockDim.x) {
+    const int c = s_cnt[e];
+    const int nu = (c + 15) >> 4;
+    for (int j = 0; j < nu; ++j) o.units[s_ub[e] + j] = make_int4(e, s_off[e] + 16 * j, min(16, c - 16 * j), 0);
+    if (c > 0 && (c & 15)) {
+      const int want = 16 * (nu - 1);  // rank of the last unit's first row
+      int seen = 0, first = 0;
+      for (int j = 0; j < W; ++j) {
+        const uint32_t m = s_pm[e * W + j];
+        const int pc = __popc(m);
+        if (seen + pc > want) {
+          uint32_t mm = m;
+          for (int q = 0; q < want - seen; ++q) mm &= mm - 1;  // drop the lower set bits
+          first = 32 * j + __ffs(mm) - 1;
+          break;
+        }
+        seen += pc;
+      }
+      for (int i = c - 16 * (nu - 1); i < 16; ++i) o.unit_rows[(s_ub[e] + nu - 1) * 16 + i] = first;
+    }
+  }
+}
+
+hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, hipStream_t st) {
+  const size_t lds = route_prefill_lds(P, E, k);
+  if (P < 1 || E > kRouteMaxE || (size_t)P * k > (size_t)kPrefillMaxPairs || lds > 65536) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_route_prefill, dim3(1), dim3(1024), lds, st, logits, P, E, k, o);
   return hipGetLastError();
 }
 

@@ -180,6 +180,62 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   return w;
 }
 
+// Prefill workspace (caller-owned, from w4_prefill_workspace_bytes): the
+// prompt's rows through every layer, attention in chunks of kPrefillChunk rows.
+constexpr int kPrefillChunk = 32;
+
+struct PfPlan {
+  size_t h, xn, qkv, attn_o, lg, ids, w, counts, offsets, inv, used, n_used, units, unit_rows, n_units, act, y,
+      part_o, part_ml, aticket, rows, logits, total;
+  size_t row_cap;  // int32 words of the rows region
+};
+
+// Words of the prefill upload: slot [P], position [P], sampling parameters,
+// then the attention work list of every chunk.
+size_t pf_row_words(const w4_model_desc& d, int P) {
+  size_t n = 0;
+  for (int i = 0; i < P; ++i) n += (size_t)attn_splits(i) * d.n_kv_heads;
+  return 2 * (size_t)P + kSampleParams + n;
+}
+
+PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
+  PfPlan w{};
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = cur;
+    cur = align_up(cur + bytes);
+    return at;
+  };
+  const size_t H = d.hidden, E = d.n_experts, k = d.top_k, I = d.moe_inter, Hq = d.n_q_heads, D = d.head_dim;
+  const size_t nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * D, pairs = (size_t)P * k;
+  const size_t ucap = E + pairs / 16 + 1, nsmax = attn_splits(cap - 1);
+  w.h = take(P * H * 2);
+  w.xn = take(P * H * 2);
+  w.qkv = take(P * nqkv * 2);
+  w.attn_o = take(P * Hq * D * 2);
+  w.lg = take(P * E * 4);
+  w.ids = take(pairs * 4);
+  w.w = take(pairs * 4);
+  w.counts = take(E * 4);
+  w.offsets = take((E + 1) * 4);
+  w.inv = take(pairs * 4);
+  w.used = take(E * 4);
+  w.n_used = take(4);
+  w.units = take(ucap * 16);
+  w.unit_rows = take(ucap * 16 * 4);
+  w.n_units = take(4);
+  w.act = take(pairs * I * 2);
+  w.y = take(pairs * H * 2);
+  w.part_o = take((size_t)kPrefillChunk * Hq * nsmax * D * 4);
+  w.part_ml = take((size_t)kPrefillChunk * Hq * nsmax * 2 * 4);
+  w.aticket = take((size_t)kPrefillChunk * d.n_kv_heads * 4);
+  w.row_cap = pf_row_words(d, P);
+  w.rows = take(w.row_cap * 4);
+  w.logits = take((size_t)d.vocab * 2);
+  w.total = cur;
+  return w;
+}
+
 }  // namespace
 
 struct Sampling {  // per slot; temperature 0 = greedy
@@ -221,6 +277,18 @@ struct w4_ctx {
   int err_rows[kRing] = {};
   int ring = 0, cur = 0;  // next entry; entry of the last upload
   std::string sticky;     // an invalid token seen in an earlier step, not yet reported
+  // prefill uploads: pinned staging (grown on demand), free again once ev_pf has passed
+  int32_t* pf_pinned = nullptr;
+  size_t pf_words = 0;
+  hipEvent_t ev_pf = nullptr;
+  bool pf_used = false;
+  // the last prefill's invalid-token flags [pf_flag_rows] (host-mapped, written
+  // by its embedding kernel), read once ev_pf_done has passed
+  int32_t* pf_flags = nullptr;
+  int32_t* pf_flags_dev = nullptr;
+  int pf_flag_cap = 0, pf_flag_rows = 0;
+  hipEvent_t ev_pf_done = nullptr;
+  bool pf_pending = false;
   std::string err;
   int launches = 0, syncs = 0;
   int last_launches = 0, last_syncs = 0;
@@ -369,6 +437,20 @@ int poll_errors(w4_ctx* c, bool wait) {
       return fail(c, W4_E_HIP, std::string("hipEventQuery: ") + hipGetErrorString(q));
     }
     take_flags(c, i);
+  }
+  if (c->pf_pending) {
+    const hipError_t q = hipEventQuery(c->ev_pf_done);
+    if (q == hipSuccess || wait) {
+      if (q != hipSuccess) {
+        HIPCHK(c, hipEventSynchronize(c->ev_pf_done));
+        c->syncs++;
+      }
+      for (int b = 0; b < c->pf_flag_rows; ++b)
+        if (c->pf_flags[b] && c->sticky.empty())
+          c->sticky = "a token id outside [0, vocab) was given at prompt position " + std::to_string(b) +
+                      " of an earlier prefill (its embedding row was taken as zero)";
+      c->pf_pending = false;
+    }
   }
   if (c->sticky.empty()) return W4_OK;
   const std::string m = c->sticky;
@@ -601,6 +683,10 @@ void w4_destroy(w4_ctx* c) {
     }
     if (c->pinned) (void)hipHostFree(c->pinned);
     if (c->flags) (void)hipHostFree(c->flags);
+    if (c->ev_pf) (void)hipEventSynchronize(c->ev_pf), (void)hipEventDestroy(c->ev_pf);
+    if (c->ev_pf_done) (void)hipEventSynchronize(c->ev_pf_done), (void)hipEventDestroy(c->ev_pf_done);
+    if (c->pf_pinned) (void)hipHostFree(c->pf_pinned);
+    if (c->pf_flags) (void)hipHostFree(c->pf_flags);
   }
   delete c;
 }
@@ -788,6 +874,161 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
   for (int b = 0; b < B; ++b) c->pos[slots[b]]++;
   c->last_launches = c->launches - l0;
   c->last_syncs = c->syncs - s0;
+  return W4_OK;
+}
+
+size_t w4_prefill_workspace_bytes(const w4_model_desc* d, int32_t max_prompt, int32_t cap) {
+  if (!geometry_ok(d, nullptr) || !sizes_ok(1, cap, nullptr) || max_prompt < 1 || max_prompt > cap) return 0;
+  if ((size_t)max_prompt * d->top_k > (size_t)kPrefillMaxPairs) return 0;
+  if (route_prefill_lds(max_prompt, d->n_experts, d->top_k) > 65536) return 0;
+  return plan_prefill(*d, max_prompt, cap).total;
+}
+
+int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev, size_t ws_bytes, void* logits,
+                    int32_t* next, int32_t* route_ids, void* stream) {
+  if (!c) return W4_E_INVALID;
+  const w4_model_desc& d = c->d;
+  if (slot < 0 || slot >= c->Bm || !c->live[slot]) return fail(c, W4_E_BAD_SLOT, "slot is not live");
+  if (!c->need_seed[slot]) return fail(c, W4_E_BAD_SLOT, "slot has no prompt waiting (prefill once per join)");
+  const int P = c->prompt[slot];
+  if (!tokens || !ws_dev) return fail(c, W4_E_INVALID, "null tokens or workspace");
+  if ((uintptr_t)ws_dev % kAlign) return fail(c, W4_E_INVALID, "prefill workspace must be 256-byte aligned");
+  if ((size_t)P * d.top_k > (size_t)kPrefillMaxPairs || route_prefill_lds(P, d.n_experts, d.top_k) > 65536)
+    return fail(c, W4_E_UNSUPPORTED, "prompt too long for the prefill routing (prompt * top_k <= 16384, and "
+                                     "n_experts * ceil(prompt / 32) * 4 + prompt * top_k <= 65536)");
+  const PfPlan pp = plan_prefill(d, P, c->cap);
+  if (ws_bytes < pp.total) return fail(c, W4_E_INVALID, "prefill workspace smaller than w4_prefill_workspace_bytes");
+  hipStream_t st = (hipStream_t)stream;
+  int rc = ensure_device(c, st);
+  if (rc) return rc;
+  rc = poll_errors(c, false);
+  if (rc) return rc;
+  const int l0 = c->launches;
+  char* ws = static_cast<char*>(ws_dev);
+  auto PW = [&](size_t off) { return ws + off; };
+  // upload: slot and position of every prompt row, the slot's sampling
+  // parameters, and each chunk's attention work list (rows relative to the chunk)
+  const size_t words = pp.row_cap;
+  if (c->pf_used && hipEventQuery(c->ev_pf) == hipErrorNotReady) {
+    HIPCHK(c, hipEventSynchronize(c->ev_pf));
+    c->syncs++;
+  }
+  if (c->pf_pending) {  // the flag buffer is reused below: collect the last prefill's flags first
+    rc = poll_errors(c, true);
+    if (rc) return rc;
+  }
+  if (P > c->pf_flag_cap) {
+    if (c->pf_flags) HIPCHK(c, hipHostFree(c->pf_flags));
+    c->pf_flags = nullptr;
+    HIPCHK(c, hipHostMalloc((void**)&c->pf_flags, sizeof(int32_t) * P, hipHostMallocMapped | hipHostMallocCoherent));
+    HIPCHK(c, hipHostGetDevicePointer((void**)&c->pf_flags_dev, c->pf_flags, 0));
+    c->pf_flag_cap = P;
+  }
+  if (!c->ev_pf_done) HIPCHK(c, hipEventCreateWithFlags(&c->ev_pf_done, hipEventDisableTiming));
+  if (words > c->pf_words) {
+    if (c->pf_pinned) HIPCHK(c, hipHostFree(c->pf_pinned));
+    c->pf_pinned = nullptr;
+    HIPCHK(c, hipHostMalloc((void**)&c->pf_pinned, words * 4, hipHostMallocDefault));
+    c->pf_words = words;
+  }
+  if (!c->ev_pf) HIPCHK(c, hipEventCreateWithFlags(&c->ev_pf, hipEventDisableTiming));
+  int32_t* hp = c->pf_pinned;
+  for (int i = 0; i < P; ++i) {
+    hp[i] = slot;
+    hp[P + i] = i;
+  }
+  {
+    const Sampling& sp = c->smp[slot];
+    int32_t* q = hp + 2 * P;
+    std::memcpy(&q[0], &sp.temperature, 4);
+    q[1] = sp.top_k;
+    std::memcpy(&q[2], &sp.top_p, 4);
+    q[3] = (int32_t)(uint32_t)(sp.seed & 0xFFFFFFFFu);
+    q[4] = (int32_t)(uint32_t)(sp.seed >> 32);
+  }
+  const int nchunks = (P + kPrefillChunk - 1) / kPrefillChunk;
+  std::vector<size_t> ch_off(nchunks), ch_n(nchunks);
+  size_t n = 2 * (size_t)P + kSampleParams;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    ch_off[ch] = n;
+    const int i0 = ch * kPrefillChunk, i1 = std::min(P, i0 + kPrefillChunk);
+    for (int i = i0; i < i1; ++i)
+      for (int sp = 0; sp < attn_splits(i); ++sp)
+        for (int g = 0; g < d.n_kv_heads; ++g) hp[n++] = ((i - i0) << 16) | (sp << 8) | g;
+    ch_n[ch] = n - ch_off[ch];
+  }
+  if (n > words) return fail(c, W4_E_INVALID, "prefill row list exceeds its workspace region");
+  int32_t* drows = reinterpret_cast<int32_t*>(PW(pp.rows));
+  HIPCHK(c, hipMemcpyAsync(drows, hp, n * 4, hipMemcpyHostToDevice, st));
+  HIPCHK(c, hipEventRecord(c->ev_pf, st));
+  c->pf_used = true;
+  HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(PW(pp.aticket)), 0u, (size_t)kPrefillChunk * d.n_kv_heads, st));
+  c->launches++;
+
+  const int H = d.hidden, E = d.n_experts, k = d.top_k, Hq = d.n_q_heads, D = d.head_dim;
+  const int nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * D, qd = Hq * D;
+  uint16_t* h = reinterpret_cast<uint16_t*>(PW(pp.h));
+  uint16_t* xn = reinterpret_cast<uint16_t*>(PW(pp.xn));
+  uint16_t* qkv = reinterpret_cast<uint16_t*>(PW(pp.qkv));
+  uint16_t* ao = reinterpret_cast<uint16_t*>(PW(pp.attn_o));
+  KV kv = c->kv();
+  RouteOut r;
+  r.w = reinterpret_cast<float*>(PW(pp.w));
+  r.counts = reinterpret_cast<int32_t*>(PW(pp.counts));
+  r.offsets = reinterpret_cast<int32_t*>(PW(pp.offsets));
+  r.pair_stream = nullptr;
+  r.pair_rank = nullptr;
+  r.inv = reinterpret_cast<int32_t*>(PW(pp.inv));
+  r.used = reinterpret_cast<int32_t*>(PW(pp.used));
+  r.n_used = reinterpret_cast<int32_t*>(PW(pp.n_used));
+  r.units = reinterpret_cast<int4*>(PW(pp.units));
+  r.unit_rows = reinterpret_cast<int32_t*>(PW(pp.unit_rows));
+  r.n_units = reinterpret_cast<int32_t*>(PW(pp.n_units));
+  r.units_cap = E + P * k / 16 + 1;
+  LCHK(c, 1, launch_embed(P, H, d.vocab, d.group, tokens, c->Bk<uint8_t>(c->bp.emb_p), c->Bk<uint16_t>(c->bp.emb_s), h,
+                          c->Bk<uint16_t>(c->bp.layers[0].attn_norm), d.rms_eps, xn, c->pf_flags_dev, st, 0));
+  for (int l = 0; l < d.n_layers; ++l) {
+    const LayerLoc& Ly = c->bp.layers[l];
+    LCHK(c, 1, launch_gemm(c->mat(Ly.qkv), P, xn, H, qkv, nqkv, EPI_F16, st));
+    LCHK(c, 1, launch_prefill_kv(P, l, slot, kv, qkv + qd, qkv + qd + d.n_kv_heads * D, nqkv,
+                                 c->W<float2>(c->wp.table), st));
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int i0 = ch * kPrefillChunk, rows = std::min(P - i0, kPrefillChunk);
+      LCHK(c, 1, launch_attention(rows, l, Hq, kv, drows + i0, drows + P + i0, drows + ch_off[ch], (int)ch_n[ch],
+                                  qkv + (size_t)i0 * nqkv, nqkv, nullptr, nullptr, nqkv, c->W<float2>(c->wp.table),
+                                  reinterpret_cast<float*>(PW(pp.part_o)), reinterpret_cast<float*>(PW(pp.part_ml)),
+                                  reinterpret_cast<unsigned*>(PW(pp.aticket)), ao + (size_t)i0 * qd, st, nullptr, 0));
+    }
+    LCHK(c, 1, launch_gemm(c->mat(Ly.o), P, ao, qd, h, H, EPI_RESID, st));
+    LCHK(c, 1, launch_rmsnorm(P, H, h, c->Bk<uint16_t>(Ly.moe_norm), d.rms_eps, xn, st, 0));
+    float* lg = reinterpret_cast<float*>(PW(pp.lg));
+    LCHK(c, 1, launch_gemm(c->mat(Ly.router), P, xn, H, lg, E, EPI_F32, st));
+    r.ids = route_ids ? route_ids + (size_t)l * P * k : reinterpret_cast<int32_t*>(PW(pp.ids));
+    LCHK(c, 1, launch_route_prefill(lg, P, E, k, r, st));
+    uint16_t* act = reinterpret_cast<uint16_t*>(PW(pp.act));
+    uint16_t* y = reinterpret_cast<uint16_t*>(PW(pp.y));
+    LCHK(c, 1, launch_moe_gateup(c->mat(Ly.gate), c->mat(Ly.up), xn, H, r, act, st));
+    LCHK(c, 1, launch_moe_down(c->mat(Ly.down), act, r, y, st));
+    const uint16_t* ng = l + 1 < d.n_layers ? c->Bk<uint16_t>(c->bp.layers[l + 1].attn_norm)
+                                            : c->Bk<uint16_t>(c->bp.final_norm);
+    LCHK(c, 1, launch_combine(P, H, k, r.w, r.inv, y, h, true, ng, d.rms_eps, xn, st, 0));
+  }
+  // the last prompt token: output projection and its next token (the slot's
+  // sampling at draw counter P - 1, the last prompt position)
+  uint16_t* lgo = logits ? static_cast<uint16_t*>(logits) : reinterpret_cast<uint16_t*>(PW(pp.logits));
+  int32_t* nx = next ? next : c->W<int32_t>(c->wp.next);
+  LCHK(c, 1, launch_gemm(c->mat(c->bp.lm), 1, xn + (size_t)(P - 1) * H, H, lgo, d.vocab, EPI_F16, st));
+  if (c->smp[slot].temperature > 0.f)
+    LCHK(c, 1, launch_sample(1, d.vocab, lgo, drows + 2 * P, drows + P + (P - 1), nx, st));
+  else
+    LCHK(c, 1, launch_argmax(1, d.vocab, lgo, nx, c->W<float>(c->wp.amax_v), c->W<int32_t>(c->wp.amax_i),
+                              c->W<unsigned>(c->wp.amax_ticket), st));
+  HIPCHK(c, hipEventRecord(c->ev_pf_done, st));
+  c->pf_pending = true;
+  c->pf_flag_rows = P;
+  c->need_seed[slot] = 0;
+  c->pos[slot] = P;
+  c->last_launches = c->launches - l0;
   return W4_OK;
 }
 

@@ -53,6 +53,9 @@ hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y,
 // experts + B*k/16 with B <= 32, k <= 16).
 constexpr int kRouteMaxE = 256;
 constexpr int kMaxUnits = kRouteMaxE + 32 * 16 / 16 + 1;
+// Prefill: at most kPrefillMaxPairs (prompt tokens x top_k) routed pairs.
+constexpr int kPrefillMaxPairs = 16384;
+constexpr int kMaxUnitsPrefill = kRouteMaxE + kPrefillMaxPairs / 16 + 1;
 
 struct RouteOut {
   int32_t* ids;          // [B][k]
@@ -134,6 +137,19 @@ hipError_t launch_router(int B, int H, int E, int k, int g, const uint16_t* h, c
 hipError_t launch_rope_table(int cap, int D, double theta, float2* table, hipStream_t st);
 hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, const uint16_t* v,
                        hipStream_t st);
+// Prefill of one layer's K/V: row i of k, v (row stride ld, [Hkv][D]) is the
+// prompt's position i; keys rotated at i through table (as the decode step's
+// append), both written at (layer, slot, i) for i < P.
+hipError_t launch_prefill_kv(int P, int layer, int slot, const KV& kv, const uint16_t* k, const uint16_t* v, int ld,
+                             const float2* table, hipStream_t st);
+// Routing of P prefill rows (P * k <= kPrefillMaxPairs, E <= kRouteMaxE) in one
+// work-group: top-k softmax per row and the (row, expert) bucketing into the
+// same outputs as launch_route (units_cap = E + P*k/16 + 1).
+hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, hipStream_t st);
+// LDS bytes launch_route_prefill needs (at most 64 KiB is allowed).
+inline size_t route_prefill_lds(int P, int E, int k) {
+  return (size_t)E * ((P + 31) / 32) * 4 + (size_t)P * k;
+}
 // positions 0..P-1 of a slot -> canonical k, v [L][P][Hkv][D]
 hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uint16_t* v, hipStream_t st);
 // split-KV decode attention; part_o [B][Hq][nchmax][D] f32, part_ml [B][Hq][nchmax][2].

@@ -84,6 +84,26 @@ class Context:
             torch.cuda.current_stream(self.device).synchronize()
         return s
 
+    def prefill(self, tokens, max_new: int, logits=None, next_ids=None, route_ids=None) -> int:
+        """A new stream whose prompt token ids go through the model (seed-at-join
+        prefill); returns its slot.  tokens: host ints or a device int32 tensor."""
+        t = tokens if isinstance(tokens, torch.Tensor) else torch.tensor(np.asarray(tokens, np.int32))
+        t = t.to(self.device, dtype=torch.int32)
+        P = int(t.numel())
+        nbytes = L.w4_prefill_workspace_bytes(self.desc, P, self.cap)
+        if not nbytes:
+            raise L.W4Error(L.W4_E_UNSUPPORTED, "prompt too long for the prefill")
+        if getattr(self, "_pf_ws", None) is None or self._pf_ws.numel() < nbytes:
+            self._pf_ws = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        s = L.w4_slot_alloc(self.ctx, P, max_new)
+        try:
+            L.w4_slot_prefill(self.ctx, s, t, self._pf_ws, self._pf_ws.numel(), logits, next_ids, route_ids,
+                              self.stream)
+        except Exception:
+            L.w4_slot_release(self.ctx, s)
+            raise
+        return s
+
     def release(self, slot: int):
         L.w4_slot_release(self.ctx, slot)
 

@@ -70,7 +70,7 @@ def lib():
         L.orc_decode_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, _i32p, _i32p, _i32p,
                                       C.c_void_p, C.c_void_p, _i32p, C.c_void_p, C.c_void_p]
         L.orc_prefill.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, C.c_void_p,
-                                  _u16p, _i32p, C.c_void_p]
+                                  _u16p, _i32p, C.c_void_p, C.c_void_p]
         L.orc_attn_step.argtypes = [C.POINTER(_Model), C.POINTER(_Arena), C.c_int, C.c_int, _i32p, _i32p,
                                     _u16p, _u16p, _u16p, _u16p]
         L.orc_splitmix.restype = C.c_uint64
@@ -361,11 +361,11 @@ def decode_step(model: Model, arena: Arena, slots, positions, tokens, want_logit
     return logits, nxt, ids, rl
 
 
-def prefill(model: Model, arena: Arena, slot: int, tokens, force=None, want_ids=False):
+def prefill(model: Model, arena: Arena, slot: int, tokens, force=None, want_ids=False, want_router=False):
     """The prompt tokens through the model at positions 0..P-1 of the slot (its K/V
-    written there); returns the last token's fp16 logits [V], its greedy id and,
-    if asked, the expert ids [n_layers, P, top_k].  force: ranked expert ids
-    [n_layers, P, top_k] replacing every top-k, or None."""
+    written there); returns the last token's fp16 logits [V], its greedy id, and, if
+    asked, the expert ids [n_layers, P, top_k] and the router logits [n_layers, P, E]
+    (else None).  force: ranked expert ids [n_layers, P, top_k] replacing every top-k."""
     tokens = _c(tokens, np.int32)
     d = model.desc
     P = len(tokens)
@@ -373,7 +373,11 @@ def prefill(model: Model, arena: Arena, slot: int, tokens, force=None, want_ids=
     logits = np.empty(d.vocab, np.uint16)
     nxt = np.empty(1, np.int32)
     ids = np.empty((d.n_layers, P, d.top_k), np.int32) if want_ids else None
-    lib().orc_prefill(C.byref(model.m), C.byref(arena.a), int(slot), P, tokens, _ptr(f), logits, nxt, _ptr(ids))
+    rl = np.empty((d.n_layers, P, d.n_experts), np.float32) if want_router else None
+    lib().orc_prefill(C.byref(model.m), C.byref(arena.a), int(slot), P, tokens, _ptr(f), logits, nxt, _ptr(ids),
+                      _ptr(rl))
+    if want_router:
+        return logits, int(nxt[0]), ids, rl
     return logits, int(nxt[0]), ids
 
 

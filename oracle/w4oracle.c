@@ -501,9 +501,11 @@ EXPORT void orc_decode_step(const orc_model* m, orc_arena* a, int B, const int32
  * to the K/V of tokens 0..t).  The slot then holds the prompt's K/V; the
  * output is the last token's logits fp16 [V] (next-token distribution) and
  * its greedy id.  force [L][P][k]: ranked expert ids replacing every top-k,
- * or NULL; ids_out [L][P][k] optional. */
+ * or NULL; ids_out [L][P][k] and router_out [L][P][E] (fp32 router logits)
+ * optional. */
 EXPORT void orc_prefill(const orc_model* m, orc_arena* a, int slot, int P, const int32_t* tokens,
-                        const int32_t* force, uint16_t* logits, int32_t* next, int32_t* ids_out) {
+                        const int32_t* force, uint16_t* logits, int32_t* next, int32_t* ids_out,
+                        float* router_out) {
   h2f_init();
   int H = m->hidden, V = m->vocab, g = m->group, k = m->top_k, L = m->n_layers;
   uint16_t* h = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)H);
@@ -512,7 +514,8 @@ EXPORT void orc_prefill(const orc_model* m, orc_arena* a, int slot, int P, const
     embed_row(m, tokens[t], h);
     for (int l = 0; l < L; l++)
       layer_one(m, a, l, slot, t, h, force ? force + ((size_t)l * P + t) * k : NULL,
-                ids_out ? ids_out + ((size_t)l * P + t) * k : NULL, NULL);
+                ids_out ? ids_out + ((size_t)l * P + t) * k : NULL,
+                router_out ? router_out + ((size_t)l * P + t) * m->n_experts : NULL);
   }
   orc_rmsnorm(H, h, m->final_norm, m->rms_eps, hn);
   orc_w4_gemm(1, V, H, g, hn, m->lm_p, m->lm_s, logits, NULL);
