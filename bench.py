@@ -78,6 +78,9 @@ def main():
                     help="measure the HBM streaming-read ceiling with the library's read probe (4 GiB, 16-byte loads)")
     ap.add_argument("--ragged", choices=("on", "off"), default="on",
                     help="continuous-batching leg: 256 steps, arrivals p=0.5, prompts U{1..2048}, lives U{16..512}")
+    ap.add_argument("--prefill", choices=("on", "off"), default="on",
+                    help="seed-at-join prefill leg: a 2048-token prompt through the model (prompt tok/s)")
+    ap.add_argument("--prefill-len", type=int, default=2048)
     ap.add_argument("--cpu-single-steps", type=int, default=2,
                     help="decode steps of one stream in the oracle's single-thread sample")
     args = ap.parse_args()
@@ -207,10 +210,11 @@ def main():
             + (f", weight stream {entry['weight_stream_GBps']:.0f} GB/s" if "weight_stream_GBps" in entry else ""))
 
     ragged = None
+    for s in slots:
+        ctx.release(s)
     if args.ragged == "on":
-        for s in slots:
-            ctx.release(s)
         ragged = ragged_leg(args, d, ctx, dev, L)
+    prefill = prefill_leg(args, d, ctx, dev, L) if args.prefill == "on" else None
 
     Bh = max(batches)
     head = sweep[Bh]
@@ -244,6 +248,7 @@ def main():
         "roofline": roof,
         "hbm_read_ceiling": ceiling,
         "ragged": ragged,
+        "prefill": prefill,
         "cpu_baseline": cpu,
         "parity_first_step": parity,
     }
@@ -343,6 +348,43 @@ def ragged_leg(args, d, ctx, dev, L):
     log(f"ragged: {out['tok_s']:.0f} tok/s over {n_steps} steps, mean B {out['mean_B']:.1f} "
         f"({out['min_B']}..{out['max_B']}, {out['B_changes']} changes), {len(admitted)} joins, {reused} slot reuses")
     del kv_dev
+    return out
+
+
+def prefill_leg(args, d, ctx, dev, L):
+    """Seed-at-join prefill on the full model: one stream's prompt of
+    --prefill-len seeded token ids through all 48 layers (w4_slot_prefill), one
+    warm-up and three timed runs (events on the stream), each on a freshly
+    allocated slot; prompt tokens per second."""
+    import torch
+
+    from int4_w4a16_group_amd import inputs
+    P = args.prefill_len
+    nbytes = L.w4_prefill_workspace_bytes(d, P, ctx.cap)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    tok = torch.tensor([int(t) for t in inputs.rng(args.seed, inputs.T_TOKENS, 77).integers(0, d.vocab, P)],
+                       dtype=torch.int32, device=dev)
+    nx = torch.empty(1, dtype=torch.int32, device=dev)
+    times = []
+    st = torch.cuda.current_stream(dev)
+    for it in range(4):
+        s = L.w4_slot_alloc(ctx.ctx, P, 16)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(st)
+        L.w4_slot_prefill(ctx.ctx, s, tok, ws, nbytes, None, nx, None, ctx.stream)
+        b.record(st)
+        torch.cuda.synchronize()
+        if it:
+            times.append(a.elapsed_time(b))
+        launches, _ = L.w4_last_step_counts(ctx.ctx)
+        L.w4_slot_release(ctx.ctx, s)
+    L.w4_check_errors(ctx.ctx)
+    ms = float(np.median(times))
+    out = dict(prompt_tokens=P, ms=ms, ms_min=float(min(times)), ms_max=float(max(times)),
+               tok_s=P / (ms * 1e-3), launches=launches, workspace_bytes=nbytes,
+               kind="one stream's prompt through all layers (M = P row products, causal attention, grouped experts)")
+    log(f"prefill: {P} tokens in {ms:.1f} ms ({out['tok_s']:.0f} prompt tok/s, {launches} launches)")
     return out
 
 

@@ -146,8 +146,8 @@ int w4_slots_advance(w4_ctx* ctx, int32_t n, const int32_t* slots_host);
  * and optionally the expert ids route_ids_dev int32 [n_layers][P][top_k].
  * workspace_dev: caller-owned, 256-byte aligned, at least
  * w4_prefill_workspace_bytes(desc, P, ctx_cap) bytes (ws_bytes gives its
- * size).  Limits: P * top_k <= 16384 and n_experts * ceil(P / 32) * 4 +
- * P * top_k <= 65536 (W4_E_UNSUPPORTED beyond).  An out-of-range token id is
+ * size).  Limits: P * top_k <= 16384 and n_experts * ceil(P / 32) * 6 <=
+ * 61440 (W4_E_UNSUPPORTED beyond).  An out-of-range token id is
  * reported like the decode step's (sticky W4_E_INVALID).  The call replaces
  * w4_slot_seed for that slot. */
 size_t w4_prefill_workspace_bytes(const w4_model_desc* desc, int32_t max_prompt, int32_t ctx_cap);

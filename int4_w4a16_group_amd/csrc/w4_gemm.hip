@@ -294,6 +294,9 @@ hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y,
   const int target = std::max(1, 4096 / NW);
   int grid = std::min(ntiles, target);
   if (NW <= 8 && ntiles >= 256 && ntiles <= 1024) grid = (ntiles + 1) / 2;
+  // many row blocks (a prompt): about 8 column tiles per work-group, so the x
+  // rows in registers serve 8 weight tiles instead of being re-read for each
+  if (row_blocks > 1) grid = std::max(1, (ntiles + 7) / 8);
   DenseArgs a{w.tiles, w.scales, w.N, w.K, ntiles, x, ldx, B, y, ldy, xrows};
   w4_launch(k, dim3(grid, row_blocks), dim3(NW * 64), 2 * NW * MT * 1024, st, a);
   return hipGetLastError();

@@ -276,12 +276,14 @@ __device__ __forceinline__ uint32_t sort_key(float v) {
 template <int EPL, class Sel>
 __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane, Sel sel) {
   uint32_t key[EPL];
+  float val[EPL];  // the row's logits, read once
   bool valid[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
     valid[j] = e < E;
-    key[j] = valid[j] ? sort_key(lg[e]) : 0u;
+    val[j] = valid[j] ? lg[e] : 0.f;
+    key[j] = valid[j] ? sort_key(val[j]) : 0u;
   }
   uint32_t prefix = 0;
   int need = k;
@@ -332,7 +334,7 @@ __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const unsigned long long m = __ballot(sl[j] && rank[j] == r);
-      if (m) v = __shfl(valid[j] ? lg[min(lane + 64 * j, E - 1)] : 0.f, __ffsll((long long)m) - 1, 64);
+      if (m) v = __shfl(val[j], __ffsll((long long)m) - 1, 64);
     }
     if (v != v) v = -INFINITY;
     if (r == 0) l0 = v;
@@ -342,7 +344,7 @@ __device__ __forceinline__ void topk_row(const float* lg, int E, int k, int lane
   for (int j = 0; j < EPL; ++j)
     if (sl[j]) {
       const int e = lane + 64 * j;
-      float v = lg[e];
+      float v = val[j];
       if (v != v) v = -INFINITY;
       sel(e, rank[j], expf(v - l0) / sum);
     }
@@ -476,41 +478,53 @@ hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut
   return hipGetLastError();
 }
 
-// Routing of the P rows of a prefill in one 1024-thread work-group, into the
-// same outputs as k_route: top-k softmax of each row (one wave per row, the
-// same arithmetic as k_route), then the bucketing by (expert, row): LDS holds
-// for every expert a P-bit mask of the rows that chose it and, per (row,
-// rank), the expert id as one byte; a pair's place within its expert is the
-// number of lower rows in that expert's mask (a prefix popcount), so the
-// pairs come out ordered by (expert, row) as in the decode step.
-__global__ void __launch_bounds__(1024) k_route_prefill(const float* __restrict__ logits, int P, int E, int k,
-                                                        RouteOut o) {
-  extern __shared__ uint32_t s_pm[];  // [E][W] row masks, then P*k expert bytes
+// Routing of the P rows of a prefill, into the same outputs as k_route, in
+// two launches.  k_topk_rows: one wave per row, the top-k softmax of k_route
+// (same arithmetic); it records the ids, the weights, each (row, rank)'s
+// expert as one byte, and sets bit b of expert e's row mask (global, zero
+// before).  k_bucket_prefill, one work-group: the pairs ordered by (expert,
+// row) -- a pair's place within its expert is the number of lower rows in the
+// expert's mask, a prefix popcount -- and the 16-row work units; it clears the
+// masks again.
+__global__ void __launch_bounds__(1024) k_topk_rows(const float* __restrict__ logits, int P, int E, int k,
+                                                    RouteOut o, uint32_t* __restrict__ mask,
+                                                    uint8_t* __restrict__ e8) {
+  const int W = (P + 31) / 32;
+  const int b = blockIdx.x * 16 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (b >= P) return;
+  auto sel = [&](int e, int r, float wt) {
+    o.ids[b * k + r] = e;
+    o.w[b * k + r] = wt;
+    e8[b * k + r] = (uint8_t)e;
+    atomicOr(&mask[e * W + (b >> 5)], 1u << (b & 31));
+  };
+  const float* lg = logits + (size_t)b * E;
+  if (E <= 64)
+    topk_row<1>(lg, E, k, lane, sel);
+  else if (E <= 128)
+    topk_row<2>(lg, E, k, lane, sel);
+  else
+    topk_row<4>(lg, E, k, lane, sel);
+}
+
+__global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, RouteOut o, uint32_t* __restrict__ mask,
+                                                         const uint8_t* __restrict__ e8) {
+  // [E][W] row masks, then [E][W] 16-bit counts of the set bits in the words
+  // before each word (a pair's place within its expert is one lookup)
+  extern __shared__ uint32_t s_pm[];
   __shared__ int s_cnt[kRouteMaxE], s_off[kRouteMaxE], s_ub[kRouteMaxE];
   const int W = (P + 31) / 32;
-  uint8_t* s_e = reinterpret_cast<uint8_t*>(s_pm + (size_t)E * W);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  for (int i = tid; i < E * W; i += blockDim.x) s_pm[i] = 0u;
+  uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_pm + (size_t)E * W);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * W; i += blockDim.x) s_pm[i] = mask[i];
   __syncthreads();
-  for (int b = w; b < P; b += 16) {
-    auto sel = [&](int e, int r, float wt) {
-      o.ids[b * k + r] = e;
-      o.w[b * k + r] = wt;
-      s_e[b * k + r] = (uint8_t)e;
-      atomicOr(&s_pm[e * W + (b >> 5)], 1u << (b & 31));
-    };
-    const float* lg = logits + (size_t)b * E;
-    if (E <= 64)
-      topk_row<1>(lg, E, k, lane, sel);
-    else if (E <= 128)
-      topk_row<2>(lg, E, k, lane, sel);
-    else
-      topk_row<4>(lg, E, k, lane, sel);
-  }
-  __syncthreads();
+  for (int i = tid; i < E * W; i += blockDim.x) mask[i] = 0u;  // zero again for the next layer
   for (int e = tid; e < E; e += blockDim.x) {
     int c = 0;
-    for (int j = 0; j < W; ++j) c += __popc(s_pm[e * W + j]);
+    for (int j = 0; j < W; ++j) {
+      s_pre[e * W + j] = (uint16_t)c;
+      c += __popc(s_pm[e * W + j]);
+    }
     s_cnt[e] = c;
   }
   __syncthreads();
@@ -532,10 +546,8 @@ __global__ void __launch_bounds__(1024) k_route_prefill(const float* __restrict_
   }
   __syncthreads();
   for (int i = tid; i < P * k; i += blockDim.x) {
-    const int b = i / k, e = s_e[i];
-    const uint32_t* m = s_pm + (size_t)e * W;
-    int r = __popc(m[b >> 5] & ((1u << (b & 31)) - 1u));
-    for (int j = 0; j < (b >> 5); ++j) r += __popc(m[j]);
+    const int b = i / k, e = e8[i];
+    const int r = s_pre[e * W + (b >> 5)] + __popc(s_pm[e * W + (b >> 5)] & ((1u << (b & 31)) - 1u));
     const int pos = s_off[e] + r;
     if (o.pair_stream) o.pair_stream[pos] = b;
     if (o.pair_rank) o.pair_rank[pos] = i - b * k;
@@ -567,10 +579,13 @@ __global__ void __launch_bounds__(1024) k_route_prefill(const float* __restrict_
   }
 }
 
-hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, hipStream_t st) {
+hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, uint32_t* mask,
+                                uint8_t* e8, hipStream_t st) {
   const size_t lds = route_prefill_lds(P, E, k);
-  if (P < 1 || E > kRouteMaxE || (size_t)P * k > (size_t)kPrefillMaxPairs || lds > 65536) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_route_prefill, dim3(1), dim3(1024), lds, st, logits, P, E, k, o);
+  if (P < 1 || E > kRouteMaxE || (size_t)P * k > (size_t)kPrefillMaxPairs || lds > 61440 || !mask || !e8)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_topk_rows, dim3((P + 15) / 16), dim3(1024), 0, st, logits, P, E, k, o, mask, e8);
+  hipLaunchKernelGGL(k_bucket_prefill, dim3(1), dim3(1024), lds, st, P, E, k, o, mask, e8);
   return hipGetLastError();
 }
 

@@ -186,7 +186,7 @@ constexpr int kPrefillChunk = 32;
 
 struct PfPlan {
   size_t h, xn, qkv, attn_o, lg, ids, w, counts, offsets, inv, used, n_used, units, unit_rows, n_units, act, y,
-      part_o, part_ml, aticket, rows, logits, total;
+      part_o, part_ml, aticket, rows, logits, rmask, re8, total;
   size_t row_cap;  // int32 words of the rows region
 };
 
@@ -232,6 +232,8 @@ PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
   w.row_cap = pf_row_words(d, P);
   w.rows = take(w.row_cap * 4);
   w.logits = take((size_t)d.vocab * 2);
+  w.rmask = take(E * (((size_t)P + 31) / 32) * 4);
+  w.re8 = take(pairs);
   w.total = cur;
   return w;
 }
@@ -880,7 +882,7 @@ int w4_decode_step(w4_ctx* c, int32_t B, const int32_t* slots, const int32_t* to
 size_t w4_prefill_workspace_bytes(const w4_model_desc* d, int32_t max_prompt, int32_t cap) {
   if (!geometry_ok(d, nullptr) || !sizes_ok(1, cap, nullptr) || max_prompt < 1 || max_prompt > cap) return 0;
   if ((size_t)max_prompt * d->top_k > (size_t)kPrefillMaxPairs) return 0;
-  if (route_prefill_lds(max_prompt, d->n_experts, d->top_k) > 65536) return 0;
+  if (route_prefill_lds(max_prompt, d->n_experts, d->top_k) > 61440) return 0;
   return plan_prefill(*d, max_prompt, cap).total;
 }
 
@@ -893,9 +895,9 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
   const int P = c->prompt[slot];
   if (!tokens || !ws_dev) return fail(c, W4_E_INVALID, "null tokens or workspace");
   if ((uintptr_t)ws_dev % kAlign) return fail(c, W4_E_INVALID, "prefill workspace must be 256-byte aligned");
-  if ((size_t)P * d.top_k > (size_t)kPrefillMaxPairs || route_prefill_lds(P, d.n_experts, d.top_k) > 65536)
+  if ((size_t)P * d.top_k > (size_t)kPrefillMaxPairs || route_prefill_lds(P, d.n_experts, d.top_k) > 61440)
     return fail(c, W4_E_UNSUPPORTED, "prompt too long for the prefill routing (prompt * top_k <= 16384, and "
-                                     "n_experts * ceil(prompt / 32) * 4 + prompt * top_k <= 65536)");
+                                     "n_experts * ceil(prompt / 32) * 6 <= 61440)");
   const PfPlan pp = plan_prefill(d, P, c->cap);
   if (ws_bytes < pp.total) return fail(c, W4_E_INVALID, "prefill workspace smaller than w4_prefill_workspace_bytes");
   hipStream_t st = (hipStream_t)stream;
@@ -963,7 +965,9 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
   HIPCHK(c, hipEventRecord(c->ev_pf, st));
   c->pf_used = true;
   HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(PW(pp.aticket)), 0u, (size_t)kPrefillChunk * d.n_kv_heads, st));
-  c->launches++;
+  HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(PW(pp.rmask)), 0u,
+                            (size_t)d.n_experts * ((P + 31) / 32), st));
+  c->launches += 2;
 
   const int H = d.hidden, E = d.n_experts, k = d.top_k, Hq = d.n_q_heads, D = d.head_dim;
   const int nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * D, qd = Hq * D;
@@ -1004,7 +1008,8 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
     float* lg = reinterpret_cast<float*>(PW(pp.lg));
     LCHK(c, 1, launch_gemm(c->mat(Ly.router), P, xn, H, lg, E, EPI_F32, st));
     r.ids = route_ids ? route_ids + (size_t)l * P * k : reinterpret_cast<int32_t*>(PW(pp.ids));
-    LCHK(c, 1, launch_route_prefill(lg, P, E, k, r, st));
+    LCHK(c, 2, launch_route_prefill(lg, P, E, k, r, reinterpret_cast<uint32_t*>(PW(pp.rmask)),
+                                    reinterpret_cast<uint8_t*>(PW(pp.re8)), st));
     uint16_t* act = reinterpret_cast<uint16_t*>(PW(pp.act));
     uint16_t* y = reinterpret_cast<uint16_t*>(PW(pp.y));
     LCHK(c, 1, launch_moe_gateup(c->mat(Ly.gate), c->mat(Ly.up), xn, H, r, act, st));

@@ -142,13 +142,17 @@ hipError_t launch_seed(int L, int P, int slot, const KV& kv, const uint16_t* k, 
 // append), both written at (layer, slot, i) for i < P.
 hipError_t launch_prefill_kv(int P, int layer, int slot, const KV& kv, const uint16_t* k, const uint16_t* v, int ld,
                              const float2* table, hipStream_t st);
-// Routing of P prefill rows (P * k <= kPrefillMaxPairs, E <= kRouteMaxE) in one
-// work-group: top-k softmax per row and the (row, expert) bucketing into the
-// same outputs as launch_route (units_cap = E + P*k/16 + 1).
-hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, hipStream_t st);
-// LDS bytes launch_route_prefill needs (at most 64 KiB is allowed).
+// Routing of P prefill rows (P * k <= kPrefillMaxPairs, E <= kRouteMaxE), two
+// launches: top-k softmax per row (one wave each) and the (row, expert)
+// bucketing into the same outputs as launch_route (units_cap = E + P*k/16 + 1).
+// mask [E][ceil(P/32)] words (zero before and after) and e8 [P*k] bytes are scratch.
+hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, uint32_t* mask,
+                                uint8_t* e8, hipStream_t st);
+// Dynamic LDS bytes of the prefill bucketing (row masks and their prefix
+// counts; at most 60 KiB is allowed, beside its static arrays).
 inline size_t route_prefill_lds(int P, int E, int k) {
-  return (size_t)E * ((P + 31) / 32) * 4 + (size_t)P * k;
+  (void)k;
+  return (size_t)E * ((P + 31) / 32) * 6;
 }
 // positions 0..P-1 of a slot -> canonical k, v [L][P][Hkv][D]
 hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uint16_t* v, hipStream_t st);
