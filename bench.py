@@ -31,12 +31,14 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 METRIC = "aggregate decode tok/s at B=1/4/8/32 + int4 weight-stream HBM GB/s vs peak"
 
-# HBM bytes per launch of the grouped gate/up kernel from two rocprofv3 --pmc
-# runs of this benchmark at B=32 (FETCH_SIZE, then WRITE_SIZE; KiB scaled by
+# HBM bytes per launch of the roofline kernel (the grouped expert products:
+# the fused launch, or the gate/up launch of the two-launch form) from two
+# rocprofv3 --pmc runs of this benchmark at B=32 (FETCH_SIZE, then WRITE_SIZE; KiB scaled by
 # what the same counters read for a 512 MiB device copy: reads x2.0, writes
 # x1.0), and the SHA-256 of the kernel sources they were taken on.  Reported
 # only while those sources are unchanged.
-TRAFFIC_GATEUP = dict(read_MB=180.11, write_MB=0.61, sources_sha256="e070c105d04760620835fe02a07d33ff629984f9c2509fce50db5b39946ae9d5")
+TRAFFIC = dict(moe_gateup=dict(read_MB=180.11, write_MB=0.61,
+                               sources_sha256="e070c105d04760620835fe02a07d33ff629984f9c2509fce50db5b39946ae9d5"))
 TRAFFIC_SOURCES = ("int4_w4a16_group_amd/csrc/w4_gemm.hip", "int4_w4a16_group_amd/csrc/w4_device.h",
                    "int4_w4a16_group_amd/csrc/w4_tile.h")
 
@@ -50,9 +52,9 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    t = TRAFFIC_GATEUP
-    if t["sources_sha256"] is None or t["sources_sha256"] != kernel_sources_sha256():
+def measured_traffic(kernel):
+    t = TRAFFIC.get(kernel)
+    if t is None or t["sources_sha256"] != kernel_sources_sha256():
         return None
     return (t["read_MB"] + t["write_MB"]) * 1e6
 
@@ -81,6 +83,10 @@ def main():
     ap.add_argument("--prefill", choices=("on", "off"), default="on",
                     help="seed-at-join prefill leg: a 2048-token prompt through the model (prompt tok/s)")
     ap.add_argument("--prefill-len", type=int, default=2048)
+    ap.add_argument("--fused-moe", choices=("on", "off"), default="off",
+                    help="grouped expert products as one launch (on) or two (off, the library default); same results")
+    ap.add_argument("--kernels", choices=("on", "off"), default="on",
+                    help="each hot kernel alone at its own shapes over >= 1 GiB of distinct operands per pass")
     ap.add_argument("--cpu-single-steps", type=int, default=2,
                     help="decode steps of one stream in the oracle's single-thread sample")
     args = ap.parse_args()
@@ -118,6 +124,7 @@ def main():
     t0 = time.time()
     ctx = Context(d, Bmax, cap, dev)
     ctx.load_model(mw)
+    L.w4_set_option(ctx.ctx, L.W4_OPT_FUSED_MOE, 1 if args.fused_moe == "on" else 0)
     log(f"bank {ctx.bank_bytes / 1e9:.3f} GB, arena {ctx.arena_bytes / 1e9:.2f} GB, loaded in {time.time() - t0:.1f}s")
 
     # ---- 32 streams join with seeded prompts
@@ -183,8 +190,10 @@ def main():
                      step_GBps=byt["total"] / (ms * 1e-3) / 1e9)
         if args.profile == "on":
             kt = {}
-            for name, kid in (("dense", L.W4_K_DENSE), ("router", L.W4_K_ROUTER), ("moe_gateup", L.W4_K_MOE_GATEUP),
-                              ("moe_down", L.W4_K_MOE_DOWN), ("attention", L.W4_K_ATTENTION)):
+            fams = [("dense", L.W4_K_DENSE), ("router", L.W4_K_ROUTER), ("attention", L.W4_K_ATTENTION)]
+            fams += [("moe", L.W4_K_MOE)] if args.fused_moe == "on" else [("moe_gateup", L.W4_K_MOE_GATEUP),
+                                                                          ("moe_down", L.W4_K_MOE_DOWN)]
+            for name, kid in fams:
                 routes2 = torch.empty_like(routes)
                 pos1 = np.array([ctx.position(s) for s in sl])
                 torch.cuda.synchronize()
@@ -199,7 +208,7 @@ def main():
                 kt[name] = dict(ms_total=kms, launches=n, avg_us=kms / max(n, 1) * 1e3,
                                 GBps=b2[name] * args.steps / (kms * 1e-3) / 1e9 if kms > 0 else None,
                                 bytes_per_launch=b2[name] * args.steps / max(n, 1))
-            wk = ("dense", "router", "moe_gateup", "moe_down")
+            wk = [k for k in ("dense", "router", "moe", "moe_gateup", "moe_down") if k in kt]
             wbytes = sum(kt[k]["bytes_per_launch"] * kt[k]["launches"] for k in wk)
             wms = sum(kt[k]["ms_total"] for k in wk)
             entry["kernels"] = kt
@@ -209,6 +218,7 @@ def main():
         log(f"B={B}: {entry['tok_s']:.0f} tok/s, {ms:.3f} ms/step, U={entry['unique_experts_per_layer']:.1f}"
             + (f", weight stream {entry['weight_stream_GBps']:.0f} GB/s" if "weight_stream_GBps" in entry else ""))
 
+    kernels = kernels_leg(args, d, mw, ctx, slots, dev, L) if args.kernels == "on" else None
     ragged = None
     for s in slots:
         ctx.release(s)
@@ -220,10 +230,14 @@ def main():
     head = sweep[Bh]
     roof = None
     if "kernels" in head:
-        k = head["kernels"]["moe_gateup"]
-        roof = dict(bound="hbm", kernel="grouped expert gate/up + SwiGLU (k_moe, gate/up)",
+        fused = "moe" in head["kernels"]
+        k = head["kernels"]["moe" if fused else "moe_gateup"]
+        roof = dict(bound="hbm",
+                    kernel="grouped expert products, one launch (k_moe_fused: gate/up + SwiGLU, then down)" if fused
+                    else "grouped expert gate/up + SwiGLU (k_moe, gate/up)",
                     achieved=k["GBps"], peak=PEAK_HBM_GBPS, unit="GB/s",
-                    frac=k["GBps"] / PEAK_HBM_GBPS if k["GBps"] else None, traffic=measured_traffic(),
+                    frac=k["GBps"] / PEAK_HBM_GBPS if k["GBps"] else None,
+                    traffic=measured_traffic("moe" if fused else "moe_gateup"),
                     bytes_per_launch=k["bytes_per_launch"], avg_launch_us=k["avg_us"])
     out = {
         "metric": METRIC,
@@ -249,6 +263,7 @@ def main():
         "hbm_read_ceiling": ceiling,
         "ragged": ragged,
         "prefill": prefill,
+        "kernels": kernels,
         "cpu_baseline": cpu,
         "parity_first_step": parity,
     }
@@ -282,8 +297,30 @@ def read_ceiling(dev, L):
     del src
     top = max(res.values())
     log(f"HBM read ceiling (probe): {top:.0f} GB/s ({res})")
+    # a phase boundary inside one persistent launch (device-wide barrier) against
+    # a launch boundary (back-to-back empty launches of the same shape)
+    scratch = torch.zeros(1 << 14, dtype=torch.uint8, device=dev)
+    sync = {}
+    for grid in (256, 512):
+        per = {}
+        for mode, name in ((0, "barrier_us"), (1, "launch_us")):
+            best = None
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                L.w4_sync_probe(mode, grid, 2000, scratch, scratch.numel(), st)
+                b.record(st)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b)
+                best = ms if best is None else min(best, ms)
+            per[name] = best * 1e3 / 2000
+        per["barrier_wait_timed_out"] = bool(scratch[4:8].view(torch.int32).item() != 0)
+        sync[str(grid)] = per
+    log(f"device-wide barrier vs launch boundary: {sync}")
     return dict(GBps=top, frac_of_peak=top / PEAK_HBM_GBPS, bytes=nbytes, by_grid=res,
-                kernel="w4_read_probe: one pass of 16-byte loads, 256-thread work-groups")
+                kernel="w4_read_probe: one pass of 16-byte loads, 256-thread work-groups",
+                sync_probe=dict(by_grid=sync, kind="w4_sync_probe: device-wide barrier among co-resident 512-thread "
+                                                     "work-groups (two-level counters) vs back-to-back empty launches"))
 
 
 def ragged_leg(args, d, ctx, dev, L):
@@ -388,6 +425,138 @@ def prefill_leg(args, d, ctx, dev, L):
     return out
 
 
+def kernels_leg(args, d, mw, ctx, slots, dev, L):
+    """Each hot kernel alone at its own shapes, timed per launch with HIP events
+    recorded by the launch's own dispatch (w4_profile_begin/end), over enough
+    distinct operands per pass (>= 1 GiB) that no launch finds them in the 256 MB
+    memory-side cache:
+    - dense W4A16 products, N x K = 5120 x 2048 (fused q/k/v) and 2048 x 4096
+      (output projection), group 128, x ~ N(0,1), B in {1, 2, 4, 8, 16, 32}: a
+      249-layer dense-only bank, one launch per distinct weight copy (199 and
+      249 copies = 1.07 and 1.08 GB);
+    - grouped experts (hidden 2048, 128 experts, intermediate 768, top-8) with
+      given router logits in the disjoint (N(0,1)) and skewed (6 shared + 2
+      private experts per stream) regimes, B in {1, 4, 8, 32}, cycling the 48
+      layers' expert banks (311 MB each);
+    - slot-indexed decode attention at the streams' current positions
+      (prompts U{1..2048}), B in {1, 4, 8, 16, 32}, cycling the 48 layers' KV.
+    Beside them, the oracle's host GB/s on the same dense and expert shapes."""
+    import dataclasses
+
+    import torch
+
+    import oracle
+    from int4_w4a16_group_amd import inputs
+    from int4_w4a16_group_amd.engine import Context
+
+    def wb(N, K):
+        return N * K // 2 + N * (K // d.group) * 2
+
+    def f16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    out = dict(dense={}, moe={}, attention={})
+    # ---- dense products
+    dd = dataclasses.replace(d, n_layers=249, n_experts=1, top_k=1, moe_inter=128, vocab=16)
+    t0 = time.time()
+    dmw = inputs.make_model(dd, args.seed + 2)
+    dctx = Context(dd, 32, 64, dev)
+    dctx.load_model(dmw)
+    log(f"dense-only bank {dctx.bank_bytes / 1e9:.2f} GB loaded in {time.time() - t0:.1f}s")
+    nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * d.head_dim
+    qd = d.n_q_heads * d.head_dim
+    for name, tensor, N, K in (("qkv_5120x2048", L.W4_T_QKV, nqkv, d.hidden), ("o_2048x4096", L.W4_T_O, d.hidden, qd)):
+        R = -(-(1 << 30) // wb(N, K))
+        res = {}
+        for B in (1, 2, 4, 8, 16, 32):
+            x = f16(inputs.normal_f16(inputs.rng(args.seed, inputs.T_X, B, N, K), (B, K)))
+            y = torch.empty((B, N), dtype=torch.int16, device=dev)
+            for l in range(R):
+                L.w4_gemm(dctx.ctx, l, tensor, 0, B, x, y, dctx.stream)
+            torch.cuda.synchronize()
+            L.w4_profile_begin(dctx.ctx, L.W4_K_DENSE)
+            for _ in range(2):
+                for l in range(R):
+                    L.w4_gemm(dctx.ctx, l, tensor, 0, B, x, y, dctx.stream)
+            kms, n = L.w4_profile_end(dctx.ctx)
+            byt = wb(N, K) + B * (K + N) * 2
+            res[str(B)] = dict(avg_us=kms / n * 1e3, GBps=byt * n / (kms * 1e-3) / 1e9, bytes_per_launch=byt)
+        # the oracle on the same shape (one distinct copy, B = 1 and 32)
+        host = {}
+        lw = dmw.layers[0].qkv if tensor == L.W4_T_QKV else dmw.layers[0].o
+        for B in (1, 32):
+            x = inputs.normal_f16(inputs.rng(args.seed, inputs.T_X, B, N, K), (B, K))
+            t1 = time.perf_counter()
+            oracle.w4_gemm(x, lw.packed, lw.scales, d.group)
+            host[str(B)] = wb(N, K) / (time.perf_counter() - t1) / 1e9
+        out["dense"][name] = dict(copies=R, distinct_GB=R * wb(N, K) / 1e9, by_B=res, oracle_host_GBps=host)
+        log(f"dense {name}: " + ", ".join(f"B={b} {v['avg_us']:.1f} us {v['GBps']:.0f} GB/s" for b, v in res.items())
+            + f"; oracle host {host}")
+    dctx.close()
+    del dmw
+    # ---- grouped experts on the full model's banks
+    wgu, wdn = 2 * wb(d.moe_inter, d.hidden), wb(d.hidden, d.moe_inter)
+    om = oracle.Model(mw)
+    io = d.top_k * (d.hidden + d.moe_inter) * 2
+    for regime in ("disjoint", "skewed"):
+        res = {}
+        for B in (1, 4, 8, 32):
+            xh, lg, _ = inputs.moe_case(args.seed, B, regime)
+            x, lgd = f16(xh), torch.from_numpy(lg).to(dev)
+            y = torch.empty((B, d.hidden), dtype=torch.int16, device=dev)
+            ids = torch.empty((d.n_layers, B, d.top_k), dtype=torch.int32, device=dev)
+            entry = {}
+            # one launch (fused) and the two-launch form, same results
+            for fused, fams in ((1, (("fused", L.W4_K_MOE),)),
+                                (0, (("gateup", L.W4_K_MOE_GATEUP), ("down", L.W4_K_MOE_DOWN)))):
+                L.w4_set_option(ctx.ctx, L.W4_OPT_FUSED_MOE, fused)
+                for l in range(4):
+                    L.w4_moe(ctx.ctx, l, B, x, lgd, y, ids[l], ctx.stream)
+                for fam, kid in fams:
+                    torch.cuda.synchronize()
+                    L.w4_profile_begin(ctx.ctx, kid)
+                    for l in range(d.n_layers):
+                        L.w4_moe(ctx.ctx, l, B, x, lgd, y, ids[l], ctx.stream)
+                    kms, n = L.w4_profile_end(ctx.ctx)
+                    r = ids.cpu().numpy()
+                    U = float(np.mean([len(np.unique(r[l])) for l in range(d.n_layers)]))
+                    wbytes = {"fused": wgu + wdn, "gateup": wgu, "down": wdn}[fam]
+                    byt = U * wbytes + B * io * (2 if fam == "fused" else 1)
+                    entry[fam] = dict(avg_us=kms / n * 1e3, GBps=byt / (kms / n * 1e-3) / 1e9, bytes_per_launch=byt)
+            L.w4_set_option(ctx.ctx, L.W4_OPT_FUSED_MOE, 1 if args.fused_moe == "on" else 0)
+            entry["unique_experts"] = U
+            res[str(B)] = entry
+        xh, lg, _ = inputs.moe_case(args.seed, 8, regime)
+        t1 = time.perf_counter()
+        _, oid, _ = oracle.moe(om, 0, xh, lg)
+        host = len(np.unique(oid)) * (wgu + wdn) / (time.perf_counter() - t1) / 1e9
+        out["moe"][regime] = dict(by_B=res, oracle_host_GBps_B8=host)
+        log(f"moe {regime}: " + ", ".join(
+            f"B={b} U={v['unique_experts']:.0f} fused {v['fused']['avg_us']:.1f} us {v['fused']['GBps']:.0f} GB/s, "
+            f"gate/up {v['gateup']['avg_us']:.1f} + down {v['down']['avg_us']:.1f} us" for b, v in res.items())
+            + f"; oracle host {host:.1f} GB/s")
+    # ---- attention at the streams' current positions
+    res = {}
+    for B in (1, 4, 8, 16, 32):
+        sl = slots[:B]
+        pos = np.array([ctx.position(s) for s in sl], np.float64)
+        q, kn, vn = (f16(a) for a in inputs.attn_step_inputs(args.seed, 0, B, d.n_q_heads, d.n_kv_heads, d.head_dim))
+        o = torch.empty((B, d.n_q_heads, d.head_dim), dtype=torch.int16, device=dev)
+        for l in range(4):
+            L.w4_attn_decode(ctx.ctx, l, sl, q, kn, vn, o, ctx.stream)
+        torch.cuda.synchronize()
+        L.w4_profile_begin(ctx.ctx, L.W4_K_ATTENTION)
+        for l in range(d.n_layers):
+            L.w4_attn_decode(ctx.ctx, l, sl, q, kn, vn, o, ctx.stream)
+        kms, n = L.w4_profile_end(ctx.ctx)
+        byt = float(np.sum(pos + 1)) * d.n_kv_heads * d.head_dim * 4 + B * (qd * 4 + d.n_kv_heads * d.head_dim * 4)
+        res[str(B)] = dict(avg_us=kms / n * 1e3, GBps=byt / (kms / n * 1e-3) / 1e9, bytes_per_launch=byt,
+                           mean_position=float(pos.mean()))
+    out["attention"] = dict(by_B=res, layers_cycled=d.n_layers)
+    log("attention: " + ", ".join(f"B={b} {v['avg_us']:.1f} us {v['GBps']:.0f} GB/s" for b, v in res.items()))
+    return out
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -418,7 +587,7 @@ def step_bytes(d, B, U, pos0, steps):
     ctxlen = pos0.astype(np.float64) + 1 + (steps - 1) / 2.0   # mean attended length over the steps
     attn = float(d.n_layers * np.sum(ctxlen) * d.n_kv_heads * d.head_dim * 2 * 2)
     emb = B * (H // 2 + (H // g) * 2)
-    return dict(dense=dense, router=router, moe_gateup=gateup, moe_down=down, attention=attn,
+    return dict(dense=dense, router=router, moe_gateup=gateup, moe_down=down, moe=gateup + down, attention=attn,
                 total=dense + router + gateup + down + attn + emb)
 
 

@@ -271,13 +271,37 @@ int w4_last_step_counts(const w4_ctx* ctx, int32_t* launches, int32_t* syncs);
  * 16-byte aligned; W4_E_INVALID otherwise.  Time it with events on `stream`. */
 int w4_read_probe(const void* src_dev, size_t bytes, void* sink_dev, int32_t grid, void* stream);
 
+/* Context options (a verification and measurement aid; the defaults are the
+ * fast path).  W4_OPT_FUSED_MOE, default 0: the grouped expert products of a
+ * layer as two launches.  1: as one launch, the down product's tiles starting
+ * on compute units whose gate/up share is done (per-unit completion counters
+ * with bounded device-side waits; a wait that runs out is reported as
+ * W4_E_HIP by the next enqueueing call or w4_check_errors); measured slower
+ * than two launches at B >= 4 and equal at B = 1 on MI355X.  The results are
+ * the same bit for bit.  The fused form applies where the gate/up reduction
+ * length is at most 2048 and the down product's is at most the gate/up's.
+ * W4_E_INVALID for an unknown option or value. */
+enum { W4_OPT_FUSED_MOE = 1 };
+int w4_set_option(w4_ctx* ctx, int32_t option, int32_t value);
+
+/* Device-wide barrier probe (a measurement aid, not part of the step): the
+ * cost of a phase boundary inside one persistent launch against that of a
+ * launch boundary.  mode 0: n barriers among `grid` co-resident 512-thread
+ * work-groups in one launch (two-level device-scope counters, bounded waits;
+ * a wait that runs out sets word 1 of scratch); grid must not exceed the
+ * work-groups the device keeps resident.  mode 1: n back-to-back launches of
+ * an empty kernel of the same shape.  scratch_dev: caller-owned, at least
+ * 2304 bytes.  W4_E_INVALID for bad arguments.  Time it with events on `stream`. */
+int w4_sync_probe(int32_t mode, int32_t grid, int32_t n, void* scratch_dev, size_t bytes, void* stream);
+
 /* Kernel families that w4_profile_begin can time. */
 enum {
   W4_K_DENSE = 1,      /* dense W4A16 products: q/k/v, o, output projection */
   W4_K_MOE_GATEUP = 2, /* grouped expert gate/up + SwiGLU */
   W4_K_MOE_DOWN = 3,   /* grouped expert down */
   W4_K_ATTENTION = 4,  /* split-KV decode attention (one launch, split combine included) */
-  W4_K_ROUTER = 5      /* MoE front end: norm, router product, top-k, bucketing (one launch) */
+  W4_K_ROUTER = 5,     /* MoE front end: norm, router product, top-k, bucketing (one launch) */
+  W4_K_MOE = 6         /* grouped expert products in one launch (gate/up + SwiGLU, then down) */
 };
 /* Record a HIP event pair around every launch of one kernel family in the
  * calls that follow (on the stream each call is given), until

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libw4moe.so")
 
 W4_OK, W4_E_INVALID, W4_E_NO_SLOT, W4_E_CONTEXT_CAP, W4_E_BAD_SLOT, W4_E_NOT_READY, W4_E_HIP, W4_E_UNSUPPORTED = \
     0, -1, -2, -3, -4, -5, -6, -7
-W4_K_DENSE, W4_K_MOE_GATEUP, W4_K_MOE_DOWN, W4_K_ATTENTION, W4_K_ROUTER = 1, 2, 3, 4, 5
+W4_K_DENSE, W4_K_MOE_GATEUP, W4_K_MOE_DOWN, W4_K_ATTENTION, W4_K_ROUTER, W4_K_MOE = 1, 2, 3, 4, 5, 6
+W4_OPT_FUSED_MOE = 1
 (W4_T_QKV, W4_T_O, W4_T_ROUTER, W4_T_GATE, W4_T_UP, W4_T_DOWN, W4_T_EMBED, W4_T_LM_HEAD, W4_T_ATTN_NORM,
  W4_T_MOE_NORM, W4_T_FINAL_NORM) = range(11)
 
@@ -54,6 +55,8 @@ _SIGS = {
     "w4_slot_prefill": (C.c_int, [_vp, _i32, _vp, _vp, _sz, _vp, _vp, _vp, _vp]),
     "w4_check_errors": (C.c_int, [_vp]),
     "w4_read_probe": (C.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "w4_sync_probe": (C.c_int, [_i32, _i32, _i32, _vp, _sz, _vp]),
+    "w4_set_option": (C.c_int, [_vp, _i32, _i32]),
     "w4_route_noalloc": (C.c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "w4_decode_step": (C.c_int, [_vp, _i32, C.POINTER(_i32), _vp, _vp, _vp, _vp, _vp]),
     "w4_gemm": (C.c_int, [_vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
@@ -207,6 +210,14 @@ def w4_slot_read_kv(ctx, slot: int, k, v, stream=None):
 
 def w4_read_probe(src, nbytes: int, sink, grid: int, stream=None):
     return _check(None, lib().w4_read_probe(_p(src), nbytes, _p(sink), grid, _s(stream)))
+
+
+def w4_set_option(ctx, option: int, value: int):
+    return _check(ctx, lib().w4_set_option(ctx, option, value))
+
+
+def w4_sync_probe(mode: int, grid: int, n: int, scratch, nbytes: int, stream=None):
+    return _check(None, lib().w4_sync_probe(mode, grid, n, _p(scratch), nbytes, _s(stream)))
 
 
 def w4_route_noalloc(B: int, n_experts: int, top_k: int, logits, ids, w, counts=None, offsets=None,

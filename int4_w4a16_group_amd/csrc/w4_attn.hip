@@ -168,8 +168,6 @@ hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uin
 struct AttnArgs {
   KV kv;
   int layer, Hq, nsmax;
-  const int32_t* slot;
-  const int32_t* pos;
   // this step's q, k, v of stream b: q at q + b*ldq ([Hq][D]), k and v at
   // knew/vnew + b*ldkv ([Hkv][D]); rotated at the stream's position through
   // table (cos, sin of p * theta^(-2i/D), [cap][D/2]) when table is not null
@@ -181,8 +179,10 @@ struct AttnArgs {
   float* part_o;      // [B][Hq][nsmax][D]  split partials (unnormalised)
   float* part_ml;     // [B][Hq][nsmax][2]  (M_s in log2 units, L_s)
   unsigned* ticket;   // [B][Hkv], zero between launches
-  const int32_t* splits;  // work-group x -> (stream b << 16 | split << 8 | kv head): every split of every
-                          // stream for every kv head, no idle groups
+  // work-group x -> 8-byte entry (stream b << 16 | split << 8 | kv head,
+  // slot << 16 | position): every split of every stream for every kv head,
+  // no idle groups
+  const int32_t* splits;
   uint16_t* o;        // [B][Hq*D]: row-major (o_rows == 0) or an activation panel with o_rows rows
   int o_rows;
   float scale;        // log2(e) / sqrt(D)
@@ -277,9 +277,9 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
   __shared__ __align__(16) uint16_t s_k[4][D];
   __shared__ int s_last;
   extern __shared__ float Ob[];  // [4 waves][G][D]
-  const int bs_ = a.splits[blockIdx.x];
-  const int b = bs_ >> 16, sp = (bs_ >> 8) & 0xFF, g = bs_ & 0xFF;
-  const int p = a.pos[b];
+  const int2 ent = reinterpret_cast<const int2*>(a.splits)[blockIdx.x];
+  const int b = ent.x >> 16, sp = (ent.x >> 8) & 0xFF, g = ent.x & 0xFF;
+  const int p = ent.y & 0xFFFF, slot_b = ent.y >> 16;
   const int nch = p / 64 + 1, ns = attn_splits(p);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int Hkv = a.kv.Hkv, G = a.Hq / Hkv;
@@ -292,7 +292,7 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f4{0.f, 0.f, 0.f, 0.f};
   if (live) {
-    const size_t base = kv_base(a.kv, a.layer, a.slot[b], g);
+    const size_t base = kv_base(a.kv, a.layer, slot_b, g);
     const int c0 = c * 64;
     const bool last = (c0 + 63 > p);
     // K operands now; V once the scores are issued, into the registers K
@@ -518,8 +518,7 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
   if (tid == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
-                            const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
+hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
                             unsigned* ticket, uint16_t* o, hipStream_t st, void* prof, int o_rows) {
   (void)B;
@@ -528,8 +527,6 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   a.layer = layer;
   a.Hq = Hq;
   a.nsmax = attn_splits(kv.cap - 1);
-  a.slot = slot;
-  a.pos = pos;
   a.q = q;
   a.knew = knew;
   a.vnew = vnew;

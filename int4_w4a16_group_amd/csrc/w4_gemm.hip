@@ -489,6 +489,265 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ fused expert products
+// The grouped gate/up (+ SwiGLU) and down products in one launch, with the
+// arithmetic of k_moe for both, bit for bit.  Work-group i:
+//   1. runs its range of gate/up items, the range and the item loop of the
+//      gate/up launch (8 waves own the K slices), but stores the activations
+//      with device-scope stores;
+//   2. once its range is done (every store complete), adds the number of
+//      items it finished of each unit to that unit's counter done[u] (zeroed
+//      by the bucketing that built the units); the work-group whose add
+//      completes a unit writes the launch's epoch into the unit's ready
+//      word, in eight copies;
+//   3. requests the weights of its first down items, then one thread waits
+//      until every unit its down range touches is ready (polling the copy
+//      blockIdx % 8, so few work-groups poll one line), and the work-group
+//      runs the range in S = NW / NWd sub-groups of NWd waves (the down
+//      product's slices), sub-group s a contiguous part of the range, reading
+//      the activations through the caches after an acquire (the waiting
+//      thread invalidates this compute unit's and this XCD's stale lines).
+// Counters and ready copies sit 256 bytes apart.  The down product's tiles
+// therefore start on compute units whose gate/up share is done while others
+// still finish theirs.  Gate/up items never wait and the grid is the number
+// of work-groups the device keeps resident, so every wait ends; one that
+// exceeds its bound sets *err (a host-visible word) and goes on.
+struct MoeFusedArgs {
+  MoeArgs gu, dn;
+  uint32_t* done;   // [units_cap] x kDoneStride words: zero for the units of this launch
+  uint32_t* ready;  // [units_cap][8] x kDoneStride words: never equal to a later epoch
+  uint32_t epoch;   // this launch's value, larger than any earlier one on these words
+  int32_t* err;     // host-mapped word
+};
+
+constexpr int kWaitSpins = 1 << 18;
+
+template <int NCH, int NCHD, int G, int LB>
+__global__ void __launch_bounds__(LB) k_moe_fused(MoeFusedArgs fa) {
+  extern __shared__ float red[];
+  const MoeArgs& a = fa.gu;
+  constexpr int NS = NCH * 128 / G;
+  const int NW = blockDim.x >> 6;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int T = a.ntiles;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int4 rec0 = a.units[min(tid, a.units_cap - 1)], rec1 = a.units[min(tid + nth, a.units_cap - 1)];
+  const int nu = *a.n_units;
+  const long long total = (long long)nu * T;
+  int f_begin, f_end;
+  {
+    const long long C = min((long long)a.ncu, (long long)gridDim.x), dq = a.dshare;
+    const long long W = C * (1000 + dq) + ((long long)gridDim.x - C) * (1000 - dq);
+    auto cum = [&](long long i) {
+      return i <= C ? i * (1000 + dq) : C * (1000 + dq) + (i - C) * (1000 - dq);
+    };
+    f_begin = (int)(cum(blockIdx.x) * total / W);
+    f_end = (int)(cum(blockIdx.x + 1) * total / W);
+  }
+  const int bufsz = 2 * NW * 256;
+  const int i16 = lane & 15;
+  const DqConst dk;
+  int4* lrec = reinterpret_cast<int4*>(red + 2 * bufsz);
+  if (tid < a.units_cap) lrec[tid] = rec0;
+  if (tid + nth < a.units_cap) lrec[tid + nth] = rec1;
+  for (int i = tid + 2 * nth; i < a.units_cap; i += nth) lrec[i] = a.units[i];
+  __syncthreads();
+
+  // ---- 1. gate/up items [f_begin, f_end)
+  if (f_begin < f_end) {
+    const int last = f_end - 1;
+    const int kbase = w * NCH * 128;
+    auto stage_load = [&](Stage<NCH, G>& g0, Stage<NCH, G>& g1, int f) {
+      const int fc = min(f, last), u = __builtin_amdgcn_readfirstlane(fc / T), t = fc - u * T;
+      const int e = lrec[u].x;
+      g0.load(a.t0 + a.tile_stride * e, a.s0 + a.scale_stride * e, a.K, t, w, lane);
+      g1.load(a.t1 + a.tile_stride * e, a.s1 + a.scale_stride * e, a.K, t, w, lane);
+    };
+    XRegs<1, NCH * 4> x;
+    int xu = -1, nrow = 0;
+    auto load_x = [&](int uv, int grow) {
+      const int u = __builtin_amdgcn_readfirstlane(uv);
+      const uint16_t* xr = a.x + (size_t)grow * a.ldx + kbase + 8 * (lane >> 4);
+#pragma unroll
+      for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
+      xu = u;
+      nrow = a.unit_rows[min(u + 1, nu - 1) * 16 + i16];
+    };
+    int buf = 0;
+    auto run = [&](const Stage<NCH, G>& g0, const Stage<NCH, G>& g1, int f, bool valid) {
+      const int u = __builtin_amdgcn_readfirstlane(min(f, last) / T), t = min(f, last) - u * T;
+      const int4 un = lrec[u];
+      const int off = un.y, m = un.z;
+      float sv0[NS], sv1[NS];
+      g0.scales_f32(sv0);
+      f4 acc0[1] = {f4{0.f, 0.f, 0.f, 0.f}}, acc1[1] = {f4{0.f, 0.f, 0.f, 0.f}};
+      tile_mac<1, NCH, G>(x, g0.w, sv0, acc0, dk);
+      g1.scales_f32(sv1);
+      tile_mac<1, NCH, G>(x, g1.w, sv1, acc1, dk);
+      float* rb = red + buf * bufsz;
+      f4* r4 = reinterpret_cast<f4*>(rb);
+      r4[w * 64 + lane] = acc0[0];
+      r4[(NW + w) * 64 + lane] = acc1[0];
+      __syncthreads();
+      constexpr int NB = LB / 64;
+      for (int ob = 0; ob < 256; ob += NW * 32) {
+        const int o = ob + w * 32 + (lane & 31), pp = lane >> 5;
+        const int oc = min(o, 255);
+        const int i = oc >> 4, j = oc & 15;
+        const float* p = rb + pp * NW * 256 + ((i >> 2) * 16 + j) * 4 + (i & 3);
+        float r[NB];
+#pragma unroll
+        for (int k = 0; k < NB; ++k) r[k] = p[min(k, NW - 1) * 256];
+        float v = r[0];
+#pragma unroll
+        for (int k = 1; k < NB; ++k) v = k < NW ? v + r[k] : v;
+        const float vu = __shfl_xor(v, 32, 64);
+        const int n = t * 16 + j;
+        if (pp == 0 && o < 256 && valid && i < m && n < a.N) {
+          const float gt = h2f(f2h(v)), up = h2f(f2h(vu));
+          const float silu = gt / (1.0f + expf(-gt));
+          __hip_atomic_store(a.out + (size_t)(off + i) * a.N + n, f2h(silu * up), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      buf ^= 1;
+    };
+    Stage<NCH, G> a0, a1, b0, b1;
+    stage_load(a0, a1, f_begin);
+    load_x(f_begin / T, a.unit_rows[(f_begin / T) * 16 + i16]);
+    stage_load(b0, b1, f_begin + 1);
+    for (int f = f_begin; f < f_end; f += 2) {
+      set_prio_level((4 * (f_end - f)) / (f_end - f_begin + 1));
+      run(a0, a1, f, true);
+      if (f + 1 < f_end && (f + 1) / T != xu) load_x((f + 1) / T, nrow);
+      stage_load(a0, a1, f + 2);
+      run(b0, b1, f + 1, f + 1 < f_end);
+      if (f + 2 < f_end && (f + 2) / T != xu) load_x((f + 2) / T, nrow);
+      stage_load(b0, b1, f + 3);
+    }
+    set_prio_level(0);
+  }
+  // ---- 2. this range's items are stored: count them per unit
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (f_begin < f_end) {
+    const int u0 = f_begin / T, u1 = (f_end - 1) / T;
+    for (int u = u0 + tid; u <= u1; u += nth) {
+      const uint32_t n = (uint32_t)(min(f_end, (u + 1) * T) - max(f_begin, u * T));
+      const uint32_t old = __hip_atomic_fetch_add(fa.done + (size_t)u * kDoneStride, n, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      if (old + n == (uint32_t)T)
+        for (int c = 0; c < 8; ++c)
+          __hip_atomic_store(fa.ready + ((size_t)u * 8 + c) * kDoneStride, fa.epoch, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // ---- 3. down items of this work-group, in sub-groups of NWd waves
+  const MoeArgs& d = fa.dn;
+  constexpr int NSD = NCHD * 128 / G;
+  const int NWd = d.K / (NCHD * 128);
+  const int S = NW / NWd;
+  const int sg = w / NWd, ws = w - sg * NWd;
+  const bool act = sg < S;
+  const int Td = d.ntiles;
+  const long long dtotal = (long long)nu * Td;
+  const int d0 = (int)(blockIdx.x * dtotal / gridDim.x), d1 = (int)((blockIdx.x + 1) * dtotal / gridDim.x);
+  const int len = d1 - d0, n_iter = (len + S - 1) / S;
+  const int sb = act ? d0 + (int)((long long)sg * len / S) : d0;
+  const int se = act ? d0 + (int)((long long)(sg + 1) * len / S) : d0;
+  const int cnt = se - sb;
+  const bool any = act && cnt > 0;
+  const int dlast = any ? se - 1 : 0;
+  const int kb = ws * NCHD * 128;
+  float* dred = red + (act ? sg : 0) * 2 * NWd * 256;
+  auto dstage = [&](Stage<NCHD, G>& g, int i) {
+    const int f = min(sb + i, dlast), u = __builtin_amdgcn_readfirstlane(f / Td), t = f - u * Td;
+    const int e = lrec[u].x;
+    g.load(d.t0 + d.tile_stride * e, d.s0 + d.scale_stride * e, d.K, t, ws, lane);
+  };
+  XRegs<1, NCHD * 4> xd;
+  int xdu = -1;
+  auto dload_x = [&](int uv) {
+    const int u = __builtin_amdgcn_readfirstlane(uv);
+    const int4 un = lrec[u];
+    const int row = un.y + min(i16, un.z - 1);
+    const uint16_t* xr = d.x + (size_t)row * d.ldx + kb + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < NCHD * 4; ++ks) xd.a[0][ks] = ld_h8(xr + ks * 32);
+    xdu = u;
+  };
+  int dbuf = 0;
+  auto drun = [&](const Stage<NCHD, G>& g, int i) {
+    const bool valid = any && i < cnt;
+    const int f = min(sb + i, dlast);
+    const int u = __builtin_amdgcn_readfirstlane(f / Td), t = f - u * Td;
+    const int4 un = lrec[u];
+    const int off = un.y, m = un.z;
+    float* rb = dred + dbuf * NWd * 256;
+    if (any) {
+      float sv[NSD];
+      g.scales_f32(sv);
+      f4 acc[1] = {f4{0.f, 0.f, 0.f, 0.f}};
+      tile_mac<1, NCHD, G>(xd, g.w, sv, acc, dk);
+      reinterpret_cast<f4*>(rb)[ws * 64 + lane] = acc[0];
+    }
+    __syncthreads();
+    if (any)
+      reduce_tile_sub<1, LB / 64>(rb, NWd, tid - sg * NWd * 64, NWd * 64, [&](int i_, int j, float v) {
+        const int n = t * 16 + j;
+        if (valid && i_ < m && n < d.N) d.out[(size_t)(off + i_) * d.N + n] = f2h(v);
+      });
+    dbuf ^= 1;
+  };
+  // three stages per sub-group: with NWd of the NW waves busy, as many tile
+  // loads in flight per compute unit as the down launch's two stages over
+  // its six three-wave work-groups
+  Stage<NCHD, G> da, db, dc;
+  if (any) {
+    dstage(da, 0);
+    dstage(db, 1);
+    dstage(dc, 2);
+  }
+  // every unit of the range ready (one thread waits; the barrier passes it on)
+  if (tid == 0 && d0 < d1) {
+    const uint32_t* rw = fa.ready + (size_t)(blockIdx.x & 7) * kDoneStride;
+    for (int u = d0 / Td; u <= (d1 - 1) / Td; ++u)
+      for (int spin = 0; __hip_atomic_load(rw + (size_t)u * 8 * kDoneStride, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) != fa.epoch;
+           ++spin) {
+        if (spin > kWaitSpins) {
+          __hip_atomic_store(fa.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    // acquire: this compute unit's and this XCD's caches hold no line of the
+    // activations from before (they were written through to memory with
+    // device-scope stores), so the plain loads below read them fresh
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  if (any) dload_x(sb / Td);
+  for (int i = 0; i < n_iter; i += 3) {
+    drun(da, i);
+    if (any) {
+      if (i + 1 < cnt && (sb + i + 1) / Td != xdu) dload_x((sb + i + 1) / Td);
+      dstage(da, i + 3);
+    }
+    drun(db, i + 1);
+    if (any) {
+      if (i + 2 < cnt && (sb + i + 2) / Td != xdu) dload_x((sb + i + 2) / Td);
+      dstage(db, i + 4);
+    }
+    drun(dc, i + 2);
+    if (any) {
+      if (i + 3 < cnt && (sb + i + 3) / Td != xdu) dload_x((sb + i + 3) / Td);
+      dstage(dc, i + 5);
+    }
+  }
+}
+
 typedef void (*MoeKernel)(MoeArgs);
 
 template <bool GU, int NCH, int LB>
@@ -519,18 +778,19 @@ static int cu_count() {
 // Grid = the number of work-groups the device keeps resident at once
 // (occupancy query, cached per kernel), so the persistent loop covers the
 // whole chip in one round.
-static int resident_grid(MoeKernel k, int threads, size_t shm) {
+static int resident_grid(const void* k, int threads, size_t shm) {
   struct Entry {
-    MoeKernel k;
+    const void* k;
     int threads;
+    size_t shm;
     int grid;
   };
   static Entry cache[64];
   static int n = 0;
   for (int i = 0; i < n; ++i)
-    if (cache[i].k == k && cache[i].threads == threads) return cache[i].grid;
+    if (cache[i].k == k && cache[i].threads == threads && cache[i].shm == shm) return cache[i].grid;
   int per_cu = 0, dev = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), threads, shm) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, threads, shm) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -541,14 +801,30 @@ static int resident_grid(MoeKernel k, int threads, size_t shm) {
   (void)hipGetDevice(&dev);
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
   const int grid = per_cu * cus;
-  if (n < 64) cache[n++] = Entry{k, threads, grid};
+  if (n < 64) cache[n++] = Entry{k, threads, shm, grid};
   return grid;
 }
+
+static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_t* x, int ldx, const RouteOut& r,
+                        uint16_t* out);
 
 static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, const uint16_t* x, int ldx,
                                     const RouteOut& r, uint16_t* out, hipStream_t st) {
   const int nch = nch_for(m0.K);
   const int NW = m0.K / (nch * 128);
+  const MoeArgs a = moe_args(gateup, m0, m1, x, ldx, r, out);
+  MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);
+  if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
+  // the records of every unit in LDS (at most kMaxUnits in a decode step, whose
+  // launch shape is kept; a prefill can have more)
+  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)std::max(r.units_cap, kMaxUnits) * 16;
+  const int grid = resident_grid(reinterpret_cast<const void*>(k), NW * 64, shm);
+  w4_launch(k, dim3(grid), dim3(NW * 64), (uint32_t)shm, st, a);
+  return hipGetLastError();
+}
+
+static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_t* x, int ldx, const RouteOut& r,
+                        uint16_t* out) {
   MoeArgs a;
   a.t0 = m0.tiles;
   a.t1 = m1 ? m1->tiles : nullptr;
@@ -568,13 +844,44 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   a.out = out;
   a.ncu = cu_count();
   a.dshare = gateup ? 75 : 0;  // measured: gate/up 38.5 us at 60-120 against 40.0 at 0
-  MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);
+  return a;
+}
+
+typedef void (*MoeFusedKernel)(MoeFusedArgs);
+template <int NCH, int NCHD>
+static MoeFusedKernel fused_pick_g(int g) {
+  switch (g) {
+    case 32: return k_moe_fused<NCH, NCHD, 32, 512>;
+    case 64: return k_moe_fused<NCH, NCHD, 64, 512>;
+    default: return k_moe_fused<NCH, NCHD, 128, 512>;
+  }
+}
+
+bool moe_fused_ok(const Mat& gate0, const Mat& down0) {
+  const int nch = nch_for(gate0.K), NW = gate0.K / (nch * 128);
+  const int nchd = nch_for(down0.K), NWd = down0.K / (nchd * 128);
+  return NW <= 8 && NWd <= NW && gate0.g == down0.g;
+}
+
+hipError_t launch_moe_fused(const Mat& gate0, const Mat& up0, const Mat& down0, const uint16_t* x, int ldx,
+                            const RouteOut& r, uint16_t* act, uint16_t* y, uint32_t* ready, uint32_t epoch,
+                            int32_t* err, hipStream_t st) {
+  if (!moe_fused_ok(gate0, down0) || !r.done || !ready || !err || epoch == 0) return hipErrorInvalidValue;
   if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
-  // the records of every unit in LDS (at most kMaxUnits in a decode step, whose
-  // launch shape is kept; a prefill can have more)
-  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)std::max(r.units_cap, kMaxUnits) * 16;
-  const int grid = resident_grid(k, NW * 64, shm);
-  w4_launch(k, dim3(grid), dim3(NW * 64), (uint32_t)shm, st, a);
+  const int nch = nch_for(gate0.K), NW = gate0.K / (nch * 128);
+  const int nchd = nch_for(down0.K);
+  MoeFusedArgs fa;
+  fa.gu = moe_args(true, gate0, &up0, x, ldx, r, act);
+  fa.dn = moe_args(false, down0, nullptr, act, down0.K, r, y);
+  fa.done = r.done;
+  fa.ready = ready;
+  fa.epoch = epoch;
+  fa.err = err;
+  MoeFusedKernel k = nch == 2 ? (nchd == 2 ? fused_pick_g<2, 2>(gate0.g) : fused_pick_g<2, 1>(gate0.g))
+                              : (nchd == 2 ? fused_pick_g<1, 2>(gate0.g) : fused_pick_g<1, 1>(gate0.g));
+  const size_t shm = 2 * (size_t)2 * NW * 1024 + (size_t)std::max(r.units_cap, kMaxUnits) * 16;
+  const int grid = resident_grid(reinterpret_cast<const void*>(k), NW * 64, shm);
+  w4_launch(k, dim3(grid), dim3(NW * 64), (uint32_t)shm, st, fa);
   return hipGetLastError();
 }
 

@@ -411,7 +411,10 @@ __device__ void bucket_core(int E, int k, int B, const int* s_ids, const BucketL
       if (o.counts) o.counts[e] = c;
       if (o.offsets) o.offsets[e] = ec;
       if (u) o.used[eu] = e;
-      for (int j = 0; j < nu; ++j) o.units[en + j] = make_int4(e, ec + 16 * j, min(16, c - 16 * j), 0);
+      for (int j = 0; j < nu; ++j) {
+        o.units[en + j] = make_int4(e, ec + 16 * j, min(16, c - 16 * j), 0);
+        if (o.done) o.done[(size_t)(en + j) * kDoneStride] = 0u;
+      }
     }
     if (e == E - 1) {
       if (o.offsets) o.offsets[E] = ec + c;
@@ -559,7 +562,10 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   for (int e = tid; e < E; e += blockDim.x) {
     const int c = s_cnt[e];
     const int nu = (c + 15) >> 4;
-    for (int j = 0; j < nu; ++j) o.units[s_ub[e] + j] = make_int4(e, s_off[e] + 16 * j, min(16, c - 16 * j), 0);
+    for (int j = 0; j < nu; ++j) {
+      o.units[s_ub[e] + j] = make_int4(e, s_off[e] + 16 * j, min(16, c - 16 * j), 0);
+      if (o.done) o.done[(size_t)(s_ub[e] + j) * kDoneStride] = 0u;
+    }
     if (c > 0 && (c & 15)) {
       const int want = 16 * (nu - 1);  // rank of the last unit's first row
       int seen = 0, first = 0;
@@ -1205,6 +1211,63 @@ __global__ void __launch_bounds__(256) k_read_probe(const uint4* __restrict__ sr
 
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {
   hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(src), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+// Device-wide barrier probe (diagnostic, not part of the step): n barriers
+// among `grid` co-resident 512-thread work-groups in one launch.  Two-level
+// counters: a work-group adds to its group's counter (8 groups by index, 256
+// bytes apart), the last arrival of a group adds to the top counter, and
+// every work-group polls the top counter with device-scope loads.  Each wait
+// is bounded; one that runs out sets ctr[1] and the launch goes on.
+// ctr: [kSyncProbeWords], zero at launch.
+constexpr int kSyncGroups = 8;
+__global__ void __launch_bounds__(512) k_barrier_probe(uint32_t* ctr, int n) {
+  const int g = blockIdx.x % kSyncGroups;
+  const unsigned per = (gridDim.x - g + kSyncGroups - 1) / kSyncGroups;
+  uint32_t* gc = ctr + 64 * (1 + g);
+  for (int i = 1; i <= n; ++i) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned old = __hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == (unsigned)i * per - 1) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned target = (unsigned)i * kSyncGroups;
+      for (int spin = 0; __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target; ++spin) {
+        if (spin > (1 << 16)) {
+          __hip_atomic_store(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// The reference for the probe above: a launch of the same shape that does nothing.
+__global__ void __launch_bounds__(512) k_empty_probe(uint32_t* ctr) {
+  if (threadIdx.x == 0 && blockIdx.x == 0x7fffffff) ctr[2] = 1u;
+}
+
+int sync_probe_max_grid() {
+  int per_cu = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_barrier_probe), 512, 0) !=
+          hipSuccess ||
+      per_cu < 1)
+    return 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
+  return per_cu * cus;
+}
+
+hipError_t launch_sync_probe(int mode, int grid, int n, uint32_t* ctr, hipStream_t st) {
+  if (mode == 0) {
+    hipError_t e = launch_fill_u32(ctr, 0u, kSyncProbeWords, st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_barrier_probe, dim3(grid), dim3(512), 0, st, ctr, n);
+  } else {
+    for (int i = 0; i < n; ++i) hipLaunchKernelGGL(k_empty_probe, dim3(grid), dim3(512), 0, st, ctr);
+  }
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ struct BankPlan {
 
 struct WsPlan {
   size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, rlg, rticket, spart, sticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
-      used, n_used, units, unit_rows, n_units, act, y, logits, next, rows, table, total;
+      used, n_used, units, unit_rows, n_units, done, ready, act, y, logits, next, rows, table, total;
 };
 
 bool geometry_ok(const w4_model_desc* d, std::string* why) {
@@ -123,9 +123,12 @@ BankPlan plan_bank(const w4_model_desc& d) {
 }
 
 // Words uploaded with each step's rows: slot [Bm], position [Bm], sampling
-// parameters [Bm][kSampleParams], then the attention work list.
+// parameters [Bm][kSampleParams], then the attention work list (two words
+// per entry, at an even word offset so its 8-byte entries align).
+size_t split_words_off(int Bm) { return ((2 + (size_t)kSampleParams) * Bm + 1) / 2 * 2; }
+
 size_t row_list_words(const w4_model_desc& d, int Bm, int cap) {
-  return (2 + (size_t)kSampleParams) * Bm + (size_t)Bm * attn_splits(cap - 1) * d.n_kv_heads;
+  return split_words_off(Bm) + 2 * (size_t)Bm * attn_splits(cap - 1) * d.n_kv_heads;
 }
 
 WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
@@ -168,6 +171,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.units = take((E + Bm * k / 16 + 1) * 16);
   w.unit_rows = take((E + Bm * k / 16 + 1) * 16 * 4);
   w.n_units = take(4);
+  w.done = take((E + Bm * k / 16 + 1) * kDoneStride * 4);
+  w.ready = take((E + Bm * k / 16 + 1) * 8 * kDoneStride * 4);
   w.act = take(Bm * k * I * 2);
   w.y = take(Bm * k * H * 2);
   w.logits = take((size_t)Bm * d.vocab * 2);
@@ -185,8 +190,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
 constexpr int kPrefillChunk = 32;
 
 struct PfPlan {
-  size_t h, xn, qkv, attn_o, lg, ids, w, counts, offsets, inv, used, n_used, units, unit_rows, n_units, act, y,
-      part_o, part_ml, aticket, rows, logits, rmask, re8, total;
+  size_t h, xn, qkv, attn_o, lg, ids, w, counts, offsets, inv, used, n_used, units, unit_rows, n_units, done, ready,
+      act, y, part_o, part_ml, aticket, rows, logits, rmask, re8, total;
   size_t row_cap;  // int32 words of the rows region
 };
 
@@ -195,7 +200,7 @@ struct PfPlan {
 size_t pf_row_words(const w4_model_desc& d, int P) {
   size_t n = 0;
   for (int i = 0; i < P; ++i) n += (size_t)attn_splits(i) * d.n_kv_heads;
-  return 2 * (size_t)P + kSampleParams + n;
+  return (2 * (size_t)P + kSampleParams + 1) / 2 * 2 + 2 * n;
 }
 
 PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
@@ -224,6 +229,8 @@ PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
   w.units = take(ucap * 16);
   w.unit_rows = take(ucap * 16 * 4);
   w.n_units = take(4);
+  w.done = take(ucap * kDoneStride * 4);
+  w.ready = take(ucap * 8 * kDoneStride * 4);
   w.act = take(pairs * I * 2);
   w.y = take(pairs * H * 2);
   w.part_o = take((size_t)kPrefillChunk * Hq * nsmax * D * 4);
@@ -265,10 +272,16 @@ struct w4_ctx {
   // memory that the embedding kernel writes through flags_dev (no copy)
   int32_t* flags = nullptr;
   int32_t* flags_dev = nullptr;
+  // a device-side wait that ran out of its bound (fused expert products):
+  // host-mapped word, nonzero once one did
+  int32_t* werr = nullptr;
+  int32_t* werr_dev = nullptr;
+  bool fused_moe = false;  // W4_OPT_FUSED_MOE
+  uint32_t moe_epoch = 0;  // last epoch of a fused expert launch on this context's ready words
   int nsplits = 0;  // attention splits of the rows last uploaded
   // uploaded with each step's rows: slot [Bm], position [Bm], sampling
   // parameters [Bm][kSampleParams], then the attention work list
-  size_t split_off() const { return (2 + (size_t)kSampleParams) * Bm; }
+  size_t split_off() const { return split_words_off(Bm); }
   size_t row_words() const { return row_list_words(d, Bm, cap); }
   const int32_t* dev_rows() { return reinterpret_cast<const int32_t*>(ws + wp.rows); }
   const int32_t* dev_splits() { return dev_rows() + split_off(); }
@@ -350,6 +363,7 @@ struct w4_ctx {
     r.unit_rows = W<int32_t>(wp.unit_rows);
     r.n_units = W<int32_t>(wp.n_units);
     r.units_cap = d.n_experts + Bm * d.top_k / 16 + 1;
+    r.done = W<uint32_t>(wp.done);
     return r;
   }
 };
@@ -379,6 +393,9 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
     HIPCHK(c, hipHostMalloc((void**)&c->flags, sizeof(int32_t) * c->Bm * kRing,
                             hipHostMallocMapped | hipHostMallocCoherent));
     HIPCHK(c, hipHostGetDevicePointer((void**)&c->flags_dev, c->flags, 0));
+    HIPCHK(c, hipHostMalloc((void**)&c->werr, 64, hipHostMallocMapped | hipHostMallocCoherent));
+    HIPCHK(c, hipHostGetDevicePointer((void**)&c->werr_dev, c->werr, 0));
+    *c->werr = 0;
     for (int i = 0; i < kRing; ++i) {
       HIPCHK(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
       HIPCHK(c, hipEventCreateWithFlags(&c->ev_err[i], hipEventDisableTiming));
@@ -393,7 +410,8 @@ int ensure_device(w4_ctx* c, hipStream_t st) {
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.amax_ticket), 0u, (size_t)c->Bm, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.rticket), 0u, (size_t)c->Bm, st));
     HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.sticket), 0u, (size_t)kSplitMaxTiles, st));
-    c->launches += 6;
+    HIPCHK(c, launch_fill_u32(c->W<uint32_t>(c->wp.ready), 0u, (c->wp.act - c->wp.ready) / 4, st));
+    c->launches += 7;
     c->table_ready = true;
   }
   return W4_OK;
@@ -454,6 +472,12 @@ int poll_errors(w4_ctx* c, bool wait) {
       c->pf_pending = false;
     }
   }
+  if (c->werr && __atomic_load_n(c->werr, __ATOMIC_ACQUIRE)) {
+    __atomic_store_n(c->werr, 0, __ATOMIC_RELEASE);
+    return fail(c, W4_E_HIP,
+                "a device-side wait of the fused expert products ran out of its bound in an earlier call (another "
+                "launch holding compute units?); that call's results are not valid");
+  }
   if (c->sticky.empty()) return W4_OK;
   const std::string m = c->sticky;
   c->sticky.clear();
@@ -495,20 +519,26 @@ int upload_rows(w4_ctx* c, int32_t B, const int32_t* slots, hipStream_t st, int*
     sampled = sampled || sp.temperature > 0.f;
     mp = std::max(mp, pos);
   }
-  // Attention work list (stream b << 16 | split << 8 | kv head), the splits
-  // with the most 64-position chunks first: work-groups are dispatched in
-  // list order, so the short tail splits are the ones that double up on a
-  // compute unit.  The order does not change any result.
+  // Attention work list, one entry (stream b << 16 | split << 8 | kv head,
+  // slot << 16 | position) per work-group, the splits with the most
+  // 64-position chunks first: work-groups are dispatched in list order, so the
+  // short tail splits are the ones that double up on a compute unit.  The
+  // order does not change any result.
   const int W = kAttnSplitChunks;
   for (int cnt = W; cnt >= 1; --cnt)
     for (int b = 0; b < B; ++b) {
-      const int nch = c->pos[slots[b]] / 64 + 1, ns = attn_splits(c->pos[slots[b]]);
+      const int pb = c->pos[slots[b]];
+      const int nch = pb / 64 + 1, ns = attn_splits(pb);
       for (int sp = 0; sp < ns; ++sp)
         if (std::min(W, nch - W * sp) == cnt)
-          for (int g = 0; g < c->d.n_kv_heads; ++g) split[n++] = (b << 16) | (sp << 8) | g;
+          for (int g = 0; g < c->d.n_kv_heads; ++g) {
+            split[2 * n] = (b << 16) | (sp << 8) | g;
+            split[2 * n + 1] = (slots[b] << 16) | pb;
+            ++n;
+          }
     }
-  if (c->split_off() + n > c->row_words()) return fail(c, W4_E_INVALID, "row list exceeds its workspace region");
-  HIPCHK(c, hipMemcpyAsync(c->W<int32_t>(c->wp.rows), p, sizeof(int32_t) * (c->split_off() + n),
+  if (c->split_off() + 2 * n > c->row_words()) return fail(c, W4_E_INVALID, "row list exceeds its workspace region");
+  HIPCHK(c, hipMemcpyAsync(c->W<int32_t>(c->wp.rows), p, sizeof(int32_t) * (c->split_off() + 2 * n),
                            hipMemcpyHostToDevice, st));
   c->any_sampled = sampled;
   HIPCHK(c, hipEventRecord(c->ev[i], st));
@@ -533,6 +563,29 @@ struct ProfScope {
     (ctx)->launches += (n);                                                                     \
     if (e_ != hipSuccess) return fail(ctx, W4_E_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
   } while (0)
+
+// The grouped expert products of one layer: one fused launch (gate/up +
+// SwiGLU, then down; see k_moe_fused) where the geometry allows and the
+// option is on, else the two launches.  Same results bit for bit.
+int launch_experts(w4_ctx* c, const LayerLoc& L, const uint16_t* xn, int ldx, const RouteOut& r, uint16_t* act,
+                   uint16_t* y, uint32_t* ready, hipStream_t st) {
+  const Mat gate = c->mat(L.gate), up = c->mat(L.up), down = c->mat(L.down);
+  if (c->fused_moe && moe_fused_ok(gate, down)) {
+    if (c->moe_epoch == 0xFFFFFFFFu) return fail(c, W4_E_UNSUPPORTED, "fused expert launch epochs exhausted");
+    ProfScope ps(c, W4_K_MOE, st);
+    LCHK(c, 1, launch_moe_fused(gate, up, down, xn, ldx, r, act, y, ready, ++c->moe_epoch, c->werr_dev, st));
+    return W4_OK;
+  }
+  {
+    ProfScope ps(c, W4_K_MOE_GATEUP, st);
+    LCHK(c, 1, launch_moe_gateup(gate, up, xn, ldx, r, act, st));
+  }
+  {
+    ProfScope ps(c, W4_K_MOE_DOWN, st);
+    LCHK(c, 1, launch_moe_down(down, act, r, y, st));
+  }
+  return W4_OK;
+}
 
 // One decoder layer on rows whose slot/pos vectors are uploaded.  Input: h
 // (residual, row-major) and xp = RMSNorm_attn(h) as an activation panel.
@@ -569,7 +622,7 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
     next_span = c->Bk<uint8_t>(Ln.attn_norm);
     next_bytes = Ln.gate.tiles - Ln.attn_norm;
   }
-  LCHK(c, 1, launch_attention(B, l, d.n_q_heads, kv, slot, pos, c->dev_splits(), c->nsplits, qkv, nqkv,
+  LCHK(c, 1, launch_attention(B, l, d.n_q_heads, kv, c->dev_splits(), c->nsplits, qkv, nqkv,
                               qkv + (size_t)d.n_q_heads * d.head_dim, qkv + (size_t)(d.n_q_heads + d.n_kv_heads) * d.head_dim,
                               nqkv, c->W<float2>(c->wp.table), c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
                               c->W<unsigned>(c->wp.aticket), o, st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
@@ -595,12 +648,9 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
                              next_span && B == 1 ? &kv : nullptr, l + 1, slot, pos));
   }
   {
-    ProfScope ps(c, W4_K_MOE_GATEUP, st);
-    LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), xn, H, r, c->W<uint16_t>(c->wp.act), st));
-  }
-  {
-    ProfScope ps(c, W4_K_MOE_DOWN, st);
-    LCHK(c, 1, launch_moe_down(c->mat(L.down), c->W<uint16_t>(c->wp.act), r, c->W<uint16_t>(c->wp.y), st));
+    int rc = launch_experts(c, L, xn, H, r, c->W<uint16_t>(c->wp.act), c->W<uint16_t>(c->wp.y),
+                            c->W<uint32_t>(c->wp.ready), st);
+    if (rc) return rc;
   }
   LCHK(c, 1, launch_combine(B, H, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), h, true, next_gamma, d.rms_eps,
                             xp, st, R));
@@ -685,6 +735,7 @@ void w4_destroy(w4_ctx* c) {
     }
     if (c->pinned) (void)hipHostFree(c->pinned);
     if (c->flags) (void)hipHostFree(c->flags);
+    if (c->werr) (void)hipHostFree(c->werr);
     if (c->ev_pf) (void)hipEventSynchronize(c->ev_pf), (void)hipEventDestroy(c->ev_pf);
     if (c->ev_pf_done) (void)hipEventSynchronize(c->ev_pf_done), (void)hipEventDestroy(c->ev_pf_done);
     if (c->pf_pinned) (void)hipHostFree(c->pf_pinned);
@@ -950,14 +1001,17 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
   }
   const int nchunks = (P + kPrefillChunk - 1) / kPrefillChunk;
   std::vector<size_t> ch_off(nchunks), ch_n(nchunks);
-  size_t n = 2 * (size_t)P + kSampleParams;
+  size_t n = (2 * (size_t)P + kSampleParams + 1) / 2 * 2;  // entries are 8-byte pairs
   for (int ch = 0; ch < nchunks; ++ch) {
     ch_off[ch] = n;
     const int i0 = ch * kPrefillChunk, i1 = std::min(P, i0 + kPrefillChunk);
     for (int i = i0; i < i1; ++i)
       for (int sp = 0; sp < attn_splits(i); ++sp)
-        for (int g = 0; g < d.n_kv_heads; ++g) hp[n++] = ((i - i0) << 16) | (sp << 8) | g;
-    ch_n[ch] = n - ch_off[ch];
+        for (int g = 0; g < d.n_kv_heads; ++g) {
+          hp[n++] = ((i - i0) << 16) | (sp << 8) | g;
+          hp[n++] = (slot << 16) | i;
+        }
+    ch_n[ch] = (n - ch_off[ch]) / 2;
   }
   if (n > words) return fail(c, W4_E_INVALID, "prefill row list exceeds its workspace region");
   int32_t* drows = reinterpret_cast<int32_t*>(PW(pp.rows));
@@ -989,6 +1043,11 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
   r.unit_rows = reinterpret_cast<int32_t*>(PW(pp.unit_rows));
   r.n_units = reinterpret_cast<int32_t*>(PW(pp.n_units));
   r.units_cap = E + P * k / 16 + 1;
+  r.done = reinterpret_cast<uint32_t*>(PW(pp.done));
+  // the fused expert launches' ready words: zero once per call (the caller's
+  // buffer may hold anything), then written with this context's epochs only
+  uint32_t* ready = reinterpret_cast<uint32_t*>(PW(pp.ready));
+  LCHK(c, 1, launch_fill_u32(ready, 0u, (pp.act - pp.ready) / 4, st));
   LCHK(c, 1, launch_embed(P, H, d.vocab, d.group, tokens, c->Bk<uint8_t>(c->bp.emb_p), c->Bk<uint16_t>(c->bp.emb_s), h,
                           c->Bk<uint16_t>(c->bp.layers[0].attn_norm), d.rms_eps, xn, c->pf_flags_dev, st, 0));
   for (int l = 0; l < d.n_layers; ++l) {
@@ -998,7 +1057,7 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
                                  c->W<float2>(c->wp.table), st));
     for (int ch = 0; ch < nchunks; ++ch) {
       const int i0 = ch * kPrefillChunk, rows = std::min(P - i0, kPrefillChunk);
-      LCHK(c, 1, launch_attention(rows, l, Hq, kv, drows + i0, drows + P + i0, drows + ch_off[ch], (int)ch_n[ch],
+      LCHK(c, 1, launch_attention(rows, l, Hq, kv, drows + ch_off[ch], (int)ch_n[ch],
                                   qkv + (size_t)i0 * nqkv, nqkv, nullptr, nullptr, nqkv, c->W<float2>(c->wp.table),
                                   reinterpret_cast<float*>(PW(pp.part_o)), reinterpret_cast<float*>(PW(pp.part_ml)),
                                   reinterpret_cast<unsigned*>(PW(pp.aticket)), ao + (size_t)i0 * qd, st, nullptr, 0));
@@ -1012,8 +1071,8 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
                                     reinterpret_cast<uint8_t*>(PW(pp.re8)), st));
     uint16_t* act = reinterpret_cast<uint16_t*>(PW(pp.act));
     uint16_t* y = reinterpret_cast<uint16_t*>(PW(pp.y));
-    LCHK(c, 1, launch_moe_gateup(c->mat(Ly.gate), c->mat(Ly.up), xn, H, r, act, st));
-    LCHK(c, 1, launch_moe_down(c->mat(Ly.down), act, r, y, st));
+    rc = launch_experts(c, Ly, xn, H, r, act, y, ready, st);
+    if (rc) return rc;
     const uint16_t* ng = l + 1 < d.n_layers ? c->Bk<uint16_t>(c->bp.layers[l + 1].attn_norm)
                                             : c->Bk<uint16_t>(c->bp.final_norm);
     LCHK(c, 1, launch_combine(P, H, k, r.w, r.inv, y, h, true, ng, d.rms_eps, xn, st, 0));
@@ -1063,6 +1122,7 @@ int w4_gemm(w4_ctx* c, int32_t layer, int32_t tensor, int32_t expert, int32_t B,
   int rc = ensure_device(c, st);
   if (rc) return rc;
   const int epi = tensor == W4_T_ROUTER ? EPI_F32 : EPI_F16;
+  ProfScope ps(c, W4_K_DENSE, st);
   LCHK(c, 1, launch_gemm(c->mat(*loc, e), B, static_cast<const uint16_t*>(x), loc->K, y, loc->N, epi, st));
   return W4_OK;
 }
@@ -1105,8 +1165,9 @@ int w4_moe(w4_ctx* c, int32_t layer, int32_t B, const void* x, const float* rout
   }
   RouteOut r = c->route_out(route_ids);
   LCHK(c, 1, launch_route(lg, B, d.n_experts, d.top_k, r, st));
-  LCHK(c, 1, launch_moe_gateup(c->mat(L.gate), c->mat(L.up), xh, d.hidden, r, c->W<uint16_t>(c->wp.act), st));
-  LCHK(c, 1, launch_moe_down(c->mat(L.down), c->W<uint16_t>(c->wp.act), r, c->W<uint16_t>(c->wp.y), st));
+  rc = launch_experts(c, L, xh, d.hidden, r, c->W<uint16_t>(c->wp.act), c->W<uint16_t>(c->wp.y),
+                      c->W<uint32_t>(c->wp.ready), st);
+  if (rc) return rc;
   LCHK(c, 1, launch_combine(B, d.hidden, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), static_cast<uint16_t*>(y),
                             false, nullptr, d.rms_eps, nullptr, st));
   return W4_OK;
@@ -1127,11 +1188,9 @@ int w4_attn_decode(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, co
   int max_pos = 0;
   rc = upload_rows(c, B, slots, st, &max_pos);
   if (rc) return rc;
-  const int32_t* slot = c->W<int32_t>(c->wp.rows);
-  const int32_t* pos = slot + c->Bm;
   KV kv = c->kv();
   const int Hq = c->d.n_q_heads, Hkv = c->d.n_kv_heads, D = c->d.head_dim;
-  LCHK(c, 1, launch_attention(B, layer, Hq, kv, slot, pos, c->dev_splits(), c->nsplits, static_cast<const uint16_t*>(q),
+  LCHK(c, 1, launch_attention(B, layer, Hq, kv, c->dev_splits(), c->nsplits, static_cast<const uint16_t*>(q),
                               Hq * D, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), Hkv * D,
                               nullptr, c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
                               c->W<unsigned>(c->wp.aticket), static_cast<uint16_t*>(o), st,
@@ -1179,7 +1238,7 @@ const char* w4_last_error(const w4_ctx* c) { return c ? c->err.c_str() : w4::g_f
 
 int w4_profile_begin(w4_ctx* c, int32_t kernel) {
   if (!c) return W4_E_INVALID;
-  if (kernel < W4_K_DENSE || kernel > W4_K_ROUTER) return fail(c, W4_E_INVALID, "unknown kernel family");
+  if (kernel < W4_K_DENSE || kernel > W4_K_MOE) return fail(c, W4_E_INVALID, "unknown kernel family");
   c->prof_kernel = kernel;
   c->prof_used = 0;
   return W4_OK;
@@ -1208,6 +1267,27 @@ int w4_read_probe(const void* src, size_t bytes, void* sink, int32_t grid, void*
     return W4_E_INVALID;
   hipError_t e = launch_read_probe(src, bytes, static_cast<uint32_t*>(sink), grid, (hipStream_t)stream);
   return e == hipSuccess ? W4_OK : W4_E_HIP;
+}
+
+int w4_sync_probe(int32_t mode, int32_t grid, int32_t n, void* scratch, size_t bytes, void* stream) {
+  if ((mode != 0 && mode != 1) || !scratch || bytes < kSyncProbeWords * 4 || n < 1 || n > 100000 || grid < 1)
+    return W4_E_INVALID;
+  if (mode == 0 && grid > sync_probe_max_grid()) return W4_E_INVALID;  // every work-group must be resident
+  if (mode == 1 && grid > (1 << 20)) return W4_E_INVALID;
+  hipError_t e = launch_sync_probe(mode, grid, n, static_cast<uint32_t*>(scratch), (hipStream_t)stream);
+  return e == hipSuccess ? W4_OK : W4_E_HIP;
+}
+
+int w4_set_option(w4_ctx* c, int32_t option, int32_t value) {
+  if (!c) return W4_E_INVALID;
+  switch (option) {
+    case W4_OPT_FUSED_MOE:
+      if (value != 0 && value != 1) return fail(c, W4_E_INVALID, "W4_OPT_FUSED_MOE takes 0 or 1");
+      c->fused_moe = value != 0;
+      return W4_OK;
+    default:
+      return fail(c, W4_E_INVALID, "unknown option");
+  }
 }
 
 int w4_check_errors(w4_ctx* c) {

@@ -71,6 +71,8 @@ struct RouteOut {
   int32_t* unit_rows;    // [same][16] stream of each unit row (rows past the count repeat row 0)
   int32_t* n_units;      // [1]
   int units_cap;         // records allocated in units (>= any n_units)
+  uint32_t* done = nullptr;  // [units_cap] x kDoneStride words or null: zeroed for every unit written
+                             // (fused expert products)
 };
 // Routing in one work-group: top-k softmax of fp32 logits [B][E], bucketing and 16-row units.  B <= 32.
 hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut& o, hipStream_t st);
@@ -92,6 +94,15 @@ hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int 
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
                              uint16_t* act, hipStream_t st);
 hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st);
+// Both grouped products in one launch (same results bit for bit); needs
+// r.done, the ready words ([units_cap][8] x kDoneStride, zeroed once, then
+// only written with epochs), a nonzero epoch larger than any earlier one on
+// them, and a host-visible error word.  moe_fused_ok: the geometries it takes.
+constexpr int kDoneStride = 64;  // words between counters (256 bytes)
+bool moe_fused_ok(const Mat& gate0, const Mat& down0);
+hipError_t launch_moe_fused(const Mat& gate0, const Mat& up0, const Mat& down0, const uint16_t* x, int ldx,
+                            const RouteOut& r, uint16_t* act, uint16_t* y, uint32_t* ready, uint32_t epoch,
+                            int32_t* err, hipStream_t st);
 // h[b] = fp16(h[b] + fp16(sum_r w[b][r] * y[inv[b][r]]))  (resid), or out = fp16(sum ...) (no resid);
 // then optionally xn[b] = RMSNorm(h[b]) * gamma.
 // Normalised outputs (xn, out) go to a panel with that many rows when
@@ -156,12 +167,12 @@ inline size_t route_prefill_lds(int P, int E, int k) {
 }
 // positions 0..P-1 of a slot -> canonical k, v [L][P][Hkv][D]
 hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uint16_t* v, hipStream_t st);
-// split-KV decode attention; part_o [B][Hq][nchmax][D] f32, part_ml [B][Hq][nchmax][2].
-// prof: when non-null, the launch is timed (prof_arm).
 // Split-KV decode attention in one launch.  A stream at position p has
-// attn_splits(p) splits of 256 positions; splits [nsplits] lists (b << 16 |
-// split << 8 | kv head) for every split of every row and kv head (built on
-// the host with the rows), one work-group each.  The
+// attn_splits(p) splits of 256 positions; splits [2 * nsplits] lists one
+// 8-byte entry (b << 16 | split << 8 | kv head, slot << 16 | p) for every
+// split of every row and kv head (built on the host with the rows, 8-byte
+// aligned), one work-group each.  part_o [B][Hq][nsmax][D] f32, part_ml
+// [B][Hq][nsmax][2]; prof: when non-null, the launch is timed (prof_arm).  The
 // last work-group of each (stream, kv head) combines the splits; ticket
 // [B][Hkv] is zero before and after.  This step's q (row stride ldq) and k,
 // v (row stride ldkv) are rotated at each stream's position through table
@@ -171,8 +182,7 @@ constexpr int kAttnSplitChunks = 4;  // 64-position chunks per split = waves per
 __host__ __device__ inline int attn_splits(int pos) {
   return (pos / 64 + kAttnSplitChunks) / kAttnSplitChunks;
 }
-hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* slot, const int32_t* pos,
-                            const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
+hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
                             unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0);
 // Kernel timing: the host arms a (start, stop) event pair for the next
@@ -208,6 +218,10 @@ __device__ __forceinline__ void touch_lines(const uint8_t* span, size_t lines, s
   }
 }
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
+// Device-wide barrier probe and its empty-launch reference (diagnostic).
+constexpr size_t kSyncProbeWords = 64 * 9;
+int sync_probe_max_grid();
+hipError_t launch_sync_probe(int mode, int grid, int n, uint32_t* ctr, hipStream_t st);
 // Message of the last failed context-free entry point on this thread.
 extern thread_local std::string g_free_err;
 // Streaming-read probe (diagnostic): src[bytes] read once with 16-byte loads; sink [grid] words.

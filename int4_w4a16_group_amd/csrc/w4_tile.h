@@ -148,11 +148,12 @@ __device__ __forceinline__ float run_sum(const float (&p)[8], int n) {
 // way.)  Consecutive threads take consecutive columns.  All NWMAX reads are
 // issued before the sums; slots w >= NW re-read the last slice and are not
 // added (selects, no branch, so the reads are never held back).
+// reduce_tile_sub: the same sums by the nt threads tid = 0 .. nt-1 of a
+// sub-group of the work-group.
 template <int MT, int NWMAX, class EpiF>
-__device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) {
+__device__ __forceinline__ void reduce_tile_sub(const float* red, int NW, int tid, int nt, EpiF epi) {
   static_assert(NWMAX >= 1 && NWMAX <= 16, "at most 16 slices");
-  const int nt = blockDim.x;
-  for (int o = threadIdx.x; o < MT * 256; o += nt) {
+  for (int o = tid; o < MT * 256; o += nt) {
     const int idx = tile_out_idx(o);
     float p[NWMAX];
 #pragma unroll
@@ -168,6 +169,20 @@ __device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) 
     }
     epi(((o >> 8) << 4) + ((o >> 4) & 15), o & 15, v);
   }
+}
+template <int MT, int NWMAX, class EpiF>
+__device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) {
+  reduce_tile_sub<MT, NWMAX>(red, NW, (int)threadIdx.x, (int)blockDim.x, epi);
+}
+
+// fp16 x8 A-operand piece written by other work-groups of the same launch:
+// two 8-byte device-scope loads.
+__device__ __forceinline__ h8 ld_h8_dev(const uint16_t* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  typedef uint64_t u2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(h8, u2{a, b});
 }
 
 }  // namespace w4

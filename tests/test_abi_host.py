@@ -201,3 +201,18 @@ def test_sampling_parameters_are_validated():
         L.w4_slot_set_sampling(c, s, 0, 0.0, 1, 1.0)                   # back to greedy
     finally:
         L.w4_destroy(c)
+
+
+def test_probe_argument_checks():
+    """The measurement probes reject bad arguments before any device call."""
+    for args in ((2, 256, 10, 1, 1 << 14), (0, 256, 0, 1, 1 << 14), (1, 256, 10, 1, 100), (0, 0, 10, 1, 1 << 14),
+                 (0, 256, 10, None, 1 << 14)):
+        mode, grid, n, scratch, nbytes = args
+        with pytest.raises(L.W4Error) as e:
+            L.w4_sync_probe(mode, grid, n, scratch, nbytes)
+        assert e.value.status == L.W4_E_INVALID, args
+    for args in ((None, 1024, 1, 16), (1, 1000, 1, 16), (16, 1024, 1, 0)):
+        src, nbytes, sink, grid = args
+        with pytest.raises(L.W4Error) as e:
+            L.w4_read_probe(src, nbytes, sink, grid)
+        assert e.value.status == L.W4_E_INVALID, args

@@ -102,3 +102,107 @@ def test_moe_router_computed_on_device(moe_ctx, gpu):
     for b in range(6):
         assert route_ok(ids[b], rl[b], TOL), f"row {b}: routing differs beyond a near-tie"
         assert_normwise(f16v(y[b]), f16v(ry[b]), TOL, f"router-on-device row {b}")
+
+
+def moe_both_forms(ctx, x, logits, dev, layer=0):
+    """w4_moe with the expert products as one launch and as two: (y, ids) each."""
+    out = []
+    for fused in (1, 0):
+        L.w4_set_option(ctx.ctx, L.W4_OPT_FUSED_MOE, fused)
+        B = x.shape[0]
+        y = empty_f16((B, ctx.desc.hidden), dev)
+        ids = torch.empty((B, ctx.desc.top_k), dtype=torch.int32, device=dev)
+        L.w4_moe(ctx.ctx, layer, B, to_dev(x, dev), to_dev(logits, dev), y, ids, ctx.stream)
+        out.append((to_host(y), to_host(ids)))
+    L.w4_set_option(ctx.ctx, L.W4_OPT_FUSED_MOE, 0)
+    L.w4_check_errors(ctx.ctx)   # no device-side wait ran out
+    return out
+
+
+@pytest.mark.parametrize("regime", ["disjoint", "skewed"])
+@pytest.mark.parametrize("B", [1, 4, 8, 32])
+def test_fused_expert_launch_matches_two_launches(moe_ctx, gpu, regime, B):
+    """The one-launch expert products (gate/up, then down on per-unit
+    completion counters) give the two-launch results bit for bit; run twice,
+    so the counters are reused across calls."""
+    ctx, _ = moe_ctx
+    for seed in (5, 6):
+        x, logits, _ = inputs.moe_case(seed, B, regime)
+        (yf, idf), (y2, id2) = moe_both_forms(ctx, x, logits, gpu)
+        assert np.array_equal(idf, id2)
+        assert np.array_equal(yf, y2), f"B={B} {regime} seed {seed}"
+
+
+@pytest.mark.parametrize("geom", [dict(), dict(moe_inter=128, n_experts=64, top_k=4),
+                                  dict(moe_inter=256, group=64, n_experts=64, top_k=4), dict(hidden=1024)])
+def test_fused_expert_launch_other_geometries(gpu, geom):
+    """Other slice counts: gate/up over 8 or 4 waves, down over 1-3 waves in
+    up to 8 sub-groups, other group sizes."""
+    d = dataclasses.replace(inputs.FULL, n_layers=1, vocab=16, **geom)
+    lw = inputs.make_layer(d, 3, 0)
+    ctx = Context(d, 32, 64)
+    try:
+        ctx.load_layer(0, lw)
+        for B in (1, 13, 32):
+            x = inputs.normal_f16(inputs.rng(3, inputs.T_X, B, 9), (B, d.hidden))
+            logits, _ = inputs.moe_logits(3, B, d.n_experts, "disjoint")
+            (yf, idf), (y2, id2) = moe_both_forms(ctx, x, logits, gpu)
+            assert np.array_equal(idf, id2) and np.array_equal(yf, y2), (geom, B)
+    finally:
+        ctx.close()
+
+
+def test_fused_expert_launch_in_decode_steps(gpu):
+    """Whole decode steps (3 layers, 6 streams, 3 steps) with the expert
+    products as one launch and as two: the same logits bit for bit."""
+    d = dataclasses.replace(inputs.FULL, n_layers=3, vocab=1000)
+    mw = inputs.make_model(d, 8, codes="zero_mean")
+    outs = []
+    for fused in (1, 0):
+        ctx = Context(d, 8, 256)
+        try:
+            ctx.load_model(mw)
+            L.w4_set_option(ctx.ctx, L.W4_OPT_FUSED_MOE, fused)
+            slots = []
+            for s, p in enumerate((5, 64, 100, 1, 77, 130)):
+                k, v = inputs.prefix_kv(8, s, d.n_layers, p, d.n_kv_heads, d.head_dim)
+                slots.append(ctx.join(p, 8, k, v))
+            tok = torch.tensor([3, 99, 500, 7, 42, 999], dtype=torch.int32, device=gpu)
+            nxt = torch.empty(6, dtype=torch.int32, device=gpu)
+            steps = []
+            for _ in range(3):
+                lg = empty_f16((6, d.vocab), gpu)
+                L.w4_decode_step(ctx.ctx, slots, tok, lg, nxt, None, ctx.stream)
+                steps.append(to_host(lg))
+                tok, nxt = nxt.clone(), tok
+            L.w4_check_errors(ctx.ctx)
+            outs.append(steps)
+        finally:
+            ctx.close()
+    for i, (a, b) in enumerate(zip(*outs)):
+        assert np.array_equal(a, b), f"step {i}"
+
+
+def test_fused_expert_launch_in_prefill(gpu):
+    """A 300-token prompt (many 16-row units per expert) through a two-layer
+    model with the expert products as one launch and as two: the same K/V,
+    last logits and next id, bit for bit."""
+    d = dataclasses.replace(inputs.FULL, n_layers=2, vocab=1000)
+    mw = inputs.make_model(d, 9, codes="zero_mean")
+    tokens = [int(t) for t in inputs.rng(9, inputs.T_TOKENS, 3).integers(0, d.vocab, 300)]
+    outs = []
+    for fused in (1, 0):
+        ctx = Context(d, 2, 384)
+        try:
+            ctx.load_model(mw)
+            L.w4_set_option(ctx.ctx, L.W4_OPT_FUSED_MOE, fused)
+            lg = empty_f16((d.vocab,), gpu)
+            nx = torch.empty(1, dtype=torch.int32, device=gpu)
+            s = ctx.prefill(tokens, 4, lg, nx)
+            k, v = ctx.read_kv(s)
+            L.w4_check_errors(ctx.ctx)
+            outs.append((k, v, to_host(lg), int(to_host(nx)[0])))
+        finally:
+            ctx.close()
+    (k1, v1, l1, n1), (k2, v2, l2, n2) = outs
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2) and np.array_equal(l1, l2) and n1 == n2
