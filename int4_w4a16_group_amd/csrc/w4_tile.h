@@ -175,14 +175,4 @@ __device__ __forceinline__ void reduce_tile(const float* red, int NW, EpiF epi) 
   reduce_tile_sub<MT, NWMAX>(red, NW, (int)threadIdx.x, (int)blockDim.x, epi);
 }
 
-// fp16 x8 A-operand piece written by other work-groups of the same launch:
-// two 8-byte device-scope loads.
-__device__ __forceinline__ h8 ld_h8_dev(const uint16_t* p) {
-  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  typedef uint64_t u2 __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(h8, u2{a, b});
-}
-
 }  // namespace w4
