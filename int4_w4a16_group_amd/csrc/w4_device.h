@@ -58,4 +58,19 @@ __device__ __forceinline__ h8 dq8(uint32_t w, const DqConst& k) {
 
 __device__ __forceinline__ h8 ld_h8(const uint16_t* p) { return *reinterpret_cast<const h8*>(p); }
 
+// Non-temporal loads (the nt bit) for data a step reads once: the weight
+// tiles and the KV chunks.  Measured on MI355X, one pass over 4 GiB with
+// 16-byte loads streams at 6.3-6.75 TB/s non-temporal against 5.4-6.0 TB/s
+// plain.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ h8 ld_h8_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const h8*>(p));
+}
+__device__ __forceinline__ uint32_t ld_u32_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint16_t ld_u16_nt(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
 }  // namespace w4

@@ -98,7 +98,7 @@ struct DenseArgs {
 // Row blocks: work-group row blockIdx.y takes rows 16*MT*blockIdx.y .. +16*MT-1
 // of a row-major x (a panel has one block); an output row depends on its own
 // input row only, so the blocking never changes a result.
-template <int MT, int NCH, int G, int EPI, int LB, bool XP>
+template <int MT, int NCH, int G, int EPI, int LB, bool XP, bool NT = false>
 __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   extern __shared__ float red[];  // two buffers of [NW][MT][64][4]
   constexpr int NS = NCH * 128 / G;
@@ -126,7 +126,7 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   int buf = 0;
   uint16_t hpre = 0;  // see the single-tile case below
   bool pre = false;
-  auto run = [&](const Stage<NCH, G>& st, int t, bool valid) {
+  auto run = [&](const Stage<NCH, G, NT>& st, int t, bool valid) {
     float sv[NS];
     st.scales_f32(sv);
     f4 acc[MT];
@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
   // with every load issued unconditionally (indices clamped to the last tile)
   const int n = (a.ntiles - (int)blockIdx.x + G0 - 1) / G0;
   const int last = blockIdx.x + (n - 1) * G0;
-  Stage<NCH, G> sa, sb;
+  Stage<NCH, G, NT> sa, sb;
   sa.load(a.tiles, a.scales, a.K, blockIdx.x, w, lane);
   if (n == 1) {
     // Residual epilogue of a single tile with one output per thread: the
@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(LB) k_gemm_dense(DenseArgs a) {
 // applies the residual epilogue: the order of the one-work-group form
 // (reduce_tile), bit for bit.  Neither work-group waits for the other.
 // part: [ntiles][2][MT * 256] fp32; ticket [ntiles], zero before and after.
-template <int MT, int G>
+template <int MT, int G, bool NT = false>
 __global__ void __launch_bounds__(512) k_gemm_resid_split(DenseArgs a, float* part, unsigned* ticket) {
   extern __shared__ float red[];  // [8 waves][MT][64][4]
   __shared__ int s_last;
@@ -202,7 +202,7 @@ __global__ void __launch_bounds__(512) k_gemm_resid_split(DenseArgs a, float* pa
   const int ws = half * 8 + w;  // this wave's K slice
   XRegs<MT, NCH * 4> x;
   load_x_panel<MT, NCH>(x, a.x, a.xrows, a.B, ws * NCH * 128, lane);
-  Stage<NCH, G> st;
+  Stage<NCH, G, NT> st;
   st.load(a.tiles, a.scales, a.K, t, ws, lane);
   float sv[NS];
   st.scales_f32(sv);
@@ -249,42 +249,48 @@ __global__ void __launch_bounds__(512) k_gemm_resid_split(DenseArgs a, float* pa
 typedef void (*DenseKernel)(DenseArgs);
 
 // LB: launch bound; 512 threads (<= 8 waves) leaves up to 256 VGPRs per lane.
-template <int MT, int NCH, int G, int LB, bool XP>
+template <int MT, int NCH, int G, int LB, bool XP, bool NT>
 static DenseKernel pick_epi(int epi) {
   switch (epi) {
-    case EPI_F16: return k_gemm_dense<MT, NCH, G, EPI_F16, LB, XP>;
-    case EPI_F32: return k_gemm_dense<MT, NCH, G, EPI_F32, LB, XP>;
-    default: return k_gemm_dense<MT, NCH, G, EPI_RESID, LB, XP>;
+    case EPI_F16: return k_gemm_dense<MT, NCH, G, EPI_F16, LB, XP, NT>;
+    case EPI_F32: return k_gemm_dense<MT, NCH, G, EPI_F32, LB, XP, NT>;
+    default: return k_gemm_dense<MT, NCH, G, EPI_RESID, LB, XP, NT>;
   }
 }
-template <int MT, int NCH, int LB, bool XP>
+template <int MT, int NCH, int LB, bool XP, bool NT>
 static DenseKernel pick_g_lb(int g, int epi) {
   switch (g) {
-    case 32: return pick_epi<MT, NCH, 32, LB, XP>(epi);
-    case 64: return pick_epi<MT, NCH, 64, LB, XP>(epi);
-    default: return pick_epi<MT, NCH, 128, LB, XP>(epi);
+    case 32: return pick_epi<MT, NCH, 32, LB, XP, NT>(epi);
+    case 64: return pick_epi<MT, NCH, 64, LB, XP, NT>(epi);
+    default: return pick_epi<MT, NCH, 128, LB, XP, NT>(epi);
   }
 }
+// non-temporal weight loads only for the decode step's panel products with
+// up to 8 waves per tile
 template <int MT, int NCH, bool XP>
-static DenseKernel pick_g(int g, int epi, int nw) {
-  return nw <= 8 ? pick_g_lb<MT, NCH, 512, XP>(g, epi) : pick_g_lb<MT, NCH, 1024, XP>(g, epi);
+static DenseKernel pick_g(int g, int epi, int nw, bool nt) {
+  if (nw <= 8) {
+    if (XP && nt) return pick_g_lb<MT, NCH, 512, XP, true>(g, epi);
+    return pick_g_lb<MT, NCH, 512, XP, false>(g, epi);
+  }
+  return pick_g_lb<MT, NCH, 1024, XP, false>(g, epi);
 }
 template <bool XP>
-static DenseKernel pick(int MT, int nch, int g, int epi, int nw) {
-  if (MT == 1) return nch == 2 ? pick_g<1, 2, XP>(g, epi, nw) : pick_g<1, 1, XP>(g, epi, nw);
-  return nch == 2 ? pick_g<2, 2, XP>(g, epi, nw) : pick_g<2, 1, XP>(g, epi, nw);
+static DenseKernel pick(int MT, int nch, int g, int epi, int nw, bool nt) {
+  if (MT == 1) return nch == 2 ? pick_g<1, 2, XP>(g, epi, nw, nt) : pick_g<1, 1, XP>(g, epi, nw, nt);
+  return nch == 2 ? pick_g<2, 2, XP>(g, epi, nw, nt) : pick_g<2, 1, XP>(g, epi, nw, nt);
 }
 
 // Slice width: 256 columns, or 128 when K is not a multiple of 256.
 static inline int nch_for(int K) { return (K % 256 == 0) ? 2 : 1; }
 
 hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi, hipStream_t st,
-                       int xrows) {
+                       int xrows, bool nt) {
   const int nch = nch_for(w.K);
   const int NW = w.K / (nch * 128);
   const int MT = B > 16 ? 2 : 1;
   if (xrows > 0 && B > 32) return hipErrorInvalidValue;  // a panel holds at most 32 rows
-  const DenseKernel k = xrows > 0 ? pick<true>(MT, nch, w.g, epi, NW) : pick<false>(MT, nch, w.g, epi, NW);
+  const DenseKernel k = xrows > 0 ? pick<true>(MT, nch, w.g, epi, NW, nt) : pick<false>(MT, nch, w.g, epi, NW, false);
   const int ntiles = w.ntiles();
   const int row_blocks = xrows > 0 ? 1 : (B + 31) / 32;  // 32-row blocks of a longer row-major x
   // enough work-groups to fill 256 CUs at ~16 waves each, each looping over
@@ -346,7 +352,7 @@ __device__ __forceinline__ void set_prio_level(int l) {
 // multiply of the previous one, with its first tiles already in flight).
 // The arithmetic of an output does not depend on which work-group computes
 // it.
-template <int NCH, int G, bool GATEUP, int LB>
+template <int NCH, int G, bool GATEUP, int LB, bool NT = false>
 __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // dynamic LDS: two buffers of [GATEUP ? 2 : 1][NW][64][4] partials, then
   // the unit records of this work-group's range
@@ -395,7 +401,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   __syncthreads();
 
   // item f's tile into a stage (past the range: the WG's last tile again)
-  auto stage_load = [&](Stage<NCH, G>& g0, Stage<NCH, G>& g1, int f) {
+  auto stage_load = [&](Stage<NCH, G, NT>& g0, Stage<NCH, G, NT>& g1, int f) {
     const int fc = min(f, last), u = __builtin_amdgcn_readfirstlane(fc / T), t = fc - u * T;
     const int e = lrec[u].x;
     g0.load(a.t0 + a.tile_stride * e, a.s0 + a.scale_stride * e, a.K, t, w, lane);
@@ -419,7 +425,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   };
 
   int buf = 0;
-  auto run = [&](const Stage<NCH, G>& g0, const Stage<NCH, G>& g1, int f, bool valid) {
+  auto run = [&](const Stage<NCH, G, NT>& g0, const Stage<NCH, G, NT>& g1, int f, bool valid) {
     const int u = __builtin_amdgcn_readfirstlane(min(f, last) / T), t = min(f, last) - u * T;
     const int4 un = lrec[u];
     const int off = un.y, m = un.z;
@@ -471,7 +477,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // Items in pairs through stages a and b.  A new unit's x is loaded after
   // the previous multiply and before the next prefetch: the multiply that
   // needs it waits for its own stage, issued earlier, in any case.
-  Stage<NCH, G> a0, a1, b0, b1;
+  Stage<NCH, G, NT> a0, a1, b0, b1;
   stage_load(a0, a1, f_begin);
   load_x(f_begin / T, GATEUP ? a.unit_rows[(f_begin / T) * 16 + i16] : 0);
   stage_load(b0, b1, f_begin + 1);
@@ -750,18 +756,22 @@ __global__ void __launch_bounds__(LB) k_moe_fused(MoeFusedArgs fa) {
 
 typedef void (*MoeKernel)(MoeArgs);
 
-template <bool GU, int NCH, int LB>
+template <bool GU, int NCH, int LB, bool NT>
 static MoeKernel moe_pick_g(int g) {
   switch (g) {
-    case 32: return k_moe<NCH, 32, GU, LB>;
-    case 64: return k_moe<NCH, 64, GU, LB>;
-    default: return k_moe<NCH, 128, GU, LB>;
+    case 32: return k_moe<NCH, 32, GU, LB, NT>;
+    case 64: return k_moe<NCH, 64, GU, LB, NT>;
+    default: return k_moe<NCH, 128, GU, LB, NT>;
   }
 }
+// nt: non-temporal weight loads (up to 8 waves per tile only)
 template <bool GU>
-static MoeKernel moe_pick(int nch, int g, int nw) {
-  if (nw <= 8) return nch == 2 ? moe_pick_g<GU, 2, 512>(g) : moe_pick_g<GU, 1, 512>(g);
-  return nch == 2 ? moe_pick_g<GU, 2, 1024>(g) : moe_pick_g<GU, 1, 1024>(g);
+static MoeKernel moe_pick(int nch, int g, int nw, bool nt) {
+  if (nw <= 8) {
+    if (nt) return nch == 2 ? moe_pick_g<GU, 2, 512, true>(g) : moe_pick_g<GU, 1, 512, true>(g);
+    return nch == 2 ? moe_pick_g<GU, 2, 512, false>(g) : moe_pick_g<GU, 1, 512, false>(g);
+  }
+  return nch == 2 ? moe_pick_g<GU, 2, 1024, false>(g) : moe_pick_g<GU, 1, 1024, false>(g);
 }
 
 static int cu_count() {
@@ -809,11 +819,11 @@ static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_
                         uint16_t* out);
 
 static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, const uint16_t* x, int ldx,
-                                    const RouteOut& r, uint16_t* out, hipStream_t st) {
+                                    const RouteOut& r, uint16_t* out, bool nt, hipStream_t st) {
   const int nch = nch_for(m0.K);
   const int NW = m0.K / (nch * 128);
   const MoeArgs a = moe_args(gateup, m0, m1, x, ldx, r, out);
-  MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW) : moe_pick<false>(nch, m0.g, NW);
+  MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW, nt) : moe_pick<false>(nch, m0.g, NW, nt);
   if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
   // the records of every unit in LDS (at most kMaxUnits in a decode step, whose
   // launch shape is kept; a prefill can have more)
@@ -885,37 +895,47 @@ hipError_t launch_moe_fused(const Mat& gate0, const Mat& up0, const Mat& down0, 
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int xrows, uint16_t* h, int ldh,
-                                  float* part, unsigned* ticket, hipStream_t st) {
-  if (w.K != 16 * 256 || w.ntiles() > kSplitMaxTiles || xrows < 1 || !part || !ticket) return hipErrorInvalidValue;
-  const int MT = B > 16 ? 2 : 1;
-  DenseArgs a{w.tiles, w.scales, w.N, w.K, w.ntiles(), xp, 0, B, h, ldh, xrows};
+template <bool NTV>
+static void launch_resid_split_nt(const Mat& w, int MT, const DenseArgs& a, float* part, unsigned* ticket,
+                                  hipStream_t st) {
   const dim3 grid(2 * w.ntiles());
   const uint32_t shm = 8 * MT * 1024;
   switch (w.g) {
     case 32:
-      MT == 2 ? w4_launch(k_gemm_resid_split<2, 32>, grid, dim3(512), shm, st, a, part, ticket)
-              : w4_launch(k_gemm_resid_split<1, 32>, grid, dim3(512), shm, st, a, part, ticket);
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 32, NTV>, grid, dim3(512), shm, st, a, part, ticket)
+              : w4_launch(k_gemm_resid_split<1, 32, NTV>, grid, dim3(512), shm, st, a, part, ticket);
       break;
     case 64:
-      MT == 2 ? w4_launch(k_gemm_resid_split<2, 64>, grid, dim3(512), shm, st, a, part, ticket)
-              : w4_launch(k_gemm_resid_split<1, 64>, grid, dim3(512), shm, st, a, part, ticket);
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 64, NTV>, grid, dim3(512), shm, st, a, part, ticket)
+              : w4_launch(k_gemm_resid_split<1, 64, NTV>, grid, dim3(512), shm, st, a, part, ticket);
       break;
     default:
-      MT == 2 ? w4_launch(k_gemm_resid_split<2, 128>, grid, dim3(512), shm, st, a, part, ticket)
-              : w4_launch(k_gemm_resid_split<1, 128>, grid, dim3(512), shm, st, a, part, ticket);
+      MT == 2 ? w4_launch(k_gemm_resid_split<2, 128, NTV>, grid, dim3(512), shm, st, a, part, ticket)
+              : w4_launch(k_gemm_resid_split<1, 128, NTV>, grid, dim3(512), shm, st, a, part, ticket);
       break;
   }
+}
+
+hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int xrows, uint16_t* h, int ldh,
+                                  float* part, unsigned* ticket, hipStream_t st, bool nt) {
+  if (w.K != 16 * 256 || w.ntiles() > kSplitMaxTiles || xrows < 1 || !part || !ticket) return hipErrorInvalidValue;
+  const int MT = B > 16 ? 2 : 1;
+  DenseArgs a{w.tiles, w.scales, w.N, w.K, w.ntiles(), xp, 0, B, h, ldh, xrows};
+  if (nt)
+    launch_resid_split_nt<true>(w, MT, a, part, ticket, st);
+  else
+    launch_resid_split_nt<false>(w, MT, a, part, ticket, st);
   return hipGetLastError();
 }
 
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
-                             uint16_t* act, hipStream_t st) {
-  return launch_moe_common(true, gate0, &up0, x, ldx, r, act, st);
+                             uint16_t* act, hipStream_t st, bool nt) {
+  return launch_moe_common(true, gate0, &up0, x, ldx, r, act, nt, st);
 }
 
-hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st) {
-  return launch_moe_common(false, down0, nullptr, act, down0.K, r, y, st);
+hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st,
+                           bool nt) {
+  return launch_moe_common(false, down0, nullptr, act, down0.K, r, y, nt, st);
 }
 
 }  // namespace w4

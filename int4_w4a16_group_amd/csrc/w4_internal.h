@@ -46,8 +46,9 @@ inline int panel_rows(int max_streams) { return (max_streams + 15) / 16 * 16; }
 hipError_t launch_repack(const uint8_t* src_packed, const uint16_t* src_scales, int count, int N, int K,
                          int g, uint4* dst_tiles, uint16_t* dst_scales, hipStream_t st);
 // xrows > 0: x is a panel with xrows rows (ldx unused); else row-major with stride ldx.
+// nt (panel products only): non-temporal weight loads (same results).
 hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y, int ldy, int epi,
-                       hipStream_t st, int xrows = 0);
+                       hipStream_t st, int xrows = 0, bool nt = false);
 
 // Routing limits: experts, and 16-row units of the grouped products (used
 // experts + B*k/16 with B <= 32, k <= 16).
@@ -88,12 +89,16 @@ int touch_groups(size_t bytes, int threads);
 // ticket [ntiles] (zero before and after) are scratch.  ntiles <= kSplitMaxTiles.
 constexpr int kSplitMaxTiles = 256;
 hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int xrows, uint16_t* h, int ldh,
-                                  float* part, unsigned* ticket, hipStream_t st);
+                                  float* part, unsigned* ticket, hipStream_t st, bool nt = false);
 
-// Grouped expert GEMMs over the bucketed pairs (persistent, work list from route).
+// Grouped expert GEMMs over the bucketed pairs (persistent, work list from
+// route).  nt: non-temporal weight loads (same results; measured faster for a
+// decode batch above 8 rows, slower below it and in a prefill, which reads
+// each expert's tiles once per 16-row unit).
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
-                             uint16_t* act, hipStream_t st);
-hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st);
+                             uint16_t* act, hipStream_t st, bool nt = false);
+hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st,
+                           bool nt = false);
 // Both grouped products in one launch (same results bit for bit); needs
 // r.done, the ready words ([units_cap][8] x kDoneStride, zeroed once, then
 // only written with epochs), a nonzero epoch larger than any earlier one on
@@ -172,7 +177,10 @@ hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uin
 // 8-byte entry (b << 16 | split << 8 | kv head, slot << 16 | p) for every
 // split of every row and kv head (built on the host with the rows, 8-byte
 // aligned), one work-group each.  part_o [B][Hq][nsmax][D] f32, part_ml
-// [B][Hq][nsmax][2]; prof: when non-null, the launch is timed (prof_arm).  The
+// [B][Hq][nsmax][2]; prof: when non-null, the launch is timed (prof_arm);
+// once: the K/V are read once in this launch's stream of work (a decode
+// step, not a prefill's chunks), so a long list may stream them
+// non-temporally.  The
 // last work-group of each (stream, kv head) combines the splits; ticket
 // [B][Hkv] is zero before and after.  This step's q (row stride ldq) and k,
 // v (row stride ldkv) are rotated at each stream's position through table
@@ -184,7 +192,8 @@ __host__ __device__ inline int attn_splits(int pos) {
 }
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
-                            unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0);
+                            unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0,
+                            bool once = false);
 // Kernel timing: the host arms a (start, stop) event pair for the next
 // launch of the profiled kernel family (prof_arm, from the context's pool);
 // that launch records them with its own dispatch (hipExtLaunchKernelGGL), so

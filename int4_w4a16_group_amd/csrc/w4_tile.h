@@ -50,12 +50,14 @@ __device__ __forceinline__ void tile_mac(const XRegs<MT, NCH * 4>& x, const uint
   }
 }
 
-template <int NCH>
+// NT: non-temporal loads (faster for a bandwidth-bound stream read once,
+// slower for a latency-bound launch; the data are the same either way).
+template <int NCH, bool NT = false>
 __device__ __forceinline__ void load_tile(const uint4* __restrict__ tiles, int K, int t, int w, int lane,
                                           uint4 (&wv)[NCH]) {
   const uint4* p = tiles + ((size_t)t * (K / 128) + (size_t)w * NCH) * 64 + lane;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) wv[c] = p[c * 64];
+  for (int c = 0; c < NCH; ++c) wv[c] = NT ? ld_nt(p + c * 64) : p[c * 64];
 }
 
 template <int NCH, int G>
@@ -70,7 +72,7 @@ __device__ __forceinline__ void load_scales(const uint16_t* __restrict__ scales,
 // K slice (scales kept as the loaded dwords, two fp16 per dword, and only
 // unpacked when the stage is used), so the loads stay in flight while the
 // other stage is computed.
-template <int NCH, int G>
+template <int NCH, int G, bool NT = false>
 struct Stage {
   static constexpr int NS = NCH * 128 / G;       // scales per lane per tile
   static constexpr int ND = NS >= 2 ? NS / 2 : 1;  // dwords holding them
@@ -78,13 +80,14 @@ struct Stage {
   uint32_t s[ND];
   __device__ __forceinline__ void load(const uint4* __restrict__ tiles, const uint16_t* __restrict__ scales, int K,
                                        int t, int wv, int lane) {
-    load_tile<NCH>(tiles, K, t, wv, lane, w);
+    load_tile<NCH, NT>(tiles, K, t, wv, lane, w);
     const uint16_t* p = scales + (size_t)(t * 16 + (lane & 15)) * (K / G) + (size_t)wv * NS;
     if (NS >= 2) {
 #pragma unroll
-      for (int i = 0; i < ND; ++i) s[i] = reinterpret_cast<const uint32_t*>(p)[i];
+      for (int i = 0; i < ND; ++i)
+        s[i] = NT ? ld_u32_nt(reinterpret_cast<const uint32_t*>(p) + i) : reinterpret_cast<const uint32_t*>(p)[i];
     } else {
-      s[0] = p[0];
+      s[0] = NT ? ld_u16_nt(p) : p[0];
     }
   }
   __device__ __forceinline__ void scales_f32(float (&sv)[NS]) const {
