@@ -273,30 +273,32 @@ def main():
 
 def read_ceiling(dev, L):
     """HBM streaming-read ceiling: the library's read probe (16-byte loads, one
-    pass) over 4 GiB, far beyond the 256 MB memory-side cache, at a few grid
-    sizes; the best of three passes each, timed with events on the stream."""
+    pass, plain and non-temporal) over 4 GiB, far beyond the 256 MB memory-side
+    cache, at a few grid sizes; the best of four passes each, timed with events
+    on the stream."""
     import torch
     nbytes = 4 << 30
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     src.fill_(1)
-    res = {}
+    res, res_nt = {}, {}
     st = torch.cuda.current_stream(dev)
-    for per_cu in (4, 8, 16):
-        grid = 256 * per_cu
-        sink = torch.empty(grid, dtype=torch.int32, device=dev)
-        best = None
-        for _ in range(4):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(st)
-            L.w4_read_probe(src, nbytes, sink, grid, st)
-            b.record(st)
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b)
-            best = ms if best is None else min(best, ms)
-        res[str(grid)] = nbytes / (best * 1e-3) / 1e9
+    for nt, out in ((0, res), (1, res_nt)):
+        for per_cu in (4, 8, 16):
+            grid = 256 * per_cu
+            sink = torch.empty(grid, dtype=torch.int32, device=dev)
+            best = None
+            for _ in range(4):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                L.w4_read_probe(src, nbytes, sink, grid, nt, st)
+                b.record(st)
+                torch.cuda.synchronize()
+                ms = a.elapsed_time(b)
+                best = ms if best is None else min(best, ms)
+            out[str(grid)] = nbytes / (best * 1e-3) / 1e9
     del src
-    top = max(res.values())
-    log(f"HBM read ceiling (probe): {top:.0f} GB/s ({res})")
+    top, top_nt = max(res.values()), max(res_nt.values())
+    log(f"HBM read ceiling (probe): plain {top:.0f} GB/s ({res}), non-temporal {top_nt:.0f} GB/s ({res_nt})")
     # a phase boundary inside one persistent launch (device-wide barrier) against
     # a launch boundary (back-to-back empty launches of the same shape)
     scratch = torch.zeros(1 << 14, dtype=torch.uint8, device=dev)
@@ -318,6 +320,7 @@ def read_ceiling(dev, L):
         sync[str(grid)] = per
     log(f"device-wide barrier vs launch boundary: {sync}")
     return dict(GBps=top, frac_of_peak=top / PEAK_HBM_GBPS, bytes=nbytes, by_grid=res,
+                nontemporal_GBps=top_nt, nontemporal_frac_of_peak=top_nt / PEAK_HBM_GBPS, nontemporal_by_grid=res_nt,
                 kernel="w4_read_probe: one pass of 16-byte loads, 256-thread work-groups",
                 sync_probe=dict(by_grid=sync, kind="w4_sync_probe: device-wide barrier among co-resident 512-thread "
                                                      "work-groups (two-level counters) vs back-to-back empty launches"))

@@ -266,10 +266,12 @@ int w4_last_step_counts(const w4_ctx* ctx, int32_t* launches, int32_t* syncs);
 
 /* Streaming-read ceiling probe (a measurement aid, not part of the step):
  * reads src_dev[0 .. bytes) once with the 16-byte loads the weight kernels
- * use, from `grid` 256-thread work-groups; sink_dev: caller-owned int32
- * [grid], almost never written.  bytes a positive multiple of 16, src_dev
- * 16-byte aligned; W4_E_INVALID otherwise.  Time it with events on `stream`. */
-int w4_read_probe(const void* src_dev, size_t bytes, void* sink_dev, int32_t grid, void* stream);
+ * use, plain (nontemporal 0) or non-temporal (1), from `grid` 256-thread
+ * work-groups; sink_dev: caller-owned int32 [grid], almost never written.
+ * bytes a positive multiple of 16, src_dev 16-byte aligned; W4_E_INVALID
+ * otherwise.  Time it with events on `stream`. */
+int w4_read_probe(const void* src_dev, size_t bytes, void* sink_dev, int32_t grid, int32_t nontemporal,
+                  void* stream);
 
 /* Context options (a verification and measurement aid; the defaults are the
  * fast path).  W4_OPT_FUSED_MOE, default 0: the grouped expert products of a

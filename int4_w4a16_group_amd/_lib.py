@@ -54,7 +54,7 @@ _SIGS = {
     "w4_prefill_workspace_bytes": (_sz, [C.POINTER(w4_model_desc), _i32, _i32]),
     "w4_slot_prefill": (C.c_int, [_vp, _i32, _vp, _vp, _sz, _vp, _vp, _vp, _vp]),
     "w4_check_errors": (C.c_int, [_vp]),
-    "w4_read_probe": (C.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "w4_read_probe": (C.c_int, [_vp, _sz, _vp, _i32, _i32, _vp]),
     "w4_sync_probe": (C.c_int, [_i32, _i32, _i32, _vp, _sz, _vp]),
     "w4_set_option": (C.c_int, [_vp, _i32, _i32]),
     "w4_route_noalloc": (C.c_int, [_i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -208,8 +208,8 @@ def w4_slot_read_kv(ctx, slot: int, k, v, stream=None):
     return _check(ctx, lib().w4_slot_read_kv(ctx, slot, _p(k), _p(v), _s(stream)))
 
 
-def w4_read_probe(src, nbytes: int, sink, grid: int, stream=None):
-    return _check(None, lib().w4_read_probe(_p(src), nbytes, _p(sink), grid, _s(stream)))
+def w4_read_probe(src, nbytes: int, sink, grid: int, nontemporal: int = 0, stream=None):
+    return _check(None, lib().w4_read_probe(_p(src), nbytes, _p(sink), grid, nontemporal, _s(stream)))
 
 
 def w4_set_option(ctx, option: int, value: int):

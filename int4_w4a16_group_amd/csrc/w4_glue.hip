@@ -1192,14 +1192,16 @@ hipError_t launch_sample(int B, int V, const uint16_t* logits, const int32_t* pa
 // words are folded into one value per thread, and a work-group stores it only
 // if it equals a constant no real data hits, so the loads stay and almost no
 // bytes are written.  Measures the HBM read ceiling with the load width the
-// weight kernels use.
+// weight kernels use, plain or non-temporal (NT).
+template <bool NT>
 __global__ void __launch_bounds__(256) k_read_probe(const uint4* __restrict__ src, size_t n16,
                                                     uint32_t* __restrict__ sink) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t acc = 0;
+  auto ld = [&](size_t j) { return NT ? ld_nt(src + j) : src[j]; };
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    const uint4 a = ld(i), b = ld(i + stride), c = ld(i + 2 * stride), d = ld(i + 3 * stride);
     acc ^= (a.x ^ a.y ^ a.z ^ a.w) + (b.x ^ b.y ^ b.z ^ b.w) + (c.x ^ c.y ^ c.z ^ c.w) + (d.x ^ d.y ^ d.z ^ d.w);
   }
   for (; i < n16; i += stride) {
@@ -1209,8 +1211,13 @@ __global__ void __launch_bounds__(256) k_read_probe(const uint4* __restrict__ sr
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
-hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {
-  hipLaunchKernelGGL(k_read_probe, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(src), bytes / 16, sink);
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, bool nt, hipStream_t st) {
+  if (nt)
+    hipLaunchKernelGGL(k_read_probe<true>, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(src), bytes / 16,
+                       sink);
+  else
+    hipLaunchKernelGGL(k_read_probe<false>, dim3(grid), dim3(256), 0, st, static_cast<const uint4*>(src), bytes / 16,
+                       sink);
   return hipGetLastError();
 }
 

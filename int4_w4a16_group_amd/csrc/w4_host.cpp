@@ -1269,11 +1269,12 @@ int w4_profile_end(w4_ctx* c, double* total_ms, int32_t* launches) {
   return W4_OK;
 }
 
-int w4_read_probe(const void* src, size_t bytes, void* sink, int32_t grid, void* stream) {
+int w4_read_probe(const void* src, size_t bytes, void* sink, int32_t grid, int32_t nontemporal, void* stream) {
   if (!src || !sink || grid < 1 || grid > (1 << 20) || bytes == 0 || bytes % 16 ||
-      ((uintptr_t)src % 16) != 0)
+      ((uintptr_t)src % 16) != 0 || (nontemporal != 0 && nontemporal != 1))
     return W4_E_INVALID;
-  hipError_t e = launch_read_probe(src, bytes, static_cast<uint32_t*>(sink), grid, (hipStream_t)stream);
+  hipError_t e = launch_read_probe(src, bytes, static_cast<uint32_t*>(sink), grid, nontemporal != 0,
+                                   (hipStream_t)stream);
   return e == hipSuccess ? W4_OK : W4_E_HIP;
 }
 

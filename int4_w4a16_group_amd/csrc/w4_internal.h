@@ -234,6 +234,6 @@ hipError_t launch_sync_probe(int mode, int grid, int n, uint32_t* ctr, hipStream
 // Message of the last failed context-free entry point on this thread.
 extern thread_local std::string g_free_err;
 // Streaming-read probe (diagnostic): src[bytes] read once with 16-byte loads; sink [grid] words.
-hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, bool nt, hipStream_t st);
 
 }  // namespace w4

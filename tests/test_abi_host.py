@@ -211,8 +211,8 @@ def test_probe_argument_checks():
         with pytest.raises(L.W4Error) as e:
             L.w4_sync_probe(mode, grid, n, scratch, nbytes)
         assert e.value.status == L.W4_E_INVALID, args
-    for args in ((None, 1024, 1, 16), (1, 1000, 1, 16), (16, 1024, 1, 0)):
-        src, nbytes, sink, grid = args
+    for args in ((None, 1024, 1, 16, 0), (1, 1000, 1, 16, 0), (16, 1024, 1, 0, 0), (16, 1024, 1, 16, 2)):
+        src, nbytes, sink, grid, nt = args
         with pytest.raises(L.W4Error) as e:
-            L.w4_read_probe(src, nbytes, sink, grid)
+            L.w4_read_probe(src, nbytes, sink, grid, nt)
         assert e.value.status == L.W4_E_INVALID, args
