@@ -521,6 +521,180 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
   if (tid == 0) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------------ prefill attention
+// Causal attention of a prompt's P rows over its own K/V in the slot (rows
+// 0..P-1 written by k_prefill_kv), one pass over the keys per query block:
+// work-group (query block qb of 64 rows, query head h) of four waves; wave w
+// takes rows 64 qb + 16 w .. +15 of head h (the MFMA A operand: row = query
+// position, k = head dimension), rotated at their positions through table.
+// For each 64-key chunk c = 0 .. qb in order, every wave:
+//   S = Q K^T (MFMA, fp32), z = S log2(e) / sqrt(D), keys past the row's
+//   position masked; m' = max(m, max_c z); a = 2^(m - m'); P = 2^(z - m');
+//   l = l a + sum P; O = O a + P V (MFMA on P split into fp16 hi + lo parts).
+// Then o = O / l, row-major fp16 [P][Hq * D].  Each row attends to keys
+// 0 .. its position, the causal definition of the prompt's attention.
+struct PfAttnArgs {
+  KV kv;
+  int layer, slot, P, Hq;
+  const uint16_t* qkv;  // q of row i, head h at qkv + i * ldq + h * D
+  int ldq;
+  const float2* table;  // rotary (cos, sin) [cap][D / 2]
+  uint16_t* o;          // [P][ldo], head h at columns h * D ..
+  int ldo;
+  float scale;          // log2(e) / sqrt(D)
+};
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) k_prefill_attn(PfAttnArgs a) {
+  constexpr int KSQ = D / 32;  // k-steps of q.K
+  constexpr int NDT = D / 16;  // output d-tiles
+  __shared__ float Pl[4][16][65];
+  const int nqb = (a.P + 63) >> 6;
+  const int qb = nqb - 1 - (int)blockIdx.x;  // the longest blocks first
+  const int h = blockIdx.y, G = a.Hq / a.kv.Hkv, g = h / G;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 15, quad = lane >> 4;
+  const int r0 = 64 * qb + 16 * w;  // this wave's first row
+  // Q operand: row col of the wave's 16, rotated pairs (i, i + D/2) =
+  // k-steps (ks, ks + KSQ/2) of the same lane
+  h8 qa[KSQ];
+  {
+    const int qp = min(r0 + col, a.P - 1);
+    const uint16_t* qrow = a.qkv + (size_t)qp * a.ldq + (size_t)h * D + 8 * quad;
+#pragma unroll
+    for (int ks = 0; ks < KSQ; ++ks) qa[ks] = ld_h8(qrow + 32 * ks);
+    const float4* tr = reinterpret_cast<const float4*>(a.table + (size_t)qp * (D / 2) + 8 * quad);
+#pragma unroll
+    for (int ks = 0; ks < KSQ / 2; ++ks) {
+      float4 t4[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) t4[jj] = tr[16 * ks + jj];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 cs = (j & 1) ? make_float2(t4[j / 2].z, t4[j / 2].w) : make_float2(t4[j / 2].x, t4[j / 2].y);
+        const float x0 = (float)qa[ks][j], x1 = (float)qa[ks + KSQ / 2][j];
+        qa[ks][j] = (_Float16)(x0 * cs.x - x1 * cs.y);
+        qa[ks + KSQ / 2][j] = (_Float16)(x0 * cs.y + x1 * cs.x);
+      }
+    }
+  }
+  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, l[4] = {0.f, 0.f, 0.f, 0.f};
+  f4 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f4{0.f, 0.f, 0.f, 0.f};
+  const size_t base = kv_base(a.kv, a.layer, a.slot, g);
+  for (int c = 0; c <= qb; ++c) {
+    const int c0 = 64 * c;
+    const uint16_t* Kc = a.kv.K + base + (size_t)c * 64 * D + lane * 8;
+    const uint16_t* Vc = a.kv.VT + base + (size_t)c * 64 * D + lane * 8;
+    h8 kb[4][KSQ];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(Kc + (pt * KSQ + ks) * 512);
+    f4 S[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(qa[ks], kb[pt][ks], acc);
+      S[pt] = acc;
+    }
+    h8 vop[NDT][2];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
+    // lane holds S[row 4 quad + r][key c0 + 16 pt + col]
+    float alpha[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int qp = r0 + 4 * quad + r;
+      float mc = -INFINITY;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int kp = c0 + pt * 16 + col;
+        const float z = S[pt][r] * a.scale;
+        S[pt][r] = kp > qp ? -INFINITY : z;
+        mc = fmaxf(mc, S[pt][r]);
+      }
+      mc = row16_max(mc);
+      const float mn = fmaxf(m[r], mc);
+      alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);
+      float ls = 0.f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const float e = __builtin_amdgcn_exp2f(S[pt][r] - mn);
+        S[pt][r] = e;
+        ls = ls + e;
+      }
+      l[r] = l[r] * alpha[r] + row16_sum(ls);
+      m[r] = mn;
+    }
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Pl[w][4 * quad + r][pt * 16 + col] = S[pt][r];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P is in LDS
+    __builtin_amdgcn_wave_barrier();
+    h8 phi[2], plo[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pv = Pl[w][col][32 * ks + 8 * quad + j];
+        const _Float16 hi = (_Float16)pv;
+        phi[ks][j] = hi;
+        plo[ks][j] = (_Float16)(pv - (float)hi);
+      }
+    __builtin_amdgcn_wave_barrier();  // Pl is rewritten by the next chunk
+    if (c0 + 63 >= a.P) {
+      // keys past the prompt hold no data of this stream: zero their V
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c0 + 32 * ks + 8 * quad + j >= a.P) vop[dt][ks][j] = (_Float16)0.0f;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      f4 o = oacc[dt];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = o[r] * alpha[r];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        o = mfma16x16x32(phi[ks], vop[dt][ks], o);
+        o = mfma16x16x32(plo[ks], vop[dt][ks], o);
+      }
+      oacc[dt] = o;
+    }
+  }
+  // o = O / l for the wave's rows below P
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qp = r0 + 4 * quad + r;
+    if (qp < a.P) {
+      uint16_t* orow = a.o + (size_t)qp * a.ldo + (size_t)h * D + col;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) orow[dt * 16] = f2h(oacc[dt][r] / l[r]);
+    }
+  }
+}
+
+hipError_t launch_prefill_attention(int P, int layer, int slot, int Hq, const KV& kv, const uint16_t* qkv, int ldq,
+                                    const float2* table, uint16_t* o, int ldo, hipStream_t st) {
+  if (P < 1 || P > kv.cap || Hq % kv.Hkv || (kv.D != 64 && kv.D != 128)) return hipErrorInvalidValue;
+  PfAttnArgs a{kv, layer, slot, P, Hq, qkv, ldq, table, o, ldo, (float)(1.4426950408889634 / sqrt((double)kv.D))};
+  const dim3 grid((P + 63) / 64, Hq);
+  if (kv.D == 128)
+    hipLaunchKernelGGL(k_prefill_attn<128>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_prefill_attn<64>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
                             unsigned* ticket, uint16_t* o, hipStream_t st, void* prof, int o_rows, bool once) {

@@ -186,21 +186,17 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
 }
 
 // Prefill workspace (caller-owned, from w4_prefill_workspace_bytes): the
-// prompt's rows through every layer, attention in chunks of kPrefillChunk rows.
-constexpr int kPrefillChunk = 32;
-
+// prompt's rows through every layer.
 struct PfPlan {
   size_t h, xn, qkv, attn_o, lg, ids, w, counts, offsets, inv, used, n_used, units, unit_rows, n_units, done, ready,
-      act, y, part_o, part_ml, aticket, rows, logits, rmask, re8, total;
+      act, y, rows, logits, rmask, re8, total;
   size_t row_cap;  // int32 words of the rows region
 };
 
-// Words of the prefill upload: slot [P], position [P], sampling parameters,
-// then the attention work list of every chunk.
+// Words of the prefill upload: slot [P], position [P], sampling parameters.
 size_t pf_row_words(const w4_model_desc& d, int P) {
-  size_t n = 0;
-  for (int i = 0; i < P; ++i) n += (size_t)attn_splits(i) * d.n_kv_heads;
-  return (2 * (size_t)P + kSampleParams + 1) / 2 * 2 + 2 * n;
+  (void)d;
+  return 2 * (size_t)P + kSampleParams;
 }
 
 PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
@@ -213,7 +209,7 @@ PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
   };
   const size_t H = d.hidden, E = d.n_experts, k = d.top_k, I = d.moe_inter, Hq = d.n_q_heads, D = d.head_dim;
   const size_t nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * D, pairs = (size_t)P * k;
-  const size_t ucap = E + pairs / 16 + 1, nsmax = attn_splits(cap - 1);
+  const size_t ucap = E + pairs / 16 + 1;
   w.h = take(P * H * 2);
   w.xn = take(P * H * 2);
   w.qkv = take(P * nqkv * 2);
@@ -233,9 +229,6 @@ PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
   w.ready = take(ucap * 8 * kDoneStride * 4);
   w.act = take(pairs * I * 2);
   w.y = take(pairs * H * 2);
-  w.part_o = take((size_t)kPrefillChunk * Hq * nsmax * D * 4);
-  w.part_ml = take((size_t)kPrefillChunk * Hq * nsmax * 2 * 4);
-  w.aticket = take((size_t)kPrefillChunk * d.n_kv_heads * 4);
   w.row_cap = pf_row_words(d, P);
   w.rows = take(w.row_cap * 4);
   w.logits = take((size_t)d.vocab * 2);
@@ -1007,29 +1000,15 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
     q[3] = (int32_t)(uint32_t)(sp.seed & 0xFFFFFFFFu);
     q[4] = (int32_t)(uint32_t)(sp.seed >> 32);
   }
-  const int nchunks = (P + kPrefillChunk - 1) / kPrefillChunk;
-  std::vector<size_t> ch_off(nchunks), ch_n(nchunks);
-  size_t n = (2 * (size_t)P + kSampleParams + 1) / 2 * 2;  // entries are 8-byte pairs
-  for (int ch = 0; ch < nchunks; ++ch) {
-    ch_off[ch] = n;
-    const int i0 = ch * kPrefillChunk, i1 = std::min(P, i0 + kPrefillChunk);
-    for (int i = i0; i < i1; ++i)
-      for (int sp = 0; sp < attn_splits(i); ++sp)
-        for (int g = 0; g < d.n_kv_heads; ++g) {
-          hp[n++] = ((i - i0) << 16) | (sp << 8) | g;
-          hp[n++] = (slot << 16) | i;
-        }
-    ch_n[ch] = (n - ch_off[ch]) / 2;
-  }
+  const size_t n = 2 * (size_t)P + kSampleParams;
   if (n > words) return fail(c, W4_E_INVALID, "prefill row list exceeds its workspace region");
   int32_t* drows = reinterpret_cast<int32_t*>(PW(pp.rows));
   HIPCHK(c, hipMemcpyAsync(drows, hp, n * 4, hipMemcpyHostToDevice, st));
   HIPCHK(c, hipEventRecord(c->ev_pf, st));
   c->pf_used = true;
-  HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(PW(pp.aticket)), 0u, (size_t)kPrefillChunk * d.n_kv_heads, st));
   HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(PW(pp.rmask)), 0u,
                             (size_t)d.n_experts * ((P + 31) / 32), st));
-  c->launches += 2;
+  c->launches += 1;
 
   const int H = d.hidden, E = d.n_experts, k = d.top_k, Hq = d.n_q_heads, D = d.head_dim;
   const int nqkv = (d.n_q_heads + 2 * d.n_kv_heads) * D, qd = Hq * D;
@@ -1063,13 +1042,7 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
     LCHK(c, 1, launch_gemm(c->mat(Ly.qkv), P, xn, H, qkv, nqkv, EPI_F16, st));
     LCHK(c, 1, launch_prefill_kv(P, l, slot, kv, qkv + qd, qkv + qd + d.n_kv_heads * D, nqkv,
                                  c->W<float2>(c->wp.table), st));
-    for (int ch = 0; ch < nchunks; ++ch) {
-      const int i0 = ch * kPrefillChunk, rows = std::min(P - i0, kPrefillChunk);
-      LCHK(c, 1, launch_attention(rows, l, Hq, kv, drows + ch_off[ch], (int)ch_n[ch],
-                                  qkv + (size_t)i0 * nqkv, nqkv, nullptr, nullptr, nqkv, c->W<float2>(c->wp.table),
-                                  reinterpret_cast<float*>(PW(pp.part_o)), reinterpret_cast<float*>(PW(pp.part_ml)),
-                                  reinterpret_cast<unsigned*>(PW(pp.aticket)), ao + (size_t)i0 * qd, st, nullptr, 0));
-    }
+    LCHK(c, 1, launch_prefill_attention(P, l, slot, Hq, kv, qkv, nqkv, c->W<float2>(c->wp.table), ao, qd, st));
     LCHK(c, 1, launch_gemm(c->mat(Ly.o), P, ao, qd, h, H, EPI_RESID, st));
     LCHK(c, 1, launch_rmsnorm(P, H, h, c->Bk<uint16_t>(Ly.moe_norm), d.rms_eps, xn, st, 0));
     float* lg = reinterpret_cast<float*>(PW(pp.lg));

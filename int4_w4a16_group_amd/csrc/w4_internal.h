@@ -170,6 +170,12 @@ inline size_t route_prefill_lds(int P, int E, int k) {
   (void)k;
   return (size_t)E * ((P + 31) / 32) * 6;
 }
+// Causal attention of a prompt's P rows (q of row i, head h at qkv + i * ldq
+// + h * D, rotated here through table) over positions 0..P-1 of the slot's
+// K/V of the layer (already written), one pass over the keys per 64-row
+// query block; o row-major [P][ldo].
+hipError_t launch_prefill_attention(int P, int layer, int slot, int Hq, const KV& kv, const uint16_t* qkv, int ldq,
+                                    const float2* table, uint16_t* o, int ldo, hipStream_t st);
 // positions 0..P-1 of a slot -> canonical k, v [L][P][Hkv][D]
 hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uint16_t* v, hipStream_t st);
 // Split-KV decode attention in one launch.  A stream at position p has
