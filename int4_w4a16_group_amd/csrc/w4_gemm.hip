@@ -352,7 +352,9 @@ __device__ __forceinline__ void set_prio_level(int l) {
 // multiply of the previous one, with its first tiles already in flight).
 // The arithmetic of an output does not depend on which work-group computes
 // it.
-template <int NCH, int G, bool GATEUP, int LB, bool NT = false>
+// ONE (gate/up of a single stream): every unit's rows are row 0 of x, so the
+// x slice is requested at the start with the unit records, not after them.
+template <int NCH, int G, bool GATEUP, int LB, bool NT = false, bool ONE = false>
 __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // dynamic LDS: two buffers of [GATEUP ? 2 : 1][NW][64][4] partials, then
   // the unit records of this work-group's range
@@ -368,6 +370,12 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   const int4 rec0 = a.units[min(tid, a.units_cap - 1)], rec1 = a.units[min(tid + nth, a.units_cap - 1)];
   const int nu = *a.n_units;
   const long long total = (long long)nu * T;
+  XRegs<1, NCH * 4> x;
+  if constexpr (ONE) {
+    const uint16_t* xr = a.x + w * NCH * 128 + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
+  }
   // Ranges by weight: the first work-group dispatched to each compute unit
   // (blockIdx < ncu) takes 1 + d shares, the other 1 - d (d = dshare/1000):
   // with equal shares the second ones were measured to finish 2-3 us later.
@@ -411,17 +419,20 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // outputs are not stored)
   // (gate/up: the next unit's row index is loaded a unit ahead, so a switch
   // does not wait for it)
-  XRegs<1, NCH * 4> x;
   int xu = -1, nrow = 0;
   auto load_x = [&](int uv, int grow) {
     const int u = __builtin_amdgcn_readfirstlane(uv);
+    if constexpr (ONE) {
+      xu = u;
+      return;
+    }
     const int4 un = lrec[u];
     const int row = GATEUP ? grow : un.y + min(i16, un.z - 1);
     const uint16_t* xr = a.x + (size_t)row * a.ldx + kbase + 8 * (lane >> 4);
 #pragma unroll
     for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
     xu = u;
-    if (GATEUP) nrow = a.unit_rows[min(u + 1, nu - 1) * 16 + i16];
+    if (GATEUP && !ONE) nrow = a.unit_rows[min(u + 1, nu - 1) * 16 + i16];
   };
 
   int buf = 0;
@@ -479,7 +490,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // needs it waits for its own stage, issued earlier, in any case.
   Stage<NCH, G, NT> a0, a1, b0, b1;
   stage_load(a0, a1, f_begin);
-  load_x(f_begin / T, GATEUP ? a.unit_rows[(f_begin / T) * 16 + i16] : 0);
+  load_x(f_begin / T, GATEUP && !ONE ? a.unit_rows[(f_begin / T) * 16 + i16] : 0);
   stage_load(b0, b1, f_begin + 1);
   for (int f = f_begin; f < f_end; f += 2) {
     // Issue priority by remaining work: the waves of the work-group with
@@ -756,19 +767,21 @@ __global__ void __launch_bounds__(LB) k_moe_fused(MoeFusedArgs fa) {
 
 typedef void (*MoeKernel)(MoeArgs);
 
-template <bool GU, int NCH, int LB, bool NT>
+template <bool GU, int NCH, int LB, bool NT, bool ONE = false>
 static MoeKernel moe_pick_g(int g) {
   switch (g) {
-    case 32: return k_moe<NCH, 32, GU, LB, NT>;
-    case 64: return k_moe<NCH, 64, GU, LB, NT>;
-    default: return k_moe<NCH, 128, GU, LB, NT>;
+    case 32: return k_moe<NCH, 32, GU, LB, NT, ONE>;
+    case 64: return k_moe<NCH, 64, GU, LB, NT, ONE>;
+    default: return k_moe<NCH, 128, GU, LB, NT, ONE>;
   }
 }
-// nt: non-temporal weight loads (up to 8 waves per tile only)
+// nt: non-temporal weight loads; one: gate/up of a single stream (both for up
+// to 8 waves per tile only)
 template <bool GU>
-static MoeKernel moe_pick(int nch, int g, int nw, bool nt) {
+static MoeKernel moe_pick(int nch, int g, int nw, bool nt, bool one) {
   if (nw <= 8) {
     if (nt) return nch == 2 ? moe_pick_g<GU, 2, 512, true>(g) : moe_pick_g<GU, 1, 512, true>(g);
+    if (GU && one) return nch == 2 ? moe_pick_g<GU, 2, 512, false, GU>(g) : moe_pick_g<GU, 1, 512, false, GU>(g);
     return nch == 2 ? moe_pick_g<GU, 2, 512, false>(g) : moe_pick_g<GU, 1, 512, false>(g);
   }
   return nch == 2 ? moe_pick_g<GU, 2, 1024, false>(g) : moe_pick_g<GU, 1, 1024, false>(g);
@@ -819,11 +832,11 @@ static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_
                         uint16_t* out);
 
 static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, const uint16_t* x, int ldx,
-                                    const RouteOut& r, uint16_t* out, bool nt, hipStream_t st) {
+                                    const RouteOut& r, uint16_t* out, bool nt, bool one, hipStream_t st) {
   const int nch = nch_for(m0.K);
   const int NW = m0.K / (nch * 128);
   const MoeArgs a = moe_args(gateup, m0, m1, x, ldx, r, out);
-  MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW, nt) : moe_pick<false>(nch, m0.g, NW, nt);
+  MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW, nt, one) : moe_pick<false>(nch, m0.g, NW, nt, false);
   if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
   // the records of every unit in LDS (at most kMaxUnits in a decode step, whose
   // launch shape is kept; a prefill can have more)
@@ -929,13 +942,13 @@ hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int 
 }
 
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
-                             uint16_t* act, hipStream_t st, bool nt) {
-  return launch_moe_common(true, gate0, &up0, x, ldx, r, act, nt, st);
+                             uint16_t* act, hipStream_t st, bool nt, bool one) {
+  return launch_moe_common(true, gate0, &up0, x, ldx, r, act, nt, one, st);
 }
 
 hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st,
                            bool nt) {
-  return launch_moe_common(false, down0, nullptr, act, down0.K, r, y, nt, st);
+  return launch_moe_common(false, down0, nullptr, act, down0.K, r, y, nt, false, st);
 }
 
 }  // namespace w4

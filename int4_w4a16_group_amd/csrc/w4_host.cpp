@@ -567,7 +567,7 @@ constexpr int kNtMinRows = 8;
 // SwiGLU, then down; see k_moe_fused) where the geometry allows and the
 // option is on, else the two launches.  Same results bit for bit.
 int launch_experts(w4_ctx* c, const LayerLoc& L, const uint16_t* xn, int ldx, const RouteOut& r, uint16_t* act,
-                   uint16_t* y, uint32_t* ready, bool nt, hipStream_t st) {
+                   uint16_t* y, uint32_t* ready, bool nt, bool one, hipStream_t st) {
   const Mat gate = c->mat(L.gate), up = c->mat(L.up), down = c->mat(L.down);
   if (c->fused_moe && moe_fused_ok(gate, down)) {
     if (c->moe_epoch == 0xFFFFFFFFu) return fail(c, W4_E_UNSUPPORTED, "fused expert launch epochs exhausted");
@@ -577,7 +577,7 @@ int launch_experts(w4_ctx* c, const LayerLoc& L, const uint16_t* xn, int ldx, co
   }
   {
     ProfScope ps(c, W4_K_MOE_GATEUP, st);
-    LCHK(c, 1, launch_moe_gateup(gate, up, xn, ldx, r, act, st, nt));
+    LCHK(c, 1, launch_moe_gateup(gate, up, xn, ldx, r, act, st, nt, one));
   }
   {
     ProfScope ps(c, W4_K_MOE_DOWN, st);
@@ -650,7 +650,7 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
   }
   {
     int rc = launch_experts(c, L, xn, H, r, c->W<uint16_t>(c->wp.act), c->W<uint16_t>(c->wp.y),
-                            c->W<uint32_t>(c->wp.ready), B > kNtMinRows, st);
+                            c->W<uint32_t>(c->wp.ready), B > kNtMinRows, B == 1, st);
     if (rc) return rc;
   }
   LCHK(c, 1, launch_combine(B, H, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), h, true, next_gamma, d.rms_eps,
@@ -1052,7 +1052,7 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
                                     reinterpret_cast<uint8_t*>(PW(pp.re8)), st));
     uint16_t* act = reinterpret_cast<uint16_t*>(PW(pp.act));
     uint16_t* y = reinterpret_cast<uint16_t*>(PW(pp.y));
-    rc = launch_experts(c, Ly, xn, H, r, act, y, ready, false, st);
+    rc = launch_experts(c, Ly, xn, H, r, act, y, ready, false, P == 1, st);
     if (rc) return rc;
     const uint16_t* ng = l + 1 < d.n_layers ? c->Bk<uint16_t>(c->bp.layers[l + 1].attn_norm)
                                             : c->Bk<uint16_t>(c->bp.final_norm);
@@ -1147,7 +1147,7 @@ int w4_moe(w4_ctx* c, int32_t layer, int32_t B, const void* x, const float* rout
   RouteOut r = c->route_out(route_ids);
   LCHK(c, 1, launch_route(lg, B, d.n_experts, d.top_k, r, st));
   rc = launch_experts(c, L, xh, d.hidden, r, c->W<uint16_t>(c->wp.act), c->W<uint16_t>(c->wp.y),
-                      c->W<uint32_t>(c->wp.ready), B > kNtMinRows, st);
+                      c->W<uint32_t>(c->wp.ready), B > kNtMinRows, B == 1, st);
   if (rc) return rc;
   LCHK(c, 1, launch_combine(B, d.hidden, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), static_cast<uint16_t*>(y),
                             false, nullptr, d.rms_eps, nullptr, st));

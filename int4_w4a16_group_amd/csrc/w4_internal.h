@@ -95,8 +95,9 @@ hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int 
 // route).  nt: non-temporal weight loads (same results; measured faster for a
 // decode batch above 8 rows, slower below it and in a prefill, which reads
 // each expert's tiles once per 16-row unit).
+// one: x holds a single stream's row (every unit's rows are row 0).
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
-                             uint16_t* act, hipStream_t st, bool nt = false);
+                             uint16_t* act, hipStream_t st, bool nt = false, bool one = false);
 hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st,
                            bool nt = false);
 // Both grouped products in one launch (same results bit for bit); needs
