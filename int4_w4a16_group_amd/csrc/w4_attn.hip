@@ -318,7 +318,7 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
     };
     if (VE) load_v();
     // this wave's chunk holds position p and the launch appends (knew given);
-    // a prefill launch finds every position's K/V in the arena already
+    // a launch without knew appends nothing: every position's K/V is in the arena
     const bool own = a.knew && c == (p >> 6);
     // The wave whose chunk holds position p: this step's k (rotated) and v go
     // into the arena at p and replace what the loads above read there.
@@ -697,7 +697,7 @@ hipError_t launch_prefill_attention(int P, int layer, int slot, int Hq, const KV
 
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
-                            unsigned* ticket, uint16_t* o, hipStream_t st, void* prof, int o_rows, bool once) {
+                            unsigned* ticket, uint16_t* o, hipStream_t st, void* prof, int o_rows) {
   (void)B;
   AttnArgs a;
   a.kv = kv;
@@ -726,7 +726,7 @@ hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_
   const bool ve = nsplits <= 128;
   // non-temporal K/V loads for a long decode list (measured: 22.5 against
   // 23.9 us at B = 32, 17.3 against 17.8 at B = 16, slower at B = 8)
-  const bool nt = once && nsplits >= 256;
+  const bool nt = nsplits >= 256;
   if (kv.D == 128) {
     if (ve)
       w4_launch(k_attn<128, true, false>, grid, dim3(256), shm, st, a);

@@ -624,8 +624,7 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
   LCHK(c, 1, launch_attention(B, l, d.n_q_heads, kv, c->dev_splits(), c->nsplits, qkv, nqkv,
                               qkv + (size_t)d.n_q_heads * d.head_dim, qkv + (size_t)(d.n_q_heads + d.n_kv_heads) * d.head_dim,
                               nqkv, c->W<float2>(c->wp.table), c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
-                              c->W<unsigned>(c->wp.aticket), o, st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R,
-                              true));
+                              c->W<unsigned>(c->wp.aticket), o, st, c->prof_kernel == W4_K_ATTENTION ? c : nullptr, R));
   // Above 16 rows (a 32-row tile) the output projection at K = 4096 runs as
   // two work-groups per tile (same sums, bit for bit; see
   // launch_gemm_resid_split).  Measured on the 48-layer model with the earlier
@@ -1175,7 +1174,7 @@ int w4_attn_decode(w4_ctx* c, int32_t layer, int32_t B, const int32_t* slots, co
                               Hq * D, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), Hkv * D,
                               nullptr, c->W<float>(c->wp.part_o), c->W<float>(c->wp.part_ml),
                               c->W<unsigned>(c->wp.aticket), static_cast<uint16_t*>(o), st,
-                              c->prof_kernel == W4_K_ATTENTION ? c : nullptr, 0, true));
+                              c->prof_kernel == W4_K_ATTENTION ? c : nullptr));
   return W4_OK;
 }
 

@@ -184,10 +184,9 @@ hipError_t launch_read_kv(int L, int P, int slot, const KV& kv, uint16_t* k, uin
 // 8-byte entry (b << 16 | split << 8 | kv head, slot << 16 | p) for every
 // split of every row and kv head (built on the host with the rows, 8-byte
 // aligned), one work-group each.  part_o [B][Hq][nsmax][D] f32, part_ml
-// [B][Hq][nsmax][2]; prof: when non-null, the launch is timed (prof_arm);
-// once: the K/V are read once in this launch's stream of work (a decode
-// step, not a prefill's chunks), so a long list may stream them
-// non-temporally.  The
+// [B][Hq][nsmax][2]; prof: when non-null, the launch is timed (prof_arm).
+// A list of 256 or more entries streams the K/V with non-temporal loads
+// (each chunk is read once per step).  The
 // last work-group of each (stream, kv head) combines the splits; ticket
 // [B][Hkv] is zero before and after.  This step's q (row stride ldq) and k,
 // v (row stride ldkv) are rotated at each stream's position through table
@@ -199,8 +198,7 @@ __host__ __device__ inline int attn_splits(int pos) {
 }
 hipError_t launch_attention(int B, int layer, int Hq, const KV& kv, const int32_t* splits, int nsplits, const uint16_t* q, int ldq, const uint16_t* knew,
                             const uint16_t* vnew, int ldkv, const float2* table, float* part_o, float* part_ml,
-                            unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0,
-                            bool once = false);
+                            unsigned* ticket, uint16_t* o, hipStream_t st, void* prof = nullptr, int o_rows = 0);
 // Kernel timing: the host arms a (start, stop) event pair for the next
 // launch of the profiled kernel family (prof_arm, from the context's pool);
 // that launch records them with its own dispatch (hipExtLaunchKernelGGL), so
