@@ -321,6 +321,8 @@ struct MoeArgs {
   int ldx;
   const int4* units;      // (expert, first pair, rows, 0) of every 16-row unit, experts ascending
   const int32_t* unit_rows;  // [unit][16] stream of each row (gate/up input rows)
+  const uint4* rows8;        // [unit] the same as 16 bytes when rows8_ok, else any readable [units_cap] array
+  int rows8_ok;
   const int32_t* n_units;
   int units_cap;          // records allocated in units, at most 2 per thread
   uint16_t* out;          // [pairs][N]
@@ -357,7 +359,8 @@ __device__ __forceinline__ void set_prio_level(int l) {
 template <int NCH, int G, bool GATEUP, int LB, bool NT = false, bool ONE = false>
 __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // dynamic LDS: two buffers of [GATEUP ? 2 : 1][NW][64][4] partials, then
-  // the unit records of this work-group's range
+  // the unit records (max(units_cap, kMaxUnits)), then for the non-temporal
+  // gate/up the unit rows as bytes (kMaxUnits x 16)
   extern __shared__ float red[];
   constexpr int NS = NCH * 128 / G;
   const int NW = blockDim.x >> 6;
@@ -368,6 +371,19 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // its records arrive in one round trip.
   const int tid = threadIdx.x, nth = blockDim.x;
   const int4 rec0 = a.units[min(tid, a.units_cap - 1)], rec1 = a.units[min(tid + nth, a.units_cap - 1)];
+  // gate/up of more than 8 streams in a decode step (the non-temporal
+  // variant): the unit rows (input row of each unit row, one byte each) come
+  // in the same round trip, so a unit's x rows are requested without waiting
+  // for its row list first (B = 32: 6288 against 6232 tok/s; at B = 4 and 8
+  // with plain loads it was measured 0.8% slower, so those keep the row list
+  // loads)
+  constexpr bool ROWS = GATEUP && !ONE && NT;
+  const bool rl = ROWS && a.rows8_ok;
+  uint4 rr0 = {0u, 0u, 0u, 0u}, rr1 = {0u, 0u, 0u, 0u};
+  if constexpr (ROWS) {
+    rr0 = a.rows8[min(tid, a.units_cap - 1)];
+    rr1 = a.rows8[min(tid + nth, a.units_cap - 1)];
+  }
   const int nu = *a.n_units;
   const long long total = (long long)nu * T;
   XRegs<1, NCH * 4> x;
@@ -406,6 +422,13 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   if (tid < a.units_cap) lrec[tid] = rec0;
   if (tid + nth < a.units_cap) lrec[tid + nth] = rec1;
   for (int i = tid + 2 * nth; i < a.units_cap; i += nth) lrec[i] = a.units[i];  // prefill: more records
+  uint4* lrow8 = reinterpret_cast<uint4*>(lrec + max(a.units_cap, kMaxUnits));
+  const uint8_t* lrow = reinterpret_cast<const uint8_t*>(lrow8);
+  if (rl) {
+    if (tid < a.units_cap) lrow8[tid] = rr0;
+    if (tid + nth < a.units_cap) lrow8[tid + nth] = rr1;
+    for (int i = tid + 2 * nth; i < a.units_cap; i += nth) lrow8[i] = a.rows8[i];
+  }
   __syncthreads();
 
   // item f's tile into a stage (past the range: the WG's last tile again)
@@ -427,12 +450,12 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
       return;
     }
     const int4 un = lrec[u];
-    const int row = GATEUP ? grow : un.y + min(i16, un.z - 1);
+    const int row = GATEUP ? (rl ? lrow[u * 16 + i16] : grow) : un.y + min(i16, un.z - 1);
     const uint16_t* xr = a.x + (size_t)row * a.ldx + kbase + 8 * (lane >> 4);
 #pragma unroll
     for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
     xu = u;
-    if (GATEUP && !ONE) nrow = a.unit_rows[min(u + 1, nu - 1) * 16 + i16];
+    if (GATEUP && !ONE && !rl) nrow = a.unit_rows[min(u + 1, nu - 1) * 16 + i16];
   };
 
   int buf = 0;
@@ -490,7 +513,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // needs it waits for its own stage, issued earlier, in any case.
   Stage<NCH, G, NT> a0, a1, b0, b1;
   stage_load(a0, a1, f_begin);
-  load_x(f_begin / T, GATEUP && !ONE ? a.unit_rows[(f_begin / T) * 16 + i16] : 0);
+  load_x(f_begin / T, GATEUP && !ONE && !rl ? a.unit_rows[(f_begin / T) * 16 + i16] : 0);
   stage_load(b0, b1, f_begin + 1);
   for (int f = f_begin; f < f_end; f += 2) {
     // Issue priority by remaining work: the waves of the work-group with
@@ -840,7 +863,9 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
   // the records of every unit in LDS (at most kMaxUnits in a decode step, whose
   // launch shape is kept; a prefill can have more)
-  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)std::max(r.units_cap, kMaxUnits) * 16;
+  // (non-temporal gate/up: then the unit rows as bytes)
+  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)std::max(r.units_cap, kMaxUnits) * 16 +
+                     (gateup && nt ? (size_t)kMaxUnits * 16 : 0);
   const int grid = resident_grid(reinterpret_cast<const void*>(k), NW * 64, shm);
   w4_launch(k, dim3(grid), dim3(NW * 64), (uint32_t)shm, st, a);
   return hipGetLastError();
@@ -862,6 +887,9 @@ static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_
   a.ldx = ldx;
   a.units = r.units;
   a.unit_rows = r.unit_rows;
+  // the byte rows fit the LDS area of a decode step's unit count only
+  a.rows8_ok = r.unit_rows8 != nullptr && r.units_cap <= kMaxUnits;
+  a.rows8 = a.rows8_ok ? r.unit_rows8 : reinterpret_cast<const uint4*>(r.unit_rows);
   a.n_units = r.n_units;
   a.units_cap = r.units_cap;
   a.out = out;

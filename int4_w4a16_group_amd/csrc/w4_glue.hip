@@ -371,7 +371,8 @@ __device__ __forceinline__ int wave_excl_sum(int v, int lane, int* total) {
 // experts (wave bit-sliced prefix sums, waves in order; needs >= 4 waves),
 // the pairs ordered by (expert, stream), and the 16-row work units of the
 // grouped products: units[u] = (expert, first pair, rows), unit_rows[u][i] =
-// the stream of the unit's row i (rows past the unit's count repeat row 0).
+// the stream of the unit's row i (rows past the unit's count repeat row 0),
+// and, when unit_rows8 is given, the same streams as bytes.
 struct BucketLds {
   unsigned* mask;  // [E]
   int* off;        // [E] first pair of the expert
@@ -440,6 +441,12 @@ __device__ void bucket_core(int E, int k, int B, const int* s_ids, const BucketL
   __syncthreads();
   const int nun = L.tot[2] + L.tot[5] + L.tot[8] + L.tot[11];  // units of all experts
   for (int i = tid; i < nun * 16; i += blockDim.x) o.unit_rows[i] = L.urows[i];
+  if (o.unit_rows8) {  // the same rows as bytes (streams < 32), four per word
+    uint32_t* r8 = reinterpret_cast<uint32_t*>(o.unit_rows8);
+    for (int i = tid; i < nun * 4; i += blockDim.x)
+      r8[i] = (uint32_t)L.urows[4 * i] | ((uint32_t)L.urows[4 * i + 1] << 8) | ((uint32_t)L.urows[4 * i + 2] << 16) |
+              ((uint32_t)L.urows[4 * i + 3] << 24);
+  }
 }
 
 // One work-group of 1024 threads: top-k softmax of every row (one wave per

@@ -44,7 +44,7 @@ struct BankPlan {
 
 struct WsPlan {
   size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, rlg, rticket, spart, sticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
-      used, n_used, units, unit_rows, n_units, done, ready, act, y, logits, next, rows, table, total;
+      used, n_used, units, unit_rows, unit_rows8, n_units, done, ready, act, y, logits, next, rows, table, total;
 };
 
 bool geometry_ok(const w4_model_desc* d, std::string* why) {
@@ -170,6 +170,7 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.n_used = take(4);
   w.units = take((E + Bm * k / 16 + 1) * 16);
   w.unit_rows = take((E + Bm * k / 16 + 1) * 16 * 4);
+  w.unit_rows8 = take((E + Bm * k / 16 + 1) * 16);
   w.n_units = take(4);
   w.done = take((E + Bm * k / 16 + 1) * kDoneStride * 4);
   w.ready = take((E + Bm * k / 16 + 1) * 8 * kDoneStride * 4);
@@ -354,6 +355,7 @@ struct w4_ctx {
     r.n_used = W<int32_t>(wp.n_used);
     r.units = W<int4>(wp.units);
     r.unit_rows = W<int32_t>(wp.unit_rows);
+    r.unit_rows8 = W<uint4>(wp.unit_rows8);
     r.n_units = W<int32_t>(wp.n_units);
     r.units_cap = d.n_experts + Bm * d.top_k / 16 + 1;
     r.done = W<uint32_t>(wp.done);

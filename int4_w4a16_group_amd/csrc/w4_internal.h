@@ -72,6 +72,7 @@ struct RouteOut {
   int32_t* unit_rows;    // [same][16] stream of each unit row (rows past the count repeat row 0)
   int32_t* n_units;      // [1]
   int units_cap;         // records allocated in units (>= any n_units)
+  uint4* unit_rows8 = nullptr;  // [units_cap] or null: byte i of record u = unit_rows[u][i] (B <= 32)
   uint32_t* done = nullptr;  // [units_cap] x kDoneStride words or null: zeroed for every unit written
                              // (fused expert products)
 };
