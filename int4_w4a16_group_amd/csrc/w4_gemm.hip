@@ -326,6 +326,7 @@ struct MoeArgs {
   const int32_t* n_units;
   int units_cap;          // records allocated in units, at most 2 per thread
   uint16_t* out;          // [pairs][N]
+  const int32_t* dst_rows;  // down: output row of each pair (null: the pair's own row)
   int ncu;                // compute units
   int dshare;             // range weight skew in 1/1000 (see k_moe)
 };
@@ -443,6 +444,14 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // (gate/up: the next unit's row index is loaded a unit ahead, so a switch
   // does not wait for it)
   int xu = -1, nrow = 0;
+  // down with dst_rows: output rows of the unit being loaded, written to
+  // s_dst[unit & 1] by the unit's first multiply (a load in flight is not
+  // waited for before the next tile loads are issued); a unit's rows are
+  // read after a barrier that every wave passes after the previous unit's
+  // last reduction
+  __shared__ int s_dst[2][16];
+  int dreg = 0;
+  bool dpend = false;
   auto load_x = [&](int uv, int grow) {
     const int u = __builtin_amdgcn_readfirstlane(uv);
     if constexpr (ONE) {
@@ -456,6 +465,10 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
     for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
     xu = u;
     if (GATEUP && !ONE && !rl) nrow = a.unit_rows[min(u + 1, nu - 1) * 16 + i16];
+    if (!GATEUP && a.dst_rows) {
+      dreg = a.dst_rows[un.y + min(i16, un.z - 1)];
+      dpend = true;
+    }
   };
 
   int buf = 0;
@@ -475,6 +488,10 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
     f4* r4 = reinterpret_cast<f4*>(rb);
     r4[w * 64 + lane] = acc0[0];
     if (GATEUP) r4[(NW + w) * 64 + lane] = acc1[0];
+    if (!GATEUP && dpend) {
+      if (tid < 16) s_dst[u & 1][tid] = dreg;
+      dpend = false;
+    }
     __syncthreads();  // this tile's partials visible; the other buffer's readers are done
     if (GATEUP) {
       // lanes l and l^32 of a wave sum the gate and the up partials of one
@@ -502,7 +519,10 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
     } else {
       reduce_tile<1, LB / 64>(rb, NW, [&](int i, int j, float v) {
         const int n = t * 16 + j;
-        if (valid && i < m && n < a.N) a.out[(size_t)(off + i) * a.N + n] = f2h(v);
+        if (valid && i < m && n < a.N) {
+          const int orow = a.dst_rows ? s_dst[u & 1][i] : off + i;
+          a.out[(size_t)orow * a.N + n] = f2h(v);
+        }
       });
     }
     buf ^= 1;
@@ -855,10 +875,15 @@ static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_
                         uint16_t* out);
 
 static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, const uint16_t* x, int ldx,
-                                    const RouteOut& r, uint16_t* out, bool nt, bool one, hipStream_t st) {
+                                    const RouteOut& r, uint16_t* out, bool nt, bool one, hipStream_t st,
+                                    bool direct = false) {
   const int nch = nch_for(m0.K);
   const int NW = m0.K / (nch * 128);
-  const MoeArgs a = moe_args(gateup, m0, m1, x, ldx, r, out);
+  MoeArgs a = moe_args(gateup, m0, m1, x, ldx, r, out);
+  if (direct) {
+    if (gateup || !r.pair_flat) return hipErrorInvalidValue;
+    a.dst_rows = r.pair_flat;
+  }
   MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW, nt, one) : moe_pick<false>(nch, m0.g, NW, nt, false);
   if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
   // the records of every unit in LDS (at most kMaxUnits in a decode step, whose
@@ -893,6 +918,7 @@ static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_
   a.n_units = r.n_units;
   a.units_cap = r.units_cap;
   a.out = out;
+  a.dst_rows = nullptr;
   a.ncu = cu_count();
   a.dshare = gateup ? 75 : 0;  // measured: gate/up 38.5 us at 60-120 against 40.0 at 0
   return a;
@@ -975,8 +1001,8 @@ hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x
 }
 
 hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st,
-                           bool nt) {
-  return launch_moe_common(false, down0, nullptr, act, down0.K, r, y, nt, false, st);
+                           bool nt, bool direct) {
+  return launch_moe_common(false, down0, nullptr, act, down0.K, r, y, nt, false, st, direct);
 }
 
 }  // namespace w4

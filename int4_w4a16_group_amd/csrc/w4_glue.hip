@@ -160,6 +160,7 @@ hipError_t launch_embed(int B, int H, int V, int g, const int32_t* tokens, const
 // memory instructions per compute unit: this launch is latency-bound).
 constexpr int kCombThreads = 256;
 
+template <bool DIRECT>
 __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const float* __restrict__ w,
                                                           const int32_t* __restrict__ inv,
                                                           const uint16_t* __restrict__ y, uint16_t* __restrict__ h,
@@ -185,8 +186,18 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
     if (resid && i < H) hres[j] = *reinterpret_cast<const uint4*>(h + (size_t)b * H + i);
     if (gamma && i < H) gv[j] = *reinterpret_cast<const uint4*>(gamma + i);
   }
+  // DIRECT (y in (stream, rank) order): the rows of the first column run are
+  // requested with the weights (their places do not depend on the routing)
+  uint4 yd[16];
+  if (DIRECT) {
+    const int i = 8 * threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      yd[r] = (r < k && i < H) ? *reinterpret_cast<const uint4*>(y + ((size_t)b * k + r) * H + i)
+                               : make_uint4(0u, 0u, 0u, 0u);
+  }
   if (threadIdx.x < k) {
-    s_inv[threadIdx.x] = inv[b * k + threadIdx.x];
+    if (!DIRECT) s_inv[threadIdx.x] = inv[b * k + threadIdx.x];
     s_w[threadIdx.x] = w[b * k + threadIdx.x];
   }
   __syncthreads();
@@ -201,7 +212,9 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
       uint4 yr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (r < k) yr[r] = *reinterpret_cast<const uint4*>(y + (size_t)s_inv[r] * H + i);
+        if (r < k)
+          yr[r] = DIRECT ? (j == 0 ? yd[r] : *reinterpret_cast<const uint4*>(y + ((size_t)b * k + r) * H + i))
+                         : *reinterpret_cast<const uint4*>(y + (size_t)s_inv[r] * H + i);
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -246,9 +259,14 @@ __global__ void __launch_bounds__(kCombThreads) k_combine(int H, int k, const fl
 }
 
 hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* inv, const uint16_t* y, uint16_t* h,
-                          bool resid, const uint16_t* gamma, float eps, uint16_t* xn, hipStream_t st, int xn_rows) {
-  hipLaunchKernelGGL(k_combine, dim3(B), dim3(kCombThreads), 0, st, H, k, w, inv, y, h, resid ? 1 : 0, gamma, eps,
-                     xn, xn_rows);
+                          bool resid, const uint16_t* gamma, float eps, uint16_t* xn, hipStream_t st, int xn_rows,
+                          bool direct) {
+  if (direct)
+    hipLaunchKernelGGL(k_combine<true>, dim3(B), dim3(kCombThreads), 0, st, H, k, w, inv, y, h, resid ? 1 : 0, gamma,
+                       eps, xn, xn_rows);
+  else
+    hipLaunchKernelGGL(k_combine<false>, dim3(B), dim3(kCombThreads), 0, st, H, k, w, inv, y, h, resid ? 1 : 0, gamma,
+                       eps, xn, xn_rows);
   return hipGetLastError();
 }
 
@@ -430,6 +448,7 @@ __device__ void bucket_core(int E, int k, int B, const int* s_ids, const BucketL
     const int pos = L.off[ex] + r;
     if (o.pair_stream) o.pair_stream[pos] = b;
     if (o.pair_rank) o.pair_rank[pos] = i - b * k;
+    if (o.pair_flat) o.pair_flat[pos] = i;
     o.inv[i] = pos;
     L.urows[(L.ubase[ex] + (r >> 4)) * 16 + (r & 15)] = b;
   }
@@ -561,6 +580,7 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
     const int pos = s_off[e] + r;
     if (o.pair_stream) o.pair_stream[pos] = b;
     if (o.pair_rank) o.pair_rank[pos] = i - b * k;
+    if (o.pair_flat) o.pair_flat[pos] = i;
     o.inv[i] = pos;
     o.unit_rows[(s_ub[e] + (r >> 4)) * 16 + (r & 15)] = b;
   }

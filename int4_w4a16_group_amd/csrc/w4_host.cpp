@@ -44,7 +44,8 @@ struct BankPlan {
 
 struct WsPlan {
   size_t h, xn, xp, qkv, attn_o, part_o, part_ml, aticket, amax_v, amax_i, amax_ticket, rlogits, ticket, rlg, rticket, spart, sticket, ids, w, counts, offsets, pair_stream, pair_rank, inv,
-      used, n_used, units, unit_rows, unit_rows8, n_units, done, ready, act, y, logits, next, rows, table, total;
+      used, n_used, units, unit_rows, unit_rows8, pair_flat, n_units, done, ready, act, y, logits, next, rows,
+      table, total;
 };
 
 bool geometry_ok(const w4_model_desc* d, std::string* why) {
@@ -171,6 +172,7 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
   w.units = take((E + Bm * k / 16 + 1) * 16);
   w.unit_rows = take((E + Bm * k / 16 + 1) * 16 * 4);
   w.unit_rows8 = take((E + Bm * k / 16 + 1) * 16);
+  w.pair_flat = take(Bm * k * 4);
   w.n_units = take(4);
   w.done = take((E + Bm * k / 16 + 1) * kDoneStride * 4);
   w.ready = take((E + Bm * k / 16 + 1) * 8 * kDoneStride * 4);
@@ -356,6 +358,7 @@ struct w4_ctx {
     r.units = W<int4>(wp.units);
     r.unit_rows = W<int32_t>(wp.unit_rows);
     r.unit_rows8 = W<uint4>(wp.unit_rows8);
+    r.pair_flat = W<int32_t>(wp.pair_flat);
     r.n_units = W<int32_t>(wp.n_units);
     r.units_cap = d.n_experts + Bm * d.top_k / 16 + 1;
     r.done = W<uint32_t>(wp.done);
@@ -567,10 +570,15 @@ constexpr int kNtMinRows = 8;
 
 // The grouped expert products of one layer: one fused launch (gate/up +
 // SwiGLU, then down; see k_moe_fused) where the geometry allows and the
-// option is on, else the two launches.  Same results bit for bit.
+// option is on, else the two launches.  Same results bit for bit.  *direct:
+// y is in (stream, rank) order (the two launches with non-temporal loads,
+// when r has pair_flat: the combine then reads it without the permutation,
+// B = 32: 6316 against 6285 tok/s; at B = 1 and 8 it measured 0.3-0.5%
+// slower), else in pair order.
 int launch_experts(w4_ctx* c, const LayerLoc& L, const uint16_t* xn, int ldx, const RouteOut& r, uint16_t* act,
-                   uint16_t* y, uint32_t* ready, bool nt, bool one, hipStream_t st) {
+                   uint16_t* y, uint32_t* ready, bool nt, bool one, hipStream_t st, bool* direct) {
   const Mat gate = c->mat(L.gate), up = c->mat(L.up), down = c->mat(L.down);
+  *direct = false;
   if (c->fused_moe && moe_fused_ok(gate, down)) {
     if (c->moe_epoch == 0xFFFFFFFFu) return fail(c, W4_E_UNSUPPORTED, "fused expert launch epochs exhausted");
     ProfScope ps(c, W4_K_MOE, st);
@@ -583,8 +591,9 @@ int launch_experts(w4_ctx* c, const LayerLoc& L, const uint16_t* xn, int ldx, co
   }
   {
     ProfScope ps(c, W4_K_MOE_DOWN, st);
-    LCHK(c, 1, launch_moe_down(down, act, r, y, st, nt));
+    LCHK(c, 1, launch_moe_down(down, act, r, y, st, nt, nt && r.pair_flat != nullptr));
   }
+  *direct = nt && r.pair_flat != nullptr;
   return W4_OK;
 }
 
@@ -649,13 +658,14 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
                              c->W<unsigned>(c->wp.rticket), st, next_span, next_bytes,
                              next_span && B == 1 ? &kv : nullptr, l + 1, slot, pos));
   }
+  bool direct = false;
   {
     int rc = launch_experts(c, L, xn, H, r, c->W<uint16_t>(c->wp.act), c->W<uint16_t>(c->wp.y),
-                            c->W<uint32_t>(c->wp.ready), B > kNtMinRows, B == 1, st);
+                            c->W<uint32_t>(c->wp.ready), B > kNtMinRows, B == 1, st, &direct);
     if (rc) return rc;
   }
   LCHK(c, 1, launch_combine(B, H, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), h, true, next_gamma, d.rms_eps,
-                            xp, st, R));
+                            xp, st, R, direct));
   return W4_OK;
 }
 
@@ -1053,11 +1063,12 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
                                     reinterpret_cast<uint8_t*>(PW(pp.re8)), st));
     uint16_t* act = reinterpret_cast<uint16_t*>(PW(pp.act));
     uint16_t* y = reinterpret_cast<uint16_t*>(PW(pp.y));
-    rc = launch_experts(c, Ly, xn, H, r, act, y, ready, false, P == 1, st);
+    bool direct = false;
+    rc = launch_experts(c, Ly, xn, H, r, act, y, ready, false, P == 1, st, &direct);
     if (rc) return rc;
     const uint16_t* ng = l + 1 < d.n_layers ? c->Bk<uint16_t>(c->bp.layers[l + 1].attn_norm)
                                             : c->Bk<uint16_t>(c->bp.final_norm);
-    LCHK(c, 1, launch_combine(P, H, k, r.w, r.inv, y, h, true, ng, d.rms_eps, xn, st, 0));
+    LCHK(c, 1, launch_combine(P, H, k, r.w, r.inv, y, h, true, ng, d.rms_eps, xn, st, 0, direct));
   }
   // the last prompt token: output projection and its next token (the slot's
   // sampling at draw counter P - 1, the last prompt position)
@@ -1147,11 +1158,12 @@ int w4_moe(w4_ctx* c, int32_t layer, int32_t B, const void* x, const float* rout
   }
   RouteOut r = c->route_out(route_ids);
   LCHK(c, 1, launch_route(lg, B, d.n_experts, d.top_k, r, st));
+  bool direct = false;
   rc = launch_experts(c, L, xh, d.hidden, r, c->W<uint16_t>(c->wp.act), c->W<uint16_t>(c->wp.y),
-                      c->W<uint32_t>(c->wp.ready), B > kNtMinRows, B == 1, st);
+                      c->W<uint32_t>(c->wp.ready), B > kNtMinRows, B == 1, st, &direct);
   if (rc) return rc;
   LCHK(c, 1, launch_combine(B, d.hidden, d.top_k, r.w, r.inv, c->W<uint16_t>(c->wp.y), static_cast<uint16_t*>(y),
-                            false, nullptr, d.rms_eps, nullptr, st));
+                            false, nullptr, d.rms_eps, nullptr, st, 0, direct));
   return W4_OK;
 }
 

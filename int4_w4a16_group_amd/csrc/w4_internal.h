@@ -73,6 +73,7 @@ struct RouteOut {
   int32_t* n_units;      // [1]
   int units_cap;         // records allocated in units (>= any n_units)
   uint4* unit_rows8 = nullptr;  // [units_cap] or null: byte i of record u = unit_rows[u][i] (B <= 32)
+  int32_t* pair_flat = nullptr;  // [B*k] or null: b*k + r of each pair, in expert order (the inverse of inv)
   uint32_t* done = nullptr;  // [units_cap] x kDoneStride words or null: zeroed for every unit written
                              // (fused expert products)
 };
@@ -99,8 +100,10 @@ hipError_t launch_gemm_resid_split(const Mat& w, int B, const uint16_t* xp, int 
 // one: x holds a single stream's row (every unit's rows are row 0).
 hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x, int ldx, const RouteOut& r,
                              uint16_t* act, hipStream_t st, bool nt = false, bool one = false);
+// direct: output row of pair p at y[r.pair_flat[p]] (the (stream, rank) order
+// the combine reads without an index), else at y[p].
 hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st,
-                           bool nt = false);
+                           bool nt = false, bool direct = false);
 // Both grouped products in one launch (same results bit for bit); needs
 // r.done, the ready words ([units_cap][8] x kDoneStride, zeroed once, then
 // only written with epochs), a nonzero epoch larger than any earlier one on
@@ -111,12 +114,13 @@ hipError_t launch_moe_fused(const Mat& gate0, const Mat& up0, const Mat& down0, 
                             const RouteOut& r, uint16_t* act, uint16_t* y, uint32_t* ready, uint32_t epoch,
                             int32_t* err, hipStream_t st);
 // h[b] = fp16(h[b] + fp16(sum_r w[b][r] * y[inv[b][r]]))  (resid), or out = fp16(sum ...) (no resid);
-// then optionally xn[b] = RMSNorm(h[b]) * gamma.
+// then optionally xn[b] = RMSNorm(h[b]) * gamma.  direct: y is in (stream, rank)
+// order, y[b*k + r] (inv unused).  Same results either way.
 // Normalised outputs (xn, out) go to a panel with that many rows when
 // xn_rows > 0, else row-major [B][H].
 hipError_t launch_combine(int B, int H, int k, const float* w, const int32_t* inv, const uint16_t* y,
                           uint16_t* h, bool resid, const uint16_t* gamma, float eps, uint16_t* xn,
-                          hipStream_t st, int xn_rows = 0);
+                          hipStream_t st, int xn_rows = 0, bool direct = false);
 hipError_t launch_rmsnorm(int B, int H, const uint16_t* x, const uint16_t* gamma, float eps, uint16_t* out,
                           hipStream_t st, int out_rows = 0);
 // bad [B]: 1 where the token id is outside [0, V) (that row is zero), else 0.
