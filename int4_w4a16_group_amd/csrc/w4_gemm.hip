@@ -357,9 +357,14 @@ __device__ __forceinline__ void set_prio_level(int l) {
 // it.
 // ONE (gate/up of a single stream): every unit's rows are row 0 of x, so the
 // x slice is requested at the start with the unit records, not after them.
-template <int NCH, int G, bool GATEUP, int LB, bool NT = false, bool ONE = false>
+// MT = 2 (a prompt's products): units of 32 rows, two 16-row MFMA tiles per
+// item sharing each converted weight operand; MFMA computes each output row
+// from its own A row, so the results are the same as with 16-row units.
+template <int NCH, int G, bool GATEUP, int LB, bool NT = false, bool ONE = false, int MT = 1>
 __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
-  // dynamic LDS: two buffers of [GATEUP ? 2 : 1][NW][64][4] partials, then
+  static_assert(MT == 1 || (!NT && !ONE), "32-row units: plain loads, several streams");
+  constexpr int US = 16 * MT;  // rows per unit
+  // dynamic LDS: two buffers of [GATEUP ? 2 : 1][NW][MT][64][4] partials, then
   // the unit records (max(units_cap, kMaxUnits)), then for the non-temporal
   // gate/up the unit rows as bytes (kMaxUnits x 16)
   extern __shared__ float red[];
@@ -387,7 +392,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   }
   const int nu = *a.n_units;
   const long long total = (long long)nu * T;
-  XRegs<1, NCH * 4> x;
+  XRegs<MT, NCH * 4> x;
   if constexpr (ONE) {
     const uint16_t* xr = a.x + w * NCH * 128 + 8 * (lane >> 4);
 #pragma unroll
@@ -413,7 +418,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   if (f_begin >= f_end) return;
   const int last = f_end - 1;
   const int kbase = w * NCH * 128;
-  const int bufsz = (GATEUP ? 2 : 1) * NW * 256;
+  const int bufsz = (GATEUP ? 2 : 1) * NW * MT * 256;
   const int i16 = lane & 15;
   const DqConst dk;
   // Unit records are read from LDS inside the loop: a record loaded from
@@ -443,7 +448,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // outputs are not stored)
   // (gate/up: the next unit's row index is loaded a unit ahead, so a switch
   // does not wait for it)
-  int xu = -1, nrow = 0;
+  int xu = -1, nrow[MT] = {};
   // down with dst_rows: output rows of the unit being loaded, written to
   // s_dst[unit & 1] by the unit's first multiply (a load in flight is not
   // waited for before the next tile loads are issued); a unit's rows are
@@ -452,19 +457,26 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   __shared__ int s_dst[2][16];
   int dreg = 0;
   bool dpend = false;
-  auto load_x = [&](int uv, int grow) {
+  auto load_x = [&](int uv, const int (&grow)[MT]) {
     const int u = __builtin_amdgcn_readfirstlane(uv);
     if constexpr (ONE) {
       xu = u;
       return;
     }
     const int4 un = lrec[u];
-    const int row = GATEUP ? (rl ? lrow[u * 16 + i16] : grow) : un.y + min(i16, un.z - 1);
-    const uint16_t* xr = a.x + (size_t)row * a.ldx + kbase + 8 * (lane >> 4);
 #pragma unroll
-    for (int ks = 0; ks < NCH * 4; ++ks) x.a[0][ks] = ld_h8(xr + ks * 32);
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row =
+          GATEUP ? (rl ? lrow[u * 16 + i16] : grow[mt]) : un.y + min(mt * 16 + i16, un.z - 1);
+      const uint16_t* xr = a.x + (size_t)row * a.ldx + kbase + 8 * (lane >> 4);
+#pragma unroll
+      for (int ks = 0; ks < NCH * 4; ++ks) x.a[mt][ks] = ld_h8(xr + ks * 32);
+    }
     xu = u;
-    if (GATEUP && !ONE && !rl) nrow = a.unit_rows[min(u + 1, nu - 1) * 16 + i16];
+    if (GATEUP && !ONE && !rl) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) nrow[mt] = a.unit_rows[min(u + 1, nu - 1) * US + mt * 16 + i16];
+    }
     if (!GATEUP && a.dst_rows) {
       dreg = a.dst_rows[un.y + min(i16, un.z - 1)];
       dpend = true;
@@ -478,16 +490,24 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
     const int off = un.y, m = un.z;
     float sv0[NS], sv1[NS];
     g0.scales_f32(sv0);
-    f4 acc0[1] = {f4{0.f, 0.f, 0.f, 0.f}}, acc1[1] = {f4{0.f, 0.f, 0.f, 0.f}};
-    tile_mac<1, NCH, G>(x, g0.w, sv0, acc0, dk);
+    f4 acc0[MT], acc1[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc0[mt] = f4{0.f, 0.f, 0.f, 0.f};
+      acc1[mt] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    tile_mac<MT, NCH, G>(x, g0.w, sv0, acc0, dk);
     if (GATEUP) {
       g1.scales_f32(sv1);
-      tile_mac<1, NCH, G>(x, g1.w, sv1, acc1, dk);
+      tile_mac<MT, NCH, G>(x, g1.w, sv1, acc1, dk);
     }
     float* rb = red + buf * bufsz;
     f4* r4 = reinterpret_cast<f4*>(rb);
-    r4[w * 64 + lane] = acc0[0];
-    if (GATEUP) r4[(NW + w) * 64 + lane] = acc1[0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      r4[(w * MT + mt) * 64 + lane] = acc0[mt];
+      if (GATEUP) r4[((NW + w) * MT + mt) * 64 + lane] = acc1[mt];
+    }
     if (!GATEUP && dpend) {
       if (tid < 16) s_dst[u & 1][tid] = dreg;
       dpend = false;
@@ -497,27 +517,27 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
       // lanes l and l^32 of a wave sum the gate and the up partials of one
       // output (slices in order, every read issued before the adds)
       constexpr int NB = LB / 64;  // >= NW
-      for (int ob = 0; ob < 256; ob += NW * 32) {  // uniform trip count
+      for (int ob = 0; ob < MT * 256; ob += NW * 32) {  // uniform trip count
         const int o = ob + w * 32 + (lane & 31), pp = lane >> 5;
-        const int oc = min(o, 255);
-        const int i = oc >> 4, j = oc & 15;
-        const float* p = rb + pp * NW * 256 + ((i >> 2) * 16 + j) * 4 + (i & 3);
+        const int oc = min(o, MT * 256 - 1);
+        const int i = ((oc >> 8) << 4) + ((oc >> 4) & 15), j = oc & 15;  // unit row, column
+        const float* p = rb + pp * NW * MT * 256 + tile_out_idx(oc);
         float r[NB];
 #pragma unroll
-        for (int k = 0; k < NB; ++k) r[k] = p[min(k, NW - 1) * 256];
+        for (int k = 0; k < NB; ++k) r[k] = p[min(k, NW - 1) * MT * 256];
         float v = r[0];
 #pragma unroll
         for (int k = 1; k < NB; ++k) v = k < NW ? v + r[k] : v;
         const float vu = __shfl_xor(v, 32, 64);
         const int n = t * 16 + j;
-        if (pp == 0 && o < 256 && valid && i < m && n < a.N) {
+        if (pp == 0 && o < MT * 256 && valid && i < m && n < a.N) {
           const float gt = h2f(f2h(v)), up = h2f(f2h(vu));
           const float silu = gt / (1.0f + expf(-gt));
           a.out[(size_t)(off + i) * a.N + n] = f2h(silu * up);
         }
       }
     } else {
-      reduce_tile<1, LB / 64>(rb, NW, [&](int i, int j, float v) {
+      reduce_tile<MT, LB / 64>(rb, NW, [&](int i, int j, float v) {
         const int n = t * 16 + j;
         if (valid && i < m && n < a.N) {
           const int orow = a.dst_rows ? s_dst[u & 1][i] : off + i;
@@ -533,7 +553,14 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // needs it waits for its own stage, issued earlier, in any case.
   Stage<NCH, G, NT> a0, a1, b0, b1;
   stage_load(a0, a1, f_begin);
-  load_x(f_begin / T, GATEUP && !ONE && !rl ? a.unit_rows[(f_begin / T) * 16 + i16] : 0);
+  {
+    int r0[MT] = {};
+    if (GATEUP && !ONE && !rl) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) r0[mt] = a.unit_rows[(f_begin / T) * US + mt * 16 + i16];
+    }
+    load_x(f_begin / T, r0);
+  }
   stage_load(b0, b1, f_begin + 1);
   for (int f = f_begin; f < f_end; f += 2) {
     // Issue priority by remaining work: the waves of the work-group with
@@ -830,6 +857,20 @@ static MoeKernel moe_pick(int nch, int g, int nw, bool nt, bool one) {
   return nch == 2 ? moe_pick_g<GU, 2, 1024, false>(g) : moe_pick_g<GU, 1, 1024, false>(g);
 }
 
+// 32-row units (a prompt's products): plain loads, up to 8 waves per tile
+template <bool GU, int NCH>
+static MoeKernel moe_pick_mt2_g(int g) {
+  switch (g) {
+    case 32: return k_moe<NCH, 32, GU, 512, false, false, 2>;
+    case 64: return k_moe<NCH, 64, GU, 512, false, false, 2>;
+    default: return k_moe<NCH, 128, GU, 512, false, false, 2>;
+  }
+}
+template <bool GU>
+static MoeKernel moe_pick_mt2(int nch, int g) {
+  return nch == 2 ? moe_pick_mt2_g<GU, 2>(g) : moe_pick_mt2_g<GU, 1>(g);
+}
+
 static int cu_count() {
   static int cus = 0;
   if (cus == 0) {
@@ -884,12 +925,16 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
     if (gateup || !r.pair_flat) return hipErrorInvalidValue;
     a.dst_rows = r.pair_flat;
   }
-  MoeKernel k = gateup ? moe_pick<true>(nch, m0.g, NW, nt, one) : moe_pick<false>(nch, m0.g, NW, nt, false);
+  const int MT = r.unit_n / 16;
+  if (r.unit_n != 16 && (r.unit_n != 32 || nt || one || direct || NW > 8)) return hipErrorInvalidValue;
+  MoeKernel k = MT == 2 ? (gateup ? moe_pick_mt2<true>(nch, m0.g) : moe_pick_mt2<false>(nch, m0.g))
+                : gateup ? moe_pick<true>(nch, m0.g, NW, nt, one)
+                         : moe_pick<false>(nch, m0.g, NW, nt, false);
   if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
   // the records of every unit in LDS (at most kMaxUnits in a decode step, whose
   // launch shape is kept; a prefill can have more)
   // (non-temporal gate/up: then the unit rows as bytes)
-  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * 1024 + (size_t)std::max(r.units_cap, kMaxUnits) * 16 +
+  const size_t shm = 2 * (size_t)(gateup ? 2 : 1) * NW * MT * 1024 + (size_t)std::max(r.units_cap, kMaxUnits) * 16 +
                      (gateup && nt ? (size_t)kMaxUnits * 16 : 0);
   const int grid = resident_grid(reinterpret_cast<const void*>(k), NW * 64, shm);
   w4_launch(k, dim3(grid), dim3(NW * 64), (uint32_t)shm, st, a);
@@ -943,7 +988,8 @@ bool moe_fused_ok(const Mat& gate0, const Mat& down0) {
 hipError_t launch_moe_fused(const Mat& gate0, const Mat& up0, const Mat& down0, const uint16_t* x, int ldx,
                             const RouteOut& r, uint16_t* act, uint16_t* y, uint32_t* ready, uint32_t epoch,
                             int32_t* err, hipStream_t st) {
-  if (!moe_fused_ok(gate0, down0) || !r.done || !ready || !err || epoch == 0) return hipErrorInvalidValue;
+  if (!moe_fused_ok(gate0, down0) || !r.done || !ready || !err || epoch == 0 || r.unit_n != 16)
+    return hipErrorInvalidValue;
   if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;
   const int nch = nch_for(gate0.K), NW = gate0.K / (nch * 128);
   const int nchd = nch_for(down0.K);

@@ -513,8 +513,8 @@ hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut
 // expert as one byte, and sets bit b of expert e's row mask (global, zero
 // before).  k_bucket_prefill, one work-group: the pairs ordered by (expert,
 // row) -- a pair's place within its expert is the number of lower rows in the
-// expert's mask, a prefix popcount -- and the 16-row work units; it clears the
-// masks again.
+// expert's mask, a prefix popcount -- and the work units of o.unit_n rows; it
+// clears the masks again.
 __global__ void __launch_bounds__(1024) k_topk_rows(const float* __restrict__ logits, int P, int E, int k,
                                                     RouteOut o, uint32_t* __restrict__ mask,
                                                     uint8_t* __restrict__ e8) {
@@ -543,6 +543,7 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   extern __shared__ uint32_t s_pm[];
   __shared__ int s_cnt[kRouteMaxE], s_off[kRouteMaxE], s_ub[kRouteMaxE];
   const int W = (P + 31) / 32;
+  const int US = o.unit_n;  // rows per unit
   uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_pm + (size_t)E * W);
   const int tid = threadIdx.x;
   for (int i = tid; i < E * W; i += blockDim.x) s_pm[i] = mask[i];
@@ -567,7 +568,7 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
       if (o.offsets) o.offsets[e] = off;
       if (c > 0) o.used[nused++] = e;
       off += c;
-      ub += (c + 15) >> 4;
+      ub += (c + US - 1) / US;
     }
     if (o.offsets) o.offsets[E] = off;
     *o.n_used = nused;
@@ -582,19 +583,19 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
     if (o.pair_rank) o.pair_rank[pos] = i - b * k;
     if (o.pair_flat) o.pair_flat[pos] = i;
     o.inv[i] = pos;
-    o.unit_rows[(s_ub[e] + (r >> 4)) * 16 + (r & 15)] = b;
+    o.unit_rows[(s_ub[e] + r / US) * US + r % US] = b;
   }
   // unit records; rows past a unit's count repeat its first row (the row of
-  // rank 16 u within the expert: found from the mask)
+  // rank US u within the expert: found from the mask)
   for (int e = tid; e < E; e += blockDim.x) {
     const int c = s_cnt[e];
-    const int nu = (c + 15) >> 4;
+    const int nu = (c + US - 1) / US;
     for (int j = 0; j < nu; ++j) {
-      o.units[s_ub[e] + j] = make_int4(e, s_off[e] + 16 * j, min(16, c - 16 * j), 0);
+      o.units[s_ub[e] + j] = make_int4(e, s_off[e] + US * j, min(US, c - US * j), 0);
       if (o.done) o.done[(size_t)(s_ub[e] + j) * kDoneStride] = 0u;
     }
-    if (c > 0 && (c & 15)) {
-      const int want = 16 * (nu - 1);  // rank of the last unit's first row
+    if (c > 0 && (c % US)) {
+      const int want = US * (nu - 1);  // rank of the last unit's first row
       int seen = 0, first = 0;
       for (int j = 0; j < W; ++j) {
         const uint32_t m = s_pm[e * W + j];
@@ -607,7 +608,7 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
         }
         seen += pc;
       }
-      for (int i = c - 16 * (nu - 1); i < 16; ++i) o.unit_rows[(s_ub[e] + nu - 1) * 16 + i] = first;
+      for (int i = c - US * (nu - 1); i < US; ++i) o.unit_rows[(s_ub[e] + nu - 1) * US + i] = first;
     }
   }
 }
@@ -615,7 +616,8 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
 hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, uint32_t* mask,
                                 uint8_t* e8, hipStream_t st) {
   const size_t lds = route_prefill_lds(P, E, k);
-  if (P < 1 || E > kRouteMaxE || (size_t)P * k > (size_t)kPrefillMaxPairs || lds > 61440 || !mask || !e8)
+  if (P < 1 || E > kRouteMaxE || (size_t)P * k > (size_t)kPrefillMaxPairs || lds > 61440 || !mask || !e8 ||
+      (o.unit_n != 16 && o.unit_n != 32))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_topk_rows, dim3((P + 15) / 16), dim3(1024), 0, st, logits, P, E, k, o, mask, e8);
   hipLaunchKernelGGL(k_bucket_prefill, dim3(1), dim3(1024), lds, st, P, E, k, o, mask, e8);

@@ -226,7 +226,7 @@ PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
   w.used = take(E * 4);
   w.n_used = take(4);
   w.units = take(ucap * 16);
-  w.unit_rows = take(ucap * 16 * 4);
+  w.unit_rows = take(ucap * 32 * 4);  // 16-row units, or half as many of 32 rows
   w.n_units = take(4);
   w.done = take(ucap * kDoneStride * 4);
   w.ready = take(ucap * 8 * kDoneStride * 4);
@@ -567,6 +567,10 @@ struct ProfScope {
 // gate/up 37.9 against 39.2 us and down 22.2 against 23.4 us at B = 32, but
 // 13.5 against 12.5 and 8.5 against 7.9 us at B = 1.
 constexpr int kNtMinRows = 8;
+
+// A prompt of at least this many rows runs its expert products over 32-row
+// units.
+constexpr int kPromptUnitRows32 = 64;
 
 // The grouped expert products of one layer: one fused launch (gate/up +
 // SwiGLU, then down; see k_moe_fused) where the geometry allows and the
@@ -1040,7 +1044,10 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
   r.units = reinterpret_cast<int4*>(PW(pp.units));
   r.unit_rows = reinterpret_cast<int32_t*>(PW(pp.unit_rows));
   r.n_units = reinterpret_cast<int32_t*>(PW(pp.n_units));
-  r.units_cap = E + P * k / 16 + 1;
+  // a long prompt's expert products take 32-row units (each converted weight
+  // operand serves two 16-row MFMA tiles; same results)
+  r.unit_n = P >= kPromptUnitRows32 && !c->fused_moe ? 32 : 16;
+  r.units_cap = E + P * k / r.unit_n + 1;
   r.done = reinterpret_cast<uint32_t*>(PW(pp.done));
   // the fused expert launches' ready words: zero once per call (the caller's
   // buffer may hold anything), then written with this context's epochs only

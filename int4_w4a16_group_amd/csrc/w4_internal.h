@@ -72,6 +72,7 @@ struct RouteOut {
   int32_t* unit_rows;    // [same][16] stream of each unit row (rows past the count repeat row 0)
   int32_t* n_units;      // [1]
   int units_cap;         // records allocated in units (>= any n_units)
+  int unit_n = 16;       // rows per unit: 16, or 32 for a prompt's products (prompt routing only)
   uint4* unit_rows8 = nullptr;  // [units_cap] or null: byte i of record u = unit_rows[u][i] (B <= 32)
   int32_t* pair_flat = nullptr;  // [B*k] or null: b*k + r of each pair, in expert order (the inverse of inv)
   uint32_t* done = nullptr;  // [units_cap] x kDoneStride words or null: zeroed for every unit written
