@@ -545,7 +545,14 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   const int W = (P + 31) / 32;
   const int US = o.unit_n;  // rows per unit
   uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_pm + (size_t)E * W);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // this thread's run of pairs (at most kPrefillMaxPairs / 1024 = 16): their
+  // experts requested first, so the pair loop below waits for nothing
+  const int PK = P * k, per = (PK + (int)blockDim.x - 1) / (int)blockDim.x, i0 = tid * per;
+  static_assert(kPrefillMaxPairs <= 16 * 1024, "16 pairs per thread");
+  uint8_t ev[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) ev[q] = (q < per && i0 + q < PK) ? e8[i0 + q] : (uint8_t)0;
   for (int i = tid; i < E * W; i += blockDim.x) s_pm[i] = mask[i];
   __syncthreads();
   for (int i = tid; i < E * W; i += blockDim.x) mask[i] = 0u;  // zero again for the next layer
@@ -558,25 +565,52 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
     s_cnt[e] = c;
   }
   __syncthreads();
-  if (tid == 0) {  // exclusive scans over the experts, in expert order
-    int off = 0, ub = 0, nused = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = s_cnt[e];
-      s_off[e] = off;
-      s_ub[e] = ub;
-      if (o.counts) o.counts[e] = c;
-      if (o.offsets) o.offsets[e] = off;
-      if (c > 0) o.used[nused++] = e;
-      off += c;
-      ub += (c + US - 1) / US;
+  // exclusive scans over the experts, in expert order: wave w takes experts
+  // 64w .. 64w+63 (ballot bit-sliced prefix sums), then the waves in order
+  __shared__ int s_tot[12];
+  int xc = 0, xu = 0, xn = 0, ec = 0, eu = 0, en = 0;
+  if (w < 4) {
+    const int e = tid;
+    xc = e < E ? s_cnt[e] : 0;
+    xu = xc > 0;
+    xn = (xc + US - 1) / US;
+    int tc, tu, tn;
+    ec = wave_excl_sum<15>(xc, lane, &tc);  // c <= P <= 16384
+    eu = wave_excl_sum<1>(xu, lane, &tu);
+    en = wave_excl_sum<11>(xn, lane, &tn);
+    if (lane == 0) {
+      s_tot[3 * w] = tc;
+      s_tot[3 * w + 1] = tu;
+      s_tot[3 * w + 2] = tn;
     }
-    if (o.offsets) o.offsets[E] = off;
-    *o.n_used = nused;
-    *o.n_units = ub;
   }
   __syncthreads();
-  for (int i = tid; i < P * k; i += blockDim.x) {
-    const int b = i / k, e = e8[i];
+  if (w < 4) {
+    const int e = tid;
+    for (int ww = 0; ww < w; ++ww) {
+      ec += s_tot[3 * ww];
+      eu += s_tot[3 * ww + 1];
+      en += s_tot[3 * ww + 2];
+    }
+    if (e < E) {
+      s_off[e] = ec;
+      s_ub[e] = en;
+      if (o.counts) o.counts[e] = xc;
+      if (o.offsets) o.offsets[e] = ec;
+      if (xu) o.used[eu] = e;
+    }
+    if (e == E - 1) {
+      if (o.offsets) o.offsets[E] = ec + xc;
+      *o.n_used = eu + xu;
+      *o.n_units = en + xn;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = i0 + q;
+    if (q >= per || i >= PK) continue;
+    const int b = i / k, e = ev[q];
     const int r = s_pre[e * W + (b >> 5)] + __popc(s_pm[e * W + (b >> 5)] & ((1u << (b & 31)) - 1u));
     const int pos = s_off[e] + r;
     if (o.pair_stream) o.pair_stream[pos] = b;
