@@ -546,13 +546,13 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   const int US = o.unit_n;  // rows per unit
   uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_pm + (size_t)E * W);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // this thread's run of pairs (at most kPrefillMaxPairs / 1024 = 16): their
-  // experts requested first, so the pair loop below waits for nothing
-  const int PK = P * k, per = (PK + (int)blockDim.x - 1) / (int)blockDim.x, i0 = tid * per;
+  // this thread's pairs tid + 1024 q (at most kPrefillMaxPairs / 1024 = 16):
+  // their experts requested first, so the pair loop below waits for nothing
+  const int PK = P * k;
   static_assert(kPrefillMaxPairs <= 16 * 1024, "16 pairs per thread");
   uint8_t ev[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) ev[q] = (q < per && i0 + q < PK) ? e8[i0 + q] : (uint8_t)0;
+  for (int q = 0; q < 16; ++q) ev[q] = tid + 1024 * q < PK ? e8[tid + 1024 * q] : (uint8_t)0;
   for (int i = tid; i < E * W; i += blockDim.x) s_pm[i] = mask[i];
   __syncthreads();
   for (int i = tid; i < E * W; i += blockDim.x) mask[i] = 0u;  // zero again for the next layer
@@ -608,8 +608,8 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    const int i = i0 + q;
-    if (q >= per || i >= PK) continue;
+    const int i = tid + 1024 * q;
+    if (i >= PK) continue;
     const int b = i / k, e = ev[q];
     const int r = s_pre[e * W + (b >> 5)] + __popc(s_pm[e * W + (b >> 5)] & ((1u << (b & 31)) - 1u));
     const int pos = s_off[e] + r;
