@@ -308,6 +308,161 @@ hipError_t launch_gemm(const Mat& w, int B, const uint16_t* x, int ldx, void* y,
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ large-M products (prompt rows)
+// y[M][N] for a prompt's M rows.  Work-group (row block of 128 rows, column
+// block of 8 tiles) of four waves in a 2 x 2 grid; wave (wm, wn) computes rows
+// 64 wm .. +63 by tiles 4 wn .. +3 (16 MFMA tiles).  K streams in 128-column
+// chunks through two LDS stages filled by direct-to-LDS loads (16 bytes per
+// lane, no registers): the block's x rows in A operand order ([row tile]
+// [k-step][lane]) and the 8 tiles' codes as stored.  The next chunk is
+// requested right after the barrier that publishes the current one, so it
+// arrives while the current one is multiplied; each wave converts its four
+// tiles' codes per k-step.  Per output: acc = fma(scale, MFMA chain of the
+// group from zero, acc) over the groups in K order, fp32 (the M-row decode
+// product adds per-slice sums instead: the same terms, rounded differently).
+struct LmArgs {
+  const uint4* tiles;
+  const uint16_t* scales;
+  int N, K, ntiles;
+  const uint16_t* x;
+  int ldx, M;
+  void* y;
+  int ldy;
+};
+
+template <int G, int EPI>
+__global__ void __launch_bounds__(256, 2) k_gemm_lm(LmArgs a) {
+  constexpr int NGC = 128 / G, SPG = G / 32;
+  constexpr int AW = 8 * 4 * 64;  // 16-byte words of a stage's A part; then 8 x 64 words of codes
+  __shared__ __align__(16) v4u lds[2][AW + 8 * 64];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, i16 = lane & 15, quad = lane >> 4;
+  const int wm = w >> 1, wn = w & 1;
+  const int m0 = blockIdx.x * 128, t0 = blockIdx.y * 8;
+  const int NK = a.K / 128, KG = a.K / G;
+  // this wave's loads of a chunk: row tiles 2w, 2w+1 (rows past M read row
+  // M-1) and the codes of tiles 2w, 2w+1 (tiles past N read tile 0; neither
+  // is stored)
+  const uint16_t* xr0 = a.x + (size_t)min(m0 + 32 * w + i16, a.M - 1) * a.ldx + 8 * quad;
+  const uint16_t* xr1 = a.x + (size_t)min(m0 + 32 * w + 16 + i16, a.M - 1) * a.ldx + 8 * quad;
+  const int tc0 = t0 + 2 * w < a.ntiles ? t0 + 2 * w : 0, tc1 = t0 + 2 * w + 1 < a.ntiles ? t0 + 2 * w + 1 : 0;
+  const uint4* bp0 = a.tiles + (size_t)tc0 * NK * 64 + lane;
+  const uint4* bp1 = a.tiles + (size_t)tc1 * NK * 64 + lane;
+  const uint16_t* sp[4];  // scales of this lane's column in the wave's four tiles
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int t = t0 + 4 * wn + c;
+    sp[c] = a.scales + (size_t)((t < a.ntiles ? t : 0) * 16 + i16) * KG;
+  }
+  uint16_t scn[4][NGC];
+  auto issue = [&](int kc, int st) {
+    v4u* L = lds[st];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      __builtin_amdgcn_global_load_lds(xr0 + kc * 128 + 32 * ks, L + ((2 * w) * 4 + ks) * 64, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(xr1 + kc * 128 + 32 * ks, L + ((2 * w + 1) * 4 + ks) * 64, 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(bp0 + kc * 64, L + AW + (2 * w) * 64, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(bp1 + kc * 64, L + AW + (2 * w + 1) * 64, 16, 0, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int gq = 0; gq < NGC; ++gq) scn[c][gq] = sp[c][kc * NGC + gq];
+  };
+  const DqConst dk;
+  f4 acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = f4{0.f, 0.f, 0.f, 0.f};
+  issue(0, 0);
+  for (int kc = 0; kc < NK; ++kc) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk kc are in LDS (and its scales in registers)
+    float sc[4][NGC];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int gq = 0; gq < NGC; ++gq) sc[c][gq] = h2f(scn[c][gq]);
+    __syncthreads();  // every wave's chunk kc is in LDS; every wave is done with chunk kc-1's stage
+    if (kc + 1 < NK) issue(kc + 1, (kc + 1) & 1);
+    const v4u* L = lds[kc & 1];
+    v4u braw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) braw[c] = L[AW + (4 * wn + c) * 64 + lane];
+#pragma unroll
+    for (int gq = 0; gq < NGC; ++gq) {
+      f4 part[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) part[r][c] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = gq * SPG; s2 < (gq + 1) * SPG; ++s2) {
+        h8 av[4], bv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[r] = __builtin_bit_cast(h8, L[((4 * wm + r) * 4 + s2) * 64 + lane]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) bv[c] = dq8(braw[c][s2], dk);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) part[r][c] = mfma16x16x32(av[r], bv[c], part[r][c]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[r][c][e] = fmaf(sc[c][gq], part[r][c][e], acc[r][c][e]);
+    }
+  }
+  // lane holds rows 4 quad + e of each row tile, column i16 of each tile
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int t = t0 + 4 * wn + c, n = t * 16 + i16;
+    if (t >= a.ntiles || n >= a.N) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + 64 * wm + 16 * r + 4 * quad + e;
+        if (row >= a.M) continue;
+        const float v = acc[r][c][e];
+        const size_t o = (size_t)row * a.ldy + n;
+        if (EPI == EPI_F32) {
+          reinterpret_cast<float*>(a.y)[o] = v;
+        } else if (EPI == EPI_F16) {
+          reinterpret_cast<uint16_t*>(a.y)[o] = f2h(v);
+        } else {
+          uint16_t* h = reinterpret_cast<uint16_t*>(a.y) + o;
+          *h = f2h(h2f(*h) + h2f(f2h(v)));
+        }
+      }
+  }
+}
+
+template <int EPI>
+static void (*lm_pick(int g))(LmArgs) {
+  switch (g) {
+    case 32: return k_gemm_lm<32, EPI>;
+    case 64: return k_gemm_lm<64, EPI>;
+    default: return k_gemm_lm<128, EPI>;
+  }
+}
+
+bool lm_ok(const Mat& w, int ldx) {
+  return w.K % 128 == 0 && (w.g == 32 || w.g == 64 || w.g == 128) && ldx % 8 == 0 && ldx >= w.K;
+}
+
+hipError_t launch_gemm_lm(const Mat& w, int M, const uint16_t* x, int ldx, void* y, int ldy, int epi,
+                          hipStream_t st) {
+  if (!lm_ok(w, ldx) || M < 1 || (reinterpret_cast<uintptr_t>(x) & 15)) return hipErrorInvalidValue;
+  LmArgs a{w.tiles, w.scales, w.N, w.K, w.ntiles(), x, ldx, M, y, ldy};
+  void (*k)(LmArgs) = epi == EPI_F32 ? lm_pick<EPI_F32>(w.g) : epi == EPI_F16 ? lm_pick<EPI_F16>(w.g)
+                                                                               : lm_pick<EPI_RESID>(w.g);
+  w4_launch(k, dim3((M + 127) / 128, (a.ntiles + 7) / 8), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------ grouped experts
 struct MoeArgs {
   const uint4* t0;        // gate (or down) tiles of expert 0; experts consecutive

@@ -572,6 +572,14 @@ constexpr int kNtMinRows = 8;
 // units.
 constexpr int kPromptUnitRows32 = 64;
 
+// Dense product of a prompt's rows: the large-M form (128 x 128 blocks) for a
+// prompt of at least 128 rows and an output of at least 64 tiles (enough
+// blocks to fill the chip), else the row-block form.
+hipError_t pf_gemm(const Mat& w, int P, const uint16_t* x, int ldx, void* y, int ldy, int epi, hipStream_t st) {
+  if (P >= 128 && w.ntiles() >= 64 && lm_ok(w, ldx)) return launch_gemm_lm(w, P, x, ldx, y, ldy, epi, st);
+  return launch_gemm(w, P, x, ldx, y, ldy, epi, st);
+}
+
 // The grouped expert products of one layer: one fused launch (gate/up +
 // SwiGLU, then down; see k_moe_fused) where the geometry allows and the
 // option is on, else the two launches.  Same results bit for bit.  *direct:
@@ -1057,11 +1065,11 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
                           c->Bk<uint16_t>(c->bp.layers[0].attn_norm), d.rms_eps, xn, c->pf_flags_dev, st, 0));
   for (int l = 0; l < d.n_layers; ++l) {
     const LayerLoc& Ly = c->bp.layers[l];
-    LCHK(c, 1, launch_gemm(c->mat(Ly.qkv), P, xn, H, qkv, nqkv, EPI_F16, st));
+    LCHK(c, 1, pf_gemm(c->mat(Ly.qkv), P, xn, H, qkv, nqkv, EPI_F16, st));
     LCHK(c, 1, launch_prefill_kv(P, l, slot, kv, qkv + qd, qkv + qd + d.n_kv_heads * D, nqkv,
                                  c->W<float2>(c->wp.table), st));
     LCHK(c, 1, launch_prefill_attention(P, l, slot, Hq, kv, qkv, nqkv, c->W<float2>(c->wp.table), ao, qd, st));
-    LCHK(c, 1, launch_gemm(c->mat(Ly.o), P, ao, qd, h, H, EPI_RESID, st));
+    LCHK(c, 1, pf_gemm(c->mat(Ly.o), P, ao, qd, h, H, EPI_RESID, st));
     LCHK(c, 1, launch_rmsnorm(P, H, h, c->Bk<uint16_t>(Ly.moe_norm), d.rms_eps, xn, st, 0));
     float* lg = reinterpret_cast<float*>(PW(pp.lg));
     LCHK(c, 1, launch_gemm(c->mat(Ly.router), P, xn, H, lg, E, EPI_F32, st));

@@ -105,6 +105,15 @@ hipError_t launch_moe_gateup(const Mat& gate0, const Mat& up0, const uint16_t* x
 // the combine reads without an index), else at y[p].
 hipError_t launch_moe_down(const Mat& down0, const uint16_t* act, const RouteOut& r, uint16_t* y, hipStream_t st,
                            bool nt = false, bool direct = false);
+// The large-M product of a prompt's rows (k_gemm_lm: 128 x 128 blocks, both
+// operands streamed through LDS by direct-to-LDS loads): x row-major [M][ldx]
+// (16-byte aligned, ldx a multiple of 8), epilogues as launch_gemm.  fp32 sums
+// of the same terms as launch_gemm, in group order over K (launch_gemm adds
+// per-slice sums), so the rounding may differ from it.  lm_ok: the
+// geometries it takes.
+bool lm_ok(const Mat& w, int ldx);
+hipError_t launch_gemm_lm(const Mat& w, int M, const uint16_t* x, int ldx, void* y, int ldy, int epi,
+                          hipStream_t st);
 // Both grouped products in one launch (same results bit for bit); needs
 // r.done, the ready words ([units_cap][8] x kDoneStride, zeroed once, then
 // only written with epochs), a nonzero epoch larger than any earlier one on
