@@ -157,11 +157,14 @@ def test_prefill_sampled_first_token_and_invalid_ids(small, gpu):
     ctx.release(s)
 
 
-def test_prefill_full_geometry_longest_prompt(gpu):
+@pytest.mark.parametrize("P", [2048, 1957])
+def test_prefill_full_geometry_longest_prompt(gpu, P):
     """Hidden 2048, 32q/4kv x 128, 128 experts top-8, intermediate 768, vocab
     151936, group 128, one layer; the longest prompt the prefill routing takes
     (2048 tokens: 16384 routed pairs, 128 + 1024 + 1 expert work units against a
-    decode step's 289, 64 attention chunks, up to 8 splits).  One layer, so the
+    decode step's 289, 64 attention chunks, up to 8 splits) and a ragged one
+    (1957 tokens: the last 128-row block of the q/k/v and output products holds
+    37 rows, under both the 256- and the 128-column blocks).  One layer, so the
     comparison starts from exact inputs: through a second free-running layer
     this random model already amplifies rounding differences to about the
     tolerance (the reason full-size decode parity is checked layer by layer);
@@ -171,7 +174,6 @@ def test_prefill_full_geometry_longest_prompt(gpu):
     ctx = Context(d, 2, 2112)
     try:
         ctx.load_model(mw)
-        P = 2048
         tokens = [int(t) for t in inputs.rng(4, inputs.T_TOKENS, 1).integers(0, d.vocab, P)]
         s, _, _ = check_prefill(ctx, gpu, mw, tokens, f"full geometry P={P}")
         ctx.release(s)
