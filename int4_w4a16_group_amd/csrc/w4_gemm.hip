@@ -592,12 +592,21 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   }
   __syncthreads();
 
-  // item f's tile into a stage (past the range: the WG's last tile again)
+  // item f's tile into a stage.  Past the range: with plain loads the WG's
+  // last tile again (a cache hit); with non-temporal loads, which do not keep
+  // that tile in the cache, every lane of a wave reads the first 16-byte word
+  // of the wave's slice of expert 0's tile (blockIdx mod tiles) instead: one
+  // line per load, spread over the cache channels, whose results are never
+  // stored.  Either way the loads are issued on every trip, so the waits in
+  // the loop stay the same (B = 32 gate/up: 180.0 against 213.4 MB fetched per
+  // launch, 1.5% more tok/s).
   auto stage_load = [&](Stage<NCH, G, NT>& g0, Stage<NCH, G, NT>& g1, int f) {
-    const int fc = min(f, last), u = __builtin_amdgcn_readfirstlane(fc / T), t = fc - u * T;
-    const int e = lrec[u].x;
-    g0.load(a.t0 + a.tile_stride * e, a.s0 + a.scale_stride * e, a.K, t, w, lane);
-    if (GATEUP) g1.load(a.t1 + a.tile_stride * e, a.s1 + a.scale_stride * e, a.K, t, w, lane);
+    const bool ok = !NT || f <= last;
+    const int fc = min(f, last), u = __builtin_amdgcn_readfirstlane(fc / T);
+    const int t = ok ? fc - u * T : (int)(blockIdx.x % T), ln = ok ? lane : 0;
+    const int e = ok ? lrec[u].x : 0;
+    g0.load(a.t0 + a.tile_stride * e, a.s0 + a.scale_stride * e, a.K, t, w, ln);
+    if (GATEUP) g1.load(a.t1 + a.tile_stride * e, a.s1 + a.scale_stride * e, a.K, t, w, ln);
   };
   // x slice of unit u (rows past the unit's count repeat row 0; their
   // outputs are not stored)
