@@ -1129,7 +1129,10 @@ static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_
   a.out = out;
   a.dst_rows = nullptr;
   a.ncu = cu_count();
-  a.dshare = gateup ? 75 : 0;  // measured: gate/up 38.5 us at 60-120 against 40.0 at 0
+  // measured: gate/up 38.5 us at 60-120 against 40.0 at 0; gate/up 120 with
+  // the down product at 60 (its first work-group per compute unit also ends
+  // earlier): about 1% fewer tok/s at B = 4, 8 and 32
+  a.dshare = gateup ? 75 : 0;
   return a;
 }
 

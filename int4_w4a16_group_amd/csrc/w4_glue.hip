@@ -459,7 +459,8 @@ __device__ void bucket_core(int E, int k, int B, const int* s_ids, const BucketL
   }
   __syncthreads();
   const int nun = L.tot[2] + L.tot[5] + L.tot[8] + L.tot[11];  // units of all experts
-  for (int i = tid; i < nun * 16; i += blockDim.x) o.unit_rows[i] = L.urows[i];
+  if (o.unit_rows)
+    for (int i = tid; i < nun * 16; i += blockDim.x) o.unit_rows[i] = L.urows[i];
   if (o.unit_rows8) {  // the same rows as bytes (streams < 32), four per word
     uint32_t* r8 = reinterpret_cast<uint32_t*>(o.unit_rows8);
     for (int i = tid; i < nun * 4; i += blockDim.x)

@@ -662,6 +662,14 @@ int layer_body(w4_ctx* c, int l, int B, int max_pos, uint16_t* h, uint16_t* xp, 
       LCHK(c, 1, launch_gemm(Om, B, o, qd, h, H, EPI_RESID, st, R, B > kNtMinRows));
   }
   RouteOut r = c->route_out(ids_out);
+  // outputs that no kernel of the step reads are not written (B = 32: +0.15%
+  // tok/s); the non-temporal gate/up (more than kNtMinRows streams) reads its
+  // unit rows as bytes, the fused expert launch as words
+  r.counts = nullptr;
+  r.offsets = nullptr;
+  r.pair_stream = nullptr;
+  r.pair_rank = nullptr;
+  if (B > kNtMinRows && !c->fused_moe) r.unit_rows = nullptr;
   {
     ProfScope ps(c, W4_K_ROUTER, st);
     const Mat Rm = c->mat(L.router);

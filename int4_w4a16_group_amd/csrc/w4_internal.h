@@ -69,7 +69,7 @@ struct RouteOut {
   int32_t* used;         // [E] used experts, ascending
   int32_t* n_used;       // [1]
   int4* units;           // [E + B*k/16 + 1] per 16-row unit of each used expert: (expert, first pair, rows, 0)
-  int32_t* unit_rows;    // [same][16] stream of each unit row (rows past the count repeat row 0)
+  int32_t* unit_rows;    // [same][16] stream of each unit row (rows past the count repeat row 0), or null
   int32_t* n_units;      // [1]
   int units_cap;         // records allocated in units (>= any n_units)
   int unit_n = 16;       // rows per unit: 16, or 32 for a prompt's products (prompt routing only)
