@@ -726,17 +726,26 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
     load_x(f_begin / T, r0);
   }
   stage_load(b0, b1, f_begin + 1);
-  for (int f = f_begin; f < f_end; f += 2) {
+  // Whole pairs in the loop; an odd range's last item after it, from the
+  // stage the loop's last trip loaded (no multiply of a stage that holds no
+  // item of the range; the loop body and its waits are the same as with the
+  // odd item inside it).
+  const int f_pairs = f_begin + ((f_end - f_begin) & ~1);
+  for (int f = f_begin; f < f_pairs; f += 2) {
     // Issue priority by remaining work: the waves of the work-group with
     // more tiles left win the compute unit's arbitration, so a work-group
     // that falls behind the one sharing its compute unit catches up.
     set_prio_level((4 * (f_end - f)) / (f_end - f_begin + 1));
     run(a0, a1, f, true);
-    if (f + 1 < f_end && (f + 1) / T != xu) load_x((f + 1) / T, nrow);
+    if ((f + 1) / T != xu) load_x((f + 1) / T, nrow);
     stage_load(a0, a1, f + 2);
-    run(b0, b1, f + 1, f + 1 < f_end);
+    run(b0, b1, f + 1, true);
     if (f + 2 < f_end && (f + 2) / T != xu) load_x((f + 2) / T, nrow);
     stage_load(b0, b1, f + 3);
+  }
+  if (f_pairs < f_end) {
+    set_prio_level(0);
+    run(a0, a1, f_pairs, true);
   }
 }
 
@@ -1091,6 +1100,8 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
   }
   const int MT = r.unit_n / 16;
   if (r.unit_n != 16 && (r.unit_n != 32 || nt || one || direct || NW > 8)) return hipErrorInvalidValue;
+  // the unit rows: as bytes (non-temporal gate/up) or as words (the other forms)
+  if (gateup && !one && !(nt && a.rows8_ok) && !r.unit_rows) return hipErrorInvalidValue;
   MoeKernel k = MT == 2 ? (gateup ? moe_pick_mt2<true>(nch, m0.g) : moe_pick_mt2<false>(nch, m0.g))
                 : gateup ? moe_pick<true>(nch, m0.g, NW, nt, one)
                          : moe_pick<false>(nch, m0.g, NW, nt, false);
