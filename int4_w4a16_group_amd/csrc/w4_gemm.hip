@@ -1140,10 +1140,11 @@ static MoeArgs moe_args(bool gateup, const Mat& m0, const Mat* m1, const uint16_
   a.out = out;
   a.dst_rows = nullptr;
   a.ncu = cu_count();
-  // measured: gate/up 38.5 us at 60-120 against 40.0 at 0; gate/up 120 with
-  // the down product at 60 (its first work-group per compute unit also ends
-  // earlier): about 1% fewer tok/s at B = 4, 8 and 32
-  a.dshare = gateup ? 75 : 0;
+  // measured (gate/up share, with an odd range's last item run alone):
+  // 40 against 0, 75 and 110: +0.3% tok/s at B = 4, 8 and 32; gate/up 120
+  // with the down product at 60 (its first work-group per compute unit also
+  // ends earlier): about 1% fewer
+  a.dshare = gateup ? 40 : 0;
   return a;
 }
 
