@@ -37,8 +37,8 @@ METRIC = "aggregate decode tok/s at B=1/4/8/32 + int4 weight-stream HBM GB/s vs 
 # what the same counters read for a 512 MiB device copy: reads x2.0, writes
 # x1.0), and the SHA-256 of the kernel sources they were taken on.  Reported
 # only while those sources are unchanged.
-TRAFFIC = dict(moe_gateup=dict(read_MB=180.43, write_MB=0.39,
-                               sources_sha256="4a618c5d28726831360f9f40d3cd41f47639cf19b860e0a95b07d60469cd3da9"))
+TRAFFIC = dict(moe_gateup=dict(read_MB=180.48, write_MB=0.39,
+                               sources_sha256="ef8f6f888fe7e991aee8a32cc923f65e944a37456d8e288a5974c9f573d441b2"))
 TRAFFIC_SOURCES = ("int4_w4a16_group_amd/csrc/w4_gemm.hip", "int4_w4a16_group_amd/csrc/w4_device.h",
                    "int4_w4a16_group_amd/csrc/w4_tile.h")
 
