@@ -613,6 +613,16 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
   // (gate/up: the next unit's row index is loaded a unit ahead, so a switch
   // does not wait for it)
   int xu = -1, nrow[MT] = {};
+  // stream of row i of unit u (rows past the unit's count: any of its rows);
+  // 64-row units (a prompt's gate/up) are runs of two 32-row units whose rows
+  // are listed from the first of them (record field w)
+  auto unit_row = [&](int u, int i) -> int {
+    if constexpr (MT == 4) {
+      const int4 un = lrec[u];
+      return a.unit_rows[un.w * 32 + min(i, un.z - 1)];
+    }
+    return a.unit_rows[u * US + i];
+  };
   // down with dst_rows: output rows of the unit being loaded, written to
   // s_dst[unit & 1] by the unit's first multiply (a load in flight is not
   // waited for before the next tile loads are issued); a unit's rows are
@@ -639,7 +649,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
     xu = u;
     if (GATEUP && !ONE && !rl) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) nrow[mt] = a.unit_rows[min(u + 1, nu - 1) * US + mt * 16 + i16];
+      for (int mt = 0; mt < MT; ++mt) nrow[mt] = unit_row(min(u + 1, nu - 1), mt * 16 + i16);
     }
     if (!GATEUP && a.dst_rows) {
       dreg = a.dst_rows[un.y + min(i16, un.z - 1)];
@@ -721,7 +731,7 @@ __global__ void __launch_bounds__(LB) k_moe(MoeArgs a) {
     int r0[MT] = {};
     if (GATEUP && !ONE && !rl) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) r0[mt] = a.unit_rows[(f_begin / T) * US + mt * 16 + i16];
+      for (int mt = 0; mt < MT; ++mt) r0[mt] = unit_row(f_begin / T, mt * 16 + i16);
     }
     load_x(f_begin / T, r0);
   }
@@ -1043,6 +1053,19 @@ template <bool GU>
 static MoeKernel moe_pick_mt2(int nch, int g) {
   return nch == 2 ? moe_pick_mt2_g<GU, 2>(g) : moe_pick_mt2_g<GU, 1>(g);
 }
+// 64-row units (gate/up of a long prompt)
+template <bool GU, int NCH>
+static MoeKernel moe_pick_mt4_g(int g) {
+  switch (g) {
+    case 32: return k_moe<NCH, 32, GU, 512, false, false, 4>;
+    case 64: return k_moe<NCH, 64, GU, 512, false, false, 4>;
+    default: return k_moe<NCH, 128, GU, 512, false, false, 4>;
+  }
+}
+template <bool GU>
+static MoeKernel moe_pick_mt4(int nch, int g) {
+  return nch == 2 ? moe_pick_mt4_g<GU, 2>(g) : moe_pick_mt4_g<GU, 1>(g);
+}
 
 static int cu_count() {
   static int cus = 0;
@@ -1099,10 +1122,14 @@ static hipError_t launch_moe_common(bool gateup, const Mat& m0, const Mat* m1, c
     a.dst_rows = r.pair_flat;
   }
   const int MT = r.unit_n / 16;
-  if (r.unit_n != 16 && (r.unit_n != 32 || nt || one || direct || NW > 8)) return hipErrorInvalidValue;
+  if (r.unit_n != 16 && ((r.unit_n != 32 && !(r.unit_n == 64 && gateup)) || nt || one || direct || NW > 8))
+    return hipErrorInvalidValue;
+  // 64-row units list their rows through the first list's (and only they do)
+  if ((r.unit_n == 64) != (r.rows_via_rec != 0)) return hipErrorInvalidValue;
   // the unit rows: as bytes (non-temporal gate/up) or as words (the other forms)
   if (gateup && !one && !(nt && a.rows8_ok) && !r.unit_rows) return hipErrorInvalidValue;
-  MoeKernel k = MT == 2 ? (gateup ? moe_pick_mt2<true>(nch, m0.g) : moe_pick_mt2<false>(nch, m0.g))
+  MoeKernel k = MT == 4   ? moe_pick_mt4<true>(nch, m0.g)
+                : MT == 2 ? (gateup ? moe_pick_mt2<true>(nch, m0.g) : moe_pick_mt2<false>(nch, m0.g))
                 : gateup ? moe_pick<true>(nch, m0.g, NW, nt, one)
                          : moe_pick<false>(nch, m0.g, NW, nt, false);
   if (r.units_cap < 1 || r.units_cap > kMaxUnitsPrefill) return hipErrorInvalidValue;

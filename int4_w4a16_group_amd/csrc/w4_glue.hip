@@ -556,8 +556,11 @@ hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut
 // expert as one byte, and sets bit b of expert e's row mask (global, zero
 // before).  k_bucket_prefill, one work-group: the pairs ordered by (expert,
 // row) -- a pair's place within its expert is the number of lower rows in the
-// expert's mask, a prefix popcount -- and the work units of o.unit_n rows; it
-// clears the masks again.
+// expert's mask, a prefix popcount -- and the work units of o.unit_n rows
+// (and, when o.units2 is given, the records of a second list of 64-row units
+// over the same pair order, each the run of two consecutive 32-row units of
+// the first: its fourth field is the first of them); it clears the masks
+// again.
 __global__ void __launch_bounds__(1024) k_topk_rows(const float* __restrict__ logits, int P, int E, int k,
                                                     RouteOut o, uint32_t* __restrict__ mask,
                                                     uint8_t* __restrict__ e8) {
@@ -584,9 +587,11 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   // [E][W] row masks, then [E][W] 16-bit counts of the set bits in the words
   // before each word (a pair's place within its expert is one lookup)
   extern __shared__ uint32_t s_pm[];
-  __shared__ int s_cnt[kRouteMaxE], s_off[kRouteMaxE], s_ub[kRouteMaxE];
+  __shared__ int s_cnt[kRouteMaxE], s_off[kRouteMaxE], s_ub[kRouteMaxE], s_ub2[kRouteMaxE];
   const int W = (P + 31) / 32;
   const int US = o.unit_n;  // rows per unit
+  const bool two = o.units2 != nullptr;
+  const int US2 = two ? o.unit_n2 : US;  // rows per unit of the second list
   uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_pm + (size_t)E * W);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   // this thread's pairs tid + 1024 q (at most kPrefillMaxPairs / 1024 = 16):
@@ -610,34 +615,39 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   __syncthreads();
   // exclusive scans over the experts, in expert order: wave w takes experts
   // 64w .. 64w+63 (ballot bit-sliced prefix sums), then the waves in order
-  __shared__ int s_tot[12];
-  int xc = 0, xu = 0, xn = 0, ec = 0, eu = 0, en = 0;
+  __shared__ int s_tot[16];
+  int xc = 0, xu = 0, xn = 0, xn2 = 0, ec = 0, eu = 0, en = 0, en2 = 0;
   if (w < 4) {
     const int e = tid;
     xc = e < E ? s_cnt[e] : 0;
     xu = xc > 0;
     xn = (xc + US - 1) / US;
-    int tc, tu, tn;
+    xn2 = (xc + US2 - 1) / US2;
+    int tc, tu, tn, tn2;
     ec = wave_excl_sum<15>(xc, lane, &tc);  // c <= P <= 16384
     eu = wave_excl_sum<1>(xu, lane, &tu);
     en = wave_excl_sum<11>(xn, lane, &tn);
+    en2 = wave_excl_sum<11>(xn2, lane, &tn2);
     if (lane == 0) {
-      s_tot[3 * w] = tc;
-      s_tot[3 * w + 1] = tu;
-      s_tot[3 * w + 2] = tn;
+      s_tot[4 * w] = tc;
+      s_tot[4 * w + 1] = tu;
+      s_tot[4 * w + 2] = tn;
+      s_tot[4 * w + 3] = tn2;
     }
   }
   __syncthreads();
   if (w < 4) {
     const int e = tid;
     for (int ww = 0; ww < w; ++ww) {
-      ec += s_tot[3 * ww];
-      eu += s_tot[3 * ww + 1];
-      en += s_tot[3 * ww + 2];
+      ec += s_tot[4 * ww];
+      eu += s_tot[4 * ww + 1];
+      en += s_tot[4 * ww + 2];
+      en2 += s_tot[4 * ww + 3];
     }
     if (e < E) {
       s_off[e] = ec;
       s_ub[e] = en;
+      s_ub2[e] = en2;
       if (o.counts) o.counts[e] = xc;
       if (o.offsets) o.offsets[e] = ec;
       if (xu) o.used[eu] = e;
@@ -646,6 +656,7 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
       if (o.offsets) o.offsets[E] = ec + xc;
       *o.n_used = eu + xu;
       *o.n_units = en + xn;
+      if (two) *o.n_units2 = en2 + xn2;
     }
   }
   __syncthreads();
@@ -687,6 +698,10 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
       }
       for (int i = c - US * (nu - 1); i < US; ++i) o.unit_rows[(s_ub[e] + nu - 1) * US + i] = first;
     }
+    if (two)
+      for (int j = 0; j < (c + US2 - 1) / US2; ++j)
+        o.units2[s_ub2[e] + j] =
+            make_int4(e, s_off[e] + US2 * j, min(US2, c - US2 * j), s_ub[e] + j * (US2 / US));
   }
 }
 
@@ -694,7 +709,8 @@ hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const 
                                 uint8_t* e8, hipStream_t st) {
   const size_t lds = route_prefill_lds(P, E, k);
   if (P < 1 || E > kRouteMaxE || (size_t)P * k > (size_t)kPrefillMaxPairs || lds > 61440 || !mask || !e8 ||
-      (o.unit_n != 16 && o.unit_n != 32))
+      (o.unit_n != 16 && o.unit_n != 32) ||
+      (o.units2 && (o.unit_n2 != 64 || o.unit_n != 32 || !o.n_units2)))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_topk_rows, dim3((P + 15) / 16), dim3(1024), 0, st, logits, P, E, k, o, mask, e8);
   hipLaunchKernelGGL(k_bucket_prefill, dim3(1), dim3(1024), lds, st, P, E, k, o, mask, e8);

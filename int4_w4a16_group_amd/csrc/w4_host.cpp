@@ -191,8 +191,8 @@ WsPlan plan_ws(const w4_model_desc& d, int Bm, int cap) {
 // Prefill workspace (caller-owned, from w4_prefill_workspace_bytes): the
 // prompt's rows through every layer.
 struct PfPlan {
-  size_t h, xn, qkv, attn_o, lg, ids, w, counts, offsets, inv, used, n_used, units, unit_rows, n_units, done, ready,
-      act, y, rows, logits, rmask, re8, total;
+  size_t h, xn, qkv, attn_o, lg, ids, w, counts, offsets, inv, used, n_used, units, unit_rows, n_units, units2,
+      n_units2, done, ready, act, y, rows, logits, rmask, re8, total;
   size_t row_cap;  // int32 words of the rows region
 };
 
@@ -228,6 +228,9 @@ PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
   w.units = take(ucap * 16);
   w.unit_rows = take(ucap * 32 * 4);  // 16-row units, or half as many of 32 rows
   w.n_units = take(4);
+  // the gate/up product's 64-row units over the same pair order
+  w.units2 = take((E + pairs / 64 + 1) * 16);
+  w.n_units2 = take(4);
   w.done = take(ucap * kDoneStride * 4);
   w.ready = take(ucap * 8 * kDoneStride * 4);
   w.act = take(pairs * I * 2);
@@ -569,8 +572,11 @@ struct ProfScope {
 constexpr int kNtMinRows = 8;
 
 // A prompt of at least this many rows runs its expert products over 32-row
-// units.
-constexpr int kPromptUnitRows32 = 64;
+// units, and from the second size on its gate/up product over 64-row units
+// (about 64 rows per expert at top-8 of 128 experts, so little padding; the
+// down product keeps 32-row units: its 64-row form holds two work-groups per
+// compute unit instead of five and was measured slower, 180 against 135 us).
+constexpr int kPromptUnitRows32 = 64, kPromptUnitRows64 = 1024;
 
 // Dense product of a prompt's rows: the large-M form (128 x 128 blocks) for a
 // prompt of at least 128 rows and an output of at least 64 tiles (enough
@@ -599,7 +605,16 @@ int launch_experts(w4_ctx* c, const LayerLoc& L, const uint16_t* xn, int ldx, co
   }
   {
     ProfScope ps(c, W4_K_MOE_GATEUP, st);
-    LCHK(c, 1, launch_moe_gateup(gate, up, xn, ldx, r, act, st, nt, one));
+    RouteOut rg = r;  // the gate/up product over the second unit list when there is one
+    if (r.units2) {
+      rg.units = r.units2;
+      rg.rows_via_rec = 1;
+      rg.n_units = r.n_units2;
+      rg.unit_n = r.unit_n2;
+      rg.units_cap = r.units_cap2;
+      rg.unit_rows8 = nullptr;
+    }
+    LCHK(c, 1, launch_moe_gateup(gate, up, xn, ldx, rg, act, st, nt, one));
   }
   {
     ProfScope ps(c, W4_K_MOE_DOWN, st);
@@ -1064,6 +1079,12 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
   // operand serves two 16-row MFMA tiles; same results)
   r.unit_n = P >= kPromptUnitRows32 && !c->fused_moe ? 32 : 16;
   r.units_cap = E + P * k / r.unit_n + 1;
+  if (r.unit_n == 32 && P >= kPromptUnitRows64) {
+    r.units2 = reinterpret_cast<int4*>(PW(pp.units2));
+    r.n_units2 = reinterpret_cast<int32_t*>(PW(pp.n_units2));
+    r.unit_n2 = 64;
+    r.units_cap2 = E + P * k / 64 + 1;
+  }
   r.done = reinterpret_cast<uint32_t*>(PW(pp.done));
   // the fused expert launches' ready words: zero once per call (the caller's
   // buffer may hold anything), then written with this context's epochs only

@@ -73,6 +73,16 @@ struct RouteOut {
   int32_t* n_units;      // [1]
   int units_cap;         // records allocated in units (>= any n_units)
   int unit_n = 16;       // rows per unit: 16, or 32 for a prompt's products (prompt routing only)
+  // prompt routing only: a second unit list of unit_n2 (64) rows per unit over the same pair order, for
+  // the gate/up product, each unit the run of two consecutive 32-row units of the first list (record
+  // field w: the first of them); null: none
+  int4* units2 = nullptr;
+  int32_t* n_units2 = nullptr;
+  int unit_n2 = 0;
+  int units_cap2 = 0;
+  // the units' row streams are unit_rows[units[u].w * 32 + i] (the first list's, 32 rows per unit)
+  // instead of unit_rows[u * unit_n + i]
+  int rows_via_rec = 0;
   uint4* unit_rows8 = nullptr;  // [units_cap] or null: byte i of record u = unit_rows[u][i] (B <= 32)
   int32_t* pair_flat = nullptr;  // [B*k] or null: b*k + r of each pair, in expert order (the inverse of inv)
   uint32_t* done = nullptr;  // [units_cap] x kDoneStride words or null: zeroed for every unit written

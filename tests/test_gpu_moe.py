@@ -183,16 +183,18 @@ def test_fused_expert_launch_in_decode_steps(gpu):
         assert np.array_equal(a, b), f"step {i}"
 
 
-def test_fused_expert_launch_in_prefill(gpu):
-    """A 300-token prompt (many 16-row units per expert) through a two-layer
-    model with the expert products as one launch and as two: the same K/V,
+@pytest.mark.parametrize("P", [300, 1100])
+def test_fused_expert_launch_in_prefill(gpu, P):
+    """A 300- or 1100-token prompt (many 16-row units per expert) through a
+    two-layer model with the expert products as one launch (16-row units) and
+    as two (32-row units at 300 tokens, 64-row units at 1100): the same K/V,
     last logits and next id, bit for bit."""
     d = dataclasses.replace(inputs.FULL, n_layers=2, vocab=1000)
     mw = inputs.make_model(d, 9, codes="zero_mean")
-    tokens = [int(t) for t in inputs.rng(9, inputs.T_TOKENS, 3).integers(0, d.vocab, 300)]
+    tokens = [int(t) for t in inputs.rng(9, inputs.T_TOKENS, 3).integers(0, d.vocab, P)]
     outs = []
     for fused in (1, 0):
-        ctx = Context(d, 2, 384)
+        ctx = Context(d, 2, (P + 4 + 63) // 64 * 64)
         try:
             ctx.load_model(mw)
             L.w4_set_option(ctx.ctx, L.W4_OPT_FUSED_MOE, fused)
