@@ -525,12 +525,20 @@ __global__ void __launch_bounds__(256, VE ? 1 : 3) k_attn(AttnArgs a) {
 // Causal attention of a prompt's P rows over its own K/V in the slot (rows
 // 0..P-1 written by k_prefill_kv), one pass over the keys per query block:
 // work-group (query block qb of 64 rows, query head h) of four waves; wave w
-// takes rows 64 qb + 16 w .. +15 of head h (the MFMA A operand: row = query
-// position, k = head dimension), rotated at their positions through table.
-// For each 64-key chunk c = 0 .. qb in order, every wave:
-//   S = Q K^T (MFMA, fp32), z = S log2(e) / sqrt(D), keys past the row's
-//   position masked; m' = max(m, max_c z); a = 2^(m - m'); P = 2^(z - m');
-//   l = l a + sum P; O = O a + P V (MFMA on P split into fp16 hi + lo parts).
+// takes rows 64 qb + 16 w .. +15 of head h, rotated at their positions
+// through table.  The products run transposed, keys (or head dimensions) as
+// the MFMA rows and the wave's 16 queries as its columns, so that lane l
+// holds query l & 15 throughout.  For each 64-key chunk c = 0 .. qb in order:
+//   S^T = K Q^T (MFMA, fp32) as four 16-key tiles, z = S log2(e) / sqrt(D),
+//   keys past the row's position masked (the chunk c = qb only);
+//   m' = max(m, max_c z) (the lane's 16 keys, then over the four lanes of
+//   the query); a = 2^(m - m'); P = 2^(z - m'); l = l a + sum P (per lane,
+//   summed over the query's four lanes at the end); O^T = O^T a + V^T P^T
+//   (MFMA on P split into fp16 hi + lo parts).
+// The tiles' rows are the keys in the order that puts each lane's P values
+// where the P^T operand wants them: tile (ks, e), row 4 q + r is key
+// 32 ks + 8 q + 4 e + r of the chunk, read from the stored K blocks by a
+// per-lane address.  No pass through LDS.
 // Then o = O / l, row-major fp16 [P][Hq * D].  Each row attends to keys
 // 0 .. its position, the causal definition of the prompt's attention.
 struct PfAttnArgs {
@@ -544,18 +552,25 @@ struct PfAttnArgs {
   float scale;          // log2(e) / sqrt(D)
 };
 
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
+
 template <int D>
-__global__ void __launch_bounds__(256, 2) k_prefill_attn(PfAttnArgs a) {
+__global__ void __launch_bounds__(256, 3) k_prefill_attn(PfAttnArgs a) {
   constexpr int KSQ = D / 32;  // k-steps of q.K
   constexpr int NDT = D / 16;  // output d-tiles
-  __shared__ float Pl[4][16][65];
+  // work-groups go out in linear order, x fastest: every head's block of one
+  // length before any shorter block (the longest first), and x -> head so
+  // that work-groups on one XCD (dispatched round-robin over 8) hold
+  // neighbouring heads, which share their kv heads
   const int nqb = (a.P + 63) >> 6;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // the longest blocks first
-  const int h = blockIdx.y, G = a.Hq / a.kv.Hkv, g = h / G;
+  const int qb = nqb - 1 - (int)blockIdx.y;
+  const int hx = blockIdx.x;
+  const int h = (a.Hq & 7) ? hx : (hx & 7) * (a.Hq >> 3) + (hx >> 3), G = a.Hq / a.kv.Hkv, g = h / G;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 15, quad = lane >> 4;
   const int r0 = 64 * qb + 16 * w;  // this wave's first row
-  // Q operand: row col of the wave's 16, rotated pairs (i, i + D/2) =
+  // Q^T operand: query col of the wave's 16, rotated pairs (i, i + D/2) =
   // k-steps (ks, ks + KSQ/2) of the same lane
   h8 qa[KSQ];
   {
@@ -578,76 +593,81 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PfAttnArgs a) {
       }
     }
   }
-  float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, l[4] = {0.f, 0.f, 0.f, 0.f};
+  const int qp = r0 + col;  // this lane's query
+  float m = -INFINITY, lp = 0.f;
   f4 oacc[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f4{0.f, 0.f, 0.f, 0.f};
   const size_t base = kv_base(a.kv, a.layer, a.slot, g);
+  // K operand of tile (ks, e): row col is key kr = 32 ks + 8 (col >> 2) + 4 e +
+  // (col & 3), stored in block kr >> 4 at lane 16 quad + (kr & 15)
+  int koff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int kr = 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
+    koff[t] = (kr >> 4) * KSQ * 512 + (16 * quad + (kr & 15)) * 8;
+  }
   for (int c = 0; c <= qb; ++c) {
     const int c0 = 64 * c;
-    const uint16_t* Kc = a.kv.K + base + (size_t)c * 64 * D + lane * 8;
+    const uint16_t* Kc = a.kv.K + base + (size_t)c * 64 * D;
     const uint16_t* Vc = a.kv.VT + base + (size_t)c * 64 * D + lane * 8;
     h8 kb[4][KSQ];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) kb[pt][ks] = ld_h8(Kc + (pt * KSQ + ks) * 512);
+      for (int ks = 0; ks < KSQ; ++ks) kb[t][ks] = ld_h8(Kc + koff[t] + ks * 512);
+    // lane holds S[query col][key c0 + 32 (t >> 1) + 8 quad + 4 (t & 1) + r]
     f4 S[4];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
+    for (int t = 0; t < 4; ++t) {
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(qa[ks], kb[pt][ks], acc);
-      S[pt] = acc;
+      for (int ks = 0; ks < KSQ; ++ks) acc = mfma16x16x32(kb[t][ks], qa[ks], acc);
+      S[t] = acc;
     }
     h8 vop[NDT][2];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) vop[dt][ks] = ld_h8(Vc + (dt * 2 + ks) * 512);
-    // lane holds S[row 4 quad + r][key c0 + 16 pt + col]
-    float alpha[4];
+    if (c == qb) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qp = r0 + 4 * quad + r;
-      float mc = -INFINITY;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const int kp = c0 + pt * 16 + col;
-        const float z = S[pt][r] * a.scale;
-        S[pt][r] = kp > qp ? -INFINITY : z;
-        mc = fmaxf(mc, S[pt][r]);
-      }
-      mc = row16_max(mc);
-      const float mn = fmaxf(m[r], mc);
-      alpha[r] = __builtin_amdgcn_exp2f(m[r] - mn);
-      float ls = 0.f;
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const float e = __builtin_amdgcn_exp2f(S[pt][r] - mn);
-        S[pt][r] = e;
-        ls = ls + e;
-      }
-      l[r] = l[r] * alpha[r] + row16_sum(ls);
-      m[r] = mn;
+        for (int r = 0; r < 4; ++r)
+          if (c0 + 32 * (t >> 1) + 8 * quad + 4 * (t & 1) + r > qp) S[t][r] = -INFINITY;
     }
+    float mc = S[0][0];
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Pl[w][4 * quad + r][pt * 16 + col] = S[pt][r];
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's P is in LDS
-    __builtin_amdgcn_wave_barrier();
+      for (int r = 0; r < 4; ++r)
+        if (t | r) mc = fmaxf(mc, S[t][r]);
+    mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
+    mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+    // the scale is positive: the max of the scaled scores is the scaled max
+    const float mn = fmaxf(m, mc * a.scale);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
+    float ls = 0.f;
     h8 phi[2], plo[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pv = Pl[w][col][32 * ks + 8 * quad + j];
-        const _Float16 hi = (_Float16)pv;
-        phi[ks][j] = hi;
-        plo[ks][j] = (_Float16)(pv - (float)hi);
+      for (int r = 0; r < 4; r += 2) {
+        const f2 e = {__builtin_amdgcn_exp2f(fmaf(S[t][r], a.scale, -mn)),
+                      __builtin_amdgcn_exp2f(fmaf(S[t][r + 1], a.scale, -mn))};
+        ls = ls + e.x;
+        ls = ls + e.y;
+        const hf2 hi = __builtin_convertvector(e, hf2);
+        const f2 hb = __builtin_convertvector(hi, f2);
+        const hf2 lo = __builtin_convertvector((f2{e.x - hb.x, e.y - hb.y}), hf2);
+        phi[t >> 1][4 * (t & 1) + r] = hi.x;
+        phi[t >> 1][4 * (t & 1) + r + 1] = hi.y;
+        plo[t >> 1][4 * (t & 1) + r] = lo.x;
+        plo[t >> 1][4 * (t & 1) + r + 1] = lo.y;
       }
-    __builtin_amdgcn_wave_barrier();  // Pl is rewritten by the next chunk
+    lp = lp * alpha + ls;
     if (c0 + 63 >= a.P) {
       // keys past the prompt hold no data of this stream: zero their V
 #pragma unroll
@@ -662,23 +682,27 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PfAttnArgs a) {
     for (int dt = 0; dt < NDT; ++dt) {
       f4 o = oacc[dt];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = o[r] * alpha[r];
+      for (int r = 0; r < 4; ++r) o[r] = o[r] * alpha;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        o = mfma16x16x32(phi[ks], vop[dt][ks], o);
-        o = mfma16x16x32(plo[ks], vop[dt][ks], o);
+        o = mfma16x16x32(vop[dt][ks], phi[ks], o);
+        o = mfma16x16x32(vop[dt][ks], plo[ks], o);
       }
       oacc[dt] = o;
     }
   }
-  // o = O / l for the wave's rows below P
+  // l over the query's four lanes; o = O / l for queries below P (lane holds
+  // O^T[16 dt + 4 quad + r][query col])
+  lp = lp + __shfl_xor(lp, 16, 64);
+  lp = lp + __shfl_xor(lp, 32, 64);
+  if (qp < a.P) {
+    uint16_t* orow = a.o + (size_t)qp * a.ldo + (size_t)h * D + 4 * quad;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int qp = r0 + 4 * quad + r;
-    if (qp < a.P) {
-      uint16_t* orow = a.o + (size_t)qp * a.ldo + (size_t)h * D + col;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) orow[dt * 16] = f2h(oacc[dt][r] / l[r]);
+    for (int dt = 0; dt < NDT; ++dt) {
+      uint2 pk;
+      pk.x = (uint32_t)f2h(oacc[dt][0] / lp) | ((uint32_t)f2h(oacc[dt][1] / lp) << 16);
+      pk.y = (uint32_t)f2h(oacc[dt][2] / lp) | ((uint32_t)f2h(oacc[dt][3] / lp) << 16);
+      *reinterpret_cast<uint2*>(orow + 16 * dt) = pk;
     }
   }
 }
@@ -686,8 +710,9 @@ __global__ void __launch_bounds__(256, 2) k_prefill_attn(PfAttnArgs a) {
 hipError_t launch_prefill_attention(int P, int layer, int slot, int Hq, const KV& kv, const uint16_t* qkv, int ldq,
                                     const float2* table, uint16_t* o, int ldo, hipStream_t st) {
   if (P < 1 || P > kv.cap || Hq % kv.Hkv || (kv.D != 64 && kv.D != 128)) return hipErrorInvalidValue;
+  if (ldo % 4 || reinterpret_cast<uintptr_t>(o) % 8) return hipErrorInvalidValue;  // 8-byte row pieces
   PfAttnArgs a{kv, layer, slot, P, Hq, qkv, ldq, table, o, ldo, (float)(1.4426950408889634 / sqrt((double)kv.D))};
-  const dim3 grid((P + 63) / 64, Hq);
+  const dim3 grid(Hq, (P + 63) / 64);
   if (kv.D == 128)
     hipLaunchKernelGGL(k_prefill_attn<128>, grid, dim3(256), 0, st, a);
   else
