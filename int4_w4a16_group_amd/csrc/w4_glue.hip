@@ -554,13 +554,17 @@ hipError_t launch_route(const float* logits, int B, int E, int k, const RouteOut
 // two launches.  k_topk_rows: one wave per row, the top-k softmax of k_route
 // (same arithmetic); it records the ids, the weights, each (row, rank)'s
 // expert as one byte, and sets bit b of expert e's row mask (global, zero
-// before).  k_bucket_prefill, one work-group: the pairs ordered by (expert,
-// row) -- a pair's place within its expert is the number of lower rows in the
-// expert's mask, a prefix popcount -- and the work units of o.unit_n rows
-// (and, when o.units2 is given, the records of a second list of 64-row units
-// over the same pair order, each the run of two consecutive 32-row units of
-// the first: its fourth field is the first of them); it clears the masks
-// again.
+// before).  k_bucket_prefill: the pairs ordered by (expert, row) -- a pair's
+// place within its expert is the number of lower rows in the expert's mask,
+// a prefix popcount -- and the work units of o.unit_n rows (and, when
+// o.units2 is given, the records of a second list of 64-row units over the
+// same pair order, each the run of two consecutive 32-row units of the first:
+// its fourth field is the first of them).  Its work-groups share the pairs'
+// stores (pair i in work-group (i / 1024) mod gridDim.x) and the unit records
+// (one wave per expert); each one computes the masks' prefix counts and the
+// scans itself, and work-group 0 alone writes the per-expert counts.  The masks are left as they are;
+// the launch clears mask_next, the next call's masks, which nothing reads
+// meanwhile.
 __global__ void __launch_bounds__(1024) k_topk_rows(const float* __restrict__ logits, int P, int E, int k,
                                                     RouteOut o, uint32_t* __restrict__ mask,
                                                     uint8_t* __restrict__ e8) {
@@ -582,7 +586,9 @@ __global__ void __launch_bounds__(1024) k_topk_rows(const float* __restrict__ lo
     topk_row<4>(lg, E, k, lane, sel);
 }
 
-__global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, RouteOut o, uint32_t* __restrict__ mask,
+__global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, RouteOut o,
+                                                         const uint32_t* __restrict__ mask,
+                                                         uint32_t* __restrict__ mask_next,
                                                          const uint8_t* __restrict__ e8) {
   // [E][W] row masks, then [E][W] 16-bit counts of the set bits in the words
   // before each word (a pair's place within its expert is one lookup)
@@ -594,23 +600,43 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   const int US2 = two ? o.unit_n2 : US;  // rows per unit of the second list
   uint16_t* s_pre = reinterpret_cast<uint16_t*>(s_pm + (size_t)E * W);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // this thread's pairs tid + 1024 q (at most kPrefillMaxPairs / 1024 = 16):
-  // their experts requested first, so the pair loop below waits for nothing
+  const int NB = gridDim.x, bx = blockIdx.x;
+  const bool lead = bx == 0;  // writes the per-expert outputs
+  // this thread's pairs tid + 1024 (bx + NB q) (at most kPrefillMaxPairs /
+  // 1024 = 16): their experts requested first, so the pair loop below waits
+  // for nothing
   const int PK = P * k;
   static_assert(kPrefillMaxPairs <= 16 * 1024, "16 pairs per thread");
   uint8_t ev[16];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) ev[q] = tid + 1024 * q < PK ? e8[tid + 1024 * q] : (uint8_t)0;
-  for (int i = tid; i < E * W; i += blockDim.x) s_pm[i] = mask[i];
+  for (int q = 0; q < 16; ++q) {
+    const int i = tid + 1024 * (bx + NB * q);
+    ev[q] = i < PK ? e8[i] : (uint8_t)0;
+  }
+  // the masks into LDS, every load requested before the first store (E W <=
+  // 10240 words: the launch's LDS bound)
+  constexpr int kMW = 10;
+  uint32_t mv[kMW];
+#pragma unroll
+  for (int q = 0; q < kMW; ++q) mv[q] = tid + 1024 * q < E * W ? mask[tid + 1024 * q] : 0u;
+#pragma unroll
+  for (int q = 0; q < kMW; ++q)
+    if (tid + 1024 * q < E * W) s_pm[tid + 1024 * q] = mv[q];
+  for (int i = bx * 1024 + tid; i < E * W; i += NB * 1024) mask_next[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < E * W; i += blockDim.x) mask[i] = 0u;  // zero again for the next layer
-  for (int e = tid; e < E; e += blockDim.x) {
+  // prefix counts of each expert's words: wave w takes experts w, w + 16, ..,
+  // its lanes 64 consecutive words at a time
+  for (int e = w; e < E; e += 16) {
     int c = 0;
-    for (int j = 0; j < W; ++j) {
-      s_pre[e * W + j] = (uint16_t)c;
-      c += __popc(s_pm[e * W + j]);
+    for (int j0 = 0; j0 < W; j0 += 64) {
+      const int j = j0 + lane;
+      const int pc = j < W ? __popc(s_pm[e * W + j]) : 0;
+      int t;
+      const int ex = wave_excl_sum<6>(pc, lane, &t);
+      if (j < W) s_pre[e * W + j] = (uint16_t)(c + ex);
+      c += t;
     }
-    s_cnt[e] = c;
+    if (lane == 0) s_cnt[e] = c;
   }
   __syncthreads();
   // exclusive scans over the experts, in expert order: wave w takes experts
@@ -648,11 +674,13 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
       s_off[e] = ec;
       s_ub[e] = en;
       s_ub2[e] = en2;
-      if (o.counts) o.counts[e] = xc;
-      if (o.offsets) o.offsets[e] = ec;
-      if (xu) o.used[eu] = e;
+      if (lead) {
+        if (o.counts) o.counts[e] = xc;
+        if (o.offsets) o.offsets[e] = ec;
+        if (xu) o.used[eu] = e;
+      }
     }
-    if (e == E - 1) {
+    if (lead && e == E - 1) {
       if (o.offsets) o.offsets[E] = ec + xc;
       *o.n_used = eu + xu;
       *o.n_units = en + xn;
@@ -662,7 +690,7 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
-    const int i = tid + 1024 * q;
+    const int i = tid + 1024 * (bx + NB * q);
     if (i >= PK) continue;
     const int b = i / k, e = ev[q];
     const int r = s_pre[e * W + (b >> 5)] + __popc(s_pm[e * W + (b >> 5)] & ((1u << (b & 31)) - 1u));
@@ -673,47 +701,48 @@ __global__ void __launch_bounds__(1024) k_bucket_prefill(int P, int E, int k, Ro
     o.inv[i] = pos;
     o.unit_rows[(s_ub[e] + r / US) * US + r % US] = b;
   }
-  // unit records; rows past a unit's count repeat its first row (the row of
-  // rank US u within the expert: found from the mask)
-  for (int e = tid; e < E; e += blockDim.x) {
+  // unit records, spread over the work-groups: wave w of work-group bx takes
+  // experts bx * 16 + w + 16 NB t, its lanes the expert's units.  Rows past a
+  // unit's count repeat its first row: the row of rank want = US (nu - 1)
+  // within the expert, in the last word whose prefix count is <= want.
+  for (int e = bx * 16 + w; e < E; e += 16 * NB) {
     const int c = s_cnt[e];
     const int nu = (c + US - 1) / US;
-    for (int j = 0; j < nu; ++j) {
+    for (int j = lane; j < nu; j += 64) {
       o.units[s_ub[e] + j] = make_int4(e, s_off[e] + US * j, min(US, c - US * j), 0);
       if (o.done) o.done[(size_t)(s_ub[e] + j) * kDoneStride] = 0u;
     }
     if (c > 0 && (c % US)) {
-      const int want = US * (nu - 1);  // rank of the last unit's first row
-      int seen = 0, first = 0;
-      for (int j = 0; j < W; ++j) {
-        const uint32_t m = s_pm[e * W + j];
-        const int pc = __popc(m);
-        if (seen + pc > want) {
-          uint32_t mm = m;
-          for (int q = 0; q < want - seen; ++q) mm &= mm - 1;  // drop the lower set bits
-          first = 32 * j + __ffs(mm) - 1;
-          break;
-        }
-        seen += pc;
+      const int want = US * (nu - 1);
+      int lo = 0, hi = W - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pre[e * W + mid] <= want)
+          lo = mid;
+        else
+          hi = mid - 1;
       }
-      for (int i = c - US * (nu - 1); i < US; ++i) o.unit_rows[(s_ub[e] + nu - 1) * US + i] = first;
+      uint32_t mm = s_pm[e * W + lo];
+      for (int q = 0; q < want - s_pre[e * W + lo]; ++q) mm &= mm - 1;  // drop the lower set bits
+      const int first = 32 * lo + __ffs(mm) - 1;
+      for (int i = c - US * (nu - 1) + lane; i < US; i += 64) o.unit_rows[(s_ub[e] + nu - 1) * US + i] = first;
     }
     if (two)
-      for (int j = 0; j < (c + US2 - 1) / US2; ++j)
-        o.units2[s_ub2[e] + j] =
-            make_int4(e, s_off[e] + US2 * j, min(US2, c - US2 * j), s_ub[e] + j * (US2 / US));
+      for (int j = lane; j < (c + US2 - 1) / US2; j += 64)
+        o.units2[s_ub2[e] + j] = make_int4(e, s_off[e] + US2 * j, min(US2, c - US2 * j), s_ub[e] + j * (US2 / US));
   }
 }
 
 hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, uint32_t* mask,
-                                uint8_t* e8, hipStream_t st) {
+                                uint32_t* mask_next, uint8_t* e8, hipStream_t st) {
   const size_t lds = route_prefill_lds(P, E, k);
-  if (P < 1 || E > kRouteMaxE || (size_t)P * k > (size_t)kPrefillMaxPairs || lds > 61440 || !mask || !e8 ||
+  if (P < 1 || E > kRouteMaxE || (size_t)P * k > (size_t)kPrefillMaxPairs || lds > 61440 || !mask || !mask_next || mask == mask_next || !e8 ||
       (o.unit_n != 16 && o.unit_n != 32) ||
       (o.units2 && (o.unit_n2 != 64 || o.unit_n != 32 || !o.n_units2)))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_topk_rows, dim3((P + 15) / 16), dim3(1024), 0, st, logits, P, E, k, o, mask, e8);
-  hipLaunchKernelGGL(k_bucket_prefill, dim3(1), dim3(1024), lds, st, P, E, k, o, mask, e8);
+  const int nb = std::min(kBucketPrefillGroups, (P * k + 1023) / 1024);
+  hipLaunchKernelGGL(k_bucket_prefill, dim3(nb), dim3(1024), lds, st, P, E, k, o, mask, mask_next, e8);
   return hipGetLastError();
 }
 

@@ -238,7 +238,7 @@ PfPlan plan_prefill(const w4_model_desc& d, int P, int cap) {
   w.row_cap = pf_row_words(d, P);
   w.rows = take(w.row_cap * 4);
   w.logits = take((size_t)d.vocab * 2);
-  w.rmask = take(E * (((size_t)P + 31) / 32) * 4);
+  w.rmask = take(2 * E * (((size_t)P + 31) / 32) * 4);  // two buffers, layers alternating
   w.re8 = take(pairs);
   w.total = cur;
   return w;
@@ -1053,7 +1053,7 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
   HIPCHK(c, hipEventRecord(c->ev_pf, st));
   c->pf_used = true;
   HIPCHK(c, launch_fill_u32(reinterpret_cast<uint32_t*>(PW(pp.rmask)), 0u,
-                            (size_t)d.n_experts * ((P + 31) / 32), st));
+                            2 * (size_t)d.n_experts * ((P + 31) / 32), st));
   c->launches += 1;
 
   const int H = d.hidden, E = d.n_experts, k = d.top_k, Hq = d.n_q_heads, D = d.head_dim;
@@ -1103,7 +1103,9 @@ int w4_slot_prefill(w4_ctx* c, int32_t slot, const int32_t* tokens, void* ws_dev
     float* lg = reinterpret_cast<float*>(PW(pp.lg));
     LCHK(c, 1, launch_gemm(c->mat(Ly.router), P, xn, H, lg, E, EPI_F32, st));
     r.ids = route_ids ? route_ids + (size_t)l * P * k : reinterpret_cast<int32_t*>(PW(pp.ids));
-    LCHK(c, 2, launch_route_prefill(lg, P, E, k, r, reinterpret_cast<uint32_t*>(PW(pp.rmask)),
+    uint32_t* rmask = reinterpret_cast<uint32_t*>(PW(pp.rmask));
+    const size_t mwords = (size_t)E * ((P + 31) / 32);
+    LCHK(c, 2, launch_route_prefill(lg, P, E, k, r, rmask + (l & 1) * mwords, rmask + ((l + 1) & 1) * mwords,
                                     reinterpret_cast<uint8_t*>(PW(pp.re8)), st));
     uint16_t* act = reinterpret_cast<uint16_t*>(PW(pp.act));
     uint16_t* y = reinterpret_cast<uint16_t*>(PW(pp.y));

@@ -187,9 +187,13 @@ hipError_t launch_prefill_kv(int P, int layer, int slot, const KV& kv, const uin
 // Routing of P prefill rows (P * k <= kPrefillMaxPairs, E <= kRouteMaxE), two
 // launches: top-k softmax per row (one wave each) and the (row, expert)
 // bucketing into the same outputs as launch_route (units_cap = E + P*k/16 + 1).
-// mask [E][ceil(P/32)] words (zero before and after) and e8 [P*k] bytes are scratch.
+// mask [E][ceil(P/32)] words (zero before, left set) and e8 [P*k] bytes are
+// scratch; mask_next, a second buffer of that size (the next call's mask), is
+// zeroed by the call.
 hipError_t launch_route_prefill(const float* logits, int P, int E, int k, const RouteOut& o, uint32_t* mask,
-                                uint8_t* e8, hipStream_t st);
+                                uint32_t* mask_next, uint8_t* e8, hipStream_t st);
+// Work-groups of the prefill bucketing (sharing the pairs' stores).
+constexpr int kBucketPrefillGroups = 16;
 // Dynamic LDS bytes of the prefill bucketing (row masks and their prefix
 // counts; at most 60 KiB is allowed, beside its static arrays).
 inline size_t route_prefill_lds(int P, int E, int k) {
