@@ -105,6 +105,23 @@ def test_prefill_small_model_vs_oracle(small, gpu, P):
         ctx.release(s)
 
 
+def test_prefill_three_layers_shared_bucketing(gpu):
+    """A 700-token prompt on the three-layer model: 1400 routed pairs, so the
+    bucketing runs as two work-groups sharing the pairs, and its row masks
+    alternate between two buffers over the layers (each layer's launch clears
+    the next one's).  Checked against the oracle like the shorter prompts."""
+    mw = inputs.make_model(SMALL, 12)
+    ctx = Context(SMALL, 2, 768)
+    try:
+        ctx.load_model(mw)
+        P = 700
+        tokens = [int(t) for t in inputs.rng(12, inputs.T_TOKENS, P).integers(0, SMALL.vocab, P)]
+        s, _, _ = check_prefill(ctx, gpu, mw, tokens, f"P={P}, three layers")
+        ctx.release(s)
+    finally:
+        ctx.close()
+
+
 def test_prefill_leaves_other_slots_alone(small, gpu):
     """A stream decoding next to another stream's prefill: its K/V and its next
     decode step are bit-identical to the same stream with no neighbour."""
