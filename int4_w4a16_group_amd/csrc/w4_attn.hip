@@ -678,11 +678,17 @@ __global__ void __launch_bounds__(256, 3) k_prefill_attn(PfAttnArgs a) {
           for (int j = 0; j < 8; ++j)
             if (c0 + 32 * ks + 8 * quad + j >= a.P) vop[dt][ks][j] = (_Float16)0.0f;
     }
+    // O a only where some query of the wave has a new max (a = 1 exactly
+    // otherwise, and O 1 = O)
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[dt][r] = oacc[dt][r] * alpha;
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       f4 o = oacc[dt];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = o[r] * alpha;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         o = mfma16x16x32(vop[dt][ks], phi[ks], o);
